@@ -1,0 +1,152 @@
+"""ctypes wrapper of the C fp64 oracle (test infrastructure only).
+
+Inputs are converted to contiguous float64 numpy arrays (bf16 and fp32 values
+convert exactly), the C routine runs the token-by-token recurrence, and the
+results come back as float64 arrays.  See ``kda_oracle.c`` for the definition
+and its sources.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2, OpenMP, no fast-math: C source file -> shared library."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-I", _HERE, "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle library next to its source."""
+    if force or not os.path.exists(_LIB):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    i64, dbl, ip = ctypes.c_int64, ctypes.c_double, ctypes.c_int
+    vp = ctypes.c_void_p
+    lib.kda_oracle_prefill_f64.argtypes = [
+        i64, vp, i64, i64, i64, dbl, ip,
+        vp, vp, vp, vp, vp, vp, vp, vp, ip]
+    lib.kda_oracle_prefill_f64.restype = ip
+    lib.kda_oracle_decode_step_f64.argtypes = [
+        i64, i64, i64, i64, dbl, vp, vp, vp, vp, vp, vp, vp, ip]
+    lib.kda_oracle_decode_step_f64.restype = ip
+    lib.kda_oracle_max_threads.restype = ip
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=False)
+            _lib = _bind(_LIB)
+    return _lib
+
+
+class OracleLib:
+    """The same API bound to another build of an oracle source (used by the
+    test that plants mistakes in copies of the oracle)."""
+
+    def __init__(self, path: str):
+        self._l = _bind(path)
+
+    def prefill(self, *a, **kw):
+        return prefill(*a, _lib=self._l, **kw)
+
+    def decode_step(self, *a, **kw):
+        return decode_step(*a, _lib=self._l, **kw)
+
+
+def _f64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor: exact widening on the host
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def max_threads() -> int:
+    return int(_load().kda_oracle_max_threads())
+
+
+def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
+            scale: float = 1.0, delta: bool = True, nthreads: int = 0,
+            _lib=None):
+    """Token-by-token fp64 KDA over a packed batch.
+
+    Shapes: q, k, g [T, H, dk]; v [T, H, dv]; beta [T, H];
+    initial_state [N, H, dk, dv] or None; cu_seqlens [N + 1] or None (one
+    sequence of length T).  Returns (o [T, H, dv], final_state [N, H, dk, dv]).
+    """
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int64))
+    N = cu.shape[0] - 1
+    assert k.shape == (T, H, dk) and g.shape == (T, H, dk)
+    assert v.shape == (T, H, dv) and beta.shape == (T, H)
+    assert int(cu[-1]) == T
+    S0 = None if initial_state is None else _f64(initial_state)
+    if S0 is not None:
+        assert S0.shape == (N, H, dk, dv)
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    S = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = (_lib or _load()).kda_oracle_prefill_f64(
+        N, _ptr(cu), H, dk, dv, float(scale), 1 if delta else 0,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+        _ptr(o), _ptr(S), int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_oracle_prefill_f64 failed with %d" % rc)
+    return o, S
+
+
+def decode_step(q, k, v, g, beta, state, scale: float = 1.0,
+                nthreads: int = 0, _lib=None):
+    """One token per (n, h).  Returns (o [N, H, dv], new_state) without
+    touching the caller's arrays."""
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    S = _f64(state).copy()
+    N, H, dk, dv = S.shape
+    assert q.shape == (N, H, dk) and k.shape == (N, H, dk)
+    assert v.shape == (N, H, dv) and g.shape == (N, H, dk)
+    assert beta.shape == (N, H)
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    rc = (_lib or _load()).kda_oracle_decode_step_f64(
+        N, H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+        _ptr(beta), _ptr(S), _ptr(o), int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_oracle_decode_step_f64 failed with %d" % rc)
+    return o, S

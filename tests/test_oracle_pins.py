@@ -1,0 +1,317 @@
+"""Pins of the fp64 oracle to facts the pages and the mathematics fix.
+
+Each test computes its expectation by a route that shares nothing with the
+oracle's token loop (printed values, closed forms, explicit matrix products,
+direct double sums, invariants), so that a dropped term, a wrong sign, a
+transposed operand, a decay on the wrong axis or a readout taken before the
+write fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _unit(x, axis=-1):
+    return x / np.linalg.norm(x, axis=axis, keepdims=True)
+
+
+def _rand_inputs(rng, T, H, dk, dv, g_scale=1.0):
+    q = _unit(rng.standard_normal((T, H, dk)))
+    k = _unit(rng.standard_normal((T, H, dk)))
+    v = rng.standard_normal((T, H, dv))
+    g = -g_scale * rng.random((T, H, dk))
+    beta = rng.random((T, H))
+    return q, k, v, g, beta
+
+
+# --------------------------------------------------------------------------
+# P1: worked example -- Hybrid Attention, "KDA: don't write the same
+# information twice": prediction 2, target 6, beta 0.5 -> 4 along the key.
+# --------------------------------------------------------------------------
+def test_p1_worked_delta_example(oracle_mod):
+    ex = json.load(open(os.path.join(GOLDEN, "worked_delta_example.json")))
+    rng = np.random.default_rng(11)
+    dk = 6
+    kk = _unit(rng.standard_normal(dk))
+    S0 = (ex["prediction"] * kk)[:, None]          # S0^T k = prediction
+    q = kk[None, None, :]
+    k = kk[None, None, :]
+    v = np.array([[[ex["target"]]]])
+    g = np.zeros((1, 1, dk))
+    beta = np.array([[ex["beta"]]])
+    o, S = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0[None, None])
+    assert o[0, 0, 0] == pytest.approx(ex["result"], abs=1e-14)
+    assert float(S[0, 0, :, 0] @ kk) == pytest.approx(ex["result"], abs=1e-14)
+    # the component orthogonal to k is untouched by the write
+    w = _unit(rng.standard_normal(dk) - (rng.standard_normal(dk) @ kk) * kk)
+    w = _unit(w - (w @ kk) * kk)
+    assert abs(float(S[0, 0, :, 0] @ w)) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# P2: beta = 1 with a unit key and no decay stores v exactly along k
+# (neuralmasteryai.com section 3); the readout uses the state after the
+# write (kimi-k3-course lesson 2), so q = k reads back v.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dk,dv", [(4, 4), (5, 3), (16, 16)])
+def test_p2_exact_recall_after_write(oracle_mod, dk, dv):
+    rng = np.random.default_rng(dk * 10 + dv)
+    T, H = 9, 2
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    # last token: beta = 1, g = 0, q = k
+    beta[-1] = 1.0
+    g[-1] = 0.0
+    q[-1] = k[-1]
+    o, S = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0)
+    np.testing.assert_allclose(o[-1], v[-1], atol=1e-13)
+    for h in range(H):
+        np.testing.assert_allclose(S[0, h].T @ k[-1, h], v[-1, h], atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P3: with the delta term removed, no decay and beta = 1 the recurrence is
+# linear attention, o_t = sum_{i<=t} (q_t . k_i) v_i (neuralmasteryai.com
+# section 2, the regrouped sum).  Computed here as a direct double sum.
+# --------------------------------------------------------------------------
+def test_p3_linear_attention_double_sum(oracle_mod):
+    rng = np.random.default_rng(3)
+    T, H, dk, dv = 12, 3, 5, 7
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    g = np.zeros((T, H, dk))
+    beta = np.ones((T, H))
+    o, S = oracle_mod.prefill(q, k, v, g, beta, delta=False)
+    ref = np.zeros_like(o)
+    for t in range(T):
+        for h in range(H):
+            for i in range(t + 1):
+                ref[t, h] += float(q[t, h] @ k[i, h]) * v[i, h]
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    for h in range(H):
+        np.testing.assert_allclose(S[0, h], sum(np.outer(k[i, h], v[i, h]) for i in range(T)),
+                                   atol=1e-12)
+
+
+# P3b: gated linear write (delta removed, decay and beta kept) has the closed
+# form S_t = Diag(e^{G_t}) S0 + sum_{i<=t} Diag(e^{G_t - G_i}) beta_i k_i v_i^T
+# with G the inclusive per-channel cumulative log-decay.
+def test_p3b_gated_linear_closed_form(oracle_mod):
+    rng = np.random.default_rng(4)
+    T, H, dk, dv = 10, 2, 6, 3
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, S = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0, delta=False,
+                              scale=0.7)
+    G = np.cumsum(g, axis=0)
+    for h in range(H):
+        for t in range(T):
+            St = np.exp(G[t, h])[:, None] * S0[0, h]
+            for i in range(t + 1):
+                St = St + np.exp(G[t, h] - G[i, h])[:, None] * beta[i, h] * np.outer(k[i, h], v[i, h])
+            np.testing.assert_allclose(o[t, h], 0.7 * St.T @ q[t, h], atol=1e-12)
+        np.testing.assert_allclose(S[0, h], St, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P4: pure decay.  beta = 0 removes every write, so S_T = Diag(e^{sum g}) S0
+# and o_t = S0^T (e^{G_t} * q_t): the decay scales key-channel ROWS
+# (Understanding Kimi K3's attention, symbol table; neuralmasteryai.com
+# section 5).  dk != dv makes a decay on the wrong axis fail to match.
+# --------------------------------------------------------------------------
+def test_p4_pure_decay_rows(oracle_mod):
+    rng = np.random.default_rng(5)
+    T, H, dk, dv = 8, 2, 6, 4
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv, g_scale=2.0)
+    beta[:] = 0.0
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, S = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0)
+    G = np.cumsum(g, axis=0)
+    for h in range(H):
+        np.testing.assert_allclose(S[0, h], np.exp(G[-1, h])[:, None] * S0[0, h], rtol=1e-14, atol=0)
+        for t in range(T):
+            np.testing.assert_allclose(o[t, h], S0[0, h].T @ (np.exp(G[t, h]) * q[t, h]),
+                                       rtol=1e-13, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# P5: the product form (I - b k k^T) Diag(a) S + b k v^T and the gradient-
+# descent form D S - b grad L(D S), grad L(X) = k (X^T k - v)^T
+# (Understanding Kimi K3's attention), evaluated with explicit matrices.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("form", ["product", "gradient"])
+def test_p5_equivalent_forms(oracle_mod, form):
+    rng = np.random.default_rng(6)
+    T, H, dk, dv = 11, 2, 5, 4
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, S = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0, scale=1.3)
+    for h in range(H):
+        St = S0[0, h].copy()
+        for t in range(T):
+            kk, vv, b = k[t, h], v[t, h], beta[t, h]
+            D = np.diag(np.exp(g[t, h]))
+            if form == "product":
+                St = (np.eye(dk) - b * np.outer(kk, kk)) @ D @ St + b * np.outer(kk, vv)
+            else:
+                X = D @ St
+                St = X - b * np.outer(kk, X.T @ kk - vv)
+            np.testing.assert_allclose(o[t, h], 1.3 * St.T @ q[t, h], atol=1e-12)
+        np.testing.assert_allclose(S[0, h], St, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P6: brute force on tiny inputs, from the unrolled sum
+#   S_t = Phi_t..Phi_1 S0 + sum_s Phi_t..Phi_{s+1} b_s k_s v_s^T,
+#   Phi_t = (I - b_t k_t k_t^T) Diag(a_t),
+# over a packed batch whose sequences restart from their own S0.
+# --------------------------------------------------------------------------
+def test_p6_brute_force_unrolled_packed(oracle_mod):
+    rng = np.random.default_rng(7)
+    lens = [3, 0, 5, 1, 8]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, H, dk, dv = int(cu[-1]), 2, 4, 3
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv, g_scale=1.5)
+    S0 = rng.standard_normal((len(lens), H, dk, dv))
+    o, S = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0, cu_seqlens=cu)
+    for n in range(len(lens)):
+        for h in range(H):
+            a, b_ = int(cu[n]), int(cu[n + 1])
+            Phi = [(np.eye(dk) - beta[t, h] * np.outer(k[t, h], k[t, h])) @ np.diag(np.exp(g[t, h]))
+                   for t in range(a, b_)]
+            for t in range(a, b_):
+                # Phi_t ... Phi_a applied to S0, then each write carried forward
+                prod_all = np.eye(dk)
+                for s in range(a, t + 1):
+                    prod_all = Phi[s - a] @ prod_all
+                St = prod_all @ S0[n, h]
+                for s in range(a, t + 1):
+                    P = np.eye(dk)
+                    for r in range(s + 1, t + 1):
+                        P = Phi[r - a] @ P
+                    St = St + P @ (beta[s, h] * np.outer(k[s, h], v[s, h]))
+                np.testing.assert_allclose(o[t, h], St.T @ q[t, h], atol=1e-13)
+            if b_ == a:
+                np.testing.assert_array_equal(S[n, h], S0[n, h])
+            else:
+                np.testing.assert_allclose(S[n, h], St, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P7: the toy memory demo of neuralmasteryai.com section 3 (d = 64, 20
+# pairs, then key 0 rewritten): printed relative errors for linear attention
+# and for the delta rule.  Inputs are drawn in the order the page describes.
+# --------------------------------------------------------------------------
+def test_p7_toy_demo_printed_errors(oracle_mod):
+    ex = json.load(open(os.path.join(GOLDEN, "toy_delta_vs_linear.json")))
+    rng = np.random.default_rng(ex["seed"])
+    d, n = ex["d"], ex["pairs"]
+    keys = []
+    for _ in range(n):
+        x = rng.standard_normal(d)
+        keys.append(x / np.linalg.norm(x))
+    vals = [rng.standard_normal(d) for _ in range(n)]
+    new_val = rng.standard_normal(d)
+    rk, pk = ex["rewrite_key"], ex["probe_key"]
+    K = np.array(keys + [keys[rk]])[:, None, :]
+    V = np.array(vals + [new_val])[:, None, :]
+    T = K.shape[0]
+    g = np.zeros((T, 1, d))
+    beta = np.ones((T, 1))
+
+    def rel(S, key, target):
+        return np.linalg.norm(S.T @ key - target) / np.linalg.norm(target)
+
+    for name, delta in (("linear_attention", False), ("delta_rule", True)):
+        _, S = oracle_mod.prefill(K, K, V, g, beta, delta=delta)
+        S = S[0, 0]
+        got = (round(rel(S, keys[rk], new_val), ex["decimals"]),
+               round(rel(S, keys[pk], vals[pk]), ex["decimals"]))
+        want = (ex[name]["rewritten_key_error"], ex[name]["probe_key_error"])
+        assert got == pytest.approx(want, abs=1e-9), name
+
+
+# --------------------------------------------------------------------------
+# P8: with unit keys, beta in [0,1], g <= 0 and v = 0 every step is a
+# contraction, so ||S_t||_F never grows (the erase factor has eigenvalues 1
+# and 1 - beta; the fade has entries in (0, 1]).
+# --------------------------------------------------------------------------
+def test_p8_contraction_invariant(oracle_mod):
+    rng = np.random.default_rng(8)
+    N, H, dk, dv = 3, 4, 8, 6
+    S = rng.standard_normal((N, H, dk, dv))
+    prev = np.linalg.norm(S, axis=(2, 3))
+    for _ in range(20):
+        q = _unit(rng.standard_normal((N, H, dk)))
+        k = _unit(rng.standard_normal((N, H, dk)))
+        v = np.zeros((N, H, dv))
+        g = -rng.random((N, H, dk))
+        beta = rng.random((N, H))
+        _, S = oracle_mod.decode_step(q, k, v, g, beta, S)
+        cur = np.linalg.norm(S, axis=(2, 3))
+        assert np.all(cur <= prev * (1 + 1e-15))
+        prev = cur
+
+
+# --------------------------------------------------------------------------
+# P9: the update is affine in (S, v), so outputs and states superpose.
+# --------------------------------------------------------------------------
+def test_p9_superposition(oracle_mod):
+    rng = np.random.default_rng(9)
+    T, H, dk, dv = 14, 2, 5, 6
+    q, k, v1, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    v2 = rng.standard_normal((T, H, dv))
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o12, S12 = oracle_mod.prefill(q, k, v1 + v2, g, beta, initial_state=S0)
+    o1, S1 = oracle_mod.prefill(q, k, v1, g, beta, initial_state=S0)
+    o2, S2 = oracle_mod.prefill(q, k, v2, g, beta)
+    np.testing.assert_allclose(o12, o1 + o2, atol=1e-12)
+    np.testing.assert_allclose(S12, S1 + S2, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# P10: entry points agree -- decode step == prefill of one token; a split
+# prefill resumed from the carried state == the whole prefill (the prefix
+# reuse of the Inside Kimi K3 page needs exactly this); packing == separate.
+# --------------------------------------------------------------------------
+def test_p10_decode_equals_prefill_one_token(oracle_mod):
+    rng = np.random.default_rng(10)
+    N, H, dk, dv = 3, 2, 5, 4
+    q, k, v, g, beta = _rand_inputs(rng, N, H, dk, dv)   # one token per sequence
+    S0 = rng.standard_normal((N, H, dk, dv))
+    od, Sd = oracle_mod.decode_step(q, k, v, g, beta, S0, scale=0.5)
+    cu = np.arange(N + 1, dtype=np.int64)
+    op, Sp = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0, cu_seqlens=cu, scale=0.5)
+    np.testing.assert_array_equal(od, op)
+    np.testing.assert_array_equal(Sd, Sp)
+
+
+def test_p10_split_resume_and_packing(oracle_mod):
+    rng = np.random.default_rng(12)
+    T1, T2, H, dk, dv = 7, 9, 2, 4, 5
+    q, k, v, g, beta = _rand_inputs(rng, T1 + T2, H, dk, dv)
+    S0 = rng.standard_normal((1, H, dk, dv))
+    o, S = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0)
+    oa, Sa = oracle_mod.prefill(q[:T1], k[:T1], v[:T1], g[:T1], beta[:T1], initial_state=S0)
+    ob, Sb = oracle_mod.prefill(q[T1:], k[T1:], v[T1:], g[T1:], beta[T1:], initial_state=Sa)
+    np.testing.assert_allclose(np.concatenate([oa, ob]), o, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(Sb, S, rtol=0, atol=1e-15)
+    # packed = separate
+    cu = np.array([0, T1, T1 + T2], dtype=np.int64)
+    S0p = np.concatenate([S0, Sa])
+    op, Sp = oracle_mod.prefill(q, k, v, g, beta, initial_state=S0p, cu_seqlens=cu)
+    np.testing.assert_array_equal(op[:T1], oa)
+    np.testing.assert_array_equal(op[T1:], oracle_mod.prefill(
+        q[T1:], k[T1:], v[T1:], g[T1:], beta[T1:], initial_state=Sa)[0])
+    np.testing.assert_array_equal(Sp[1], Sb[0])
+
+
+def test_oracle_rejects_bad_cu(oracle_mod):
+    q = np.zeros((4, 1, 2)); v = np.zeros((4, 1, 2)); beta = np.zeros((4, 1))
+    with pytest.raises(ValueError):
+        oracle_mod.prefill(q, q, v, q, beta, cu_seqlens=np.array([0, 3, 2, 4]))
