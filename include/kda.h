@@ -1,0 +1,165 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) core.
+ *
+ * The operation (per sequence n, per head h, tokens t in order):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = scale * S_t^T q_t
+ *
+ * with S a d_k x d_v fp32 state whose rows are key channels, exp(g_t) a
+ * per-key-channel retention, beta_t a scalar write strength, and the readout
+ * taken after the token's own write.  Sources: "Understanding Kimi K3's
+ * attention" (dhruvpendharkar.github.io) -- symbol table, state-update and
+ * readout equations, and the g_min = -5 bound on the log-decay; "KDA: the
+ * memory matrix" (kimi-k3-course.pages.dev, lesson 2) -- the three per-token
+ * operations and the read-after-write rule; "Inside Kimi K3" (flozi.net),
+ * section "Sequence mixing" -- chunkwise prefill with state passed between
+ * chunks, a causal intra-chunk matrix that includes its diagonal, 16-token
+ * tiles whose cumulative log-decay stays above -80, and KDA state restored at
+ * a token boundary for prefix reuse.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous, and
+ *     must be 16-byte aligned.  The caller owns every buffer; the library
+ *     allocates no device memory and keeps no mutable global state.
+ *   - Element offsets are 64-bit; token counts up to 2^31 - 1 per call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous on it; a KDA_OK return means the work was launched.
+ *   - Every argument is validated on the host before any HIP call, so an
+ *     error return has touched no device memory.  Errors are returned, never
+ *     printed or raised; nothing aborts.
+ *   - Device-side preconditions, documented and not checked: g in [-5, 0]
+ *     (the chunked kernels rely on a 16-token cumulative log-decay >= -80),
+ *     beta in [0, 1], finite inputs, and cu_seqlens non-decreasing from 0 to
+ *     total_tokens.  A violation changes the numbers, never the memory the
+ *     kernels touch: sequence bounds read from cu_seqlens are clamped to
+ *     [0, total_tokens] on the device.
+ *   - qkv_dtype selects the dtype of q, k, v and o: KDA_DTYPE_BF16 (bf16
+ *     storage, bf16 MFMA products with fp32 accumulation, fp32 state) or
+ *     KDA_DTYPE_F32 (fp32 throughout, fp32 MFMA).  g, beta and the state are
+ *     always fp32.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_DTYPE_F32 = 0,
+    KDA_DTYPE_BF16 = 1
+} kda_dtype;
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                       */
+    KDA_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes                     */
+    KDA_ERR_UNSUPPORTED = 3,  /* valid but not built: (dtype, d_k, d_v, chunk)     */
+    KDA_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned                  */
+    KDA_ERR_WORKSPACE = 5,    /* workspace smaller than kda_prefill_workspace_bytes */
+    KDA_ERR_HIP = 6           /* the HIP runtime reported an error at launch       */
+} kda_status;
+
+/* KDA_ABI_VERSION of the built library. */
+int32_t kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *kda_status_string(int32_t status);
+
+/* 1 if (qkv_dtype, d_k, d_v, chunk_size) has a built prefill kernel, else 0.
+ * chunk_size 0 asks for the library default (64 for bf16, 16 for fp32). */
+int32_t kda_prefill_supported(int32_t qkv_dtype, int32_t d_k, int32_t d_v,
+                              int32_t chunk_size);
+
+/* 1 if (qkv_dtype, d_k, d_v) has a built decode kernel, else 0. */
+int32_t kda_decode_supported(int32_t qkv_dtype, int32_t d_k, int32_t d_v);
+
+/*
+ * Bytes of device workspace kda_prefill needs for these sizes (0 = none;
+ * then workspace may be NULL).  Returns 0 as well for unsupported or invalid
+ * sizes, which kda_prefill itself rejects.
+ */
+size_t kda_prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens,
+                                   int32_t num_heads, int32_t d_k, int32_t d_v,
+                                   int32_t qkv_dtype, int32_t chunk_size);
+
+/*
+ * kda_prefill -- the whole recurrence over a packed batch of sequences,
+ * computed chunkwise: inside a chunk the tokens are processed in parallel
+ * (cumulative log-decay per chunk, the causal intra-chunk matrix including
+ * its diagonal, and the triangular solve of I + strictly-lower A), and the
+ * state is passed from chunk to chunk ("Inside Kimi K3", flozi.net, section
+ * "Sequence mixing"; "Hybrid Attention", kimi-k3.adriaflores.com, section
+ * "But isn't a recurrent update sequential?").  The result equals the
+ * token-by-token recurrence up to rounding.
+ *
+ *   num_seqs      N >= 0 sequences.
+ *   total_tokens  T_total >= 0 tokens over all sequences.
+ *   num_heads     H >= 1;  d_k, d_v: head dims (see kda_prefill_supported).
+ *   qkv_dtype     kda_dtype of q, k, v and o.
+ *   chunk_size    tokens per chunk (16, 32 or 64), or 0 for the default.
+ *   scale         readout scale; 1.0f gives o_t = S_t^T q_t exactly.
+ *   q, k          [T_total, H, d_k]  qkv_dtype
+ *   v             [T_total, H, d_v]  qkv_dtype
+ *   g             [T_total, H, d_k]  fp32 log-decay (alpha = exp(g))
+ *   beta          [T_total, H]       fp32
+ *   initial_state [N, H, d_k, d_v]   fp32, or NULL for zeros
+ *   cu_seqlens    [N + 1] int32 device array of sequence offsets (cu[0] = 0,
+ *                 cu[N] = T_total), or NULL for N equal-length sequences of
+ *                 T_total / N tokens (T_total must then divide by N).
+ *                 Empty sequences are allowed: their final state is their
+ *                 initial state and they produce no outputs.
+ *   o             [T_total, H, d_v]  qkv_dtype, written.  Must not overlap
+ *                 an input; o equal to an input pointer is rejected with
+ *                 KDA_ERR_BAD_SHAPE (partial overlap is not detected).
+ *   final_state   [N, H, d_k, d_v]   fp32, written, or NULL to skip.  May be
+ *                 the same pointer as initial_state (in-place carry).
+ *   workspace     device buffer of workspace_bytes (may be NULL when the
+ *                 workspace query returns 0).
+ *
+ * Errors: KDA_ERR_NULL_POINTER, KDA_ERR_BAD_SHAPE, KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_MISALIGNED, KDA_ERR_WORKSPACE, KDA_ERR_HIP.  N = 0 or T_total = 0
+ * with N > 0 is valid: final_state receives the initial state (or zeros).
+ */
+kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens,
+                       int32_t num_heads, int32_t d_k, int32_t d_v,
+                       int32_t qkv_dtype, int32_t chunk_size, float scale,
+                       const void *q, const void *k, const void *v,
+                       const float *g, const float *beta,
+                       const float *initial_state, const int32_t *cu_seqlens,
+                       void *o, float *final_state,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_decode_step -- one new token per sequence, state updated in place
+ * (serving needs a dedicated decode kernel: "Kimi K3.1 and the Road From
+ * Softmax Attention to KDA", neuralmasteryai.com, section 8; constant cost
+ * per token: "KDA: the memory matrix", lesson 2).  Per (n, h):
+ *   S <- Diag(exp g) S;  a = S^T k;  S <- S + beta k (v - a)^T;  o = scale S^T q
+ * streaming each fp32 state through HBM once (read once, written once).
+ *
+ *   num_seqs  N >= 0;  num_heads H >= 1;  d_k, d_v: see kda_decode_supported.
+ *   q, k      [N, H, d_k] qkv_dtype;  v [N, H, d_v] qkv_dtype
+ *   g         [N, H, d_k] fp32;       beta [N, H] fp32
+ *   state     [N, H, d_k, d_v] fp32, read and overwritten in place
+ *   o         [N, H, d_v] qkv_dtype, written; must not overlap state or an
+ *             input (equal pointers are rejected with KDA_ERR_BAD_SHAPE)
+ *
+ * Errors as for kda_prefill.  N = 0 is a valid no-op.
+ */
+kda_status kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t d_k,
+                           int32_t d_v, int32_t qkv_dtype, float scale,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *state,
+                           void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

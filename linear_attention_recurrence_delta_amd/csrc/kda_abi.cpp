@@ -1,0 +1,180 @@
+// kda_abi.cpp -- the extern "C" boundary declared in include/kda.h.
+//
+// Every argument is validated here, on the host, before the first HIP call;
+// an error return has launched nothing and touched no device memory.  Then
+// the matching kernel variant is picked and launched on the caller's stream.
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+using kda::PrefillVariant;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int default_chunk(int32_t dtype) { return dtype == KDA_DTYPE_BF16 ? 64 : 16; }
+
+int resolve_chunk(int32_t dtype, int32_t chunk) { return chunk == 0 ? default_chunk(dtype) : chunk; }
+
+const PrefillVariant* variants(int32_t dtype, int* count) {
+    if (dtype == KDA_DTYPE_BF16) return kda::prefill_variants_bf16(count);
+    if (dtype == KDA_DTYPE_F32) return kda::prefill_variants_f32(count);
+    *count = 0;
+    return nullptr;
+}
+
+// Column waves per workgroup.  Fewer waves per (sequence, head) means more
+// workgroups (d_v slabs) and fills more compute units when there are few
+// (sequence, head) recurrences; more waves share the d_k-side work of a head
+// among more value columns.  KDA_PREFILL_WAVES overrides the choice.
+const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units) {
+    int count = 0;
+    const PrefillVariant* tab = variants(dtype, &count);
+    int want = 0;
+    if (const char* env = getenv("KDA_PREFILL_WAVES")) want = atoi(env);
+    if (want <= 0) {
+        // Aim for at least ~2 workgroups per compute unit (256 on MI355X).
+        const int64_t target = 512;
+        want = 8;
+        while (want > 1 && units * (D / (16 * want)) < target) want /= 2;
+    }
+    // the largest built wave count not above the wanted one, else the smallest built
+    const PrefillVariant* best = nullptr;
+    const PrefillVariant* smallest = nullptr;
+    for (int i = 0; i < count; ++i) {
+        const PrefillVariant& v = tab[i];
+        if (v.D != D || v.C != C) continue;
+        if (!smallest || v.nwc < smallest->nwc) smallest = &v;
+        if (v.nwc <= want && (!best || v.nwc > best->nwc)) best = &v;
+    }
+    return best ? best : smallest;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int32_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK: success";
+        case KDA_ERR_NULL_POINTER: return "KDA_ERR_NULL_POINTER: a required pointer is NULL";
+        case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: negative or inconsistent sizes";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: no kernel built for this dtype / head dim / chunk size";
+        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_prefill_workspace_bytes";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+        default: return "unknown kda_status";
+    }
+}
+
+int32_t kda_prefill_supported(int32_t dtype, int32_t d_k, int32_t d_v, int32_t chunk_size) {
+    if (d_k != d_v) return 0;
+    int count = 0;
+    const PrefillVariant* tab = variants(dtype, &count);
+    const int C = resolve_chunk(dtype, chunk_size);
+    for (int i = 0; i < count; ++i)
+        if (tab[i].D == d_k && tab[i].C == C) return 1;
+    return 0;
+}
+
+int32_t kda_decode_supported(int32_t dtype, int32_t d_k, int32_t d_v) {
+    if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return 0;
+    return d_k == d_v && kda::decode_d_supported(d_k) ? 1 : 0;
+}
+
+size_t kda_prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                                   int32_t d_v, int32_t dtype, int32_t chunk_size) {
+    (void)num_seqs;
+    (void)total_tokens;
+    (void)num_heads;
+    (void)d_k;
+    (void)d_v;
+    (void)dtype;
+    (void)chunk_size;
+    return 0;  // the fused chunk kernel keeps everything on chip
+}
+
+kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v,
+                       int32_t dtype, int32_t chunk_size, float scale, const void* q, const void* k,
+                       const void* v, const float* g, const float* beta, const float* initial_state,
+                       const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
+    if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 && total_tokens > 0) return KDA_ERR_BAD_SHAPE;
+    if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
+    if (!kda_prefill_supported(dtype, d_k, d_v, chunk_size)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, g, beta, initial_state, cu_seqlens, o, final_state, workspace};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+    if (o && (o == q || o == k || o == v || o == g || o == beta)) return KDA_ERR_BAD_SHAPE;
+    const size_t need = kda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+    if (num_seqs == 0) return KDA_OK;
+    if (total_tokens == 0 && !final_state) return KDA_OK;
+
+    const int C = resolve_chunk(dtype, chunk_size);
+    const int64_t units = (int64_t)num_seqs * num_heads;
+    const PrefillVariant* var = pick_variant(dtype, d_k, C, units);
+    if (!var) return KDA_ERR_UNSUPPORTED;
+    const int nslab = d_v / (16 * var->nwc);
+    if (units * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+
+    kda::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.S0 = initial_state;
+    p.cu = cu_seqlens;
+    p.o = o;
+    p.Sout = final_state;
+    p.T_total = total_tokens;
+    p.N = num_seqs;
+    p.H = num_heads;
+    p.seq_len = cu_seqlens ? 0 : (int32_t)(total_tokens / num_seqs);
+    p.nslab = nslab;
+    p.scale = scale;
+    const hipError_t err = var->launch(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v, int32_t dtype,
+                           float scale, const void* q, const void* k, const void* v, const float* g,
+                           const float* beta, float* state, void* o, void* stream) {
+    if (num_seqs < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
+    if (!kda_decode_supported(dtype, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)num_seqs * num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs > 0 && (!q || !k || !v || !g || !beta || !state || !o)) return KDA_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+    if (o && (o == q || o == k || o == v || o == g || o == beta || o == state)) return KDA_ERR_BAD_SHAPE;
+    if (num_seqs == 0) return KDA_OK;
+
+    kda::DecodeParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.S = state;
+    p.o = o;
+    p.units = (int64_t)num_seqs * num_heads;
+    p.scale = scale;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = dtype == KDA_DTYPE_BF16 ? kda::launch_decode_bf16(d_k, p, s)
+                                                   : kda::launch_decode_f32(d_k, p, s);
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

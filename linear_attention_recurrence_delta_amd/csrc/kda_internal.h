@@ -1,0 +1,60 @@
+// kda_internal.h -- host-side declarations shared by the C-ABI layer and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Everything a prefill launch needs; pointers are device pointers.
+struct PrefillParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* S0;        // [N,H,D,D] or nullptr (zeros)
+    const int32_t* cu;      // [N+1] or nullptr (dense)
+    void* o;
+    float* Sout;            // [N,H,D,D] or nullptr
+    int64_t T_total;
+    int32_t N;
+    int32_t H;
+    int32_t seq_len;        // dense sequences: tokens per sequence
+    int32_t nslab;          // d_v column slabs per (sequence, head)
+    float scale;
+};
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* S;
+    void* o;
+    int64_t units;          // N * H
+    float scale;
+};
+
+// One entry per built prefill kernel.
+struct PrefillVariant {
+    int dtype;              // kda_dtype
+    int D;                  // d_k = d_v
+    int C;                  // chunk size
+    int nwc;                // column waves per workgroup (16 d_v columns each)
+    size_t lds_bytes;
+    hipError_t (*launch)(const PrefillParams&, hipStream_t);
+};
+
+// Tables defined in the kernel translation units.
+const PrefillVariant* prefill_variants_bf16(int* count);
+const PrefillVariant* prefill_variants_f32(int* count);
+
+// Decode launchers; return hipErrorInvalidValue for an unsupported D.
+hipError_t launch_decode_bf16(int D, const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_f32(int D, const DecodeParams& p, hipStream_t s);
+bool decode_d_supported(int D);
+
+}  // namespace kda

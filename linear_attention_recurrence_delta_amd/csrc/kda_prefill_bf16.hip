@@ -1,0 +1,24 @@
+// kda_prefill_bf16.hip -- bf16 q/k/v instantiations of the chunked prefill
+// (bf16 MFMA products, fp32 accumulation, fp32 state).
+#include "kda_prefill_impl.h"
+
+namespace kda {
+
+static const PrefillVariant kBf16Variants[] = {
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 8),
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 4),
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 2),
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 2, 8),
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 2, 4),
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 2, 2),
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 1, 8),
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 1, 4),
+    KDA_PREFILL_VARIANT(1, bf16_t, 128, 1, 2),
+};
+
+const PrefillVariant* prefill_variants_bf16(int* count) {
+    *count = static_cast<int>(sizeof(kBf16Variants) / sizeof(kBf16Variants[0]));
+    return kBf16Variants;
+}
+
+}  // namespace kda

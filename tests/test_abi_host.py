@@ -1,0 +1,155 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/kda.h declares, and
+reject bad arguments on the host before any HIP call.  The fake device
+pointers used here are never dereferenced: every call below returns from
+validation (or is a no-op) before anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULLP, BAD, UNSUP, MISAL, WS, HIP = 0, 1, 2, 3, 4, 5, 6
+BF16, F32 = 1, 0
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_attention_recurrence_delta_amd._lib import lib as _lib
+    return _lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for must in ("kda_prefill", "kda_decode_step", "kda_prefill_workspace_bytes",
+                 "kda_status_string", "kda_abi_version"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in header_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_declares_every_header_function():
+    from linear_attention_recurrence_delta_amd._lib import SIGNATURES
+    assert sorted(SIGNATURES) == header_functions()
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for s in range(7):
+        txt = lib.kda_status_string(s).decode()
+        assert txt.startswith("KDA_")
+    assert "unknown" in lib.kda_status_string(99).decode()
+
+
+def test_supported_sets(lib):
+    for c in (0, 16, 32, 64):
+        assert lib.kda_prefill_supported(BF16, 128, 128, c) == 1
+    for d in (16, 32, 64, 128):
+        assert lib.kda_prefill_supported(F32, d, d, 16) == 1
+        assert lib.kda_decode_supported(F32, d, d) == 1
+        assert lib.kda_decode_supported(BF16, d, d) == 1
+    assert lib.kda_prefill_supported(BF16, 128, 64, 64) == 0
+    assert lib.kda_prefill_supported(BF16, 100, 100, 64) == 0
+    assert lib.kda_prefill_supported(BF16, 128, 128, 48) == 0
+    assert lib.kda_prefill_supported(7, 128, 128, 64) == 0
+    assert lib.kda_decode_supported(BF16, 128, 64) == 0
+    assert lib.kda_decode_supported(3, 128, 128) == 0
+
+
+def _prefill(lib, N=1, T=64, H=2, dk=128, dv=128, dt=BF16, C=64, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+             beta=FAKE, S0=None, cu=None, o=FAKE + 0x100000, fs=None, ws=None, wsb=0):
+    return lib.kda_prefill(N, T, H, dk, dv, dt, C, 1.0, q, k, v, g, beta, S0, cu, o, fs, ws, wsb, None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, N=-1) == BAD
+    assert _prefill(lib, T=-5) == BAD
+    assert _prefill(lib, H=0) == BAD
+    assert _prefill(lib, N=0, T=10) == BAD            # tokens without sequences
+    assert _prefill(lib, N=3, T=64) == BAD            # dense length must divide
+    assert _prefill(lib, dk=100, dv=100) == UNSUP
+    assert _prefill(lib, dk=128, dv=64) == UNSUP
+    assert _prefill(lib, C=48) == UNSUP
+    assert _prefill(lib, dt=5) == UNSUP
+    assert _prefill(lib, T=1 << 31) == UNSUP
+    assert _prefill(lib, q=None) == NULLP
+    assert _prefill(lib, beta=None) == NULLP
+    assert _prefill(lib, o=None) == NULLP
+    assert _prefill(lib, k=FAKE + 8) == MISAL
+    assert _prefill(lib, S0=FAKE + 4) == MISAL
+    assert _prefill(lib, cu=FAKE + 2, N=2) == MISAL
+    assert _prefill(lib, o=FAKE) == BAD               # o == q
+    # no-ops that launch nothing
+    assert _prefill(lib, N=0, T=0) == OK
+    assert _prefill(lib, N=0, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+    assert _prefill(lib, N=2, T=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+
+
+def test_workspace_query(lib):
+    assert lib.kda_prefill_workspace_bytes(1, 4096, 8, 128, 128, BF16, 64) == 0
+
+
+def _decode(lib, N=4, H=2, d=128, dt=BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
+            S=FAKE + 0x200000, o=FAKE + 0x100000):
+    return lib.kda_decode_step(N, H, d, d, dt, 1.0, q, k, v, g, beta, S, o, None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, N=-1) == BAD
+    assert _decode(lib, H=0) == BAD
+    assert _decode(lib, d=100) == UNSUP
+    assert _decode(lib, dt=9) == UNSUP
+    assert _decode(lib, S=None) == NULLP
+    assert _decode(lib, q=None) == NULLP
+    assert _decode(lib, v=FAKE + 4) == MISAL
+    assert _decode(lib, o=FAKE + 0x200000) == BAD     # o == state
+    assert _decode(lib, N=0, q=None, k=None, v=None, g=None, beta=None, S=None, o=None) == OK
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    from linear_attention_recurrence_delta_amd import kda_prefill, kda_decode_step
+    x = torch.zeros(4, 1, 16)
+    b = torch.zeros(4, 1)
+    with pytest.raises(ValueError):
+        kda_prefill(x, x, x, x, b)
+    with pytest.raises(ValueError):
+        kda_decode_step(x, x, x, x, b, torch.zeros(4, 1, 16, 16))
+
+
+def test_varlen_recipe():
+    from linear_attention_recurrence_delta_amd.synth import varlen_lengths
+    L = varlen_lengths()
+    assert len(L) == 16 and sum(L) == 32768
+    assert min(L) >= 256 and max(L) <= 8192
+    assert any(x % 64 for x in L)  # ragged tails are exercised
+    assert varlen_lengths() == L   # seeded
+
+
+def test_library_has_no_oracle_dependency():
+    """The product library must not link or name the oracle."""
+    from linear_attention_recurrence_delta_amd._lib import LIB_PATH
+    blob = open(LIB_PATH, "rb").read()
+    assert b"kda_oracle" not in blob
+    src_dir = os.path.join(ROOT, "linear_attention_recurrence_delta_amd")
+    for dirpath, _, files in os.walk(src_dir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "kda_oracle" not in txt, f

@@ -1,0 +1,226 @@
+"""GPU parity of kda_prefill against the fp64 oracle, through the C ABI.
+
+Element-by-element comparison on the same seeded inputs, at sizes the oracle
+finishes in seconds while still spanning several chunks and a ragged tail,
+plus the special cases the method has.  Tolerances (max |d| / max |ref|):
+1e-4 for fp32 q/k/v, 2e-2 for bf16 q/k/v (fp32 state).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_common import TOL, f64, oracle_units, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import linear_attention_recurrence_delta_amd as m
+    return m
+
+
+def _inputs(T, H, d, dtype, seed, g_mode="k3", N=None, lengths=None, init_std=None):
+    from linear_attention_recurrence_delta_amd import synth
+    q, k, v, g, beta, gen = synth.token_inputs(T, H, d, d, dtype, seed, DEV, g_mode)
+    if lengths is None:
+        lengths = [T]
+    N = len(lengths)
+    cu_list = [0] + list(np.cumsum(lengths))
+    S0 = synth.initial_state(N, H, d, d, init_std, gen, DEV) if init_std else None
+    return dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, lengths=lengths, cu_list=[int(x) for x in cu_list])
+
+
+def _check_all(kda, oracle, inp, chunk, scale=1.0, tol=None, label=""):
+    d = inp["q"].shape[-1]
+    H = inp["q"].shape[1]
+    dtype = inp["q"].dtype
+    N = len(inp["lengths"])
+    cu = torch.tensor(inp["cu_list"], dtype=torch.int32, device=DEV) if N > 1 else None
+    say("CASE", label, "T=%d N=%d H=%d d=%d dtype=%s chunk=%d" % (inp["q"].shape[0], N, H, d, dtype, chunk))
+    o, S = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], cu,
+                           chunk_size=chunk, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle_units(oracle_mod_global, inp, [(n, h) for n in range(N) for h in range(H)],
+                       inp["cu_list"], scale=scale)
+    o_np, S_np = f64(o), f64(S)
+    tol = tol or TOL[dtype]
+    worst_o, worst_s = 0.0, 0.0
+    o_ref = np.zeros_like(o_np)
+    for (n, h), (ro, rs) in ref.items():
+        a, b = inp["cu_list"][n], inp["cu_list"][n + 1]
+        o_ref[a:b, h] = ro[:, 0]
+        worst_s = max(worst_s, rel_err(S_np[n, h], rs))
+    worst_o = rel_err(o_np, o_ref)
+    say("  rel err o=%.3e S=%.3e (tol %.1e)" % (worst_o, worst_s, tol))
+    assert np.all(np.isfinite(o_np)) and np.all(np.isfinite(S_np))
+    assert worst_o <= tol, worst_o
+    assert worst_s <= tol, worst_s
+    return o, S
+
+
+oracle_mod_global = None
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _oracle(oracle_mod):
+    global oracle_mod_global
+    oracle_mod_global = oracle_mod
+    yield
+
+
+# ---------------------------------------------------------------- workloads
+def test_single_head_fp32_workload(kda):
+    from linear_attention_recurrence_delta_amd import synth
+    w = synth.workload_inputs("single_head_fp32", DEV)
+    inp = dict(q=w["q"], k=w["k"], v=w["v"], g=w["g"], beta=w["beta"], S0=w["S0"], lengths=w["lengths"],
+               cu_list=[0, w["T"]])
+    _check_all(kda, None, inp, chunk=16, label="single_head_fp32 T=64 d=16 C=16")
+
+
+def test_multi_head_bf16_workload(kda):
+    from linear_attention_recurrence_delta_amd import synth
+    w = synth.workload_inputs("multi_head_bf16", DEV)
+    inp = dict(q=w["q"], k=w["k"], v=w["v"], g=w["g"], beta=w["beta"], S0=w["S0"], lengths=w["lengths"],
+               cu_list=[0, w["T"]])
+    _check_all(kda, None, inp, chunk=64, label="multi_head_bf16 T=4096 H=8 C=64 S0~N(0,.02)")
+
+
+# ---------------------------------------------------------------- fp32 path
+@pytest.mark.parametrize("d,chunk", [(16, 16), (16, 32), (16, 64), (32, 16), (32, 64), (64, 16),
+                                     (64, 32), (64, 64), (128, 16), (128, 32)])
+def test_fp32_ragged_varlen(kda, d, chunk):
+    lengths = [37, 0, 64, 1, 130]
+    T = sum(lengths)
+    inp = _inputs(T, 2, d, torch.float32, 100 + d + chunk, lengths=lengths, init_std=0.3)
+    _check_all(kda, None, inp, chunk=chunk, scale=0.75, label="fp32 varlen")
+
+
+# ---------------------------------------------------------------- bf16 path
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_bf16_ragged_varlen(kda, chunk):
+    lengths = [1, 0, 17, 64, 130, 255, 700]
+    inp = _inputs(sum(lengths), 3, 128, torch.bfloat16, 200 + chunk, lengths=lengths, init_std=0.05)
+    _check_all(kda, None, inp, chunk=chunk, label="bf16 varlen")
+
+
+@pytest.mark.parametrize("g_mode", ["mild", "zero"])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_bf16_weak_decay_long_memory(kda, g_mode, chunk):
+    # Weak or no decay keeps the state across many chunks, so state passing
+    # between chunks and the conditioning of the solve are exercised.
+    inp = _inputs(1500, 2, 128, torch.bfloat16, 300 + chunk, g_mode=g_mode, init_std=0.05)
+    _check_all(kda, None, inp, chunk=chunk, label="bf16 g=%s" % g_mode)
+
+
+@pytest.mark.parametrize("g_mode", ["mild", "k3"])
+def test_fp32_d128_long(kda, g_mode):
+    inp = _inputs(600, 2, 128, torch.float32, 400, g_mode=g_mode, init_std=0.05)
+    _check_all(kda, None, inp, chunk=32, label="fp32 d128 g=%s" % g_mode)
+
+
+def test_g_at_lower_bound(kda):
+    # g = g_min everywhere: a 16-token sub-tile decays by exactly -80, the edge
+    # of the range the sub-tile factorisation is built for.
+    inp = _inputs(300, 2, 128, torch.bfloat16, 500, init_std=0.05)
+    inp["g"].fill_(-5.0)
+    _check_all(kda, None, inp, chunk=64, label="bf16 g=-5")
+    inp32 = _inputs(300, 1, 64, torch.float32, 501, init_std=0.05)
+    inp32["g"].fill_(-5.0)
+    _check_all(kda, None, inp32, chunk=64, label="fp32 g=-5")
+
+
+# ---------------------------------------------------------------- special cases
+def test_beta_zero_is_pure_decay(kda):
+    inp = _inputs(200, 2, 128, torch.float32, 600, g_mode="mild", init_std=0.5)
+    inp["beta"].zero_()
+    _check_all(kda, None, inp, chunk=16, label="beta=0")
+
+
+def test_exact_recall_when_beta_one_and_q_equals_k(kda):
+    # g = 0, beta = 1, q = k, unit keys: every token reads back its own value.
+    for dtype, tol in ((torch.float32, 1e-4), (torch.bfloat16, 2e-2)):
+        inp = _inputs(256, 2, 128, dtype, 700, g_mode="zero", init_std=0.1)
+        inp["beta"].fill_(1.0)
+        inp["q"].copy_(inp["k"])
+        say("CASE exact recall dtype=%s" % dtype)
+        o, S = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"],
+                               chunk_size=64 if dtype == torch.bfloat16 else 16)
+        torch.cuda.synchronize()
+        assert rel_err(f64(o), f64(inp["v"])) <= tol
+
+
+def test_empty_batch_and_empty_sequences(kda):
+    H, d = 2, 128
+    say("CASE empty sequences")
+    S0 = torch.randn(3, H, d, d, device=DEV)
+    e = torch.empty(0, H, d, dtype=torch.bfloat16, device=DEV)
+    ef = torch.empty(0, H, d, dtype=torch.float32, device=DEV)
+    eb = torch.empty(0, H, dtype=torch.float32, device=DEV)
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    o, S = kda.kda_prefill(e, e, e, ef, eb, S0, cu)
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, d)
+    assert torch.equal(S, S0)
+    o, S = kda.kda_prefill(e, e, e, ef, eb, None, cu)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S) == 0
+
+
+def test_in_place_state_carry(kda):
+    inp = _inputs(400, 2, 128, torch.bfloat16, 800, init_std=0.05)
+    o1, S1 = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    carry = inp["S0"].clone()
+    o2, S2 = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], carry, final_state=carry)
+    torch.cuda.synchronize()
+    assert S2.data_ptr() == carry.data_ptr()
+    assert torch.equal(S1, carry) and torch.equal(o1, o2)
+
+
+def test_split_prefill_resumes(kda):
+    # prefill(T1 + T2) == prefill(T2, initial = final(T1)): the state restored
+    # at a token boundary, as prefix reuse needs.
+    inp = _inputs(1000, 2, 128, torch.bfloat16, 900, g_mode="mild", init_std=0.05)
+    T1 = 333
+    o, S = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    sl = lambda x, a, b: x[a:b].contiguous()
+    oa, Sa = kda.kda_prefill(*(sl(inp[n], 0, T1) for n in ("q", "k", "v", "g", "beta")), inp["S0"])
+    ob, Sb = kda.kda_prefill(*(sl(inp[n], T1, 1000) for n in ("q", "k", "v", "g", "beta")), Sa)
+    torch.cuda.synchronize()
+    assert rel_err(f64(torch.cat([oa, ob])), f64(o)) <= 2e-2
+    assert rel_err(f64(Sb), f64(S)) <= 2e-2
+
+
+def test_run_to_run_bitwise_deterministic(kda):
+    inp = _inputs(2000, 4, 128, torch.bfloat16, 1000, init_std=0.05)
+    r1 = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    r2 = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
+
+
+@pytest.mark.parametrize("waves", ["2", "4", "8"])
+def test_value_slab_split_invariance(kda, waves, monkeypatch):
+    # Splitting d_v across workgroups (column separability of the update)
+    # must not change a single bit: every column is computed identically.
+    inp = _inputs(700, 2, 128, torch.bfloat16, 1100, init_std=0.05)
+    monkeypatch.setenv("KDA_PREFILL_WAVES", "8")
+    ref = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    monkeypatch.setenv("KDA_PREFILL_WAVES", waves)
+    got = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+
+
+def test_dense_batch_layout_matches_packed(kda):
+    B, T, H, d = 3, 200, 2, 128
+    inp = _inputs(B * T, H, d, torch.bfloat16, 1200, lengths=[T] * B, init_std=0.05)
+    cu = torch.tensor(inp["cu_list"], dtype=torch.int32, device=DEV)
+    o_p, S_p = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], cu)
+    v4 = lambda x: x.view(B, T, *x.shape[1:])
+    o_d, S_d = kda.kda_prefill(v4(inp["q"]), v4(inp["k"]), v4(inp["v"]), v4(inp["g"]), v4(inp["beta"]),
+                               inp["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o_p.view(B, T, H, d), o_d) and torch.equal(S_p, S_d)
