@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA core on one MI355X.
+
+Metric: KDA prefill tokens/s at H = 96, d_k = d_v = 128, T = 32K (bf16 q/k/v,
+fp32 g/beta/state), plus decode-step state HBM GB/s at 256 sequences x 96
+heads with fp32 128 x 128 states.  Synthetic inputs (see synth.py) stand in
+for K3 KDA-layer activations.
+
+One "step" is one prefill of the dense workload (B = 1, T = 32768, H = 96):
+every prefill row of the method (decay cumsum, scaled tiles, Gram tiles,
+triangular solve, WY products, state pass, stores) runs once over the whole
+batch.  The packed-varlen prefill (16 sequences, 32768 tokens) and the decode
+step (256 x 96 states, read once and written once per step) are timed in the
+same run and reported under "prefill_varlen" and "decode".
+
+Timing: inputs are resident in HBM before the timed region; W untimed
+warm-up steps, then K timed steps bracketed by torch.cuda.synchronize();
+per-launch durations come from HIP events recorded on the stream the
+kernels are launched on (torch's current stream, which the binding passes
+to the C ABI).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
+
+# Algorithmic bytes per token-head of the bf16 prefill: q, k, v (3 x 256),
+# g (512), beta (4), o (256).  The per-head state I/O (64 KiB) is excluded.
+PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256
+# Chunked flop count at the reference chunk C = 64, d = 128, causal tiles:
+# A, P, W, U~ and P U at C^2 d each, plus W S, Q~ S and Kbar^T U at 2 C d^2
+# each, per chunk of C tokens -> 5 C d + 6 d^2 per token-head.
+PREFILL_FLOP_PER_TOKEN_HEAD = 5 * 64 * 128 + 6 * 128 * 128
+# Decode: state read + write (2 x 64 KiB) + q, k, v (bf16) + g (fp32) + beta + o (bf16).
+DECODE_BYTES_PER_UNIT = 2 * 128 * 128 * 4 + 3 * 128 * 2 + 128 * 4 + 4 + 128 * 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_recurrence_delta_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_digest") != kernel_source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def time_launches(fn, reps, stream):
+    """Run fn reps times; return per-launch ms from events on `stream`."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(w, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the dense workload."""
+    import oracle
+    import torch
+
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    H = w["H"]
+    nh = min(H, max(1, threads))
+    T_s = 512
+    while True:
+        sl = lambda x: x[:T_s, :nh].detach().to("cpu").to(torch.float64).numpy()
+        args = [sl(w[n]) for n in ("q", "k", "v", "g")]
+        beta = w["beta"][:T_s, :nh].detach().cpu().double().numpy()
+        t0 = time.perf_counter()
+        oracle.prefill(*args, beta)
+        dt = time.perf_counter() - t0
+        if dt >= 0.3 * target_s or T_s >= w["T"]:
+            break
+        T_s = int(min(w["T"], max(2 * T_s, T_s * target_s / max(dt, 1e-3))))
+    token_heads_per_s = nh * T_s / dt
+    return {
+        "value": token_heads_per_s / H,
+        "unit": "tokens/s",
+        "cores": min(nh, threads),
+        "kind": "oracle",
+        "sample": "first %d tokens of %d of the %d heads of the dense workload; %.1f s of fp64 "
+                  "token-by-token recurrence; tokens/s = token-heads/s / %d heads" % (T_s, nh, H, dt, H),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=200, help="decode steps timed after the prefill steps")
+    ap.add_argument("--chunk", type=int, default=0, help="prefill chunk size (0 = library default)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each (sequence, head) "
+              "recurrence is independent; sharding is described in DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_recurrence_delta_amd as kda
+    from linear_attention_recurrence_delta_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    result = {}
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x 1 GiB device-to-device")
+        del src, dst
+
+    # ---------------------------------------------------------------- prefill
+    log("generating k3_dense_32k / k3_varlen_32k inputs")
+    wd = synth.workload_inputs("k3_dense_32k", dev)
+    wv = synth.workload_inputs("k3_varlen_32k", dev)
+    C = args.chunk or 0
+    o_d = torch.empty_like(wd["v"])
+    s_d = torch.empty((wd["N"], wd["H"], wd["d"], wd["d"]), dtype=torch.float32, device=dev)
+    o_v = torch.empty_like(wv["v"])
+    s_v = torch.empty((wv["N"], wv["H"], wv["d"], wv["d"]), dtype=torch.float32, device=dev)
+
+    def run_dense():
+        kda.kda_prefill(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"], None, None, chunk_size=C,
+                        out=o_d, final_state=s_d)
+
+    def run_varlen():
+        kda.kda_prefill(wv["q"], wv["k"], wv["v"], wv["g"], wv["beta"], None, wv["cu"], chunk_size=C,
+                        out=o_v, final_state=s_v)
+
+    token_heads = wd["T"] * wd["H"]
+    if args.only in ("all", "prefill"):
+        for _ in range(args.warmup):
+            run_dense()
+            run_varlen()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dense_ms = time_launches(run_dense, args.steps, stream)
+        wall_s = time.perf_counter() - t0
+        varlen_ms = time_launches(run_varlen, args.steps, stream)
+        d_avg = sum(dense_ms) / len(dense_ms)
+        v_avg = sum(varlen_ms) / len(varlen_ms)
+        log("dense prefill avg %.3f ms (min %.3f), varlen avg %.3f ms, wall %.3f s" %
+            (d_avg, min(dense_ms), v_avg, wall_s))
+        bytes_launch = PREFILL_BYTES_PER_TOKEN_HEAD * token_heads
+        flop_launch = PREFILL_FLOP_PER_TOKEN_HEAD * token_heads
+        achieved = bytes_launch / (d_avg * 1e-3) / 1e9
+        result.update({
+            "value": wd["T"] / (d_avg * 1e-3),
+            "ms_per_step": d_avg,
+            "roofline": {
+                "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("kda_prefill_k3_dense_32k"),
+                "kernel": "kda_prefill_kernel (bf16, d=128)", "bytes_per_launch": bytes_launch,
+            },
+            "mfma": {
+                "flop_per_launch": flop_launch,
+                "achieved_tflops": flop_launch / (d_avg * 1e-3) / 1e12,
+                "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
+                "frac": flop_launch / (d_avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            },
+            "prefill_varlen": {
+                "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
+                "hbm_gbs": PREFILL_BYTES_PER_TOKEN_HEAD * wv["T"] * wv["H"] / (v_avg * 1e-3) / 1e9,
+                "lengths": wv["lengths"],
+            },
+        })
+        del o_v, s_v
+
+    # ---------------------------------------------------------------- decode
+    if args.only in ("all", "decode"):
+        N, H, d = 256, 96, 128
+        ring = 16  # distinct input sets (about 500 MB, more than the 256 MB MALL)
+        log("generating decode state and %d input sets" % ring)
+        S = synth.decode_state(N, H, d, 0.05, 4, dev)
+        sets = [synth.decode_inputs(N, H, d, torch.bfloat16, 1000 + i, dev) for i in range(ring)]
+        o_dec = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+        it = [0]
+
+        def run_decode():
+            q, k, v, g, beta = sets[it[0] % ring]
+            it[0] += 1
+            kda.kda_decode_step(q, k, v, g, beta, S, out=o_dec)
+
+        for _ in range(max(args.warmup, 5)):
+            run_decode()
+        dec_ms = time_launches(run_decode, args.decode_steps, stream)
+        dec_avg = sum(dec_ms) / len(dec_ms)
+        dec_bytes = DECODE_BYTES_PER_UNIT * N * H
+        dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+        log("decode avg %.4f ms/step, %.1f GB/s" % (dec_avg, dec_gbs))
+        result["decode"] = {
+            "workload": "256 sequences x 96 heads, fp32 128x128 states, bf16 q/k/v, fp32 g/beta",
+            "ms_per_step": dec_avg, "steps": args.decode_steps, "state_hbm_gbs": dec_gbs,
+            "tokens_per_s": N / (dec_avg * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dec_gbs / HBM_PEAK_GBS, "traffic": measured_traffic("kda_decode_256x96"),
+                         "kernel": "kda_decode_kernel<bf16,128>", "bytes_per_launch": dec_bytes},
+        }
+        del S, sets
+
+    line = {
+        "metric": "KDA prefill tokens/s (H=96,d=128,T=32K) + decode state HBM GB/s",
+        "value": result.get("value"),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": result.get("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "k3_dense_32k: B=1 T=32768 H=96 d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state",
+                   "global_batch": 1, "seq_len": 32768, "heads": 96, "d_k": 128, "d_v": 128,
+                   "chunk": C or 64, "parallelism": "none (1 GPU)"},
+    }
+    for key in ("roofline", "mfma", "prefill_varlen", "decode"):
+        if key in result:
+            line[key] = result[key]
+
+    if not args.no_cpu_baseline and args.only in ("all", "prefill"):
+        log("timing the oracle (cpu_baseline)")
+        line["cpu_baseline"] = cpu_baseline(wd, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

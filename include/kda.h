@@ -19,8 +19,10 @@
  * a token boundary for prefix reuse.
  *
  * Conventions shared by every entry point
- *   - All tensor pointers are DEVICE pointers, row-major and contiguous, and
- *     must be 16-byte aligned.  The caller owns every buffer; the library
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous.
+ *     q, k, v, g, o and the state buffers must be 16-byte aligned (the
+ *     kernels use 16-byte vector accesses); beta and cu_seqlens need only
+ *     their natural 4-byte alignment.  The caller owns every buffer; the library
  *     allocates no device memory and keeps no mutable global state.
  *   - Element offsets are 64-bit; token counts up to 2^31 - 1 per call.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
@@ -61,7 +63,7 @@ typedef enum {
     KDA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                       */
     KDA_ERR_BAD_SHAPE = 2,    /* negative / inconsistent sizes                     */
     KDA_ERR_UNSUPPORTED = 3,  /* valid but not built: (dtype, d_k, d_v, chunk)     */
-    KDA_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned                  */
+    KDA_ERR_MISALIGNED = 4,   /* a pointer breaks the alignment rule above         */
     KDA_ERR_WORKSPACE = 5,    /* workspace smaller than kda_prefill_workspace_bytes */
     KDA_ERR_HIP = 6           /* the HIP runtime reported an error at launch       */
 } kda_status;

@@ -14,6 +14,7 @@ namespace {
 using kda::PrefillVariant;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int default_chunk(int32_t dtype) { return dtype == KDA_DTYPE_BF16 ? 64 : 16; }
 
@@ -27,19 +28,18 @@ const PrefillVariant* variants(int32_t dtype, int* count) {
 }
 
 // Column waves per workgroup.  Fewer waves per (sequence, head) means more
-// workgroups (d_v slabs) and fills more compute units when there are few
-// (sequence, head) recurrences; more waves share the d_k-side work of a head
-// among more value columns.  KDA_PREFILL_WAVES overrides the choice.
+// workgroups (d_v slabs), which fills more compute units when there are few
+// (sequence, head) recurrences but repeats the d_k-side work per slab; more
+// waves share that work among more value columns.  KDA_PREFILL_WAVES (an
+// integer) overrides the choice; results are bitwise identical either way.
 const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units) {
     int count = 0;
     const PrefillVariant* tab = variants(dtype, &count);
-    int want = 0;
-    if (const char* env = getenv("KDA_PREFILL_WAVES")) want = atoi(env);
-    if (want <= 0) {
-        // Aim for at least ~2 workgroups per compute unit (256 on MI355X).
-        const int64_t target = 512;
-        want = 8;
-        while (want > 1 && units * (D / (16 * want)) < target) want /= 2;
+    (void)units;
+    int want = 8;  // measured fastest on MI355X for the K3 shapes at every batch size tried
+    if (const char* env = getenv("KDA_PREFILL_WAVES")) {
+        const int e = atoi(env);
+        if (e > 0) want = e;
     }
     // the largest built wave count not above the wanted one, else the smallest built
     const PrefillVariant* best = nullptr;
@@ -65,7 +65,7 @@ const char* kda_status_string(int32_t s) {
         case KDA_ERR_NULL_POINTER: return "KDA_ERR_NULL_POINTER: a required pointer is NULL";
         case KDA_ERR_BAD_SHAPE: return "KDA_ERR_BAD_SHAPE: negative or inconsistent sizes";
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: no kernel built for this dtype / head dim / chunk size";
-        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a pointer is not 16-byte aligned";
+        case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a tensor pointer is not 16-byte aligned (beta, cu_seqlens: 4-byte)";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_prefill_workspace_bytes";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
         default: return "unknown kda_status";
@@ -111,9 +111,10 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads
     if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
     if (!kda_prefill_supported(dtype, d_k, d_v, chunk_size)) return KDA_ERR_UNSUPPORTED;
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, g, beta, initial_state, cu_seqlens, o, final_state, workspace};
+    const void* ptrs[] = {q, k, v, g, initial_state, o, final_state, workspace};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+    if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return KDA_ERR_MISALIGNED;
     if (o && (o == q || o == k || o == v || o == g || o == beta)) return KDA_ERR_BAD_SHAPE;
     const size_t need = kda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
@@ -155,9 +156,10 @@ kda_status kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t d_k, int
     if (!kda_decode_supported(dtype, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)num_seqs * num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (num_seqs > 0 && (!q || !k || !v || !g || !beta || !state || !o)) return KDA_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, g, beta, state, o};
+    const void* ptrs[] = {q, k, v, g, state, o};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+    if (beta && !aligned4(beta)) return KDA_ERR_MISALIGNED;
     if (o && (o == q || o == k || o == v || o == g || o == beta || o == state)) return KDA_ERR_BAD_SHAPE;
     if (num_seqs == 0) return KDA_OK;
 

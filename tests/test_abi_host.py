@@ -93,6 +93,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, k=FAKE + 8) == MISAL
     assert _prefill(lib, S0=FAKE + 4) == MISAL
     assert _prefill(lib, cu=FAKE + 2, N=2) == MISAL
+    assert _prefill(lib, beta=FAKE + 2) == MISAL
+    assert _prefill(lib, g=FAKE + 4) == MISAL
     assert _prefill(lib, o=FAKE) == BAD               # o == q
     # no-ops that launch nothing
     assert _prefill(lib, N=0, T=0) == OK
@@ -117,6 +119,8 @@ def test_decode_validation(lib):
     assert _decode(lib, S=None) == NULLP
     assert _decode(lib, q=None) == NULLP
     assert _decode(lib, v=FAKE + 4) == MISAL
+    assert _decode(lib, S=FAKE + 0x200008) == MISAL
+    assert _decode(lib, beta=FAKE + 1) == MISAL
     assert _decode(lib, o=FAKE + 0x200000) == BAD     # o == state
     assert _decode(lib, N=0, q=None, k=None, v=None, g=None, beta=None, S=None, o=None) == OK
 
