@@ -88,15 +88,17 @@ def time_launches(fn, reps, stream):
 
 
 def cpu_baseline(w, target_s):
-    """The fp64 oracle, as it stands, on a bounded sample of the dense workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the dense workload.
+
+    The sample grows (tokens, then heads, then repeats of the same slice)
+    until about target_s seconds of CPU work have run."""
     import oracle
     import torch
 
     oracle.build(force=False)
     threads = oracle.max_threads()
-    H = w["H"]
-    nh = min(H, max(1, threads))
-    T_s = 512
+    H, T = w["H"], w["T"]
+    nh, T_s = min(H, max(1, threads)), 1024
     while True:
         sl = lambda x: x[:T_s, :nh].detach().to("cpu").to(torch.float64).numpy()
         args = [sl(w[n]) for n in ("q", "k", "v", "g")]
@@ -104,17 +106,27 @@ def cpu_baseline(w, target_s):
         t0 = time.perf_counter()
         oracle.prefill(*args, beta)
         dt = time.perf_counter() - t0
-        if dt >= 0.3 * target_s or T_s >= w["T"]:
+        if dt >= 0.25 * target_s or (T_s >= T and nh >= H):
             break
-        T_s = int(min(w["T"], max(2 * T_s, T_s * target_s / max(dt, 1e-3))))
-    token_heads_per_s = nh * T_s / dt
+        grow = max(2.0, 0.5 * target_s / max(dt, 1e-3))
+        if T_s < T:
+            T_s = int(min(T, T_s * grow))
+        else:
+            nh = int(min(H, nh * grow))
+    reps = max(1, int(round(target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.prefill(*args, beta)
+    total = time.perf_counter() - t0
+    token_heads_per_s = reps * nh * T_s / total
     return {
         "value": token_heads_per_s / H,
         "unit": "tokens/s",
         "cores": min(nh, threads),
         "kind": "oracle",
-        "sample": "first %d tokens of %d of the %d heads of the dense workload; %.1f s of fp64 "
-                  "token-by-token recurrence; tokens/s = token-heads/s / %d heads" % (T_s, nh, H, dt, H),
+        "sample": "%d run(s) of the first %d tokens x %d of the %d heads of the dense workload, %.1f s "
+                  "of fp64 token-by-token recurrence on %d OpenMP threads; tokens/s = token-heads/s / %d heads"
+                  % (reps, T_s, nh, H, total, min(nh, threads), H),
     }
 
 
