@@ -16,7 +16,7 @@ using kda::PrefillVariant;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int default_chunk(int32_t dtype) { return dtype == KDA_DTYPE_BF16 ? 64 : 16; }
+int default_chunk(int32_t dtype) { return dtype == KDA_DTYPE_BF16 ? 32 : 16; }
 
 int resolve_chunk(int32_t dtype, int32_t chunk) { return chunk == 0 ? default_chunk(dtype) : chunk; }
 

@@ -117,6 +117,21 @@ __device__ __forceinline__ void mma32(f32x4& acc, const uint2& a0, const uint2& 
                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
+// Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16r..16r+15):
+// lane l ends with x[16r] + ... + x[l].  Each step adds the value of the lane
+// n places lower in the row (DPP row_shr:n); lanes with no such lane add 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_shr(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_inclusive_sum16(float x) {
+    x += dpp_row_shr<0x111>(x);  // row_shr:1
+    x += dpp_row_shr<0x112>(x);  // row_shr:2
+    x += dpp_row_shr<0x114>(x);  // row_shr:4
+    x += dpp_row_shr<0x118>(x);  // row_shr:8
+    return x;
+}
+
 __device__ __forceinline__ f32x4 zero4() {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
     return z;

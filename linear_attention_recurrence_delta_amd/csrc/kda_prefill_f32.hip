@@ -13,7 +13,6 @@ static const PrefillVariant kF32Variants[] = {
     KDA_PREFILL_VARIANT(0, float, 32, 4, 2),
     KDA_PREFILL_VARIANT(0, float, 64, 1, 4),
     KDA_PREFILL_VARIANT(0, float, 64, 2, 4),
-    KDA_PREFILL_VARIANT(0, float, 64, 4, 4),
     KDA_PREFILL_VARIANT(0, float, 128, 1, 8),
     KDA_PREFILL_VARIANT(0, float, 128, 2, 8),
 };

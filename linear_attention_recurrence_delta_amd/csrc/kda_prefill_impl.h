@@ -59,7 +59,7 @@ struct PrefillCfg {
     static constexpr int PAD = Elem<TIn>::pad;
     static constexpr int PD = D + PAD;       // pitch of [C][D] tiles
     static constexpr int PC = C + PAD;       // pitch of [*][C] tiles
-    static constexpr int PV = DVW + PAD;     // pitch of the V tile
+    static constexpr int PV = DVW;           // pitch of the V tile
     static constexpr int PT = 16 + PAD;      // pitch of a T_ii block
     static constexpr int PA = 20;            // pitch (floats) of an fp32 A_ii block
     static constexpr int NP = NS * (NS + 1) / 2;  // sub-tile pairs i >= j
@@ -67,7 +67,8 @@ struct PrefillCfg {
 
     static constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t SZ_TILE = al16(sizeof(TIn) * C * PD);
-    static constexpr size_t OFF_QB = 0;                      // also the V tile
+    static constexpr size_t OFF_V = 0;                       // [C][DVW], unpadded
+    static constexpr size_t OFF_QB = OFF_V + al16(sizeof(TIn) * C * DVW);
     static constexpr size_t OFF_KB = OFF_QB + SZ_TILE;
     static constexpr size_t OFF_KR = OFF_KB + SZ_TILE;
     static constexpr size_t OFF_QT = OFF_KR + SZ_TILE;
@@ -78,7 +79,7 @@ struct PrefillCfg {
     static constexpr size_t OFF_T = OFF_AO + al16(sizeof(TIn) * C * PC);
     static constexpr size_t OFF_AD = OFF_T + al16(sizeof(TIn) * NS * 16 * PT);
     static constexpr size_t OFF_F = OFF_AD + al16(sizeof(float) * NS * 16 * PA);
-    static constexpr size_t OFF_GAM = OFF_F + al16(sizeof(float) * NS * NS * D);
+    static constexpr size_t OFF_GAM = OFF_F + al16(sizeof(float) * NP * D);
     static constexpr size_t OFF_TOT = OFF_GAM + al16(sizeof(float) * D);
     static constexpr size_t OFF_BETA = OFF_TOT + al16(sizeof(float) * NS * D);
     static constexpr size_t LDS = OFF_BETA + al16(sizeof(float) * C);
@@ -86,7 +87,6 @@ struct PrefillCfg {
     static_assert(D % 16 == 0 && D >= 16, "head dim");
     static_assert(DVW <= D && D % DVW == 0, "value slab");
     static_assert(D % (16 * KSTEP) == 0, "K steps");
-    static_assert(sizeof(TIn) * C * PV <= sizeof(TIn) * C * PD, "V tile aliases QB");
     static_assert(LDS <= 160 * 1024, "LDS budget (160 KiB per CU on gfx950)");
 };
 
@@ -126,8 +126,8 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
     constexpr int NKB = D / 16;  // K blocks over d_k
 
     __shared__ __align__(16) char smem[Cfg::LDS];
+    TIn* sV = reinterpret_cast<TIn*>(smem + Cfg::OFF_V);
     TIn* sQB = reinterpret_cast<TIn*>(smem + Cfg::OFF_QB);
-    TIn* sV = sQB;  // the V tile reuses QB once the Gram tiles are done
     TIn* sKB = reinterpret_cast<TIn*>(smem + Cfg::OFF_KB);
     TIn* sKR = reinterpret_cast<TIn*>(smem + Cfg::OFF_KR);
     TIn* sQT = reinterpret_cast<TIn*>(smem + Cfg::OFF_QT);
@@ -183,88 +183,134 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
             Sm[ct][pp] = p.S0 ? p.S0[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col0 + l16] : 0.f;
     }
 
-    constexpr int NITEM = D * NS;                  // (channel, sub-tile) items
-    constexpr int IPT = (NITEM + NT - 1) / NT;     // items per thread
+    // Prologue items: wave-item wi = (sub-tile i, 16-channel block cb); lane
+    // (g4, l16) holds token 16 i + l16 and channels 16 cb + 4 g4 .. + 3 -- the
+    // MFMA operand layout -- so the 16 tokens of a sub-tile sit in one 16-lane
+    // DPP row and the per-channel cumulative decay is a row prefix scan.
+    constexpr int NCB = D / 16;
+    constexpr int NWI = NS * NCB;
+    constexpr int IPT = (NWI + NWC - 1) / NWC;     // wave-items per wave
     constexpr int VE = 16 / sizeof(TIn);           // V elements per 16-byte load
     constexpr int VCPR = DVW / VE;                 // 16-byte chunks per V row
     constexpr int VPT = (C * VCPR + NT - 1) / NT;  // V chunks per thread
+
+    // Next-chunk inputs, loaded while the current chunk computes.
+    float4 pg[IPT];
+    Frag pq[IPT], pk[IPT];
+    uint4 pv[VPT];
+    float pb = 0.f;
+    auto prefetch = [&](int64_t tn, int nvn) {
+#pragma unroll
+        for (int it = 0; it < IPT; ++it) {
+            const int wi = w + NWC * it;
+            const int i = wi / NCB, cb = wi % NCB;
+            const int row = 16 * i + l16;
+            pg[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+            pq[it] = E::zero();
+            pk[it] = E::zero();
+            if (wi < NWI && row < nvn) {
+                const int64_t off = ((tn + row) * H + h) * D + 16 * cb + 4 * g4;
+                pg[it] = *reinterpret_cast<const float4*>(p.g + off);
+                pq[it] = ld_frag(gq + off);
+                pk[it] = ld_frag(gk + off);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < VPT; ++it) {
+            const int idx = tid + it * NT;
+            const int row = idx / VCPR, ch = idx % VCPR;
+            pv[it] = make_uint4(0u, 0u, 0u, 0u);
+            if (idx < C * VCPR && row < nvn)
+                pv[it] = *reinterpret_cast<const uint4*>(gv + ((tn + row) * H + h) * D + z * DVW + ch * VE);
+        }
+        pb = 0.f;
+        if (tid < C && tid < nvn) pb = p.beta[(tn + tid) * H + h];
+    };
+    if (t_begin < t_end) prefetch(t_begin, (t_end - t_begin) < C ? (int)(t_end - t_begin) : C);
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += C) {
         const int nv = (t_end - t0) < C ? (int)(t_end - t0) : C;
 
         // ================= stage 1: decay, scaled operand tiles =================
+        // 1a: inclusive cumulative log-decay inside each 16-token sub-tile.
+        float4 cum[IPT];
 #pragma unroll
         for (int it = 0; it < IPT; ++it) {
-            const int item = tid + it * NT;
-            if (item < NITEM) {
-                const int c = item % D, i = item / D;
-                float cum = 0.f;
+            const int wi = w + NWC * it;
+            float x[4] = {pg[it].x, pg[it].y, pg[it].z, pg[it].w};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 16 * i + r;
-                    cum += row < nv ? p.g[((t0 + row) * H + h) * D + c] : 0.f;
-                }
-                sTot[i * D + c] = cum;
+            for (int ch = 0; ch < 4; ++ch) x[ch] = row_inclusive_sum16(x[ch]);
+            cum[it] = make_float4(x[0], x[1], x[2], x[3]);
+            if (wi < NWI && l16 == 15) {
+                const int i = wi / NCB, cb = wi % NCB;
+                *reinterpret_cast<float4*>(sTot + i * D + 16 * cb + 4 * g4) = cum[it];
             }
         }
-        uint4 vreg[VPT];
 #pragma unroll
         for (int it = 0; it < VPT; ++it) {
             const int idx = tid + it * NT;
             const int row = idx / VCPR, ch = idx % VCPR;
-            vreg[it] = make_uint4(0u, 0u, 0u, 0u);
-            if (idx < C * VCPR && row < nv)
-                vreg[it] = *reinterpret_cast<const uint4*>(gv + ((t0 + row) * H + h) * D + z * DVW + ch * VE);
+            if (idx < C * VCPR) *reinterpret_cast<uint4*>(sV + row * PV + ch * VE) = pv[it];
         }
-        if (tid < C) sBeta[tid] = tid < nv ? p.beta[(t0 + tid) * H + h] : 0.f;
+        if (tid < C) sBeta[tid] = pb;
         __syncthreads();
 
-#pragma unroll 1
+        // 1b: scaled tiles from the registers, pair factors, chunk decay.
+#pragma unroll
         for (int it = 0; it < IPT; ++it) {
-            const int item = tid + it * NT;
-            if (item < NITEM) {
-                const int c = item % D, i = item / D;
-                float b_i = 0.f, b_all = 0.f, tot_i = 0.f;
+            const int wi = w + NWC * it;
+            if (wi < NWI) {
+                const int i = wi / NCB, cb = wi % NCB;
+                const int c0 = 16 * cb + 4 * g4;
+                const int row = 16 * i + l16;
+                float L[4] = {cum[it].x, cum[it].y, cum[it].z, cum[it].w};
+                float qv[4], kv[4], qb[4], kb[4], kr[4], qt[4], kt[4], kbar[4];
 #pragma unroll
-                for (int ii = 0; ii < NS; ++ii) {
-                    const float t = sTot[ii * D + c];
-                    if (ii < i) b_i += t;
-                    if (ii == i) tot_i = t;
-                    b_all += t;
-                }
-                const float e_bi = __expf(b_i);                  // chunk start -> sub-tile start
-                const float e_kbar = __expf(b_all - b_i - tot_i);  // sub-tile end -> chunk end
-                float cum = 0.f;
-#pragma unroll 4
-                for (int r = 0; r < 16; ++r) {
-                    const int row = 16 * i + r;
-                    const int64_t off = ((t0 + row) * H + h) * D + c;
-                    const bool ok = row < nv;
-                    const float qv = ok ? E::load(gq + off) : 0.f;
-                    const float kv = ok ? E::load(gk + off) : 0.f;
-                    cum += ok ? p.g[off] : 0.f;  // second read of g: L2-resident
-                    const float e1 = __expf(cum);          // e^{L_r}, in [e^-80, 1]
-                    const float e2 = __expf(tot_i - cum);  // e^{tot_i - L_r}, in [e^-80, 1]
-                    const float qb = qv * e1, kb = kv * e1, kr = kv * e2;
-                    sQB[row * PD + c] = E::from_f32(qb);
-                    sKB[row * PD + c] = E::from_f32(kb);
-                    sKR[row * PD + c] = E::from_f32(kr);
-                    sQT[row * PD + c] = E::from_f32(qb * e_bi);
-                    sKT[row * PD + c] = E::from_f32(kb * e_bi);
-                    sKbT[c * PC + row] = E::from_f32(kr * e_kbar);
-                }
-                // Gram scale factors per sub-tile pair (i, j <= i), on the left operand.
-                float b_j1 = 0.f;  // decay before sub-tile j + 1
+                for (int ch = 0; ch < 4; ++ch) {
+                    qv[ch] = E::get(pq[it], ch);
+                    kv[ch] = E::get(pk[it], ch);
+                    float b_i = 0.f, b_all = 0.f, tot_i = 0.f;
 #pragma unroll
-                for (int j = 0; j < NS; ++j) {
-                    if (j <= i) {
-                        b_j1 += sTot[j * D + c];
-                        sF[(i * NS + j) * D + c] = (j == i) ? __expf(-tot_i) : __expf(b_i - b_j1);
+                    for (int ii = 0; ii < NS; ++ii) {
+                        const float t = sTot[ii * D + c0 + ch];
+                        if (ii < i) b_i += t;
+                        if (ii == i) tot_i = t;
+                        b_all += t;
+                    }
+                    const float e1 = __expf(L[ch]);          // e^{L_r}, in [e^-80, 1]
+                    const float e2 = __expf(tot_i - L[ch]);  // e^{tot_i - L_r}, in [e^-80, 1]
+                    qb[ch] = qv[ch] * e1;
+                    kb[ch] = kv[ch] * e1;
+                    kr[ch] = kv[ch] * e2;
+                    const float e_bi = __expf(b_i);            // chunk start -> sub-tile start
+                    const float e_kbar = __expf(b_all - b_i - tot_i);  // sub-tile end -> chunk end
+                    qt[ch] = qb[ch] * e_bi;
+                    kt[ch] = kb[ch] * e_bi;
+                    kbar[ch] = kr[ch] * e_kbar;
+                    if (l16 == 0) {
+                        // Gram scale factors of pairs (i, j <= i), applied to the left operand.
+                        float b_j1 = 0.f;  // decay before sub-tile j + 1
+#pragma unroll
+                        for (int j = 0; j < NS; ++j) {
+                            if (j <= i) {
+                                b_j1 += sTot[j * D + c0 + ch];
+                                sF[(i * (i + 1) / 2 + j) * D + c0 + ch] = (j == i) ? __expf(-tot_i) : __expf(b_i - b_j1);
+                            }
+                        }
+                        if (i == NS - 1) sGam[c0 + ch] = __expf(b_all);
                     }
                 }
-                if (i == NS - 1) sGam[c] = __expf(b_all);
+                st_frag(sQB + row * PD + c0, E::make(qb[0], qb[1], qb[2], qb[3]));
+                st_frag(sKB + row * PD + c0, E::make(kb[0], kb[1], kb[2], kb[3]));
+                st_frag(sKR + row * PD + c0, E::make(kr[0], kr[1], kr[2], kr[3]));
+                st_frag(sQT + row * PD + c0, E::make(qt[0], qt[1], qt[2], qt[3]));
+                st_frag(sKT + row * PD + c0, E::make(kt[0], kt[1], kt[2], kt[3]));
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) sKbT[(c0 + ch) * PC + row] = E::from_f32(kbar[ch]);
             }
         }
+        // The registers are free again: start loading the next chunk.
+        if (t0 + C < t_end) prefetch(t0 + C, (t_end - t0 - C) < C ? (int)(t_end - t0 - C) : C);
         __syncthreads();
 
         // ================= stage 2: Gram tiles A and P (MFMA) =================
@@ -275,7 +321,7 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
             const int j = pp;
             const TIn* xrow = (which ? sQB : sKB) + (16 * i + l16) * PD + 4 * g4;
             const TIn* krow = sKR + (16 * j + l16) * PD + 4 * g4;
-            const float* frow = sF + (i * NS + j) * D + 4 * g4;
+            const float* frow = sF + (i * (i + 1) / 2 + j) * D + 4 * g4;
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < NKB; kb += KSTEP) {
@@ -314,12 +360,6 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
         __syncthreads();
 
         // ================= stage 3: V tile, T_ii solve, X = Kt S0, Qt S0 =================
-#pragma unroll
-        for (int it = 0; it < VPT; ++it) {
-            const int idx = tid + it * NT;
-            const int row = idx / VCPR, ch = idx % VCPR;
-            if (idx < C * VCPR) *reinterpret_cast<uint4*>(sV + row * PV + ch * VE) = vreg[it];
-        }
         if (w == 0 && lane < 16 * NS) {
             // T_ii = (I + A_ii)^{-1} by forward substitution, one column per lane.
             const int i = lane >> 4, col = l16;
