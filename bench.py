@@ -272,7 +272,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "k3_dense_32k: B=1 T=32768 H=96 d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state",
                    "global_batch": 1, "seq_len": 32768, "heads": 96, "d_k": 128, "d_v": 128,
-                   "chunk": C or 64, "parallelism": "none (1 GPU)"},
+                   "chunk": C or 16, "parallelism": "none (1 GPU)"},
     }
     for key in ("roofline", "mfma", "prefill_varlen", "decode"):
         if key in result:

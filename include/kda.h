@@ -75,7 +75,7 @@ int32_t kda_abi_version(void);
 const char *kda_status_string(int32_t status);
 
 /* 1 if (qkv_dtype, d_k, d_v, chunk_size) has a built prefill kernel, else 0.
- * chunk_size 0 asks for the library default (32 for bf16, 16 for fp32). */
+ * chunk_size 0 asks for the library default (16 for both dtypes). */
 int32_t kda_prefill_supported(int32_t qkv_dtype, int32_t d_k, int32_t d_v,
                               int32_t chunk_size);
 

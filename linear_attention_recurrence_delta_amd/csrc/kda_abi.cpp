@@ -16,7 +16,7 @@ using kda::PrefillVariant;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-int default_chunk(int32_t dtype) { return dtype == KDA_DTYPE_BF16 ? 32 : 16; }
+int default_chunk(int32_t dtype) { (void)dtype; return 16; }
 
 int resolve_chunk(int32_t dtype, int32_t chunk) { return chunk == 0 ? default_chunk(dtype) : chunk; }
 
@@ -33,20 +33,27 @@ const PrefillVariant* variants(int32_t dtype, int* count) {
 // waves share that work among more value columns.  KDA_PREFILL_WAVES (an
 // integer) overrides the choice; results are bitwise identical either way.
 const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units) {
+    (void)units;
     int count = 0;
     const PrefillVariant* tab = variants(dtype, &count);
-    (void)units;
     int want = 8;  // measured fastest on MI355X for the K3 shapes at every batch size tried
     if (const char* env = getenv("KDA_PREFILL_WAVES")) {
         const int e = atoi(env);
         if (e > 0) want = e;
     }
-    // the largest built wave count not above the wanted one, else the smallest built
+    int want_kind = 1;  // the wave-specialised pipeline where it is built
+    if (const char* env = getenv("KDA_PREFILL_KIND")) want_kind = atoi(env);
+    // Among (D, C) matches: the wanted kind if built; then the largest wave
+    // count not above the wanted one, else the smallest built.
+    bool have_kind = false;
+    for (int i = 0; i < count; ++i)
+        if (tab[i].D == D && tab[i].C == C && tab[i].kind == want_kind) have_kind = true;
     const PrefillVariant* best = nullptr;
     const PrefillVariant* smallest = nullptr;
     for (int i = 0; i < count; ++i) {
         const PrefillVariant& v = tab[i];
         if (v.D != D || v.C != C) continue;
+        if (have_kind && v.kind != want_kind) continue;
         if (!smallest || v.nwc < smallest->nwc) smallest = &v;
         if (v.nwc <= want && (!best || v.nwc > best->nwc)) best = &v;
     }

@@ -40,6 +40,7 @@ struct DecodeParams {
 
 // One entry per built prefill kernel.
 struct PrefillVariant {
+    int kind;               // 0: chunk-staged kernel, 1: wave-specialised pipeline
     int dtype;              // kda_dtype
     int D;                  // d_k = d_v
     int C;                  // chunk size

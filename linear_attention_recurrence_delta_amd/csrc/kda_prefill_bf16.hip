@@ -1,10 +1,13 @@
 // kda_prefill_bf16.hip -- bf16 q/k/v instantiations of the chunked prefill
 // (bf16 MFMA products, fp32 accumulation, fp32 state).
 #include "kda_prefill_impl.h"
+#include "kda_prefill_ws.h"
 
 namespace kda {
 
 static const PrefillVariant kBf16Variants[] = {
+    // wave-specialised pipeline: 4 consumer waves x 32 columns, 4 stage-A waves
+    {1, 1, 128, 16, 8, WsCfg<4, 2, 4>::LDS, &launch_prefill_ws<4, 2, 4>},
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 8),
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 4),
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 2),

@@ -444,6 +444,6 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t s) {
 }
 
 #define KDA_PREFILL_VARIANT(DT, TIN, D, NS, NWC) \
-    { DT, D, 16 * NS, NWC, PrefillCfg<TIN, D, NS, NWC>::LDS, &launch_prefill<TIN, D, NS, NWC> }
+    { 0, DT, D, 16 * NS, NWC, PrefillCfg<TIN, D, NS, NWC>::LDS, &launch_prefill<TIN, D, NS, NWC> }
 
 }  // namespace kda

@@ -1,0 +1,547 @@
+// kda_prefill_ws.h -- wave-specialised, software-pipelined KDA prefill for
+// bf16 q/k/v, d_k = d_v = 128, 16-token chunks (gfx950).
+//
+// Same chunk algebra as kda_prefill_impl.h with one 16-token sub-tile per
+// chunk (so Kt = k e^G, Qt = q e^G and Kbar = k e^{G_C - G} need no extra
+// factors), but the work of a chunk is split over waves with different jobs
+// that run concurrently on consecutive chunks:
+//
+//   stage A   (NSA waves)  chunk c = m + 3: cumulative log-decay L (DPP row
+//                          scan), scaled tiles QB = q e^L, KB = k e^L,
+//                          KL = k e^{-L} and its transpose, gamma = e^{L_15},
+//                          beta; prefetches the raw inputs of chunk c + 1.
+//   Gram      (1 wave)     chunk m + 2: P = incl-lower(QB KL^T) and
+//                          A = strict-lower(diag(beta) KB KL^T) on MFMA:
+//                          e^{L_r - L_s} = e^{L_r} e^{-L_s} with
+//                          e^{L_r} in [e^-80, 1] and e^{-L_s} in [1, e^80]
+//                          (a 16-token tile decays by at least -80), so no
+//                          factor leaves the bf16/fp32 exponent range.
+//   solve     (1 wave)     chunk m + 1: T = (I + A)^{-1} by a column sweep
+//                          (fp32; 15-way independent updates per step).
+//   consumers (NCW waves)  chunk m: X = Kt S, Qt S, U = T diag(beta)(V - X),
+//                          O = Qt S + P U, S <- Diag(gamma)(S + KL^T U)
+//                          (= Diag(gamma) S + Kbar^T U, Kbar = k e^{tot-L}:
+//                          the decay of each contribution is applied to the
+//                          sum, which is also exact up to relative rounding
+//                          because e^{-L_s} <= 1/gamma); each
+//                          wave owns TPW x 16 value columns of the fp32 state
+//                          in registers (see kda_device.h for the MFMA
+//                          layout that chains the products in registers).
+//
+// Iteration m ends with the only barrier.  LDS slots rotate with the chunk
+// index: QB/KB/KL^T/gamma/beta live 4 iterations, P 3, KL, A, T and V 2, so no
+// slot is written while another wave still reads it.  Raw q/k/g/beta are
+// prefetched one iteration ahead into the stage-A waves' registers; the V
+// tile travels through the Gram wave's registers into a 2-deep LDS slot; the loop body is unrolled
+// twice so both register sets have fixed names, and every load is issued
+// unconditionally (rows clamped into the sequence) so the compiler's counted
+// waits never collapse to a full drain.  Rows past the end of a sequence keep
+// the clamped (finite) q, k, v but get g = 0 and beta = 0: then their A rows,
+// Y rows and hence U rows are zero, they change neither the state nor the
+// earlier rows, and their outputs are not stored.
+//
+// Sources for what is computed: as in kda_prefill_impl.h ("Understanding Kimi
+// K3's attention" state-update / readout / g_min equations; "Inside Kimi K3",
+// section "Sequence mixing"; "Hybrid Attention", section "But isn't a
+// recurrent update sequential?").
+#pragma once
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int NCW, int TPW, int NSA>
+struct WsCfg {
+    static constexpr int D = 128;
+    static constexpr int C = 16;
+    static constexpr int NCB = D / 16;               // 16-channel blocks
+    static constexpr int NWAVES = NCW + 2 + NSA;
+    static constexpr int NT = 64 * NWAVES;
+    static constexpr int DVW = NCW * TPW * 16;       // value columns per workgroup
+    static constexpr int W_SOLVE = NCW;
+    static constexpr int W_GRAM = NCW + 1;
+    static constexpr int W_A0 = NCW + 2;             // first stage-A wave
+    static constexpr int IPW = NCB / NSA;            // stage-A items (16-channel blocks) per wave
+
+    static constexpr int PD = D + 8;                 // bf16 pitch of [16][D] tiles
+    static constexpr int PK = C + 8;                 // bf16 pitch of KL^T [D][16] and of 16x16 tiles
+    static constexpr int PA = 20;                    // fp32 pitch of A^T
+
+    static constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
+    // 4-deep slot: QB, KB, KL^T, gamma, beta
+    static constexpr size_t S4_QB = 0;
+    static constexpr size_t S4_KB = S4_QB + al16(2 * C * PD);
+    static constexpr size_t S4_KT = S4_KB + al16(2 * C * PD);
+    static constexpr size_t S4_GAM = S4_KT + al16(2 * D * PK);
+    static constexpr size_t S4_BETA = S4_GAM + al16(4 * D);
+    static constexpr size_t S4 = S4_BETA + al16(4 * C);
+    // 2-deep slot: KL (row-major, the Gram right operand)
+    static constexpr size_t S2_KL = 0;
+    static constexpr size_t S2 = S2_KL + al16(2 * C * PD);
+    static constexpr size_t SP = al16(2 * C * PK);   // P (3-deep) and T (2-deep)
+    static constexpr size_t SA = al16(4 * C * PA);   // A^T (2-deep)
+    static constexpr int PV = DVW + 8;               // bf16 pitch of the V tile
+    static constexpr size_t SV = al16(2 * C * PV);   // V tile (2-deep)
+    static constexpr int VCH = C * DVW / 8 / 64;     // 16-byte V chunks per Gram-wave lane (4)
+
+    static constexpr size_t OFF4 = 0;
+    static constexpr size_t OFF2 = OFF4 + 4 * S4;
+    static constexpr size_t OFFP = OFF2 + 2 * S2;
+    static constexpr size_t OFFT = OFFP + 3 * SP;
+    static constexpr size_t OFFA = OFFT + 2 * SP;
+    static constexpr size_t OFFV = OFFA + 2 * SA;
+    static constexpr size_t LDS = OFFV + 2 * SV;
+
+    static_assert(DVW <= D && D % DVW == 0, "value slab");
+    static_assert(NCB % NSA == 0, "stage-A waves split the channel blocks evenly");
+    static_assert(C * DVW / 8 == 64 * VCH && VCH == 4, "V tile = four 16-byte chunks per Gram-wave lane");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// Raw inputs of one chunk held by a stage-A wave: per item (16-channel
+// block) one token x 4 channels of g, q, k per lane, plus beta for item 0.
+template <int IPW>
+struct RawSet {
+    float4 g[IPW];
+    uint2 q[IPW];
+    uint2 k[IPW];
+    float beta;
+};
+
+// V tile of one chunk held by the Gram wave between its load and its copy
+// into LDS: four 16-byte chunks per lane (named registers, no array, so the
+// compiler keeps them in VGPRs), written out untouched.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct VRegs {
+    u32x4 a, b, c, d;
+};
+
+// Broadcast lane 15 of each 16-lane row to the whole row.
+__device__ __forceinline__ float row_bcast15(float x) {
+    // ds_swizzle bit mode inside 32-lane halves: lane' = (lane & 0x10) | 0x0f
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
+}
+
+template <int NCW, int TPW, int NSA>
+__global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
+    typedef WsCfg<NCW, TPW, NSA> Cfg;
+    typedef Elem<bf16_t> E;
+    typedef uint2 Frag;
+    constexpr int D = Cfg::D, C = Cfg::C, NCB = Cfg::NCB, DVW = Cfg::DVW, IPW = Cfg::IPW;
+    constexpr int PD = Cfg::PD, PK = Cfg::PK, PA = Cfg::PA;
+
+    __shared__ __align__(16) char smem[Cfg::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int g4 = lane >> 4;
+    const int l16 = lane & 15;
+
+    const int bid = blockIdx.x;
+    const int z = bid % p.nslab;
+    const int uh = bid / p.nslab;
+    const int h = uh % p.H;
+    const int n = uh / p.H;
+    const int H = p.H;
+    int64_t t_begin, t_end;
+    if (p.cu) {
+        int64_t a = p.cu[n], b = p.cu[n + 1];
+        a = a < 0 ? 0 : (a > p.T_total ? p.T_total : a);
+        b = b < a ? a : (b > p.T_total ? p.T_total : b);
+        t_begin = a;
+        t_end = b;
+    } else {
+        t_begin = (int64_t)n * p.seq_len;
+        t_end = t_begin + p.seq_len;
+    }
+    const int64_t ntok = t_end - t_begin;
+    const int nch = (int)((ntok + C - 1) / C);
+    const int64_t sbase = ((int64_t)n * H + h) * D * D;
+
+    const bf16_t* gq = static_cast<const bf16_t*>(p.q);
+    const bf16_t* gk = static_cast<const bf16_t*>(p.k);
+    const bf16_t* gv = static_cast<const bf16_t*>(p.v);
+    bf16_t* go = static_cast<bf16_t*>(p.o);
+
+    auto slot4 = [&](int c) { return smem + Cfg::OFF4 + (size_t)(c & 3) * Cfg::S4; };
+    auto slot2 = [&](int c) { return smem + Cfg::OFF2 + (size_t)(c & 1) * Cfg::S2; };
+    auto slotP = [&](int c) { return smem + Cfg::OFFP + (size_t)(c % 3) * Cfg::SP; };
+    auto slotT = [&](int c) { return smem + Cfg::OFFT + (size_t)(c & 1) * Cfg::SP; };
+    auto slotA = [&](int c) { return smem + Cfg::OFFA + (size_t)(c & 1) * Cfg::SA; };
+    auto slotV = [&](int c) { return smem + Cfg::OFFV + (size_t)(c & 1) * Cfg::SV; };
+    // Token row of chunk c, clamped into the sequence (loads never leave it).
+    auto tok_row = [&](int c, int r) -> int64_t {
+        int64_t t = t_begin + (int64_t)c * C + r;
+        return t < t_end ? t : t_end - 1;
+    };
+    // Element offset of token row 0 of chunk c for head h (uniform per wave).
+    auto chunk_base = [&](int c) -> int64_t { return ((t_begin + (int64_t)c * C) * H + h) * D; };
+    auto rows_valid = [&](int c) -> int {
+        const int64_t left = ntok - (int64_t)c * C;
+        return left >= C ? C : (int)left;
+    };
+
+    // ------------------------------------------------------------ role setup
+    const bool is_cons = w < NCW;
+    const bool is_stageA = w >= Cfg::W_A0;
+    const int sa = w - Cfg::W_A0;  // stage-A wave index
+    const int col_base = z * DVW + (is_cons ? w * TPW * 16 : 0);
+
+
+    auto load_raw = [&](int c, RawSet<IPW>& R) {
+        const int cc = c < nch ? c : nch - 1;
+        const int64_t row = tok_row(cc, l16);
+#pragma unroll
+        for (int it = 0; it < IPW; ++it) {
+            const int cb = sa + NSA * it;
+            const int64_t off = (row * H + h) * D + 16 * cb + 4 * g4;
+            R.g[it] = *reinterpret_cast<const float4*>(p.g + off);
+            R.q[it] = ld_frag(gq + off);
+            R.k[it] = ld_frag(gk + off);
+        }
+        R.beta = p.beta[tok_row(cc, l16) * H + h];
+    };
+    // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / (DVW / 8),
+    // 8 bf16 columns.  Rows past the end reload the last valid row (their
+    // beta is 0).
+    constexpr int VCPR = DVW / 8;
+    auto v_src = [&](int c, int i) -> const u32x4* {
+        const int cc = c < 0 ? 0 : (c < nch ? c : nch - 1);
+        const int nvc = rows_valid(cc);
+        const int idx = lane + 64 * i;
+        const int r = idx / VCPR, ch = idx % VCPR;
+        const int rr = r < nvc ? r : nvc - 1;
+        return reinterpret_cast<const u32x4*>(gv + chunk_base(cc) + z * DVW + (int64_t)rr * H * D + 8 * ch);
+    };
+    auto v_dst = [&](int c, int i) -> u32x4* {
+        const int idx = lane + 64 * i;
+        const int r = idx / VCPR, ch = idx % VCPR;
+        return reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(slotV(c)) + r * Cfg::PV + 8 * ch);
+    };
+    auto load_v = [&](int c, VRegs& V) {
+        V.a = *v_src(c, 0);
+        V.b = *v_src(c, 1);
+        V.c = *v_src(c, 2);
+        V.d = *v_src(c, 3);
+    };
+    auto store_v = [&](int c, const VRegs& V) {
+        *v_dst(c, 0) = V.a;
+        *v_dst(c, 1) = V.b;
+        *v_dst(c, 2) = V.c;
+        *v_dst(c, 3) = V.d;
+    };
+
+    // ------------------------------------------------------------ stage A
+    auto stage_a = [&](int c, const RawSet<IPW>& R) {
+        const int nv = rows_valid(c);
+        const bool ok = l16 < nv;
+        char* s4 = slot4(c);
+        bf16_t* QB = reinterpret_cast<bf16_t*>(s4 + Cfg::S4_QB);
+        bf16_t* KB = reinterpret_cast<bf16_t*>(s4 + Cfg::S4_KB);
+        bf16_t* KLT = reinterpret_cast<bf16_t*>(s4 + Cfg::S4_KT);
+        float* GAM = reinterpret_cast<float*>(s4 + Cfg::S4_GAM);
+        float* BETA = reinterpret_cast<float*>(s4 + Cfg::S4_BETA);
+        bf16_t* KL = reinterpret_cast<bf16_t*>(slot2(c) + Cfg::S2_KL);
+        constexpr float LOG2E = 1.4426950408889634f;
+        // Cumulative log-decay in base-2 units, all items and channels
+        // interleaved so the dependent DPP steps of one scan overlap the others.
+        float L[IPW][4];
+#pragma unroll
+        for (int it = 0; it < IPW; ++it) {
+            L[it][0] = ok ? R.g[it].x * LOG2E : 0.f;
+            L[it][1] = ok ? R.g[it].y * LOG2E : 0.f;
+            L[it][2] = ok ? R.g[it].z * LOG2E : 0.f;
+            L[it][3] = ok ? R.g[it].w * LOG2E : 0.f;
+        }
+#pragma unroll
+        for (int it = 0; it < IPW; ++it)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) L[it][ch] += dpp_row_shr<0x111>(L[it][ch]);
+#pragma unroll
+        for (int it = 0; it < IPW; ++it)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) L[it][ch] += dpp_row_shr<0x112>(L[it][ch]);
+#pragma unroll
+        for (int it = 0; it < IPW; ++it)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) L[it][ch] += dpp_row_shr<0x114>(L[it][ch]);
+#pragma unroll
+        for (int it = 0; it < IPW; ++it)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) L[it][ch] += dpp_row_shr<0x118>(L[it][ch]);
+#pragma unroll
+        for (int it = 0; it < IPW; ++it) {
+            const int c0 = 16 * (sa + NSA * it) + 4 * g4;
+            float e1[4], qb[4], kb[4], kl[4];
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                e1[ch] = __builtin_amdgcn_exp2f(L[it][ch]);         // e^{L_r}  in [e^-80, 1]
+                const float e2 = __builtin_amdgcn_exp2f(-L[it][ch]);  // e^{-L_r} in [1, e^80]
+                const float qv = E::get(R.q[it], ch), kv = E::get(R.k[it], ch);
+                qb[ch] = qv * e1[ch];
+                kb[ch] = kv * e1[ch];
+                kl[ch] = kv * e2;
+            }
+            const Frag klf = E::make(kl[0], kl[1], kl[2], kl[3]);
+            st_frag(QB + l16 * PD + c0, E::make(qb[0], qb[1], qb[2], qb[3]));
+            st_frag(KB + l16 * PD + c0, E::make(kb[0], kb[1], kb[2], kb[3]));
+            st_frag(KL + l16 * PD + c0, klf);
+            uint16_t* klt = reinterpret_cast<uint16_t*>(KLT) + l16;
+            klt[(c0 + 0) * PK] = (uint16_t)(klf.x & 0xffffu);
+            klt[(c0 + 1) * PK] = (uint16_t)(klf.x >> 16);
+            klt[(c0 + 2) * PK] = (uint16_t)(klf.y & 0xffffu);
+            klt[(c0 + 3) * PK] = (uint16_t)(klf.y >> 16);
+            if (l16 == 15)  // e^{L_15} is the decay of the whole chunk
+                *reinterpret_cast<float4*>(GAM + c0) = make_float4(e1[0], e1[1], e1[2], e1[3]);
+        }
+        if (sa == 0 && lane < C) BETA[lane] = ok ? R.beta : 0.f;
+    };
+
+    // ------------------------------------------------------------ Gram tiles
+    auto gram = [&](int c) {
+        char* s4 = slot4(c);
+        const bf16_t* QB = reinterpret_cast<const bf16_t*>(s4 + Cfg::S4_QB);
+        const bf16_t* KB = reinterpret_cast<const bf16_t*>(s4 + Cfg::S4_KB);
+        const float* BETA = reinterpret_cast<const float*>(s4 + Cfg::S4_BETA);
+        const bf16_t* KL = reinterpret_cast<const bf16_t*>(slot2(c) + Cfg::S2_KL);
+        f32x4 accA = zero4(), accP = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NCB; kb += 2) {
+            const int c0 = 16 * kb + 4 * g4;
+            const Frag a0 = ld_frag(KL + l16 * PD + c0), a1 = ld_frag(KL + l16 * PD + c0 + 16);
+            const Frag k0 = ld_frag(KB + l16 * PD + c0), k1 = ld_frag(KB + l16 * PD + c0 + 16);
+            const Frag q0 = ld_frag(QB + l16 * PD + c0), q1 = ld_frag(QB + l16 * PD + c0 + 16);
+            mma32(accA, a0, a1, k0, k1);
+            mma32(accP, a0, a1, q0, q1);
+        }
+        // acc[pp] = M[s = 4 g4 + pp][r = l16] = sum_c KL[s][c] X[r][c]
+        bf16_t* P = reinterpret_cast<bf16_t*>(slotP(c));
+        float* AT = reinterpret_cast<float*>(slotA(c));
+        const int r = l16;
+        f32x4 pv;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? accP[pp] : 0.f;
+        st_frag(P + r * PK + 4 * g4, E::make(pv));
+        const float br = BETA[r];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+            const int s = 4 * g4 + pp;
+            AT[s * PA + r] = (r > s) ? br * accA[pp] : 0.f;  // AT[s][r] = A[r][s]
+        }
+    };
+
+    // ------------------------------------------------------------ solve
+    auto solve = [&](int c) {
+        const float* AT = reinterpret_cast<const float*>(slotA(c));
+        bf16_t* T = reinterpret_cast<bf16_t*>(slotT(c));
+        if (lane < 16) {
+            const int col = lane;
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
+            // Column sweep: once T[s][col] is final, remove its contribution
+            // A[r][s] T[s][col] from every later row r (all independent).  Row
+            // s + 1 of A^T is loaded while step s computes.
+            float4 cur[4], nxt[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cur[q] = reinterpret_cast<const float4*>(AT)[q];
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                if (s + 1 < 15) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) nxt[q] = reinterpret_cast<const float4*>(AT + (s + 1) * PA)[q];
+                }
+                const float av[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z, cur[1].w,
+                                      cur[2].x, cur[2].y, cur[2].z, cur[2].w, cur[3].x, cur[3].y, cur[3].z, cur[3].w};
+                const float ts = x[s];
+#pragma unroll
+                for (int r = s + 1; r < 16; ++r) x[r] -= av[r] * ts;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+            }
+            uint16_t* tcol = reinterpret_cast<uint16_t*>(T) + col;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const uint32_t pr = pack_bf16x2(x[r], x[r + 1]);
+                tcol[r * PK] = (uint16_t)(pr & 0xffffu);
+                tcol[(r + 1) * PK] = (uint16_t)(pr >> 16);
+            }
+        }
+    };
+
+    // ------------------------------------------------------------ consumers
+    auto consume = [&](int c, f32x4 (&Sm)[TPW][NCB]) {
+        const int nv = rows_valid(c);
+        char* s4 = slot4(c);
+        const bf16_t* QB = reinterpret_cast<const bf16_t*>(s4 + Cfg::S4_QB);
+        const bf16_t* KB = reinterpret_cast<const bf16_t*>(s4 + Cfg::S4_KB);
+        const bf16_t* KT = reinterpret_cast<const bf16_t*>(s4 + Cfg::S4_KT);
+        const float* GAM = reinterpret_cast<const float*>(s4 + Cfg::S4_GAM);
+        const float* BETA = reinterpret_cast<const float*>(s4 + Cfg::S4_BETA);
+        const bf16_t* P = reinterpret_cast<const bf16_t*>(slotP(c));
+        const bf16_t* T = reinterpret_cast<const bf16_t*>(slotT(c));
+        uint16_t* ob = reinterpret_cast<uint16_t*>(go) + chunk_base(c) + col_base + l16;
+        const uint16_t* sv = reinterpret_cast<const uint16_t*>(slotV(c)) + (col_base - z * DVW) + l16;
+
+        Frag Sop[TPW][NCB];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int ct = 0; ct < NCB; ++ct) Sop[t][ct] = E::make(Sm[t][ct]);
+        f32x4 X[TPW], QS[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            X[t] = zero4();
+            QS[t] = zero4();
+        }
+#pragma unroll
+        for (int kb = 0; kb < NCB; kb += 2) {
+            const Frag k0 = ld_frag(KB + l16 * PD + 16 * kb + 4 * g4);
+            const Frag k1 = ld_frag(KB + l16 * PD + 16 * (kb + 1) + 4 * g4);
+            const Frag q0 = ld_frag(QB + l16 * PD + 16 * kb + 4 * g4);
+            const Frag q1 = ld_frag(QB + l16 * PD + 16 * (kb + 1) + 4 * g4);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                mma32(X[t], k0, k1, Sop[t][kb], Sop[t][kb + 1]);
+                mma32(QS[t], q0, q1, Sop[t][kb], Sop[t][kb + 1]);
+            }
+        }
+        const Frag Tf = ld_frag(T + l16 * PK + 4 * g4);
+        const Frag Pf = ld_frag(P + l16 * PK + 4 * g4);
+        const float4 b4 = *reinterpret_cast<const float4*>(BETA + 4 * g4);
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        Frag Uf[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            f32x4 Z;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                Z[pp] = bb[pp] * (bf16_to_f32(sv[(4 * g4 + pp) * Cfg::PV + 16 * t]) - X[t][pp]);
+            }
+            f32x4 U = zero4();
+            mma16(U, Tf, E::make(Z));
+            Uf[t] = E::make(U);
+            f32x4 O = QS[t];
+            mma16(O, Pf, Uf[t]);
+            const uint32_t o01 = pack_bf16x2(p.scale * O[0], p.scale * O[1]);
+            const uint32_t o23 = pack_bf16x2(p.scale * O[2], p.scale * O[3]);
+            const uint16_t ov[4] = {(uint16_t)(o01 & 0xffffu), (uint16_t)(o01 >> 16), (uint16_t)(o23 & 0xffffu),
+                                    (uint16_t)(o23 >> 16)};
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int row = 4 * g4 + pp;
+                if (row < nv) ob[row * H * D + 16 * t] = ov[pp];
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct) {
+            const Frag a = ld_frag(KT + (16 * ct + l16) * PK + 4 * g4);
+            const float4 gm = *reinterpret_cast<const float4*>(GAM + 16 * ct + 4 * g4);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                f32x4 acc = Sm[t][ct];
+                mma16(acc, a, Uf[t]);  // S + KL^T U
+                acc[0] *= gm.x;        // then the chunk decay, per key channel
+                acc[1] *= gm.y;
+                acc[2] *= gm.z;
+                acc[3] *= gm.w;
+                Sm[t][ct] = acc;
+            }
+        }
+    };
+
+    // ------------------------------------------------------------ pipeline
+    // Iteration j works on: stage A chunk j, Gram chunk j-1, solve chunk j-2,
+    // consumers chunk j-3, and ends with the workgroup barrier.  Each role
+    // runs its own copy of the loop (the role is uniform per wave and every
+    // copy passes the same number of barriers), so the register live ranges
+    // of different roles never overlap.  The stage-A and consumer loops are
+    // unrolled twice so their two prefetch register sets have fixed names.
+    if (nch > 0) {
+        const int iters = nch + 3;
+        if (is_stageA) {
+            RawSet<IPW> rawA, rawB;
+            load_raw(0, rawA);
+            for (int j = 0; j < iters; j += 2) {
+                load_raw(j + 1, rawB);  // inputs of chunk j + 1 arrive during iteration j
+                if (j < nch) stage_a(j, rawA);
+                __syncthreads();
+                if (j + 1 < iters) {
+                    load_raw(j + 2, rawA);
+                    if (j + 1 < nch) stage_a(j + 1, rawB);
+                    __syncthreads();
+                }
+            }
+        } else if (w == Cfg::W_GRAM) {
+            // This wave also moves V: chunk c is loaded into registers in
+            // iteration c + 1, copied verbatim into V slot (c & 1) in
+            // iteration c + 2 and read by the consumers in iteration c + 3;
+            // the slot is next written (chunk c + 2) in iteration c + 4.
+            // Only a memory instruction touches the loaded registers, so the
+            // copy cannot be hoisted above the barrier that follows the load.
+            VRegs va, vb;
+            for (int j = 0; j < iters; j += 2) {
+                load_v(j - 1, vb);
+                if (j - 2 >= 0 && j - 2 < nch) store_v(j - 2, va);
+                if (j - 1 >= 0 && j - 1 < nch) gram(j - 1);
+                __syncthreads();
+                if (j + 1 < iters) {
+                    load_v(j, va);
+                    if (j - 1 >= 0 && j - 1 < nch) store_v(j - 1, vb);
+                    if (j < nch) gram(j);
+                    __syncthreads();
+                }
+            }
+        } else if (w == Cfg::W_SOLVE) {
+            for (int j = 0; j < iters; ++j) {
+                if (j - 2 >= 0 && j - 2 < nch) solve(j - 2);
+                __syncthreads();
+            }
+        } else {
+            // Consumer state: Sm[t][ct][pp] = S[16 ct + 4 g4 + pp][col_base + 16 t + l16]
+            f32x4 Sm[TPW][NCB];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp)
+                        Sm[t][ct][pp] =
+                            p.S0 ? p.S0[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + 16 * t + l16] : 0.f;
+            for (int j = 0; j < iters; ++j) {
+                if (j - 3 >= 0) consume(j - 3, Sm);
+                __syncthreads();
+            }
+            if (p.Sout) {
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp)
+                            p.Sout[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + 16 * t + l16] =
+                                Sm[t][ct][pp];
+            }
+        }
+    } else if (is_cons && p.Sout) {
+        // empty sequence: the final state is the initial state
+        for (int t = 0; t < TPW; ++t)
+            for (int ct = 0; ct < NCB; ++ct)
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int64_t off = sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + 16 * t + l16;
+                    p.Sout[off] = p.S0 ? p.S0[off] : 0.f;
+                }
+    }
+}
+
+template <int NCW, int TPW, int NSA>
+hipError_t launch_prefill_ws(const PrefillParams& p, hipStream_t s) {
+    const int64_t blocks = (int64_t)p.N * p.H * p.nslab;
+    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA>), dim3((unsigned)blocks),
+                       dim3(64 * (NCW + 2 + NSA)), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -80,12 +80,13 @@ def test_single_head_fp32_workload(kda):
     _check_all(kda, None, inp, chunk=16, label="single_head_fp32 T=64 d=16 C=16")
 
 
-def test_multi_head_bf16_workload(kda):
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_multi_head_bf16_workload(kda, chunk):
     from linear_attention_recurrence_delta_amd import synth
     w = synth.workload_inputs("multi_head_bf16", DEV)
     inp = dict(q=w["q"], k=w["k"], v=w["v"], g=w["g"], beta=w["beta"], S0=w["S0"], lengths=w["lengths"],
                cu_list=[0, w["T"]])
-    _check_all(kda, None, inp, chunk=64, label="multi_head_bf16 T=4096 H=8 C=64 S0~N(0,.02)")
+    _check_all(kda, None, inp, chunk=chunk, label="multi_head_bf16 T=4096 H=8 C=%d S0~N(0,.02)" % chunk)
 
 
 # ---------------------------------------------------------------- fp32 path
@@ -126,7 +127,8 @@ def test_g_at_lower_bound(kda):
     # of the range the sub-tile factorisation is built for.
     inp = _inputs(300, 2, 128, torch.bfloat16, 500, init_std=0.05)
     inp["g"].fill_(-5.0)
-    _check_all(kda, None, inp, chunk=64, label="bf16 g=-5")
+    for chunk in (16, 64):
+        _check_all(kda, None, inp, chunk=chunk, label="bf16 g=-5 C=%d" % chunk)
     inp32 = _inputs(300, 1, 32, torch.float32, 501, init_std=0.05)
     inp32["g"].fill_(-5.0)
     _check_all(kda, None, inp32, chunk=64, label="fp32 g=-5")
@@ -202,14 +204,17 @@ def test_run_to_run_bitwise_deterministic(kda):
 
 
 @pytest.mark.parametrize("waves", ["2", "4", "8"])
-def test_value_slab_split_invariance(kda, waves, monkeypatch):
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_value_slab_split_invariance(kda, waves, chunk, monkeypatch):
     # Splitting d_v across workgroups (column separability of the update)
     # must not change a single bit: every column is computed identically.
-    inp = _inputs(700, 2, 128, torch.bfloat16, 1100, init_std=0.05)
+    # The chunk-staged kernel is the one built with several slab widths.
+    inp = _inputs(700, 2, 128, torch.bfloat16, 1100 + chunk, init_std=0.05)
+    monkeypatch.setenv("KDA_PREFILL_KIND", "0")
     monkeypatch.setenv("KDA_PREFILL_WAVES", "8")
-    ref = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    ref = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], chunk_size=chunk)
     monkeypatch.setenv("KDA_PREFILL_WAVES", waves)
-    got = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    got = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], chunk_size=chunk)
     torch.cuda.synchronize()
     assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
 
@@ -224,3 +229,14 @@ def test_dense_batch_layout_matches_packed(kda):
                                inp["S0"])
     torch.cuda.synchronize()
     assert torch.equal(o_p.view(B, T, H, d), o_d) and torch.equal(S_p, S_d)
+
+
+@pytest.mark.parametrize("kind", ["0", "1"])
+def test_bf16_c16_both_kernels(kda, kind, monkeypatch):
+    # C = 16 is built twice: the chunk-staged kernel and the wave-specialised
+    # pipeline (the default).  Both must meet the oracle on ragged varlen
+    # input with an initial state.
+    monkeypatch.setenv("KDA_PREFILL_KIND", kind)
+    lengths = [5, 16, 33, 300, 0, 1000, 47]
+    inp = _inputs(sum(lengths), 4, 128, torch.bfloat16, 1300, lengths=lengths, init_std=0.05)
+    _check_all(kda, None, inp, chunk=16, label="bf16 C=16 kind=%s" % kind)
