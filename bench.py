@@ -209,7 +209,7 @@ def main():
             "roofline": {
                 "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic("kda_prefill_k3_dense_32k"),
-                "kernel": "kda_prefill_kernel (bf16, d=128)", "bytes_per_launch": bytes_launch,
+                "kernel": "kda_prefill_ws_kernel (bf16, d=128, chunk 16)", "bytes_per_launch": bytes_launch,
             },
             "mfma": {
                 "flop_per_launch": flop_launch,
