@@ -9,9 +9,12 @@ for K3 KDA-layer activations.
 One "step" is one prefill of the dense workload (B = 1, T = 32768, H = 96):
 every prefill row of the method (decay cumsum, scaled tiles, Gram tiles,
 triangular solve, WY products, state pass, stores) runs once over the whole
-batch.  The packed-varlen prefill (16 sequences, 32768 tokens) and the decode
-step (256 x 96 states, read once and written once per step) are timed in the
-same run and reported under "prefill_varlen" and "decode".
+batch.  The packed-varlen prefill (16 sequences, 32768 tokens), the
+long-context prefill (one sequence of 1,048,576 tokens, 16 heads) and the
+decode step (256 x 96 states, read once and written once per step, averaged
+over 1000 steps) are timed in the same run and reported under
+"prefill_varlen", "prefill_long_1m" and "decode"; "device_copy" gives the
+bandwidth of a plain device copy as context for the HBM fractions.
 
 Timing: inputs are resident in HBM before the timed region; W untimed
 warm-up steps, then K timed steps bracketed by torch.cuda.synchronize();
@@ -49,18 +52,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest():
+# Sources each measured kernel is compiled from; a counter record is used only
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "kda_prefill_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
+    "kda_prefill_k3_varlen_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
+    "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
+}
+
+
+def kernel_source_digest(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_recurrence_delta_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
+    was taken on the current sources of that kernel; else None."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
@@ -69,7 +80,7 @@ def measured_traffic(kernel):
     except ValueError:
         return None
     ent = rec.get(kernel)
-    if not ent or ent.get("source_digest") != kernel_source_digest():
+    if not ent or ent.get("source_digest") != kernel_source_digest(kernel):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -135,11 +146,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=200, help="decode steps timed after the prefill steps")
+    ap.add_argument("--decode-steps", type=int, default=1000, help="decode steps timed after the prefill steps")
+    ap.add_argument("--long-steps", type=int, default=3,
+                    help="timed runs of the 1M-token, 16-head prefill (0 skips it)")
     ap.add_argument("--chunk", type=int, default=0, help="prefill chunk size (0 = library default)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "long"], default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -225,6 +238,30 @@ def main():
         })
         del o_v, s_v
 
+    # ---------------------------------------------------- long-context prefill
+    if args.only in ("all", "long") and args.long_steps > 0:
+        log("generating long_1m_h16 inputs (T = 1048576, H = 16)")
+        wl = synth.workload_inputs("long_1m_h16", dev)
+        o_l = torch.empty_like(wl["v"])
+        s_l = torch.empty((wl["N"], wl["H"], wl["d"], wl["d"]), dtype=torch.float32, device=dev)
+
+        def run_long():
+            kda.kda_prefill(wl["q"], wl["k"], wl["v"], wl["g"], wl["beta"], None, None, chunk_size=C,
+                            out=o_l, final_state=s_l)
+
+        run_long()
+        long_ms = time_launches(run_long, args.long_steps, stream)
+        l_avg = sum(long_ms) / len(long_ms)
+        l_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * wl["T"] * wl["H"]
+        log("long prefill avg %.3f ms" % l_avg)
+        result["prefill_long_1m"] = {
+            "workload": "long_1m_h16: B=1 T=1048576 H=16 d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state",
+            "tokens_per_s": wl["T"] / (l_avg * 1e-3), "ms": l_avg, "runs": args.long_steps,
+            "hbm_gbs": l_bytes / (l_avg * 1e-3) / 1e9,
+        }
+        del wl, o_l, s_l
+        torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- decode
     if args.only in ("all", "decode"):
         N, H, d = 256, 96, 128
@@ -274,7 +311,16 @@ def main():
                    "global_batch": 1, "seq_len": 32768, "heads": 96, "d_k": 128, "d_v": 128,
                    "chunk": C or 16, "parallelism": "none (1 GPU)"},
     }
-    for key in ("roofline", "mfma", "prefill_varlen", "decode"):
+    # Context: what a plain device-to-device copy reaches on this GPU.
+    src = torch.ones(1 << 29, dtype=torch.float32, device=dev)  # 2 GiB
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_ms = time_launches(lambda: dst.copy_(src), 5, stream)
+    result["device_copy"] = {"bytes_per_copy": 2 * src.numel() * 4,
+                             "gbs": 2 * src.numel() * 4 / (min(copy_ms) * 1e-3) / 1e9,
+                             "note": "best of 5 torch copy_ launches of 2 GiB (read + write bytes)"}
+    del src, dst
+    for key in ("roofline", "mfma", "prefill_varlen", "prefill_long_1m", "decode", "device_copy"):
         if key in result:
             line[key] = result[key]
 

@@ -23,19 +23,28 @@
  *     q, k, v, g, o and the state buffers must be 16-byte aligned (the
  *     kernels use 16-byte vector accesses); beta and cu_seqlens need only
  *     their natural 4-byte alignment.  The caller owns every buffer; the library
- *     allocates no device memory and keeps no mutable global state.
+ *     allocates no device memory and keeps no mutable global state (except
+ *     the one flag word of the KDA_VALIDATE check below).
  *   - Element offsets are 64-bit; token counts up to 2^31 - 1 per call.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous on it; a KDA_OK return means the work was launched.
  *   - Every argument is validated on the host before any HIP call, so an
  *     error return has touched no device memory.  Errors are returned, never
  *     printed or raised; nothing aborts.
- *   - Device-side preconditions, documented and not checked: g in [-5, 0]
- *     (the chunked kernels rely on a 16-token cumulative log-decay >= -80),
- *     beta in [0, 1], finite inputs, and cu_seqlens non-decreasing from 0 to
- *     total_tokens.  A violation changes the numbers, never the memory the
- *     kernels touch: sequence bounds read from cu_seqlens are clamped to
- *     [0, total_tokens] on the device.
+ *   - Device-side preconditions: g in [-5, 0] (the chunked kernels rely on
+ *     a 16-token cumulative log-decay >= -80), beta in [0, 1], finite inputs,
+ *     and cu_seqlens non-decreasing from 0 to total_tokens.  By default they
+ *     are not checked: a violation changes the numbers, never the memory the
+ *     kernels touch (sequence bounds read from cu_seqlens are clamped to
+ *     [0, total_tokens] on the device).  When the environment variable
+ *     KDA_VALIDATE is "1" at the time of a call, kda_prefill and
+ *     kda_decode_step first read g, beta and cu_seqlens on the device, wait
+ *     for the stream, and return KDA_ERR_DOMAIN without launching the
+ *     computation if one of them is violated (NaN in g or beta counts as a
+ *     violation).  That mode blocks the calling thread, cannot be used under
+ *     graph capture, and uses one __device__ flag word per GPU, so two calls
+ *     validating on one GPU at the same time may report each other's
+ *     violation.
  *   - qkv_dtype selects the dtype of q, k, v and o: KDA_DTYPE_BF16 (bf16
  *     storage, bf16 MFMA products with fp32 accumulation, fp32 state) or
  *     KDA_DTYPE_F32 (fp32 throughout, fp32 MFMA).  g, beta and the state are
@@ -65,7 +74,9 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = 3,  /* valid but not built: (dtype, d_k, d_v, chunk)     */
     KDA_ERR_MISALIGNED = 4,   /* a pointer breaks the alignment rule above         */
     KDA_ERR_WORKSPACE = 5,    /* workspace smaller than kda_prefill_workspace_bytes */
-    KDA_ERR_HIP = 6           /* the HIP runtime reported an error at launch       */
+    KDA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch       */
+    KDA_ERR_DOMAIN = 7        /* g, beta or cu_seqlens break the preconditions;    */
+                              /* returned only when KDA_VALIDATE=1                 */
 } kda_status;
 
 /* KDA_ABI_VERSION of the built library. */
@@ -126,7 +137,8 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens,
  *                 workspace query returns 0).
  *
  * Errors: KDA_ERR_NULL_POINTER, KDA_ERR_BAD_SHAPE, KDA_ERR_UNSUPPORTED,
- * KDA_ERR_MISALIGNED, KDA_ERR_WORKSPACE, KDA_ERR_HIP.  N = 0 or T_total = 0
+ * KDA_ERR_MISALIGNED, KDA_ERR_WORKSPACE, KDA_ERR_HIP, and KDA_ERR_DOMAIN
+ * (only under KDA_VALIDATE=1).  N = 0 or T_total = 0
  * with N > 0 is valid: final_state receives the initial state (or zeros).
  */
 kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens,

@@ -16,6 +16,12 @@ using kda::PrefillVariant;
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// KDA_VALIDATE=1 turns on the device-side precondition check (read per call).
+bool validate_enabled() {
+    const char* env = getenv("KDA_VALIDATE");
+    return env && env[0] == '1' && env[1] == '\0';
+}
+
 int default_chunk(int32_t dtype) { (void)dtype; return 16; }
 
 int resolve_chunk(int32_t dtype, int32_t chunk) { return chunk == 0 ? default_chunk(dtype) : chunk; }
@@ -75,6 +81,7 @@ const char* kda_status_string(int32_t s) {
         case KDA_ERR_MISALIGNED: return "KDA_ERR_MISALIGNED: a tensor pointer is not 16-byte aligned (beta, cu_seqlens: 4-byte)";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_prefill_workspace_bytes";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+        case KDA_ERR_DOMAIN: return "KDA_ERR_DOMAIN: g outside [-5, 0], beta outside [0, 1] or malformed cu_seqlens (KDA_VALIDATE=1)";
         default: return "unknown kda_status";
     }
 }
@@ -129,6 +136,15 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads
     if (num_seqs == 0) return KDA_OK;
     if (total_tokens == 0 && !final_state) return KDA_OK;
 
+    if (validate_enabled()) {
+        unsigned int bad = 0;
+        const int64_t n_beta = total_tokens * num_heads;
+        if (kda::check_inputs(g, n_beta * d_k, beta, n_beta, cu_seqlens, num_seqs, total_tokens,
+                              static_cast<hipStream_t>(stream), &bad) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (bad) return KDA_ERR_DOMAIN;
+    }
+
     const int C = resolve_chunk(dtype, chunk_size);
     const int64_t units = (int64_t)num_seqs * num_heads;
     const PrefillVariant* var = pick_variant(dtype, d_k, C, units);
@@ -169,6 +185,14 @@ kda_status kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t d_k, int
     if (beta && !aligned4(beta)) return KDA_ERR_MISALIGNED;
     if (o && (o == q || o == k || o == v || o == g || o == beta || o == state)) return KDA_ERR_BAD_SHAPE;
     if (num_seqs == 0) return KDA_OK;
+    if (validate_enabled()) {
+        unsigned int bad = 0;
+        const int64_t units = (int64_t)num_seqs * num_heads;
+        if (kda::check_inputs(g, units * d_k, beta, units, nullptr, 0, 0, static_cast<hipStream_t>(stream), &bad) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        if (bad) return KDA_ERR_DOMAIN;
+    }
 
     kda::DecodeParams p;
     p.q = q;

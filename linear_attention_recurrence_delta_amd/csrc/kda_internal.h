@@ -53,6 +53,17 @@ struct PrefillVariant {
 const PrefillVariant* prefill_variants_bf16(int* count);
 const PrefillVariant* prefill_variants_f32(int* count);
 
+// Opt-in input check (KDA_VALIDATE=1): violation bits reported by check_inputs.
+enum : unsigned int {
+    KDA_VIOLATION_G = 1u,     // g outside [-5, 0] or NaN
+    KDA_VIOLATION_BETA = 2u,  // beta outside [0, 1] or NaN
+    KDA_VIOLATION_CU = 4u,    // cu_seqlens not 0 = cu[0] <= ... <= cu[N] = total_tokens
+};
+// Reads g [n_g], beta [n_beta] and cu [n_seqs + 1] (cu may be nullptr) on
+// stream s, waits for it, and stores the violation bits in *violation.
+hipError_t check_inputs(const float* g, int64_t n_g, const float* beta, int64_t n_beta, const int32_t* cu,
+                        int32_t n_seqs, int64_t total_tokens, hipStream_t s, unsigned int* violation);
+
 // Decode launchers; return hipErrorInvalidValue for an unsupported D.
 hipError_t launch_decode_bf16(int D, const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_f32(int D, const DecodeParams& p, hipStream_t s);

@@ -48,12 +48,33 @@ def test_binding_declares_every_header_function():
     assert sorted(SIGNATURES) == header_functions()
 
 
+def header_statuses():
+    text = open(HEADER).read()
+    body = re.search(r"typedef enum \{([^}]*)\} kda_status;", text).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    return {int(v): n for n, v in re.findall(r"(KDA_[A-Z_]+)\s*=\s*(\d+)", body)}
+
+
 def test_version_and_status_strings(lib):
     assert lib.kda_abi_version() == 1
-    for s in range(7):
+    statuses = header_statuses()
+    assert sorted(statuses) == list(range(8))
+    for s, name in statuses.items():
         txt = lib.kda_status_string(s).decode()
-        assert txt.startswith("KDA_")
+        assert txt.startswith(name + ":"), (s, txt)
     assert "unknown" in lib.kda_status_string(99).decode()
+
+
+def test_validate_mode_keeps_host_checks_first(lib, monkeypatch):
+    # KDA_VALIDATE=1 adds a device check after the host checks: invalid
+    # arguments still fail on the host, before any HIP call.
+    monkeypatch.setenv("KDA_VALIDATE", "1")
+    v = ctypes.c_void_p
+    assert lib.kda_prefill(1, 64, 2, 128, 128, BF16, 0, 1.0, v(FAKE), v(FAKE), v(FAKE), v(FAKE + 8), v(FAKE),
+                           None, None, v(FAKE * 2), None, None, 0, None) == MISAL
+    assert lib.kda_prefill(1, 64, 2, 128, 128, BF16, 0, 1.0, None, v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                           None, None, v(FAKE * 2), None, None, 0, None) == NULLP
+    assert lib.kda_decode_step(0, 4, 128, 128, BF16, 1.0, None, None, None, None, None, None, None, None) == OK
 
 
 def test_supported_sets(lib):

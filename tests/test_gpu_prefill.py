@@ -100,11 +100,13 @@ def test_fp32_ragged_varlen(kda, d, chunk):
 
 
 # ---------------------------------------------------------------- bf16 path
+@pytest.mark.parametrize("scale", [1.0, 0.0883883])
 @pytest.mark.parametrize("chunk", [16, 32, 64])
-def test_bf16_ragged_varlen(kda, chunk):
+def test_bf16_ragged_varlen(kda, chunk, scale):
+    # scale = 1/sqrt(128) as a readout scale that is not 1
     lengths = [1, 0, 17, 64, 130, 255, 700]
     inp = _inputs(sum(lengths), 3, 128, torch.bfloat16, 200 + chunk, lengths=lengths, init_std=0.05)
-    _check_all(kda, None, inp, chunk=chunk, label="bf16 varlen")
+    _check_all(kda, None, inp, chunk=chunk, scale=scale, label="bf16 varlen scale=%g" % scale)
 
 
 @pytest.mark.parametrize("g_mode", ["mild", "zero"])
@@ -235,8 +237,8 @@ def test_dense_batch_layout_matches_packed(kda):
 def test_bf16_c16_both_kernels(kda, kind, monkeypatch):
     # C = 16 is built twice: the chunk-staged kernel and the wave-specialised
     # pipeline (the default).  Both must meet the oracle on ragged varlen
-    # input with an initial state.
+    # input with an initial state and a readout scale.
     monkeypatch.setenv("KDA_PREFILL_KIND", kind)
     lengths = [5, 16, 33, 300, 0, 1000, 47]
     inp = _inputs(sum(lengths), 4, 128, torch.bfloat16, 1300, lengths=lengths, init_std=0.05)
-    _check_all(kda, None, inp, chunk=16, label="bf16 C=16 kind=%s" % kind)
+    _check_all(kda, None, inp, chunk=16, scale=0.5, label="bf16 C=16 kind=%s scale=0.5" % kind)
