@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "kda.h"
 #include "kda_internal.h"
 
@@ -33,27 +35,47 @@ const PrefillVariant* variants(int32_t dtype, int* count) {
     return nullptr;
 }
 
-// Column waves per workgroup.  Fewer waves per (sequence, head) means more
-// workgroups (d_v slabs), which fills more compute units when there are few
-// (sequence, head) recurrences but repeats the d_k-side work per slab; more
-// waves share that work among more value columns.  KDA_PREFILL_WAVES (an
-// integer) overrides the choice; results are bitwise identical either way.
+// Compute units of the current device, queried once per device.
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// Value columns per workgroup, in 16-column waves.  Fewer columns per
+// (sequence, head) means more workgroups (d_v slabs): that fills more compute
+// units when there are few (sequence, head) recurrences, and each workgroup's
+// serial chain of chunks gets shorter, but every slab repeats the d_k-side
+// work (decay, Gram, solve).  The chunk-staged kernel keeps whole heads (8
+// waves, fastest on MI355X for the K3 shapes at every batch size tried).  The
+// pipelined kernel halves the slab while the grid still fits in one pass over
+// the compute units (96 heads -> 2 slabs, 16 heads -> 8).  KDA_PREFILL_WAVES
+// (an integer) overrides the choice and KDA_PREFILL_KIND the kernel; results
+// are bitwise identical across slab widths.
 const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units) {
-    (void)units;
     int count = 0;
     const PrefillVariant* tab = variants(dtype, &count);
-    int want = 8;  // measured fastest on MI355X for the K3 shapes at every batch size tried
+    int want_kind = 1;  // the wave-specialised pipeline where it is built
+    if (const char* env = getenv("KDA_PREFILL_KIND")) want_kind = atoi(env);
+    bool have_kind = false;
+    for (int i = 0; i < count; ++i)
+        if (tab[i].D == D && tab[i].C == C && tab[i].kind == want_kind) have_kind = true;
+    int want = D / 16;
+    if (have_kind && want_kind == 1) {
+        const int64_t cus = device_cu_count();
+        while (want > 1 && units * (D / (16 * want)) * 2 <= cus) want /= 2;
+    }
     if (const char* env = getenv("KDA_PREFILL_WAVES")) {
         const int e = atoi(env);
         if (e > 0) want = e;
     }
-    int want_kind = 1;  // the wave-specialised pipeline where it is built
-    if (const char* env = getenv("KDA_PREFILL_KIND")) want_kind = atoi(env);
     // Among (D, C) matches: the wanted kind if built; then the largest wave
     // count not above the wanted one, else the smallest built.
-    bool have_kind = false;
-    for (int i = 0; i < count; ++i)
-        if (tab[i].D == D && tab[i].C == C && tab[i].kind == want_kind) have_kind = true;
     const PrefillVariant* best = nullptr;
     const PrefillVariant* smallest = nullptr;
     for (int i = 0; i < count; ++i) {
@@ -65,7 +87,6 @@ const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t 
     }
     return best ? best : smallest;
 }
-
 }  // namespace
 
 extern "C" {
@@ -150,7 +171,7 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads
     const PrefillVariant* var = pick_variant(dtype, d_k, C, units);
     if (!var) return KDA_ERR_UNSUPPORTED;
     const int nslab = d_v / (16 * var->nwc);
-    if (units * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if ((units + 7) / 8 * 8 * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // padded grid
 
     kda::PrefillParams p;
     p.q = q;

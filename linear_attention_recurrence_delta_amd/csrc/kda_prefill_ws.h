@@ -46,6 +46,8 @@
 // recurrent update sequential?").
 #pragma once
 
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -83,7 +85,9 @@ struct WsCfg {
     static constexpr size_t SA = al16(4 * C * PA);   // A^T (2-deep)
     static constexpr int PV = DVW + 8;               // bf16 pitch of the V tile
     static constexpr size_t SV = al16(2 * C * PV);   // V tile (2-deep)
-    static constexpr int VCH = C * DVW / 8 / 64;     // 16-byte V chunks per Gram-wave lane (4)
+    static constexpr int VLB = C * DVW * 2 / 64;     // V tile bytes per Gram-wave lane
+    static constexpr int VCB = VLB >= 16 ? 16 : 8;   // bytes per V chunk (one load)
+    static constexpr int VCH = VLB / VCB;            // V chunks per Gram-wave lane: 4, 2 or 1
 
     static constexpr size_t OFF4 = 0;
     static constexpr size_t OFF2 = OFF4 + 4 * S4;
@@ -95,7 +99,7 @@ struct WsCfg {
 
     static_assert(DVW <= D && D % DVW == 0, "value slab");
     static_assert(NCB % NSA == 0, "stage-A waves split the channel blocks evenly");
-    static_assert(C * DVW / 8 == 64 * VCH && VCH == 4, "V tile = four 16-byte chunks per Gram-wave lane");
+    static_assert(VLB == VCB * VCH && (VCH == 1 || VCH == 2 || VCH == 4), "V tile split over the Gram wave");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -110,11 +114,14 @@ struct RawSet {
 };
 
 // V tile of one chunk held by the Gram wave between its load and its copy
-// into LDS: four 16-byte chunks per lane (named registers, no array, so the
-// compiler keeps them in VGPRs), written out untouched.
+// into LDS: up to four chunks of 16 (or 8) bytes per lane, in named
+// registers (no array, so the compiler keeps them in VGPRs), written out
+// untouched.  Only the first VCH members are used.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename T>
 struct VRegs {
-    u32x4 a, b, c, d;
+    T a, b, c, d;
 };
 
 // Broadcast lane 15 of each 16-lane row to the whole row.
@@ -139,9 +146,18 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     const int g4 = lane >> 4;
     const int l16 = lane & 15;
 
+    // XCD-aware block order: the dispatcher deals consecutive workgroups to the
+    // 8 XCDs in turn, so block b runs on XCD b % 8.  All slabs of one (sequence,
+    // head) get the same b % 8 and neighbouring b / 8, so they run on one XCD
+    // at the same pace and the q, k, g and beta they all read come from that
+    // XCD's L2 after the first slab's miss.  The grid is padded to whole groups
+    // of 8 units; padding blocks exit at once.
     const int bid = blockIdx.x;
-    const int z = bid % p.nslab;
-    const int uh = bid / p.nslab;
+    const int xcd = bid & 7;
+    const int rest = bid >> 3;
+    const int z = rest % p.nslab;
+    const int uh = (rest / p.nslab) * 8 + xcd;
+    if (uh >= p.N * p.H) return;
     const int h = uh % p.H;
     const int n = uh / p.H;
     const int H = p.H;
@@ -203,34 +219,40 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         }
         R.beta = p.beta[tok_row(cc, l16) * H + h];
     };
-    // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / (DVW / 8),
-    // 8 bf16 columns.  Rows past the end reload the last valid row (their
-    // beta is 0).
-    constexpr int VCPR = DVW / 8;
-    auto v_src = [&](int c, int i) -> const u32x4* {
+    // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / VCPR,
+    // VCB / 2 bf16 columns.  Rows past the end reload the last valid row
+    // (their beta is 0).
+    typedef typename std::conditional<Cfg::VCB == 16, u32x4, u32x2>::type VChunk;
+    constexpr int VCOL = Cfg::VCB / 2;  // bf16 columns per chunk
+    constexpr int VCPR = DVW / VCOL;    // chunks per row
+    auto v_src = [&](int c, int i) -> const VChunk* {
         const int cc = c < 0 ? 0 : (c < nch ? c : nch - 1);
         const int nvc = rows_valid(cc);
         const int idx = lane + 64 * i;
         const int r = idx / VCPR, ch = idx % VCPR;
         const int rr = r < nvc ? r : nvc - 1;
-        return reinterpret_cast<const u32x4*>(gv + chunk_base(cc) + z * DVW + (int64_t)rr * H * D + 8 * ch);
+        return reinterpret_cast<const VChunk*>(gv + chunk_base(cc) + z * DVW + (int64_t)rr * H * D + VCOL * ch);
     };
-    auto v_dst = [&](int c, int i) -> u32x4* {
+    auto v_dst = [&](int c, int i) -> VChunk* {
         const int idx = lane + 64 * i;
         const int r = idx / VCPR, ch = idx % VCPR;
-        return reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(slotV(c)) + r * Cfg::PV + 8 * ch);
+        return reinterpret_cast<VChunk*>(reinterpret_cast<bf16_t*>(slotV(c)) + r * Cfg::PV + VCOL * ch);
     };
-    auto load_v = [&](int c, VRegs& V) {
+    auto load_v = [&](int c, VRegs<VChunk>& V) {
         V.a = *v_src(c, 0);
-        V.b = *v_src(c, 1);
-        V.c = *v_src(c, 2);
-        V.d = *v_src(c, 3);
+        if constexpr (Cfg::VCH > 1) V.b = *v_src(c, 1);
+        if constexpr (Cfg::VCH > 2) {
+            V.c = *v_src(c, 2);
+            V.d = *v_src(c, 3);
+        }
     };
-    auto store_v = [&](int c, const VRegs& V) {
+    auto store_v = [&](int c, const VRegs<VChunk>& V) {
         *v_dst(c, 0) = V.a;
-        *v_dst(c, 1) = V.b;
-        *v_dst(c, 2) = V.c;
-        *v_dst(c, 3) = V.d;
+        if constexpr (Cfg::VCH > 1) *v_dst(c, 1) = V.b;
+        if constexpr (Cfg::VCH > 2) {
+            *v_dst(c, 2) = V.c;
+            *v_dst(c, 3) = V.d;
+        }
     };
 
     // ------------------------------------------------------------ stage A
@@ -481,7 +503,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             // the slot is next written (chunk c + 2) in iteration c + 4.
             // Only a memory instruction touches the loaded registers, so the
             // copy cannot be hoisted above the barrier that follows the load.
-            VRegs va, vb;
+            VRegs<VChunk> va, vb;
             for (int j = 0; j < iters; j += 2) {
                 load_v(j - 1, vb);
                 if (j - 2 >= 0 && j - 2 < nch) store_v(j - 2, va);
@@ -538,7 +560,8 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 
 template <int NCW, int TPW, int NSA>
 hipError_t launch_prefill_ws(const PrefillParams& p, hipStream_t s) {
-    const int64_t blocks = (int64_t)p.N * p.H * p.nslab;
+    const int64_t units = (int64_t)p.N * p.H;
+    const int64_t blocks = (units + 7) / 8 * 8 * p.nslab;  // whole groups of 8 units
     hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA>), dim3((unsigned)blocks),
                        dim3(64 * (NCW + 2 + NSA)), 0, s, p);
     return hipGetLastError();

@@ -205,14 +205,15 @@ def test_run_to_run_bitwise_deterministic(kda):
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
 
 
-@pytest.mark.parametrize("waves", ["2", "4", "8"])
-@pytest.mark.parametrize("chunk", [16, 32])
-def test_value_slab_split_invariance(kda, waves, chunk, monkeypatch):
+@pytest.mark.parametrize("waves", ["1", "2", "4", "8"])
+@pytest.mark.parametrize("kind,chunk", [("0", 16), ("0", 32), ("1", 16)])
+def test_value_slab_split_invariance(kda, waves, kind, chunk, monkeypatch):
     # Splitting d_v across workgroups (column separability of the update)
     # must not change a single bit: every column is computed identically.
-    # The chunk-staged kernel is the one built with several slab widths.
+    # Both kernels are built with several slab widths (16 * waves columns;
+    # the chunk-staged kernel's narrowest is 32).
     inp = _inputs(700, 2, 128, torch.bfloat16, 1100 + chunk, init_std=0.05)
-    monkeypatch.setenv("KDA_PREFILL_KIND", "0")
+    monkeypatch.setenv("KDA_PREFILL_KIND", kind)
     monkeypatch.setenv("KDA_PREFILL_WAVES", "8")
     ref = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], chunk_size=chunk)
     monkeypatch.setenv("KDA_PREFILL_WAVES", waves)
