@@ -133,6 +133,16 @@ __device__ __forceinline__ float row_inclusive_sum16(float x) {
     return x;
 }
 
+// 0 in a VGPR that the compiler cannot fold.  A wave-uniform LDS base plus
+// this value stays in one VGPR, so a run of reads at constant distances from
+// it is addressed by instruction offsets instead of one copied address
+// register per read.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
 __device__ __forceinline__ f32x4 zero4() {
     f32x4 z = {0.f, 0.f, 0.f, 0.f};
     return z;

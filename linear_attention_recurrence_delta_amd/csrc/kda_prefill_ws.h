@@ -100,6 +100,7 @@ struct WsCfg {
     static_assert(DVW <= D && D % DVW == 0, "value slab");
     static_assert(NCB % NSA == 0, "stage-A waves split the channel blocks evenly");
     static_assert(VLB == VCB * VCH && (VCH == 1 || VCH == 2 || VCH == 4), "V tile split over the Gram wave");
+    static_assert(PA % 4 == 0, "rows of A^T are read as float4");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform by construction
     const int g4 = lane >> 4;
     const int l16 = lane & 15;
 
@@ -206,18 +207,30 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     const int col_base = z * DVW + (is_cons ? w * TPW * 16 : 0);
 
 
+    // Raw q, k, g, beta of chunk c for this stage-A wave: a wave-uniform base
+    // (chunk, head, the wave's first channel block) plus a per-lane byte
+    // offset: token row l16, clamped into the sequence by one min against a
+    // per-chunk limit, and the lane's 4 channels.  Channel blocks of the wave
+    // are a constant distance apart.
+    const uint32_t lrow_q = (uint32_t)l16 * (uint32_t)(H * D) * 2u;  // bytes to row l16, bf16 rows
+    const uint32_t lrow_b = (uint32_t)l16 * (uint32_t)H * 4u;        // bytes to row l16 of beta
     auto load_raw = [&](int c, RawSet<IPW>& R) {
         const int cc = c < nch ? c : nch - 1;
-        const int64_t row = tok_row(cc, l16);
+        const uint32_t last = (uint32_t)(rows_valid(cc) - 1);
+        const uint32_t oq = min(lrow_q, last * (uint32_t)(H * D) * 2u) + 8u * (uint32_t)g4;
+        const uint32_t og = 2u * oq;  // fp32 rows and channels are twice as wide
+        const int64_t base = chunk_base(cc) + 16 * sa;
+        const char* gb = reinterpret_cast<const char*>(p.g + base);
+        const char* qb = reinterpret_cast<const char*>(gq + base);
+        const char* kb = reinterpret_cast<const char*>(gk + base);
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
-            const int cb = sa + NSA * it;
-            const int64_t off = (row * H + h) * D + 16 * cb + 4 * g4;
-            R.g[it] = *reinterpret_cast<const float4*>(p.g + off);
-            R.q[it] = ld_frag(gq + off);
-            R.k[it] = ld_frag(gk + off);
+            R.g[it] = *reinterpret_cast<const float4*>(gb + og + 64 * NSA * it);
+            R.q[it] = *reinterpret_cast<const uint2*>(qb + oq + 32 * NSA * it);
+            R.k[it] = *reinterpret_cast<const uint2*>(kb + oq + 32 * NSA * it);
         }
-        R.beta = p.beta[tok_row(cc, l16) * H + h];
+        const char* bb = reinterpret_cast<const char*>(p.beta + (t_begin + (int64_t)cc * C) * H + h);
+        R.beta = *reinterpret_cast<const float*>(bb + min(lrow_b, last * (uint32_t)H * 4u));
     };
     // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / VCPR,
     // VCB / 2 bf16 columns.  Rows past the end reload the last valid row
@@ -269,13 +282,15 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         constexpr float LOG2E = 1.4426950408889634f;
         // Cumulative log-decay in base-2 units, all items and channels
         // interleaved so the dependent DPP steps of one scan overlap the others.
+        // Rows past the end of the sequence get g = 0 through the same multiply.
+        const float lscale = ok ? LOG2E : 0.f;
         float L[IPW][4];
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
-            L[it][0] = ok ? R.g[it].x * LOG2E : 0.f;
-            L[it][1] = ok ? R.g[it].y * LOG2E : 0.f;
-            L[it][2] = ok ? R.g[it].z * LOG2E : 0.f;
-            L[it][3] = ok ? R.g[it].w * LOG2E : 0.f;
+            L[it][0] = R.g[it].x * lscale;
+            L[it][1] = R.g[it].y * lscale;
+            L[it][2] = R.g[it].z * lscale;
+            L[it][3] = R.g[it].w * lscale;
         }
 #pragma unroll
         for (int it = 0; it < IPW; ++it)
@@ -356,7 +371,9 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 
     // ------------------------------------------------------------ solve
     auto solve = [&](int c) {
-        const float* AT = reinterpret_cast<const float*>(slotA(c));
+        // Rows of A^T are read by all 16 active lanes at once (broadcast),
+        // through one VGPR base and immediate offsets.
+        const float4* AT4 = reinterpret_cast<const float4*>(slotA(c)) + opaque_zero();
         bf16_t* T = reinterpret_cast<bf16_t*>(slotT(c));
         if (lane < 16) {
             const int col = lane;
@@ -368,12 +385,12 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             // s + 1 of A^T is loaded while step s computes.
             float4 cur[4], nxt[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) cur[q] = reinterpret_cast<const float4*>(AT)[q];
+            for (int q = 0; q < 4; ++q) cur[q] = AT4[q];
 #pragma unroll
             for (int s = 0; s < 15; ++s) {
                 if (s + 1 < 15) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) nxt[q] = reinterpret_cast<const float4*>(AT + (s + 1) * PA)[q];
+                    for (int q = 0; q < 4; ++q) nxt[q] = AT4[(s + 1) * (PA / 4) + q];
                 }
                 const float av[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z, cur[1].w,
                                       cur[2].x, cur[2].y, cur[2].z, cur[2].w, cur[3].x, cur[3].y, cur[3].z, cur[3].w};
@@ -407,6 +424,31 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         uint16_t* ob = reinterpret_cast<uint16_t*>(go) + chunk_base(c) + col_base + l16;
         const uint16_t* sv = reinterpret_cast<const uint16_t*>(slotV(c)) + (col_base - z * DVW) + l16;
 
+        // Every LDS operand of this step is requested up front, so their
+        // latency overlaps the state conversion and the X / QS products.
+        Frag kf[NCB], qf[NCB];
+#pragma unroll
+        for (int kb = 0; kb < NCB; ++kb) {
+            kf[kb] = ld_frag(KB + l16 * PD + 16 * kb + 4 * g4);
+            qf[kb] = ld_frag(QB + l16 * PD + 16 * kb + 4 * g4);
+        }
+        const Frag Tf = ld_frag(T + l16 * PK + 4 * g4);
+        const Frag Pf = ld_frag(P + l16 * PK + 4 * g4);
+        const float4 b4 = *reinterpret_cast<const float4*>(BETA + 4 * g4);
+        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        float vv[TPW][4];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) vv[t][pp] = bf16_to_f32(sv[(4 * g4 + pp) * Cfg::PV + 16 * t]);
+        Frag ktf[NCB];
+        float4 gm[NCB];
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct) {
+            ktf[ct] = ld_frag(KT + (16 * ct + l16) * PK + 4 * g4);
+            gm[ct] = *reinterpret_cast<const float4*>(GAM + 16 * ct + 4 * g4);
+        }
+
         Frag Sop[TPW][NCB];
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
@@ -419,58 +461,63 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             QS[t] = zero4();
         }
 #pragma unroll
-        for (int kb = 0; kb < NCB; kb += 2) {
-            const Frag k0 = ld_frag(KB + l16 * PD + 16 * kb + 4 * g4);
-            const Frag k1 = ld_frag(KB + l16 * PD + 16 * (kb + 1) + 4 * g4);
-            const Frag q0 = ld_frag(QB + l16 * PD + 16 * kb + 4 * g4);
-            const Frag q1 = ld_frag(QB + l16 * PD + 16 * (kb + 1) + 4 * g4);
+        for (int kb = 0; kb < NCB; kb += 2)
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
-                mma32(X[t], k0, k1, Sop[t][kb], Sop[t][kb + 1]);
-                mma32(QS[t], q0, q1, Sop[t][kb], Sop[t][kb + 1]);
+                mma32(X[t], kf[kb], kf[kb + 1], Sop[t][kb], Sop[t][kb + 1]);
+                mma32(QS[t], qf[kb], qf[kb + 1], Sop[t][kb], Sop[t][kb + 1]);
             }
-        }
-        const Frag Tf = ld_frag(T + l16 * PK + 4 * g4);
-        const Frag Pf = ld_frag(P + l16 * PK + 4 * g4);
-        const float4 b4 = *reinterpret_cast<const float4*>(BETA + 4 * g4);
-        const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        // U = T diag(beta) (V - X), all tiles side by side.
         Frag Uf[TPW];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             f32x4 Z;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                Z[pp] = bb[pp] * (bf16_to_f32(sv[(4 * g4 + pp) * Cfg::PV + 16 * t]) - X[t][pp]);
-            }
+            for (int pp = 0; pp < 4; ++pp) Z[pp] = bb[pp] * (vv[t][pp] - X[t][pp]);
             f32x4 U = zero4();
             mma16(U, Tf, E::make(Z));
             Uf[t] = E::make(U);
+        }
+        // The state update (the chain into the next step) is issued before the
+        // output path, whose work then fills the products' latency.
+#pragma unroll
+        for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) mma16(Sm[t][ct], ktf[ct], Uf[t]);  // S + KL^T U
+        uint32_t ov[TPW][2];  // bf16 outputs, rows 4 g4 + (0, 1) and (2, 3)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
             f32x4 O = QS[t];
             mma16(O, Pf, Uf[t]);
-            const uint32_t o01 = pack_bf16x2(p.scale * O[0], p.scale * O[1]);
-            const uint32_t o23 = pack_bf16x2(p.scale * O[2], p.scale * O[3]);
-            const uint16_t ov[4] = {(uint16_t)(o01 & 0xffffu), (uint16_t)(o01 >> 16), (uint16_t)(o23 & 0xffffu),
-                                    (uint16_t)(o23 >> 16)};
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const int row = 4 * g4 + pp;
-                if (row < nv) ob[row * H * D + 16 * t] = ov[pp];
-            }
+            ov[t][0] = pack_bf16x2(p.scale * O[0], p.scale * O[1]);
+            ov[t][1] = pack_bf16x2(p.scale * O[2], p.scale * O[3]);
         }
 #pragma unroll
-        for (int ct = 0; ct < NCB; ++ct) {
-            const Frag a = ld_frag(KT + (16 * ct + l16) * PK + 4 * g4);
-            const float4 gm = *reinterpret_cast<const float4*>(GAM + 16 * ct + 4 * g4);
+        for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
-                f32x4 acc = Sm[t][ct];
-                mma16(acc, a, Uf[t]);  // S + KL^T U
-                acc[0] *= gm.x;        // then the chunk decay, per key channel
-                acc[1] *= gm.y;
-                acc[2] *= gm.z;
-                acc[3] *= gm.w;
-                Sm[t][ct] = acc;
+                Sm[t][ct][0] *= gm[ct].x;  // then the chunk decay, per key channel
+                Sm[t][ct][1] *= gm[ct].y;
+                Sm[t][ct][2] *= gm[ct].z;
+                Sm[t][ct][3] *= gm[ct].w;
             }
+        // Every chunk but a sequence's last is full: there the stores need no
+        // per-row mask, and the wave-uniform branch keeps them free of
+        // exec-mask splits that would cut the surrounding code into blocks.
+        if (nv == C) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp)
+                    ob[(4 * g4 + pp) * H * D + 16 * t] = (uint16_t)(ov[t][pp >> 1] >> (16 * (pp & 1)));
+        } else {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int row = 4 * g4 + pp;
+                    if (row < nv) ob[row * H * D + 16 * t] = (uint16_t)(ov[t][pp >> 1] >> (16 * (pp & 1)));
+                }
         }
     };
 
