@@ -182,14 +182,16 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------------- prefill
-    log("generating k3_dense_32k / k3_varlen_32k inputs")
-    wd = synth.workload_inputs("k3_dense_32k", dev)
-    wv = synth.workload_inputs("k3_varlen_32k", dev)
     C = args.chunk or 0
-    o_d = torch.empty_like(wd["v"])
-    s_d = torch.empty((wd["N"], wd["H"], wd["d"], wd["d"]), dtype=torch.float32, device=dev)
-    o_v = torch.empty_like(wv["v"])
-    s_v = torch.empty((wv["N"], wv["H"], wv["d"], wv["d"]), dtype=torch.float32, device=dev)
+    wd = None
+    if args.only in ("all", "prefill"):
+        log("generating k3_dense_32k / k3_varlen_32k inputs")
+        wd = synth.workload_inputs("k3_dense_32k", dev)
+        wv = synth.workload_inputs("k3_varlen_32k", dev)
+        o_d = torch.empty_like(wd["v"])
+        s_d = torch.empty((wd["N"], wd["H"], wd["d"], wd["d"]), dtype=torch.float32, device=dev)
+        o_v = torch.empty_like(wv["v"])
+        s_v = torch.empty((wv["N"], wv["H"], wv["d"], wv["d"]), dtype=torch.float32, device=dev)
 
     def run_dense():
         kda.kda_prefill(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"], None, None, chunk_size=C,
@@ -199,8 +201,8 @@ def main():
         kda.kda_prefill(wv["q"], wv["k"], wv["v"], wv["g"], wv["beta"], None, wv["cu"], chunk_size=C,
                         out=o_v, final_state=s_v)
 
-    token_heads = wd["T"] * wd["H"]
     if args.only in ("all", "prefill"):
+        token_heads = wd["T"] * wd["H"]
         for _ in range(args.warmup):
             run_dense()
             run_varlen()
