@@ -66,8 +66,10 @@ struct WsCfg {
     static constexpr int W_A0 = NCW + 2;             // first stage-A wave
     static constexpr int IPW = NCB / NSA;            // stage-A items (16-channel blocks) per wave
 
-    static constexpr int PD = D + 8;                 // bf16 pitch of [16][D] tiles
-    static constexpr int PK = C + 8;                 // bf16 pitch of KL^T [D][16] and of 16x16 tiles
+    // Row pitches chosen so that the 8-byte fragment accesses of 16 lanes (16
+    // rows, one fragment each) hit 32 distinct banks: 66 and 10 dwords.
+    static constexpr int PD = D + 4;                 // bf16 pitch of [16][D] tiles
+    static constexpr int PK = C + 4;                 // bf16 pitch of KL^T [D][16] and of 16x16 tiles
     static constexpr int PA = 20;                    // fp32 pitch of A^T
 
     static constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
@@ -106,11 +108,12 @@ struct WsCfg {
 
 // Raw inputs of one chunk held by a stage-A wave: per item (16-channel
 // block) one token x 4 channels of g, q, k per lane, plus beta for item 0.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int IPW>
 struct RawSet {
-    float4 g[IPW];
-    uint2 q[IPW];
-    uint2 k[IPW];
+    f32x4 g[IPW];   // 4 channels of g
+    u32x4 qk[IPW];  // 4 bf16 channels of q (words 0, 1) and of k (words 2, 3)
     float beta;
 };
 
@@ -118,8 +121,6 @@ struct RawSet {
 // into LDS: up to four chunks of 16 (or 8) bytes per lane, in named
 // registers (no array, so the compiler keeps them in VGPRs), written out
 // untouched.  Only the first VCH members are used.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <typename T>
 struct VRegs {
     T a, b, c, d;
@@ -225,9 +226,10 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         const char* kb = reinterpret_cast<const char*>(gk + base);
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
-            R.g[it] = *reinterpret_cast<const float4*>(gb + og + 64 * NSA * it);
-            R.q[it] = *reinterpret_cast<const uint2*>(qb + oq + 32 * NSA * it);
-            R.k[it] = *reinterpret_cast<const uint2*>(kb + oq + 32 * NSA * it);
+            R.g[it] = *reinterpret_cast<const f32x4*>(gb + og + 64 * NSA * it);
+            const u32x2 qv = *reinterpret_cast<const u32x2*>(qb + oq + 32 * NSA * it);
+            const u32x2 kv = *reinterpret_cast<const u32x2*>(kb + oq + 32 * NSA * it);
+            R.qk[it] = u32x4{qv[0], qv[1], kv[0], kv[1]};
         }
         const char* bb = reinterpret_cast<const char*>(p.beta + (t_begin + (int64_t)cc * C) * H + h);
         R.beta = *reinterpret_cast<const float*>(bb + min(lrow_b, last * (uint32_t)H * 4u));
@@ -287,10 +289,10 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         float L[IPW][4];
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
-            L[it][0] = R.g[it].x * lscale;
-            L[it][1] = R.g[it].y * lscale;
-            L[it][2] = R.g[it].z * lscale;
-            L[it][3] = R.g[it].w * lscale;
+            L[it][0] = R.g[it][0] * lscale;
+            L[it][1] = R.g[it][1] * lscale;
+            L[it][2] = R.g[it][2] * lscale;
+            L[it][3] = R.g[it][3] * lscale;
         }
 #pragma unroll
         for (int it = 0; it < IPW; ++it)
@@ -316,7 +318,9 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             for (int ch = 0; ch < 4; ++ch) {
                 e1[ch] = __builtin_amdgcn_exp2f(L[it][ch]);         // e^{L_r}  in [e^-80, 1]
                 const float e2 = __builtin_amdgcn_exp2f(-L[it][ch]);  // e^{-L_r} in [1, e^80]
-                const float qv = E::get(R.q[it], ch), kv = E::get(R.k[it], ch);
+                const uint32_t qw = R.qk[it][ch >> 1], kw = R.qk[it][2 + (ch >> 1)];
+                const float qv = __uint_as_float((ch & 1) ? (qw & 0xffff0000u) : (qw << 16));
+                const float kv = __uint_as_float((ch & 1) ? (kw & 0xffff0000u) : (kw << 16));
                 qb[ch] = qv * e1[ch];
                 kb[ch] = kv * e1[ch];
                 kl[ch] = kv * e2;
