@@ -31,14 +31,15 @@
 // Iteration m ends with the only barrier.  LDS slots rotate with the chunk
 // index: QB/KB/KL^T/gamma/beta live 4 iterations, P 3, KL, A, T and V 2, so no
 // slot is written while another wave still reads it.  Raw q/k/g/beta are
-// prefetched one iteration ahead into the stage-A waves' registers; the V
+// requested two iterations ahead by the stage-A waves and parked in a
+// lane-private LDS slot for the last of them; the V
 // tile travels through the Gram wave's registers into a 2-deep LDS slot; the loop body is unrolled
 // twice so both register sets have fixed names, and every load is issued
-// unconditionally (rows clamped into the sequence) so the compiler's counted
-// waits never collapse to a full drain.  Rows past the end of a sequence keep
-// the clamped (finite) q, k, v but get g = 0 and beta = 0: then their A rows,
-// Y rows and hence U rows are zero, they change neither the state nor the
-// earlier rows, and their outputs are not stored.
+// unconditionally (buffer loads, rows past the end of the tensor read as 0)
+// so the compiler's counted waits never collapse to a full drain.  Rows past
+// the end of a sequence hold other (finite) tokens or zeros but get g = 0 and
+// beta = 0: then their A rows, Y rows and hence U rows are zero, they change
+// neither the state nor the earlier rows, and their outputs are not stored.
 //
 // Sources for what is computed: as in kda_prefill_impl.h ("Understanding Kimi
 // K3's attention" state-update / readout / g_min equations; "Inside Kimi K3",
@@ -96,8 +97,13 @@ struct WsCfg {
     static constexpr size_t OFFP = OFF2 + 2 * S2;
     static constexpr size_t OFFT = OFFP + 3 * SP;
     static constexpr size_t OFFA = OFFT + 2 * SP;
+    // Raw inputs parked by the stage-A waves, lane-private, component-major:
+    // per wave and item 64 lanes x 16 B of g and 64 x 16 B of q|k, then beta.
+    static constexpr size_t RW = (size_t)IPW * 2 * 64 * 16 + 64 * 4;  // bytes per wave
+    static constexpr size_t SR = NSA * RW;                              // one chunk
     static constexpr size_t OFFV = OFFA + 2 * SA;
-    static constexpr size_t LDS = OFFV + 2 * SV;
+    static constexpr size_t OFFR = OFFV + 2 * SV;
+    static constexpr size_t LDS = OFFR + 2 * SR;
 
     static_assert(DVW <= D && D % DVW == 0, "value slab");
     static_assert(NCB % NSA == 0, "stage-A waves split the channel blocks evenly");
@@ -107,7 +113,7 @@ struct WsCfg {
 };
 
 // Raw inputs of one chunk held by a stage-A wave: per item (16-channel
-// block) one token x 4 channels of g, q, k per lane, plus beta for item 0.
+// block) one token x 4 channels of g, q, k per lane, plus beta.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int IPW>
@@ -189,11 +195,6 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     auto slotT = [&](int c) { return smem + Cfg::OFFT + (size_t)(c & 1) * Cfg::SP; };
     auto slotA = [&](int c) { return smem + Cfg::OFFA + (size_t)(c & 1) * Cfg::SA; };
     auto slotV = [&](int c) { return smem + Cfg::OFFV + (size_t)(c & 1) * Cfg::SV; };
-    // Token row of chunk c, clamped into the sequence (loads never leave it).
-    auto tok_row = [&](int c, int r) -> int64_t {
-        int64_t t = t_begin + (int64_t)c * C + r;
-        return t < t_end ? t : t_end - 1;
-    };
     // Element offset of token row 0 of chunk c for head h (uniform per wave).
     auto chunk_base = [&](int c) -> int64_t { return ((t_begin + (int64_t)c * C) * H + h) * D; };
     auto rows_valid = [&](int c) -> int {
@@ -208,45 +209,87 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     const int col_base = z * DVW + (is_cons ? w * TPW * 16 : 0);
 
 
-    // Raw q, k, g, beta of chunk c for this stage-A wave: a wave-uniform base
-    // (chunk, head, the wave's first channel block) plus a per-lane byte
-    // offset: token row l16, clamped into the sequence by one min against a
-    // per-chunk limit, and the lane's 4 channels.  Channel blocks of the wave
-    // are a constant distance apart.
-    const uint32_t lrow_q = (uint32_t)l16 * (uint32_t)(H * D) * 2u;  // bytes to row l16, bf16 rows
-    const uint32_t lrow_b = (uint32_t)l16 * (uint32_t)H * 4u;        // bytes to row l16 of beta
+    // Global reads of the per-chunk inputs are buffer loads: a wave-uniform
+    // resource per chunk (base = the chunk's first token row for this head,
+    // size = the bytes left to the end of the tensor) and a per-lane byte
+    // offset that is the same for every chunk.  Rows past the end of a
+    // sequence read the next tokens of the tensor (finite by precondition) or,
+    // past its end, zeros; they are masked (g and beta are zeroed, outputs not
+    // stored).  No per-lane address is recomputed per chunk, so issuing the
+    // next chunk's loads never waits on the registers of loads in flight.
+    const int64_t n_tok_elems = p.T_total * H * D;  // elements of q, k, g (and v)
+    auto rsrc = [](const void* base, int64_t bytes_left) {
+        const int num = bytes_left > 0x7fffffff ? 0x7fffffff : (int)bytes_left;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num, 0x00020000);
+    };
+    // Raw q, k, g, beta of chunk c for this stage-A wave: token row l16 and the
+    // lane's 4 channels of each of the wave's IPW adjacent channel blocks (a
+    // wave reads whole contiguous pieces of each token row).
+    const uint32_t lq = (uint32_t)l16 * (uint32_t)(H * D) * 2u + 8u * (uint32_t)g4;  // q, k bytes
+    const uint32_t lg = 2u * lq;                                                     // g bytes
+    const uint32_t lb = (uint32_t)l16 * (uint32_t)H * 4u;                            // beta bytes
     auto load_raw = [&](int c, RawSet<IPW>& R) {
         const int cc = c < nch ? c : nch - 1;
-        const uint32_t last = (uint32_t)(rows_valid(cc) - 1);
-        const uint32_t oq = min(lrow_q, last * (uint32_t)(H * D) * 2u) + 8u * (uint32_t)g4;
-        const uint32_t og = 2u * oq;  // fp32 rows and channels are twice as wide
-        const int64_t base = chunk_base(cc) + 16 * sa;
-        const char* gb = reinterpret_cast<const char*>(p.g + base);
-        const char* qb = reinterpret_cast<const char*>(gq + base);
-        const char* kb = reinterpret_cast<const char*>(gk + base);
+        const int64_t base = chunk_base(cc) + 16 * IPW * sa;
+        const auto rg = rsrc(p.g + base, (n_tok_elems - base) * 4);
+        const auto rq = rsrc(gq + base, (n_tok_elems - base) * 2);
+        const auto rk = rsrc(gk + base, (n_tok_elems - base) * 2);
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
-            R.g[it] = *reinterpret_cast<const f32x4*>(gb + og + 64 * NSA * it);
-            const u32x2 qv = *reinterpret_cast<const u32x2*>(qb + oq + 32 * NSA * it);
-            const u32x2 kv = *reinterpret_cast<const u32x2*>(kb + oq + 32 * NSA * it);
+            R.g[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, lg + 64 * it, 0, 0));
+            const u32x2 qv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, lq + 32 * it, 0, 0));
+            const u32x2 kv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, lq + 32 * it, 0, 0));
             R.qk[it] = u32x4{qv[0], qv[1], kv[0], kv[1]};
         }
-        const char* bb = reinterpret_cast<const char*>(p.beta + (t_begin + (int64_t)cc * C) * H + h);
-        R.beta = *reinterpret_cast<const float*>(bb + min(lrow_b, last * (uint32_t)H * 4u));
+        // beta only in the wave that stores it (its 16 rows are 16 cache lines)
+        R.beta = 0.f;
+        if (sa == 0) {
+            const int64_t bbase = (t_begin + (int64_t)cc * C) * H + h;
+            const auto rb = rsrc(p.beta + bbase, (p.T_total * H - bbase) * 4);
+            R.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lb, 0, 0));
+        }
     };
+    // Parking slot of chunk c for this stage-A wave (two slots in rotation).
+    auto raw_slot = [&](int c) {
+        return smem + Cfg::OFFR + (size_t)(c & 1) * Cfg::SR + (size_t)sa * Cfg::RW;
+    };
+    auto park_raw = [&](int c, const RawSet<IPW>& R) {
+        char* b = raw_slot(c);
+#pragma unroll
+        for (int it = 0; it < IPW; ++it) {
+            reinterpret_cast<f32x4*>(b + it * 2048)[lane] = R.g[it];
+            reinterpret_cast<u32x4*>(b + it * 2048 + 1024)[lane] = R.qk[it];
+        }
+        reinterpret_cast<float*>(b + IPW * 2048)[lane] = R.beta;
+    };
+    auto fetch_raw = [&](int c, RawSet<IPW>& R) {
+        const char* b = raw_slot(c);
+#pragma unroll
+        for (int it = 0; it < IPW; ++it) {
+            R.g[it] = reinterpret_cast<const f32x4*>(b + it * 2048)[lane];
+            R.qk[it] = reinterpret_cast<const u32x4*>(b + it * 2048 + 1024)[lane];
+        }
+        R.beta = reinterpret_cast<const float*>(b + IPW * 2048)[lane];
+    };
+
     // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / VCPR,
-    // VCB / 2 bf16 columns.  Rows past the end reload the last valid row
-    // (their beta is 0).
+    // VCB / 2 bf16 columns (buffer loads as above; rows past the end of the
+    // sequence have beta = 0).
     typedef typename std::conditional<Cfg::VCB == 16, u32x4, u32x2>::type VChunk;
     constexpr int VCOL = Cfg::VCB / 2;  // bf16 columns per chunk
     constexpr int VCPR = DVW / VCOL;    // chunks per row
-    auto v_src = [&](int c, int i) -> const VChunk* {
-        const int cc = c < 0 ? 0 : (c < nch ? c : nch - 1);
-        const int nvc = rows_valid(cc);
+    auto v_off = [&](int i) -> uint32_t {
         const int idx = lane + 64 * i;
-        const int r = idx / VCPR, ch = idx % VCPR;
-        const int rr = r < nvc ? r : nvc - 1;
-        return reinterpret_cast<const VChunk*>(gv + chunk_base(cc) + z * DVW + (int64_t)rr * H * D + VCOL * ch);
+        return (uint32_t)(idx / VCPR) * (uint32_t)(H * D) * 2u + (uint32_t)(VCOL * (idx % VCPR)) * 2u;
+    };
+    auto v_load = [&](int c, int i) -> VChunk {
+        const int cc = c < 0 ? 0 : (c < nch ? c : nch - 1);
+        const int64_t base = chunk_base(cc) + z * DVW;
+        const auto rv = rsrc(gv + base, (n_tok_elems - base) * 2);
+        if constexpr (Cfg::VCB == 16)
+            return __builtin_bit_cast(VChunk, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off(i), 0, 0));
+        else
+            return __builtin_bit_cast(VChunk, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off(i), 0, 0));
     };
     auto v_dst = [&](int c, int i) -> VChunk* {
         const int idx = lane + 64 * i;
@@ -254,11 +297,11 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         return reinterpret_cast<VChunk*>(reinterpret_cast<bf16_t*>(slotV(c)) + r * Cfg::PV + VCOL * ch);
     };
     auto load_v = [&](int c, VRegs<VChunk>& V) {
-        V.a = *v_src(c, 0);
-        if constexpr (Cfg::VCH > 1) V.b = *v_src(c, 1);
+        V.a = v_load(c, 0);
+        if constexpr (Cfg::VCH > 1) V.b = v_load(c, 1);
         if constexpr (Cfg::VCH > 2) {
-            V.c = *v_src(c, 2);
-            V.d = *v_src(c, 3);
+            V.c = v_load(c, 2);
+            V.d = v_load(c, 3);
         }
     };
     auto store_v = [&](int c, const VRegs<VChunk>& V) {
@@ -312,7 +355,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             for (int ch = 0; ch < 4; ++ch) L[it][ch] += dpp_row_shr<0x118>(L[it][ch]);
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
-            const int c0 = 16 * (sa + NSA * it) + 4 * g4;
+            const int c0 = 16 * (IPW * sa + it) + 4 * g4;
             float e1[4], qb[4], kb[4], kl[4];
 #pragma unroll
             for (int ch = 0; ch < 4; ++ch) {
@@ -535,15 +578,30 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     if (nch > 0) {
         const int iters = nch + 3;
         if (is_stageA) {
-            RawSet<IPW> rawA, rawB;
+            // Iteration j requests chunk j + 2, works on chunk j (read back
+            // from LDS) and parks chunk j + 1, requested one iteration earlier:
+            // each load has almost two iterations to arrive (loaded-memory
+            // latency is about one iteration) while only two register sets are
+            // in flight.
+            RawSet<IPW> rawA, rawB, cur;
             load_raw(0, rawA);
+            load_raw(1, rawB);
+            park_raw(0, rawA);
             for (int j = 0; j < iters; j += 2) {
-                load_raw(j + 1, rawB);  // inputs of chunk j + 1 arrive during iteration j
-                if (j < nch) stage_a(j, rawA);
+                load_raw(j + 2, rawA);
+                if (j < nch) {
+                    fetch_raw(j, cur);
+                    stage_a(j, cur);
+                }
+                park_raw(j + 1, rawB);
                 __syncthreads();
                 if (j + 1 < iters) {
-                    load_raw(j + 2, rawA);
-                    if (j + 1 < nch) stage_a(j + 1, rawB);
+                    load_raw(j + 3, rawB);
+                    if (j + 1 < nch) {
+                        fetch_raw(j + 1, cur);
+                        stage_a(j + 1, cur);
+                    }
+                    park_raw(j + 2, rawA);
                     __syncthreads();
                 }
             }
