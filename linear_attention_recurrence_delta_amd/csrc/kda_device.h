@@ -94,6 +94,13 @@ __device__ __forceinline__ void st_frag(T* p, const typename Elem<T>::frag& f) {
 // ---------------------------------------------------------------------------
 // 16x16 products with fp32 accumulation.
 //   mma16: one K block (16).      mma32: two K blocks (32).
+//
+// An accumulator chain stays within one instruction shape.  A bf16 16x16x16
+// product that takes the result of a 16x16x32 product as its accumulator
+// input a few instructions later read part of it before it was written
+// (some lanes and registers kept the older value): the compiler inserts no
+// wait there, as it does for a chain of one shape.  Products of different
+// shapes go to separate accumulators and are added with VALU.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void mma16(f32x4& acc, const float4& a, const float4& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);

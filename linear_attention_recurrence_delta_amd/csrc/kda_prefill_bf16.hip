@@ -7,10 +7,10 @@ namespace kda {
 
 static const PrefillVariant kBf16Variants[] = {
     // wave-specialised pipeline: 4 consumer waves x 32 columns, 4 stage-A waves
-    {1, 1, 128, 16, 8, WsCfg<4, 2, 4>::LDS, &launch_prefill_ws<4, 2, 4>},
-    {1, 1, 128, 16, 4, WsCfg<2, 2, 4>::LDS, &launch_prefill_ws<2, 2, 4>},
-    {1, 1, 128, 16, 2, WsCfg<1, 2, 4>::LDS, &launch_prefill_ws<1, 2, 4>},
-    {1, 1, 128, 16, 1, WsCfg<1, 1, 4>::LDS, &launch_prefill_ws<1, 1, 4>},
+    {1, 1, 128, 16, 8, WsCfg<4, 2, 8>::LDS, &launch_prefill_ws<4, 2, 8>},
+    {1, 1, 128, 16, 4, WsCfg<2, 2, 8>::LDS, &launch_prefill_ws<2, 2, 8>},
+    {1, 1, 128, 16, 2, WsCfg<1, 2, 8>::LDS, &launch_prefill_ws<1, 2, 8>},
+    {1, 1, 128, 16, 1, WsCfg<1, 1, 8>::LDS, &launch_prefill_ws<1, 1, 8>},
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 8),
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 4),
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 2),

@@ -407,12 +407,15 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
         }
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
-            f32x4 O = QS[i];
-            mma_rowblocks_n<TIn, NS>(O, sP + (16 * i + l16) * PC + 4 * g4, Uf, i + 1);
+            // P U gets its own accumulator: QS comes from 32-deep products,
+            // and an MFMA of another shape does not take it as its
+            // accumulator input straight after it (see kda_device.h).
+            f32x4 PU = zero4();
+            mma_rowblocks_n<TIn, NS>(PU, sP + (16 * i + l16) * PC + 4 * g4, Uf, i + 1);
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int row = 16 * i + 4 * g4 + q4;
-                if (row < nv) go[((t0 + row) * H + h) * D + col0 + l16] = E::from_f32(p.scale * O[q4]);
+                if (row < nv) go[((t0 + row) * H + h) * D + col0 + l16] = E::from_f32(p.scale * (QS[i][q4] + PU[q4]));
             }
         }
 #pragma unroll

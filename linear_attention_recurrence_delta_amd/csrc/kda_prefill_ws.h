@@ -9,7 +9,7 @@
 //   stage A   (NSA waves)  chunk c = m + 3: cumulative log-decay L (DPP row
 //                          scan), scaled tiles QB = q e^L, KB = k e^L,
 //                          KL = k e^{-L} and its transpose, gamma = e^{L_15},
-//                          beta; prefetches the raw inputs of chunk c + 1.
+//                          beta; requests the raw inputs of chunk c + 3.
 //   Gram      (1 wave)     chunk m + 2: P = incl-lower(QB KL^T) and
 //                          A = strict-lower(diag(beta) KB KL^T) on MFMA:
 //                          e^{L_r - L_s} = e^{L_r} e^{-L_s} with
@@ -31,12 +31,15 @@
 // Iteration m ends with the only barrier.  LDS slots rotate with the chunk
 // index: QB/KB/KL^T/gamma/beta live 4 iterations, P 3, KL, A, T and V 2, so no
 // slot is written while another wave still reads it.  Raw q/k/g/beta are
-// requested two iterations ahead by the stage-A waves and parked in a
-// lane-private LDS slot for the last of them; the V
-// tile travels through the Gram wave's registers into a 2-deep LDS slot; the loop body is unrolled
-// twice so both register sets have fixed names, and every load is issued
-// unconditionally (buffer loads, rows past the end of the tensor read as 0)
-// so the compiler's counted waits never collapse to a full drain.  Rows past
+// requested three iterations ahead by the stage-A waves, each wave loading
+// whole cache lines of its share of the chunk; the pieces are assembled
+// row-major in LDS and read back in the compute layout one iteration ahead.
+// The V tile travels through the Gram wave's registers into a 2-deep LDS
+// slot.  The load loops are unrolled twice so both register sets have fixed
+// names, and every load is issued unconditionally (buffer loads, rows past
+// the end of the tensor read as 0) so the compiler's counted waits never
+// collapse to a full drain.  The consumers write each 16-token output tile
+// with one 16-byte store per lane.  Rows past
 // the end of a sequence hold other (finite) tokens or zeros but get g = 0 and
 // beta = 0: then their A rows, Y rows and hence U rows are zero, they change
 // neither the state nor the earlier rows, and their outputs are not stored.
@@ -97,25 +100,45 @@ struct WsCfg {
     static constexpr size_t OFFP = OFF2 + 2 * S2;
     static constexpr size_t OFFT = OFFP + 3 * SP;
     static constexpr size_t OFFA = OFFT + 2 * SP;
-    // Raw inputs parked by the stage-A waves, lane-private, component-major:
-    // per wave and item 64 lanes x 16 B of g and 64 x 16 B of q|k, then beta.
-    static constexpr size_t RW = (size_t)IPW * 2 * 64 * 16 + 64 * 4;  // bytes per wave
-    static constexpr size_t SR = NSA * RW;                              // one chunk
+    // Raw q, k, g, beta of one chunk, row-major, assembled in LDS by the
+    // stage-A waves (2-deep).  A q or k load covers 4 token rows (1056 B of
+    // the tile at pitch PD), a g load 2 rows (1056 B at pitch PG): the same
+    // step, so every parking store has a constant offset.
+    static constexpr int PG = D + 4;                 // fp32 pitch of the raw g tile
+    static constexpr size_t R_Q = 0;
+    static constexpr size_t R_K = R_Q + al16(2 * C * PD);
+    static constexpr size_t R_G = R_K + al16(2 * C * PD);
+    static constexpr size_t R_B = R_G + al16(4 * C * PG);
+    static constexpr size_t SR = R_B + 4 * 64 * NSA;  // beta: 64 floats per stage-A wave
+    static constexpr int RAW_STEP = 4 * 2 * PD;      // LDS bytes per raw load
     static constexpr size_t OFFV = OFFA + 2 * SA;
     static constexpr size_t OFFR = OFFV + 2 * SV;
     static constexpr size_t LDS = OFFR + 2 * SR;
 
     static_assert(DVW <= D && D % DVW == 0, "value slab");
+    static constexpr int LPW = 16 / NSA;             // raw loads per stage-A wave and chunk
+    static_assert(NSA == 4 || NSA == 8, "a stage-A wave's raw loads stay within one of q, k, g");
+    static_assert(2 * 4 * PG == RAW_STEP, "q/k and g raw loads step equally through LDS");
+    static_assert(TPW == 1 || TPW == 2, "a consumer lane stores 4 TPW adjacent outputs");
     static_assert(NCB % NSA == 0, "stage-A waves split the channel blocks evenly");
     static_assert(VLB == VCB * VCH && (VCH == 1 || VCH == 2 || VCH == 4), "V tile split over the Gram wave");
     static_assert(PA % 4 == 0, "rows of A^T are read as float4");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// Raw inputs of one chunk held by a stage-A wave: per item (16-channel
-// block) one token x 4 channels of g, q, k per lane, plus beta.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One stage-A wave's share of a chunk's raw inputs, as loaded: LPW 16-byte
+// pieces of whole token rows per lane (plus beta in wave 0).
+template <int LPW>
+struct LoadSet {
+    u32x4 x[LPW];
+    float beta;
+};
+
+// Raw inputs of one chunk as a stage-A wave computes on them: per item
+// (16-channel block) one token x 4 channels of g, q, k per lane, plus beta.
 template <int IPW>
 struct RawSet {
     f32x4 g[IPW];   // 4 channels of g
@@ -207,6 +230,9 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     const bool is_stageA = w >= Cfg::W_A0;
     const int sa = w - Cfg::W_A0;  // stage-A wave index
     const int col_base = z * DVW + (is_cons ? w * TPW * 16 : 0);
+    // Value column of MFMA column j of consumer tile t, relative to col_base:
+    // the 4 TPW columns a lane's outputs fall on (see consume) are adjacent.
+    auto vcol = [&](int t, int j) { return 4 * TPW * (j >> 2) + 4 * t + (j & 3); };
 
 
     // Global reads of the per-chunk inputs are buffer loads: a wave-uniform
@@ -222,54 +248,64 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         const int num = bytes_left > 0x7fffffff ? 0x7fffffff : (int)bytes_left;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num, 0x00020000);
     };
-    // Raw q, k, g, beta of chunk c for this stage-A wave: token row l16 and the
-    // lane's 4 channels of each of the wave's IPW adjacent channel blocks (a
-    // wave reads whole contiguous pieces of each token row).
-    const uint32_t lq = (uint32_t)l16 * (uint32_t)(H * D) * 2u + 8u * (uint32_t)g4;  // q, k bytes
-    const uint32_t lg = 2u * lq;                                                     // g bytes
-    const uint32_t lb = (uint32_t)l16 * (uint32_t)H * 4u;                            // beta bytes
-    auto load_raw = [&](int c, RawSet<IPW>& R) {
+    // Raw q, k, g, beta of chunk c.  A chunk is 16 loads of 16 B per lane
+    // over whole token rows: units 0-3 the q tile and 4-7 the k tile (4 rows
+    // of 256 B each), units 8-15 the g tile (2 rows of 512 B each).  Stage-A
+    // wave sa issues units LPW sa .. LPW sa + LPW - 1 (all of one tensor) and
+    // wave 0 also beta, so every cache line is requested by exactly one load
+    // instruction.  The pieces are parked row-major in LDS and read back
+    // after a barrier in the layout stage A computes on.
+    constexpr int LPW = Cfg::LPW;
+    const int ld_u0 = sa * LPW;
+    const bool ld_bf16 = ld_u0 < 8;
+    const int ld_lpr = ld_bf16 ? 16 : 32;  // lanes per token row
+    const int ld_row = (ld_bf16 ? 4 * (ld_u0 & 3) : 2 * (ld_u0 - 8)) + lane / ld_lpr;
+    const int ld_es = ld_bf16 ? 2 : 4;    // element bytes
+    const char* ld_base = ld_u0 < 4 ? reinterpret_cast<const char*>(gq)
+                        : ld_u0 < 8 ? reinterpret_cast<const char*>(gk)
+                                    : reinterpret_cast<const char*>(p.g);
+    const uint32_t ld_step = 8u * (uint32_t)(H * D);  // global bytes per load (4 bf16 or 2 fp32 rows)
+    const uint32_t ld_voff = (uint32_t)ld_row * (uint32_t)(H * D) * (uint32_t)ld_es + 16u * (uint32_t)(lane % ld_lpr);
+    // beta bytes; the other waves read out of range (zeros, no memory request)
+    // so that the load and its use stay unconditional
+    const uint32_t lb = sa == 0 ? (uint32_t)l16 * (uint32_t)H * 4u : 0x80000000u;
+    auto load_raw = [&](int c, LoadSet<LPW>& R) {
         const int cc = c < nch ? c : nch - 1;
-        const int64_t base = chunk_base(cc) + 16 * IPW * sa;
-        const auto rg = rsrc(p.g + base, (n_tok_elems - base) * 4);
-        const auto rq = rsrc(gq + base, (n_tok_elems - base) * 2);
-        const auto rk = rsrc(gk + base, (n_tok_elems - base) * 2);
+        const int64_t e0 = chunk_base(cc);
+        const auto r = rsrc(ld_base + e0 * ld_es, (n_tok_elems - e0) * ld_es);
 #pragma unroll
-        for (int it = 0; it < IPW; ++it) {
-            R.g[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, lg + 64 * it, 0, 0));
-            const u32x2 qv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, lq + 32 * it, 0, 0));
-            const u32x2 kv = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, lq + 32 * it, 0, 0));
-            R.qk[it] = u32x4{qv[0], qv[1], kv[0], kv[1]};
-        }
-        // beta only in the wave that stores it (its 16 rows are 16 cache lines)
-        R.beta = 0.f;
-        if (sa == 0) {
-            const int64_t bbase = (t_begin + (int64_t)cc * C) * H + h;
-            const auto rb = rsrc(p.beta + bbase, (p.T_total * H - bbase) * 4);
-            R.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lb, 0, 0));
-        }
+        for (int i = 0; i < LPW; ++i)
+            R.x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ld_voff + i * ld_step, 0, 0));
+        const int64_t bbase = (t_begin + (int64_t)cc * C) * H + h;
+        const auto rb = rsrc(p.beta + bbase, (p.T_total * H - bbase) * 4);
+        R.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lb, 0, 0));
     };
-    // Parking slot of chunk c for this stage-A wave (two slots in rotation).
-    auto raw_slot = [&](int c) {
-        return smem + Cfg::OFFR + (size_t)(c & 1) * Cfg::SR + (size_t)sa * Cfg::RW;
-    };
-    auto park_raw = [&](int c, const RawSet<IPW>& R) {
-        char* b = raw_slot(c);
+    // Raw tile of chunk c (two slots in rotation).
+    auto raw_slot = [&](int c) { return smem + Cfg::OFFR + (size_t)(c & 1) * Cfg::SR; };
+    const uint32_t park_off = (uint32_t)(ld_u0 < 4 ? Cfg::R_Q : ld_u0 < 8 ? Cfg::R_K : Cfg::R_G) +
+                              (uint32_t)ld_row * (uint32_t)(ld_bf16 ? 2 * PD : 4 * Cfg::PG) + 16u * (uint32_t)(lane % ld_lpr);
+    auto park_raw = [&](int c, const LoadSet<LPW>& R) {
+        char* b = raw_slot(c) + park_off;
 #pragma unroll
-        for (int it = 0; it < IPW; ++it) {
-            reinterpret_cast<f32x4*>(b + it * 2048)[lane] = R.g[it];
-            reinterpret_cast<u32x4*>(b + it * 2048 + 1024)[lane] = R.qk[it];
+        for (int i = 0; i < LPW; ++i) {
+            // q/k rows are only 8-byte aligned (pitch PD): two 8-byte halves
+            *reinterpret_cast<u32x2*>(b + i * Cfg::RAW_STEP) = R.x[i].xy;
+            *reinterpret_cast<u32x2*>(b + i * Cfg::RAW_STEP + 8) = R.x[i].zw;
         }
-        reinterpret_cast<float*>(b + IPW * 2048)[lane] = R.beta;
+        reinterpret_cast<float*>(raw_slot(c) + Cfg::R_B)[64 * sa + lane] = R.beta;  // wave 0's rows 0-15 are used
     };
+    // Stage-A layout: token row l16, channels c0..c0+3 of each item.
     auto fetch_raw = [&](int c, RawSet<IPW>& R) {
         const char* b = raw_slot(c);
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
-            R.g[it] = reinterpret_cast<const f32x4*>(b + it * 2048)[lane];
-            R.qk[it] = reinterpret_cast<const u32x4*>(b + it * 2048 + 1024)[lane];
+            const int c0 = 16 * (IPW * sa + it) + 4 * g4;
+            R.g[it] = *reinterpret_cast<const f32x4*>(b + Cfg::R_G + (l16 * Cfg::PG + c0) * 4);
+            const u32x2 qv = *reinterpret_cast<const u32x2*>(b + Cfg::R_Q + (l16 * PD + c0) * 2);
+            const u32x2 kv = *reinterpret_cast<const u32x2*>(b + Cfg::R_K + (l16 * PD + c0) * 2);
+            R.qk[it] = u32x4{qv.x, qv.y, kv.x, kv.y};
         }
-        R.beta = reinterpret_cast<const float*>(b + IPW * 2048)[lane];
+        R.beta = reinterpret_cast<const float*>(b + Cfg::R_B)[l16];
     };
 
     // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / VCPR,
@@ -428,24 +464,30 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
             // Column sweep: once T[s][col] is final, remove its contribution
-            // A[r][s] T[s][col] from every later row r (all independent).  Row
-            // s + 1 of A^T is loaded while step s computes.
-            float4 cur[4], nxt[4];
+            // A[r][s] T[s][col] from every later row r (all independent).
+            // Row s of A^T is requested W steps before step s uses it, and
+            // only its quads that reach past the diagonal (r > s), so the
+            // sweep waits on LDS latency once rather than at every step.
+            constexpr int W = 4;
+            f32x4 row[15][4];  // fully unrolled: named registers
+            auto request = [&](int s) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) cur[q] = AT4[q];
+                for (int q = (s + 1) / 4; q < 4; ++q)
+                    row[s][q] = *reinterpret_cast<const f32x4*>(AT4 + s * (PA / 4) + q);
+            };
+#pragma unroll
+            for (int s = 0; s < W; ++s) request(s);
 #pragma unroll
             for (int s = 0; s < 15; ++s) {
-                if (s + 1 < 15) {
+                if (s + W < 15) request(s + W);
+                // whole quads stay whole: no narrowing into 4-byte reads
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) nxt[q] = AT4[(s + 1) * (PA / 4) + q];
-                }
-                const float av[16] = {cur[0].x, cur[0].y, cur[0].z, cur[0].w, cur[1].x, cur[1].y, cur[1].z, cur[1].w,
-                                      cur[2].x, cur[2].y, cur[2].z, cur[2].w, cur[3].x, cur[3].y, cur[3].z, cur[3].w};
+                for (int q = (s + 1) / 4; q < 4; ++q) asm volatile("" ::"v"(row[s][q]));
                 const float ts = x[s];
 #pragma unroll
-                for (int r = s + 1; r < 16; ++r) x[r] -= av[r] * ts;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
+                for (int r = s + 1; r < 16; ++r) {
+                    x[r] -= row[s][r >> 2][r & 3] * ts;
+                }
             }
             uint16_t* tcol = reinterpret_cast<uint16_t*>(T) + col;
 #pragma unroll
@@ -458,6 +500,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     };
 
     // ------------------------------------------------------------ consumers
+    const uint32_t o_voff = (uint32_t)l16 * (uint32_t)(H * D) * 2u + (uint32_t)(col_base + 4 * TPW * g4) * 2u;
     auto consume = [&](int c, f32x4 (&Sm)[TPW][NCB]) {
         const int nv = rows_valid(c);
         char* s4 = slot4(c);
@@ -468,8 +511,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         const float* BETA = reinterpret_cast<const float*>(s4 + Cfg::S4_BETA);
         const bf16_t* P = reinterpret_cast<const bf16_t*>(slotP(c));
         const bf16_t* T = reinterpret_cast<const bf16_t*>(slotT(c));
-        uint16_t* ob = reinterpret_cast<uint16_t*>(go) + chunk_base(c) + col_base + l16;
-        const uint16_t* sv = reinterpret_cast<const uint16_t*>(slotV(c)) + (col_base - z * DVW) + l16;
+        const uint16_t* sv = reinterpret_cast<const uint16_t*>(slotV(c)) + (col_base - z * DVW) + vcol(0, l16);
 
         // Every LDS operand of this step is requested up front, so their
         // latency overlaps the state conversion and the X / QS products.
@@ -487,7 +529,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) vv[t][pp] = bf16_to_f32(sv[(4 * g4 + pp) * Cfg::PV + 16 * t]);
+            for (int pp = 0; pp < 4; ++pp) vv[t][pp] = bf16_to_f32(sv[(4 * g4 + pp) * Cfg::PV + 4 * t]);
         Frag ktf[NCB];
         float4 gm[NCB];
 #pragma unroll
@@ -501,6 +543,8 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
             for (int ct = 0; ct < NCB; ++ct) Sop[t][ct] = E::make(Sm[t][ct]);
+        // X = Kt S as is (its rows feed U); Qt S transposed, by swapping the
+        // operands, so that the output ends up token-major in the lanes.
         f32x4 X[TPW], QS[TPW];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -512,7 +556,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 mma32(X[t], kf[kb], kf[kb + 1], Sop[t][kb], Sop[t][kb + 1]);
-                mma32(QS[t], qf[kb], qf[kb + 1], Sop[t][kb], Sop[t][kb + 1]);
+                mma32(QS[t], Sop[t][kb], Sop[t][kb + 1], qf[kb], qf[kb + 1]);
             }
         // U = T diag(beta) (V - X), all tiles side by side.
         Frag Uf[TPW];
@@ -531,13 +575,17 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
             for (int t = 0; t < TPW; ++t) mma16(Sm[t][ct], ktf[ct], Uf[t]);  // S + KL^T U
-        uint32_t ov[TPW][2];  // bf16 outputs, rows 4 g4 + (0, 1) and (2, 3)
+        // O^T = (Qt S)^T + U^T P^T: lane (g4, l16) holds token l16 at the
+        // value columns vcol(t, 4 g4 + pp) = 4 TPW g4 + 4 t + pp, adjacent.
+        uint32_t ov[TPW][2];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            f32x4 O = QS[t];
-            mma16(O, Pf, Uf[t]);
-            ov[t][0] = pack_bf16x2(p.scale * O[0], p.scale * O[1]);
-            ov[t][1] = pack_bf16x2(p.scale * O[2], p.scale * O[3]);
+            // (P U)^T in its own accumulator, added to the 32-deep QS
+            // product by VALU (kda_device.h: no SrcC chain across shapes)
+            f32x4 PU = zero4();
+            mma16(PU, Uf[t], Pf);
+            ov[t][0] = pack_bf16x2(p.scale * (QS[t][0] + PU[0]), p.scale * (QS[t][1] + PU[1]));
+            ov[t][1] = pack_bf16x2(p.scale * (QS[t][2] + PU[2]), p.scale * (QS[t][3] + PU[3]));
         }
 #pragma unroll
         for (int ct = 0; ct < NCB; ++ct)
@@ -548,24 +596,15 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                 Sm[t][ct][2] *= gm[ct].z;
                 Sm[t][ct][3] *= gm[ct].w;
             }
-        // Every chunk but a sequence's last is full: there the stores need no
-        // per-row mask, and the wave-uniform branch keeps them free of
-        // exec-mask splits that would cut the surrounding code into blocks.
-        if (nv == C) {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp)
-                    ob[(4 * g4 + pp) * H * D + 16 * t] = (uint16_t)(ov[t][pp >> 1] >> (16 * (pp & 1)));
-        } else {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp) {
-                    const int row = 4 * g4 + pp;
-                    if (row < nv) ob[row * H * D + 16 * t] = (uint16_t)(ov[t][pp >> 1] >> (16 * (pp & 1)));
-                }
-        }
+        // One store per lane; rows past the end of the sequence get an offset
+        // beyond the buffer's range, and buffer stores out of range are dropped.
+        const int64_t e0 = chunk_base(c);
+        const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
+        const uint32_t oo = l16 < nv ? o_voff : 0x80000000u;
+        if constexpr (TPW == 2)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{ov[0][0], ov[0][1]}, ro, oo, 0, 0);
     };
 
     // ------------------------------------------------------------ pipeline
@@ -573,35 +612,40 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     // consumers chunk j-3, and ends with the workgroup barrier.  Each role
     // runs its own copy of the loop (the role is uniform per wave and every
     // copy passes the same number of barriers), so the register live ranges
-    // of different roles never overlap.  The stage-A and consumer loops are
+    // of different roles never overlap.  The stage-A and Gram loops are
     // unrolled twice so their two prefetch register sets have fixed names.
     if (nch > 0) {
         const int iters = nch + 3;
         if (is_stageA) {
-            // Iteration j requests chunk j + 2, works on chunk j (read back
-            // from LDS) and parks chunk j + 1, requested one iteration earlier:
-            // each load has almost two iterations to arrive (loaded-memory
-            // latency is about one iteration) while only two register sets are
-            // in flight.
-            RawSet<IPW> rawA, rawB, cur;
+            // Iteration j requests chunk j + 3, works on chunk j (already in
+            // registers), parks chunk j + 2 (requested one iteration earlier)
+            // and reads back its part of chunk j + 1 (parked one iteration
+            // earlier by all stage-A waves) just before the barrier, so the
+            // LDS latency of that read overlaps the barrier wait.  Chunk c
+            // uses raw slot c & 1 from its parking (iteration c - 2) to its
+            // read (iteration c - 1); chunk c + 2 is parked after the barrier
+            // that ends iteration c - 1.
+            LoadSet<LPW> rawA, rawB;
+            RawSet<IPW> cur;
             load_raw(0, rawA);
             load_raw(1, rawB);
             park_raw(0, rawA);
+            __syncthreads();  // prologue 1: chunk 0 parked
+            load_raw(2, rawA);
+            park_raw(1, rawB);
+            fetch_raw(0, cur);
+            __syncthreads();  // prologue 2: chunk 1 parked, chunk 0 read
             for (int j = 0; j < iters; j += 2) {
-                load_raw(j + 2, rawA);
-                if (j < nch) {
-                    fetch_raw(j, cur);
-                    stage_a(j, cur);
-                }
-                park_raw(j + 1, rawB);
+                load_raw(j + 3, rawB);
+                if (j < nch) stage_a(j, cur);
+                park_raw(j + 2, rawA);
+                fetch_raw(j + 1, cur);
                 __syncthreads();
                 if (j + 1 < iters) {
-                    load_raw(j + 3, rawB);
-                    if (j + 1 < nch) {
-                        fetch_raw(j + 1, cur);
-                        stage_a(j + 1, cur);
-                    }
-                    park_raw(j + 2, rawA);
+                    load_raw(j + 4, rawA);
+                    if (j + 1 < nch) stage_a(j + 1, cur);
+                    park_raw(j + 3, rawB);
+                    fetch_raw(j + 2, cur);
                     __syncthreads();
                 }
             }
@@ -613,6 +657,8 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             // Only a memory instruction touches the loaded registers, so the
             // copy cannot be hoisted above the barrier that follows the load.
             VRegs<VChunk> va, vb;
+            __syncthreads();  // the two prologue barriers of the stage-A waves
+            __syncthreads();
             for (int j = 0; j < iters; j += 2) {
                 load_v(j - 1, vb);
                 if (j - 2 >= 0 && j - 2 < nch) store_v(j - 2, va);
@@ -626,12 +672,14 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                 }
             }
         } else if (w == Cfg::W_SOLVE) {
+            __syncthreads();
+            __syncthreads();
             for (int j = 0; j < iters; ++j) {
                 if (j - 2 >= 0 && j - 2 < nch) solve(j - 2);
                 __syncthreads();
             }
         } else {
-            // Consumer state: Sm[t][ct][pp] = S[16 ct + 4 g4 + pp][col_base + 16 t + l16]
+            // Consumer state: Sm[t][ct][pp] = S[16 ct + 4 g4 + pp][col_base + vcol(t, l16)]
             f32x4 Sm[TPW][NCB];
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
@@ -640,7 +688,9 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 #pragma unroll
                     for (int pp = 0; pp < 4; ++pp)
                         Sm[t][ct][pp] =
-                            p.S0 ? p.S0[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + 16 * t + l16] : 0.f;
+                            p.S0 ? p.S0[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + vcol(t, l16)] : 0.f;
+            __syncthreads();
+            __syncthreads();
             for (int j = 0; j < iters; ++j) {
                 if (j - 3 >= 0) consume(j - 3, Sm);
                 __syncthreads();
@@ -652,7 +702,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                     for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
                         for (int pp = 0; pp < 4; ++pp)
-                            p.Sout[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + 16 * t + l16] =
+                            p.Sout[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + vcol(t, l16)] =
                                 Sm[t][ct][pp];
             }
         }
