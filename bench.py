@@ -85,6 +85,26 @@ def measured_traffic(kernel):
     return ent.get("hbm_bytes_per_launch")
 
 
+def measured_mfma(kernel):
+    """MFMA counters of the committed rocprofv3 summary (same source-digest rule
+    as measured_traffic): executed bf16 MFMA flops per launch (512 per
+    SQ_INSTS_VALU_MFMA_MOPS_BF16) and SQ_VALU_MFMA_BUSY_CYCLES as a fraction of
+    the SIMD-cycles of the launch (GRBM_GUI_ACTIVE is summed over the XCDs)."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        ent = json.load(open(path)).get(kernel)
+    except ValueError:
+        return None
+    if not ent or ent.get("source_digest") != kernel_source_digest(kernel) or "mfma_counters" not in ent:
+        return None
+    c = ent["mfma_counters"]
+    simd_cycles = c["grbm_gui_active"] / c["xcds"] * c["simds"]
+    return {"executed_bf16_flop_per_launch": c["mops_bf16"] * 512.0,
+            "busy_frac_of_simd_cycles": c["busy_cycles"] / simd_cycles}
+
+
 def time_launches(fn, reps, stream):
     """Run fn reps times; return per-launch ms from events on `stream`."""
     import torch
@@ -231,6 +251,7 @@ def main():
                 "achieved_tflops": flop_launch / (d_avg * 1e-3) / 1e12,
                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
                 "frac": flop_launch / (d_avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                "counters": measured_mfma("kda_prefill_k3_dense_32k"),
             },
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
