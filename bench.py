@@ -231,6 +231,17 @@ def main():
         dense_ms = time_launches(run_dense, args.steps, stream)
         wall_s = time.perf_counter() - t0
         varlen_ms = time_launches(run_varlen, args.steps, stream)
+        # the dense workload again with a state checkpoint every 1024 tokens
+        ck_interval = 1024
+        ck_buf = torch.empty((wd["T"] // ck_interval, wd["H"], wd["d"], wd["d"]), dtype=torch.float32, device=dev)
+
+        def run_dense_ck():
+            kda.kda_prefill_checkpointed(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"], None, None,
+                                         checkpoint_interval=ck_interval, chunk_size=C, out=o_d,
+                                         final_state=s_d, checkpoints=ck_buf)
+
+        run_dense_ck()
+        ck_ms = time_launches(run_dense_ck, args.steps, stream)
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)
         log("dense prefill avg %.3f ms (min %.3f), varlen avg %.3f ms, wall %.3f s" %
@@ -252,6 +263,12 @@ def main():
                 "peak_tflops": BF16_MFMA_PEAK_TFLOPS,
                 "frac": flop_launch / (d_avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                 "counters": measured_mfma("kda_prefill_k3_dense_32k"),
+            },
+            "prefill_checkpoints": {
+                "workload": "k3_dense_32k with a state checkpoint every %d tokens (%d per head, %.0f MB)"
+                            % (ck_interval, wd["T"] // ck_interval, ck_buf.numel() * 4 / 1e6),
+                "ms": sum(ck_ms) / len(ck_ms),
+                "overhead_vs_plain": (sum(ck_ms) / len(ck_ms)) / d_avg - 1.0,
             },
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
@@ -343,7 +360,8 @@ def main():
                              "gbs": 2 * src.numel() * 4 / (min(copy_ms) * 1e-3) / 1e9,
                              "note": "best of 5 torch copy_ launches of 2 GiB (read + write bytes)"}
     del src, dst
-    for key in ("roofline", "mfma", "prefill_varlen", "prefill_long_1m", "decode", "device_copy"):
+    for key in ("roofline", "mfma", "prefill_varlen", "prefill_checkpoints", "prefill_long_1m", "decode",
+                "device_copy"):
         if key in result:
             line[key] = result[key]
 

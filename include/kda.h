@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_DTYPE_F32 = 0,
@@ -149,6 +149,51 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens,
                        const float *initial_state, const int32_t *cu_seqlens,
                        void *o, float *final_state,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill_checkpointed -- kda_prefill that also emits the state at every
+ * checkpoint_interval tokens of each sequence, for restoring the KDA state at
+ * a token boundary when a prompt prefix is reused ("Inside Kimi K3",
+ * flozi.net, section "Sequence mixing": prefix caching must restore the
+ * state at a token boundary).  All arguments shared with kda_prefill mean
+ * the same and are validated the same way; in addition:
+ *
+ *   checkpoint_interval  tokens between checkpoints, >= 1 and a multiple of
+ *                        the chunk size in use (chunk_size, or 16 for 0).
+ *   checkpoints          [checkpoint_capacity, H, d_k, d_v] fp32 device
+ *                        buffer, 16-byte aligned, written; may be NULL only
+ *                        when checkpoint_capacity is 0.
+ *   checkpoint_capacity  slots in checkpoints; must be at least
+ *                        floor(total_tokens / checkpoint_interval), which
+ *                        is never less than the number of checkpoints.
+ *
+ * Sequence n (tokens cu[n] .. cu[n+1]-1, length L_n) has floor(L_n /
+ * checkpoint_interval) checkpoints.  Its checkpoint j (0-based) is the state
+ * after its first (j + 1) * checkpoint_interval tokens, starting from its
+ * initial state, and is stored in slot  sum_{m < n} floor(L_m / interval) + j.
+ * Slots past the last checkpoint are not written.  A sequence whose length
+ * is a multiple of the interval has its final state as its last checkpoint.
+ * The buffer must not be an input or output pointer of the call (equal
+ * pointers are rejected with KDA_ERR_BAD_SHAPE).
+ *
+ * Errors as for kda_prefill; KDA_ERR_BAD_SHAPE also for an interval that is
+ * not a positive multiple of the chunk or a capacity below the bound above,
+ * KDA_ERR_NULL_POINTER for a NULL buffer with capacity > 0.
+ */
+kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens,
+                                    int32_t num_heads, int32_t d_k, int32_t d_v,
+                                    int32_t qkv_dtype, int32_t chunk_size,
+                                    float scale, const void *q, const void *k,
+                                    const void *v, const float *g,
+                                    const float *beta,
+                                    const float *initial_state,
+                                    const int32_t *cu_seqlens, void *o,
+                                    float *final_state,
+                                    int32_t checkpoint_interval,
+                                    float *checkpoints,
+                                    int64_t checkpoint_capacity,
+                                    void *workspace, size_t workspace_bytes,
+                                    void *stream);
 
 /*
  * kda_decode_step -- one new token per sequence, state updated in place

@@ -12,6 +12,7 @@ from .kda import (  # noqa: F401
     kda_decode_step,
     kda_decode_supported,
     kda_prefill,
+    kda_prefill_checkpointed,
     kda_prefill_supported,
     kda_prefill_workspace_bytes,
 )

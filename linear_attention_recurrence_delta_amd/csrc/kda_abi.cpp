@@ -89,6 +89,85 @@ const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t 
 }
 }  // namespace
 
+static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                               int32_t d_v, int32_t dtype, int32_t chunk_size, float scale, const void* q,
+                               const void* k, const void* v, const float* g, const float* beta,
+                               const float* initial_state, const int32_t* cu_seqlens, void* o,
+                               float* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                               int32_t ckpt_interval, float* checkpoints, int64_t ckpt_capacity) {
+    if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
+    if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 && total_tokens > 0) return KDA_ERR_BAD_SHAPE;
+    if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
+    if (!kda_prefill_supported(dtype, d_k, d_v, chunk_size)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    const void* ptrs[] = {q, k, v, g, initial_state, o, final_state, workspace, checkpoints};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+    if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return KDA_ERR_MISALIGNED;
+    if (o && (o == q || o == k || o == v || o == g || o == beta)) return KDA_ERR_BAD_SHAPE;
+    // Checkpoints (ckpt_interval 0: none).  The interval is a positive multiple
+    // of the chunk in use; the buffer holds at least floor(T_total / interval)
+    // states, which bounds the sum of floor(length / interval) over sequences.
+    const int C_use = resolve_chunk(dtype, chunk_size);
+    if (ckpt_interval < 0 || ckpt_capacity < 0) return KDA_ERR_BAD_SHAPE;
+    if (ckpt_interval > 0) {
+        if (ckpt_interval % C_use != 0) return KDA_ERR_BAD_SHAPE;
+        if (ckpt_capacity < total_tokens / ckpt_interval) return KDA_ERR_BAD_SHAPE;
+        if (ckpt_capacity > 0 && !checkpoints) return KDA_ERR_NULL_POINTER;
+        if ((int64_t)num_heads * d_k * d_v > INT64_MAX / (ckpt_capacity > 0 ? ckpt_capacity : 1))
+            return KDA_ERR_BAD_SHAPE;
+        const void* ins[] = {q, k, v, g, beta, o, initial_state, final_state};
+        for (const void* ptr : ins)
+            if (checkpoints && ptr == checkpoints) return KDA_ERR_BAD_SHAPE;
+    }
+    const size_t need = kda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+    if (num_seqs == 0) return KDA_OK;
+    if (total_tokens == 0 && !final_state) return KDA_OK;
+
+    if (validate_enabled()) {
+        unsigned int bad = 0;
+        const int64_t n_beta = total_tokens * num_heads;
+        if (kda::check_inputs(g, n_beta * d_k, beta, n_beta, cu_seqlens, num_seqs, total_tokens,
+                              static_cast<hipStream_t>(stream), &bad) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (bad) return KDA_ERR_DOMAIN;
+    }
+
+    const int C = resolve_chunk(dtype, chunk_size);
+    const int64_t units = (int64_t)num_seqs * num_heads;
+    const PrefillVariant* var = pick_variant(dtype, d_k, C, units);
+    if (!var) return KDA_ERR_UNSUPPORTED;
+    const int nslab = d_v / (16 * var->nwc);
+    if ((units + 7) / 8 * 8 * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // padded grid
+
+    kda::PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.S0 = initial_state;
+    p.cu = cu_seqlens;
+    p.o = o;
+    p.Sout = final_state;
+    p.T_total = total_tokens;
+    p.N = num_seqs;
+    p.H = num_heads;
+    p.seq_len = cu_seqlens ? 0 : (int32_t)(total_tokens / num_seqs);
+    p.nslab = nslab;
+    p.scale = scale;
+    p.ckpt = (ckpt_interval > 0 && total_tokens / ckpt_interval > 0) ? checkpoints : nullptr;
+    p.ckpt_cap = ckpt_capacity;
+    p.ckpt_interval = ckpt_interval > 0 ? ckpt_interval : 1;
+    const hipError_t err = var->launch(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+
 extern "C" {
 
 int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
@@ -139,58 +218,22 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads
                        const void* v, const float* g, const float* beta, const float* initial_state,
                        const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
                        size_t workspace_bytes, void* stream) {
-    if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
-    if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return KDA_ERR_UNSUPPORTED;
-    if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-    if (num_seqs == 0 && total_tokens > 0) return KDA_ERR_BAD_SHAPE;
-    if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
-    if (!kda_prefill_supported(dtype, d_k, d_v, chunk_size)) return KDA_ERR_UNSUPPORTED;
-    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, g, initial_state, o, final_state, workspace};
-    for (const void* ptr : ptrs)
-        if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
-    if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return KDA_ERR_MISALIGNED;
-    if (o && (o == q || o == k || o == v || o == g || o == beta)) return KDA_ERR_BAD_SHAPE;
-    const size_t need = kda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    return prefill_impl(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale, q, k, v, g, beta,
+                        initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes, stream, 0, nullptr,
+                        0);
+}
 
-    if (num_seqs == 0) return KDA_OK;
-    if (total_tokens == 0 && !final_state) return KDA_OK;
-
-    if (validate_enabled()) {
-        unsigned int bad = 0;
-        const int64_t n_beta = total_tokens * num_heads;
-        if (kda::check_inputs(g, n_beta * d_k, beta, n_beta, cu_seqlens, num_seqs, total_tokens,
-                              static_cast<hipStream_t>(stream), &bad) != hipSuccess)
-            return KDA_ERR_HIP;
-        if (bad) return KDA_ERR_DOMAIN;
-    }
-
-    const int C = resolve_chunk(dtype, chunk_size);
-    const int64_t units = (int64_t)num_seqs * num_heads;
-    const PrefillVariant* var = pick_variant(dtype, d_k, C, units);
-    if (!var) return KDA_ERR_UNSUPPORTED;
-    const int nslab = d_v / (16 * var->nwc);
-    if ((units + 7) / 8 * 8 * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // padded grid
-
-    kda::PrefillParams p;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.g = g;
-    p.beta = beta;
-    p.S0 = initial_state;
-    p.cu = cu_seqlens;
-    p.o = o;
-    p.Sout = final_state;
-    p.T_total = total_tokens;
-    p.N = num_seqs;
-    p.H = num_heads;
-    p.seq_len = cu_seqlens ? 0 : (int32_t)(total_tokens / num_seqs);
-    p.nslab = nslab;
-    p.scale = scale;
-    const hipError_t err = var->launch(p, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                                    int32_t d_v, int32_t dtype, int32_t chunk_size, float scale, const void* q,
+                                    const void* k, const void* v, const float* g, const float* beta,
+                                    const float* initial_state, const int32_t* cu_seqlens, void* o,
+                                    float* final_state, int32_t checkpoint_interval, float* checkpoints,
+                                    int64_t checkpoint_capacity, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    if (checkpoint_interval < 1) return KDA_ERR_BAD_SHAPE;
+    return prefill_impl(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale, q, k, v, g, beta,
+                        initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes, stream,
+                        checkpoint_interval, checkpoints, checkpoint_capacity);
 }
 
 kda_status kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v, int32_t dtype,

@@ -125,6 +125,14 @@ __device__ __forceinline__ void mma32(f32x4& acc, const uint2& a0, const uint2& 
                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (stride 0; accesses past
+// `bytes` read zeros and drop stores).  Store data taken from an element of an
+// ext-vector goes through __float_as_uint: __builtin_bit_cast of such an
+// element (v[i] as an lvalue) compiled to element 0 for every i.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 // Inclusive prefix sum over the 16 lanes of each DPP row (lanes 16r..16r+15):
 // lane l ends with x[16r] + ... + x[l].  Each step adds the value of the lane
 // n places lower in the row (DPP row_shr:n); lanes with no such lane add 0.

@@ -1,5 +1,6 @@
-// kda_internal.h -- host-side declarations shared by the C-ABI layer and the
-// kernel translation units.  Not part of the public ABI.
+// kda_internal.h -- declarations shared by the C-ABI layer and the kernel
+// translation units (plus two small device helpers over the launch
+// parameters).  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,7 +25,47 @@ struct PrefillParams {
     int32_t seq_len;        // dense sequences: tokens per sequence
     int32_t nslab;          // d_v column slabs per (sequence, head)
     float scale;
+    // State checkpoints (ckpt == nullptr: none).  Checkpoint j of sequence n
+    // is the state after its first (j + 1) * ckpt_interval tokens, stored at
+    // slot ckpt_first_slot(n) + j of [ckpt_cap, H, D, D]; ckpt_interval is a
+    // multiple of the kernel's chunk.
+    float* ckpt;
+    int64_t ckpt_cap;
+    int32_t ckpt_interval;
 };
+
+// Token range [*a, *b) of sequence n, with the bounds read from cu clamped to
+// [0, T_total] and b >= a (malformed offsets change the numbers, never the
+// memory touched).  Every prefill kernel uses these bounds.
+__device__ inline void seq_bounds(const PrefillParams& p, int n, int64_t* a, int64_t* b) {
+    if (p.cu) {
+        int64_t x = p.cu[n], y = p.cu[n + 1];
+        x = x < 0 ? 0 : (x > p.T_total ? p.T_total : x);
+        y = y < x ? x : (y > p.T_total ? p.T_total : y);
+        *a = x;
+        *b = y;
+    } else {
+        *a = (int64_t)n * p.seq_len;
+        *b = *a + p.seq_len;
+    }
+}
+
+// First checkpoint slot of sequence n: the checkpoints of the sequences before
+// it, floor(length / interval) each.  Called by every lane of a wave (the
+// lanes split the sequences, then a butterfly sum); returns the same value in
+// all lanes.
+__device__ inline int64_t ckpt_first_slot(const PrefillParams& p, int n, int lane) {
+    if (!p.cu) return (int64_t)n * (p.seq_len / p.ckpt_interval);
+    int part = 0;  // at most T_total / interval < 2^31
+    for (int m = lane; m < n; m += 64) {
+        int64_t a, b;
+        seq_bounds(p, m, &a, &b);
+        part += (int)((b - a) / p.ckpt_interval);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+    return part;
+}
 
 struct DecodeParams {
     const void* q;

@@ -156,16 +156,7 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
     const int n = uh / p.H;
     const int H = p.H;
     int64_t t_begin, t_end;
-    if (p.cu) {
-        int64_t a = p.cu[n], b = p.cu[n + 1];
-        a = a < 0 ? 0 : (a > p.T_total ? p.T_total : a);  // clamp: every access stays in bounds
-        b = b < a ? a : (b > p.T_total ? p.T_total : b);
-        t_begin = a;
-        t_end = b;
-    } else {
-        t_begin = (int64_t)n * p.seq_len;
-        t_end = t_begin + p.seq_len;
-    }
+    seq_bounds(p, n, &t_begin, &t_end);
     const int col0 = z * DVW + w * 16;  // first value column of this wave
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
 
@@ -175,12 +166,19 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
     TIn* go = static_cast<TIn*>(p.o);
 
     // ---- fp32 master state slice: Sm[ct][pp] = S[16ct + 4g4 + pp][col0 + l16] ----
+    // Buffer accesses: one per-lane offset, rows as wave-uniform offsets;
+    // without an initial state the range is empty and the loads read 0.
+    const uint32_t s_voff = (uint32_t)(4 * g4 * D + col0 + l16) * 4u;
     f32x4 Sm[NKB];
+    {
+        const auto rs = p.S0 ? buffer_rsrc(p.S0 + sbase, D * D * 4) : buffer_rsrc(p.g, 0);
 #pragma unroll
-    for (int ct = 0; ct < NKB; ++ct) {
+        for (int ct = 0; ct < NKB; ++ct) {
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp)
-            Sm[ct][pp] = p.S0 ? p.S0[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col0 + l16] : 0.f;
+            for (int pp = 0; pp < 4; ++pp)
+                Sm[ct][pp] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, (16 * ct + pp) * D * 4, 0));
+        }
     }
 
     // Prologue items: wave-item wi = (sub-tile i, 16-channel block cb); lane
@@ -228,6 +226,7 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
     };
     if (t_begin < t_end) prefetch(t_begin, (t_end - t_begin) < C ? (int)(t_end - t_begin) : C);
 
+    const int ck0 = p.ckpt ? __builtin_amdgcn_readfirstlane((int)ckpt_first_slot(p, n, lane)) : 0;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += C) {
         const int nv = (t_end - t0) < C ? (int)(t_end - t0) : C;
 
@@ -426,15 +425,32 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
             mma_rowblocks<TIn, NS>(acc, sKbT + (16 * ct + l16) * PC + 4 * g4, Uf);
             Sm[ct] = acc;
         }
+        // State checkpoint when the tokens done so far are a whole number of
+        // intervals (the interval is a multiple of C, so only at chunk ends).
+        if (p.ckpt && t0 + C <= t_end && (t0 + C - t_begin) % p.ckpt_interval == 0) {
+            const int64_t slot = (int64_t)ck0 + (t0 + C - t_begin) / p.ckpt_interval - 1;
+            if (slot < p.ckpt_cap) {
+                // one per-lane offset; rows as wave-uniform offsets
+                const auto rc = buffer_rsrc(p.ckpt + (slot * H + h) * D * D, D * D * 4);
+#pragma unroll
+                for (int ct = 0; ct < NKB; ++ct)
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Sm[ct][pp]), rc, s_voff,
+                                                              (16 * ct + pp) * D * 4, 0);
+            }
+        }
         __syncthreads();
     }
 
     if (p.Sout) {
+        const auto rs = buffer_rsrc(p.Sout + sbase, D * D * 4);
 #pragma unroll
         for (int ct = 0; ct < NKB; ++ct) {
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp)
-                p.Sout[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col0 + l16] = Sm[ct][pp];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Sm[ct][pp]), rs, s_voff,
+                                                      (16 * ct + pp) * D * 4, 0);
         }
     }
 }

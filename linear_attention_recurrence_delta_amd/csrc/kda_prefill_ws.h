@@ -193,16 +193,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     const int n = uh / p.H;
     const int H = p.H;
     int64_t t_begin, t_end;
-    if (p.cu) {
-        int64_t a = p.cu[n], b = p.cu[n + 1];
-        a = a < 0 ? 0 : (a > p.T_total ? p.T_total : a);
-        b = b < a ? a : (b > p.T_total ? p.T_total : b);
-        t_begin = a;
-        t_end = b;
-    } else {
-        t_begin = (int64_t)n * p.seq_len;
-        t_end = t_begin + p.seq_len;
-    }
+    seq_bounds(p, n, &t_begin, &t_end);
     const int64_t ntok = t_end - t_begin;
     const int nch = (int)((ntok + C - 1) / C);
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
@@ -680,30 +671,63 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             }
         } else {
             // Consumer state: Sm[t][ct][pp] = S[16 ct + 4 g4 + pp][col_base + vcol(t, l16)]
+            // The state slice moves through buffer accesses: one per-lane
+            // offset (row 4 g4, the lane's column), rows as wave-uniform offsets.
+            // Without an initial state the range is empty and the loads read 0.
+            const uint32_t s_voff = (uint32_t)(4 * g4 * D + col_base + vcol(0, l16)) * 4u;
             f32x4 Sm[TPW][NCB];
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                for (int ct = 0; ct < NCB; ++ct)
-#pragma unroll
-                    for (int pp = 0; pp < 4; ++pp)
-                        Sm[t][ct][pp] =
-                            p.S0 ? p.S0[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + vcol(t, l16)] : 0.f;
-            __syncthreads();
-            __syncthreads();
-            for (int j = 0; j < iters; ++j) {
-                if (j - 3 >= 0) consume(j - 3, Sm);
-                __syncthreads();
-            }
-            if (p.Sout) {
+            {
+                const auto rs = p.S0 ? buffer_rsrc(p.S0 + sbase, D * D * 4) : buffer_rsrc(p.g, 0);
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
 #pragma unroll
                     for (int ct = 0; ct < NCB; ++ct)
 #pragma unroll
                         for (int pp = 0; pp < 4; ++pp)
-                            p.Sout[sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + vcol(t, l16)] =
-                                Sm[t][ct][pp];
+                            Sm[t][ct][pp] = __builtin_bit_cast(
+                                float, __builtin_amdgcn_raw_buffer_load_b32(rs, s_voff + 16 * t, (16 * ct + pp) * D * 4, 0));
+            }
+            // State checkpoints: after chunk c when (c + 1) C tokens of the
+            // sequence are done and that count is a multiple of the interval.
+            // (uniform values kept in scalar registers: the consumer is at its
+            // vector-register limit in the 14-wave workgroup)
+            const int ck0 = p.ckpt ? __builtin_amdgcn_readfirstlane((int)ckpt_first_slot(p, n, lane)) : 0;
+            const int ck_chunks = p.ckpt ? p.ckpt_interval / C : 1;
+            __syncthreads();
+            __syncthreads();
+            for (int j = 0; j < iters; ++j) {
+                if (j - 3 >= 0) {
+                    consume(j - 3, Sm);
+                    const int c = j - 3;
+                    if (p.ckpt && (c + 1) % ck_chunks == 0 && (int64_t)(c + 1) * C <= ntok) {
+                        const int64_t slot = (int64_t)ck0 + (c + 1) / ck_chunks - 1;
+                        if (slot < p.ckpt_cap) {
+                            // one per-lane offset; rows as wave-uniform offsets
+                            const auto rc = buffer_rsrc(p.ckpt + (slot * H + h) * D * D, D * D * 4);
+#pragma unroll
+                            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                                for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                                    for (int pp = 0; pp < 4; ++pp)
+                                        __builtin_amdgcn_raw_buffer_store_b32(
+                                            __float_as_uint(Sm[t][ct][pp]), rc, s_voff + 16 * t,
+                                            (16 * ct + pp) * D * 4, 0);
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+            if (p.Sout) {
+                const auto rs = buffer_rsrc(p.Sout + sbase, D * D * 4);
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Sm[t][ct][pp]), rs,
+                                                                  s_voff + 16 * t, (16 * ct + pp) * D * 4, 0);
             }
         }
     } else if (is_cons && p.Sout) {

@@ -67,17 +67,9 @@ def kda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dty
                                                  _DTYPES.get(dtype, -1), chunk_size))
 
 
-def kda_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_size: int = 0,
-                scale: float = 1.0, output_final_state: bool = True, num_seqs: int | None = None,
-                out=None, final_state=None):
-    """Chunked KDA prefill over a packed batch.
-
-    q, k, g: [T, H, d_k]; v: [T, H, d_v]; beta: [T, H].  A dense batch may be
-    passed as [B, T, H, d] (and beta [B, T, H]); it is the packed layout with
-    B equal-length sequences.  cu_seqlens: int32 device tensor [N + 1] or None.
-    initial_state: fp32 [N, H, d_k, d_v] or None (zeros).
-    Returns (o, final_state); final_state is None if output_final_state is False.
-    """
+def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state):
+    """Shared argument handling of the prefill entry points (shapes, dtypes,
+    output allocation).  Returns a dict of the marshalled arguments."""
     dense_batch = q.dim() == 4
     if dense_batch:
         B = q.shape[0]
@@ -114,17 +106,83 @@ def kda_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_
     if output_final_state:
         fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
         _need(fs, "final_state", torch.float32, 4)
-    dt = _DTYPES[qdt]
-    ws_bytes = int(lib().kda_prefill_workspace_bytes(N, T, H, dk, dv, dt, chunk_size))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
-    with torch.cuda.device(dev):
-        _check(lib().kda_prefill(N, T, H, dk, dv, dt, chunk_size, float(scale),
-                                 _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                 _ptr(initial_state), _ptr(cu_seqlens), _ptr(o), _ptr(fs),
-                                 _ptr(ws), ws_bytes, _stream(dev)))
-    if dense_batch:
-        o = o.view(N, T // max(N, 1), H, dv)
-    return o, fs
+    return dict(dense_batch=dense_batch, q=q, k=k, v=v, g=g, beta=beta, T=T, H=H, dk=dk, dv=dv, N=N, dev=dev,
+                o=o, fs=fs, dt=_DTYPES[qdt])
+
+
+def _workspace(a, chunk_size):
+    ws_bytes = int(lib().kda_prefill_workspace_bytes(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a["dev"]) if ws_bytes else None
+    return ws, ws_bytes
+
+
+def kda_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_size: int = 0,
+                scale: float = 1.0, output_final_state: bool = True, num_seqs: int | None = None,
+                out=None, final_state=None):
+    """Chunked KDA prefill over a packed batch.
+
+    q, k, g: [T, H, d_k]; v: [T, H, d_v]; beta: [T, H].  A dense batch may be
+    passed as [B, T, H, d] (and beta [B, T, H]); it is the packed layout with
+    B equal-length sequences.  cu_seqlens: int32 device tensor [N + 1] or None.
+    initial_state: fp32 [N, H, d_k, d_v] or None (zeros).
+    Returns (o, final_state); final_state is None if output_final_state is False.
+    """
+    a = _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state)
+    ws, ws_bytes = _workspace(a, chunk_size)
+    with torch.cuda.device(a["dev"]):
+        _check(lib().kda_prefill(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
+                                 _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a["beta"]),
+                                 _ptr(initial_state), _ptr(cu_seqlens), _ptr(a["o"]), _ptr(a["fs"]),
+                                 _ptr(ws), ws_bytes, _stream(a["dev"])))
+    o = a["o"]
+    if a["dense_batch"]:
+        o = o.view(a["N"], a["T"] // max(a["N"], 1), a["H"], a["dv"])
+    return o, a["fs"]
+
+
+def kda_prefill_checkpointed(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, checkpoint_interval: int,
+                             chunk_size: int = 0, scale: float = 1.0, output_final_state: bool = True,
+                             num_seqs: int | None = None, out=None, final_state=None, checkpoints=None):
+    """kda_prefill that also returns the state after every checkpoint_interval
+    tokens of each sequence (a multiple of the chunk size in use).
+
+    Returns (o, final_state, checkpoints, first_slot): checkpoints is fp32
+    [T // checkpoint_interval, H, d_k, d_v]; first_slot is an int64 device
+    tensor [N + 1] whose entry n is the slot of sequence n's first checkpoint
+    (sequence n owns slots first_slot[n] .. first_slot[n + 1] - 1, checkpoint j
+    being the state after its first (j + 1) * checkpoint_interval tokens).
+    Slots from first_slot[N] on are not written.
+    """
+    a = _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state)
+    interval = int(checkpoint_interval)
+    if interval < 1:
+        raise ValueError("checkpoint_interval must be positive")
+    cap = a["T"] // interval
+    ck = checkpoints if checkpoints is not None else torch.empty((cap, a["H"], a["dk"], a["dv"]),
+                                                                  dtype=torch.float32, device=a["dev"])
+    _need(ck, "checkpoints", torch.float32, 4)
+    if ck.shape[1:] != (a["H"], a["dk"], a["dv"]) or ck.shape[0] < cap:
+        raise ValueError("checkpoints must be [>= T // checkpoint_interval, H, d_k, d_v]")
+    # slot bookkeeping for the caller (the kernels derive the same offsets from cu_seqlens)
+    if cu_seqlens is not None:
+        counts = (cu_seqlens[1:] - cu_seqlens[:-1]).to(torch.int64) // interval
+    else:
+        counts = torch.full((a["N"],), (a["T"] // max(a["N"], 1)) // interval, dtype=torch.int64, device=a["dev"])
+    first_slot = torch.zeros(a["N"] + 1, dtype=torch.int64, device=a["dev"])
+    if a["N"] > 0:
+        first_slot[1:] = torch.cumsum(counts, 0)
+    ws, ws_bytes = _workspace(a, chunk_size)
+    with torch.cuda.device(a["dev"]):
+        _check(lib().kda_prefill_checkpointed(
+            a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
+            _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a["beta"]),
+            _ptr(initial_state), _ptr(cu_seqlens), _ptr(a["o"]), _ptr(a["fs"]),
+            interval, _ptr(ck) if ck.numel() else None, int(ck.shape[0]),
+            _ptr(ws), ws_bytes, _stream(a["dev"])))
+    o = a["o"]
+    if a["dense_batch"]:
+        o = o.view(a["N"], a["T"] // max(a["N"], 1), a["H"], a["dv"])
+    return o, a["fs"], ck, first_slot
 
 
 def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, out=None):

@@ -12,4 +12,5 @@ from .kda_oracle import (  # noqa: F401
     lib_path,
     max_threads,
     prefill,
+    prefill_checkpoints,
 )

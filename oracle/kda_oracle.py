@@ -133,6 +133,41 @@ def prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None,
     return o, S
 
 
+def prefill_checkpoints(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
+                        interval: int, scale: float = 1.0, nthreads: int = 0):
+    """States at token boundaries, by definition: checkpoint j of sequence n
+    is the final state of the token-by-token recurrence (prefill above) over
+    that sequence's first (j + 1) * interval tokens, from its initial state.
+    The KDA state restored at a token boundary for prefix reuse ("Inside
+    Kimi K3", section "Sequence mixing").
+
+    Returns (checkpoints [sum_n floor(L_n / interval), H, dk, dv],
+    first_slot [N + 1]) with sequence n's checkpoints in slots
+    first_slot[n] .. first_slot[n + 1] - 1.  Slow on purpose: one prefill per
+    checkpoint."""
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    S0 = None if initial_state is None else _f64(initial_state)
+    counts = [int(cu[n + 1] - cu[n]) // int(interval) for n in range(N)]
+    first_slot = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    ck = np.zeros((int(first_slot[-1]), H, dk, dv), dtype=np.float64)
+    for n in range(N):
+        a = int(cu[n])
+        for j in range(counts[n]):
+            b = a + (j + 1) * int(interval)
+            init = None if S0 is None else S0[n:n + 1]
+            _, S = prefill(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], initial_state=init,
+                           scale=scale, nthreads=nthreads)
+            ck[first_slot[n] + j] = S[0]
+    return ck, first_slot
+
+
 def decode_step(q, k, v, g, beta, state, scale: float = 1.0,
                 nthreads: int = 0, _lib=None):
     """One token per (n, h).  Returns (o [N, H, dv], new_state) without

@@ -56,7 +56,7 @@ def header_statuses():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     statuses = header_statuses()
     assert sorted(statuses) == list(range(8))
     for s, name in statuses.items():
@@ -178,3 +178,28 @@ def test_library_has_no_oracle_dependency():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "kda_oracle" not in txt, f
+
+
+def _prefill_ck(lib, N=1, T=64, H=2, d=128, C=0, interval=16, ck=FAKE + 0x400000, cap=4, o=FAKE + 0x100000,
+                fs=None, cu=None):
+    return lib.kda_prefill_checkpointed(N, T, H, d, d, BF16, C, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, None, cu, o, fs,
+                                        interval, ck, cap, None, 0, None)
+
+
+def test_prefill_checkpointed_validation(lib):
+    assert _prefill_ck(lib, interval=0) == BAD          # no interval
+    assert _prefill_ck(lib, interval=-16) == BAD
+    assert _prefill_ck(lib, interval=24) == BAD         # not a multiple of the default chunk 16
+    assert _prefill_ck(lib, C=64, interval=32) == BAD   # not a multiple of chunk 64
+    assert _prefill_ck(lib, cap=3) == BAD               # floor(64 / 16) = 4 slots needed
+    assert _prefill_ck(lib, cap=-1) == BAD
+    assert _prefill_ck(lib, ck=None) == NULLP
+    assert _prefill_ck(lib, ck=FAKE + 0x400008) == MISAL
+    assert _prefill_ck(lib, ck=FAKE) == BAD             # checkpoints == q
+    assert _prefill_ck(lib, ck=FAKE + 0x100000) == BAD  # checkpoints == o
+    assert _prefill_ck(lib, d=100) == UNSUP
+    # checks shared with kda_prefill still come first
+    assert _prefill_ck(lib, o=None) == NULLP
+    assert _prefill_ck(lib, N=3) == BAD
+    # no checkpoint fits: capacity 0 and a NULL buffer are fine (nothing launched for N = 0)
+    assert _prefill_ck(lib, N=0, T=0, interval=16, ck=None, cap=0) == OK

@@ -140,3 +140,37 @@ def test_k3_decode_1000_steps_tracked_units(kda, oracle_mod):
     say("  after %d steps: worst rel err o=%.3e, tracked states %.3e" % (steps, worst_o, es))
     assert torch.isfinite(S).all()
     assert worst_o <= BF16_TOL and es <= BF16_TOL
+
+
+def test_k3_dense_32k_checkpoints(kda, oracle_mod):
+    """State checkpoints every 4096 tokens of the dense workload: sampled
+    checkpoints against the oracle, the last one equal to the final state,
+    and prefill resumed from a checkpoint reproducing the rest of the run."""
+    from linear_attention_recurrence_delta_amd import synth
+    say("CASE k3_dense_32k checkpoints every 4096 tokens")
+    w = synth.workload_inputs("k3_dense_32k", DEV)
+    names = ("q", "k", "v", "g", "beta")
+    I = 4096
+    o, S, ck, first = kda.kda_prefill_checkpointed(*(w[n] for n in names), None, None, checkpoint_interval=I)
+    o_ref, S_ref = kda.kda_prefill(*(w[n] for n in names), None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    assert ck.shape[0] == w["T"] // I == 8 and first.cpu().tolist() == [0, 8]
+    assert torch.equal(ck[7], S[0])
+    # checkpoint 0 of three heads against the oracle's 4096-token prefix
+    heads = [0, 41, 95]
+    hi = torch.tensor(heads, device=DEV)
+    sl = lambda x: f64(x[:I].index_select(1, hi))
+    _, rs = oracle_mod.prefill(sl(w["q"]), sl(w["k"]), sl(w["v"]), sl(w["g"]), sl(w["beta"]))
+    err = rel_err(f64(ck[0].index_select(0, hi)), rs[0])
+    say("  checkpoint 0, heads %s: rel err %.3e" % (heads, err))
+    assert err <= BF16_TOL
+    # resume from checkpoint 3 (after 16384 tokens): the rest of the run again
+    R = 4 * I
+    rest = {n: w[n][R:].contiguous() for n in names}
+    o_r, S_r = kda.kda_prefill(*(rest[n] for n in names), ck[3:4].contiguous(), None)
+    torch.cuda.synchronize()
+    e_o = (o_r.float() - o[R:].float()).abs().max().item() / o[R:].float().abs().max().item()
+    e_s = (S_r - S).abs().max().item() / S.abs().max().item()
+    say("  resumed from checkpoint 3: rel err o=%.3e S=%.3e" % (e_o, e_s))
+    assert e_o <= 1e-6 and e_s <= 1e-6

@@ -315,3 +315,46 @@ def test_oracle_rejects_bad_cu(oracle_mod):
     q = np.zeros((4, 1, 2)); v = np.zeros((4, 1, 2)); beta = np.zeros((4, 1))
     with pytest.raises(ValueError):
         oracle_mod.prefill(q, q, v, q, beta, cu_seqlens=np.array([0, 3, 2, 4]))
+
+
+# --------------------------------------------------------------------------
+# P11: state checkpoints at token boundaries (prefix reuse restores the KDA
+# state at a token boundary: Inside Kimi K3, "Sequence mixing").  With
+# beta = 0 the state after t tokens of a sequence is exp(sum of its first t
+# g rows) applied to the key rows of its initial state, so every checkpoint
+# has a closed form; a boundary off by one token changes the exponent.
+# --------------------------------------------------------------------------
+def test_p11_checkpoints_pure_decay_closed_form(oracle_mod):
+    rng = np.random.default_rng(13)
+    lengths = [10, 0, 25, 15, 4]
+    interval = 5
+    T, H, dk, dv = sum(lengths), 2, 3, 4
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv, g_scale=0.7)
+    beta[:] = 0.0
+    N = len(lengths)
+    S0 = rng.standard_normal((N, H, dk, dv))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    ck, first = oracle_mod.prefill_checkpoints(q, k, v, g, beta, initial_state=S0, cu_seqlens=cu,
+                                               interval=interval)
+    assert list(first) == [0, 2, 2, 7, 10, 10]
+    assert ck.shape == (10, H, dk, dv)
+    for n in range(N):
+        for j in range(lengths[n] // interval):
+            t = (j + 1) * interval
+            G = g[cu[n]:cu[n] + t].sum(axis=0)  # [H, dk]
+            for h in range(H):
+                np.testing.assert_allclose(ck[first[n] + j, h], np.exp(G[h])[:, None] * S0[n, h],
+                                           rtol=1e-13, atol=0)
+
+
+def test_p11b_last_checkpoint_is_final_state(oracle_mod):
+    rng = np.random.default_rng(14)
+    lengths = [12, 8]
+    T, H, dk, dv = sum(lengths), 1, 4, 3
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    cu = np.array([0, 12, 20], dtype=np.int64)
+    ck, first = oracle_mod.prefill_checkpoints(q, k, v, g, beta, cu_seqlens=cu, interval=4)
+    _, S = oracle_mod.prefill(q, k, v, g, beta, cu_seqlens=cu)
+    assert list(first) == [0, 3, 5]
+    np.testing.assert_array_equal(ck[2], S[0])
+    np.testing.assert_array_equal(ck[4], S[1])
