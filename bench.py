@@ -173,6 +173,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "long"], default="all")
+    ap.add_argument("--no-checkpoints", action="store_true",
+                    help="skip the checkpointed prefill timing (counter runs per kernel launch)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -240,8 +242,10 @@ def main():
                                          checkpoint_interval=ck_interval, chunk_size=C, out=o_d,
                                          final_state=s_d, checkpoints=ck_buf)
 
-        run_dense_ck()
-        ck_ms = time_launches(run_dense_ck, args.steps, stream)
+        ck_ms = None
+        if not args.no_checkpoints:
+            run_dense_ck()
+            ck_ms = time_launches(run_dense_ck, args.steps, stream)
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)
         log("dense prefill avg %.3f ms (min %.3f), varlen avg %.3f ms, wall %.3f s" %
@@ -264,7 +268,7 @@ def main():
                 "frac": flop_launch / (d_avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                 "counters": measured_mfma("kda_prefill_k3_dense_32k"),
             },
-            "prefill_checkpoints": {
+            "prefill_checkpoints": None if ck_ms is None else {
                 "workload": "k3_dense_32k with a state checkpoint every %d tokens (%d per head, %.0f MB)"
                             % (ck_interval, wd["T"] // ck_interval, ck_buf.numel() * 4 / 1e6),
                 "ms": sum(ck_ms) / len(ck_ms),
