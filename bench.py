@@ -40,6 +40,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 # Algorithmic bytes per token-head of the bf16 prefill: q, k, v (3 x 256),
 # g (512), beta (4), o (256).  The per-head state I/O (64 KiB) is excluded.
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256
+# The fused entry reads bf16 decay logits z (256) instead of fp32 g.
+FUSED_BYTES_PER_TOKEN_HEAD = 3 * 256 + 256 + 4 + 256
 # Chunked flop count at the reference chunk C = 64, d = 128, causal tiles:
 # A, P, W, U~ and P U at C^2 d each, plus W S, Q~ S and Kbar^T U at 2 C d^2
 # each, per chunk of C tokens -> 5 C d + 6 d^2 per token-head.
@@ -246,6 +248,18 @@ def main():
         if not args.no_checkpoints:
             run_dense_ck()
             ck_ms = time_launches(run_dense_ck, args.steps, stream)
+        # the dense workload through the fused entry (gate and q/k norm in the kernel)
+        fu_ms = None
+        if kda.kda_prefill_fused_supported(torch.bfloat16, wd["d"], wd["d"], C):
+            fq, fk, fv, fz, fa, fb, _ = synth.fused_inputs(wd["T"], wd["H"], wd["d"], torch.bfloat16, 7, dev,
+                                                           a_log_std=0.0)
+
+            def run_fused():
+                kda.kda_prefill_fused(fq, fk, fv, fz, fa, fb, None, None, chunk_size=C, out=o_d, final_state=s_d)
+
+            run_fused()
+            fu_ms = time_launches(run_fused, args.steps, stream)
+            del fq, fk, fv, fz, fa, fb
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)
         log("dense prefill avg %.3f ms (min %.3f), varlen avg %.3f ms, wall %.3f s" %
@@ -273,6 +287,14 @@ def main():
                             % (ck_interval, wd["T"] // ck_interval, ck_buf.numel() * 4 / 1e6),
                 "ms": sum(ck_ms) / len(ck_ms),
                 "overhead_vs_plain": (sum(ck_ms) / len(ck_ms)) / d_avg - 1.0,
+            },
+            "prefill_fused": None if fu_ms is None else {
+                "workload": "k3_dense_32k through kda_prefill_fused: raw q/k normalised and g = -5 sigmoid(e^A z) "
+                            "formed in the kernel from bf16 z (A = 0)",
+                "ms": sum(fu_ms) / len(fu_ms),
+                "tokens_per_s": wd["T"] / (sum(fu_ms) / len(fu_ms) * 1e-3),
+                "hbm_gbs": FUSED_BYTES_PER_TOKEN_HEAD * token_heads / (sum(fu_ms) / len(fu_ms) * 1e-3) / 1e9,
+                "bytes_per_token_head": FUSED_BYTES_PER_TOKEN_HEAD,
             },
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
@@ -364,8 +386,8 @@ def main():
                              "gbs": 2 * src.numel() * 4 / (min(copy_ms) * 1e-3) / 1e9,
                              "note": "best of 5 torch copy_ launches of 2 GiB (read + write bytes)"}
     del src, dst
-    for key in ("roofline", "mfma", "prefill_varlen", "prefill_checkpoints", "prefill_long_1m", "decode",
-                "device_copy"):
+    for key in ("roofline", "mfma", "prefill_varlen", "prefill_checkpoints", "prefill_fused", "prefill_long_1m",
+                "decode", "device_copy"):
         if key in result:
             line[key] = result[key]
 

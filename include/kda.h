@@ -195,6 +195,43 @@ kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens,
                                     void *workspace, size_t workspace_bytes,
                                     void *stream);
 
+/* 1 if (qkv_dtype, d_k, d_v, chunk_size) has a built kda_prefill_fused
+ * kernel, else 0 (chunk_size 0 = the default, 16). */
+int32_t kda_prefill_fused_supported(int32_t qkv_dtype, int32_t d_k, int32_t d_v,
+                                    int32_t chunk_size);
+
+/*
+ * kda_prefill_fused -- kda_prefill with the decay gate and the L2
+ * normalisation of queries and keys computed inside the kernel, so that the
+ * gate logits and the raw projections are read once and no normalised copy
+ * or fp32 g is written beforehand.  The pages define q_t and k_t as
+ * L2-normalised vectors (symbol table) and the log-decay as
+ * g_t = g_min Sigmoid(e^{A_h} z_t) with g_min = -5 and a per-head log-scale
+ * A_h ("Understanding Kimi K3's attention", gate equation).  Arguments as for
+ * kda_prefill, except:
+ *
+ *   q, k    [T_total, H, d_k] qkv_dtype, NOT normalised: each (token, head)
+ *           vector is divided by its L2 norm in the kernel (a zero vector
+ *           stays zero).
+ *   z       [T_total, H, d_k] qkv_dtype, the decay logits (16-byte aligned).
+ *   a_log   [H] fp32, A_h of each head.
+ *   (no g)  g = -5 / (1 + exp(-exp(a_log[h]) z)) per channel, in (-5, 0).
+ *
+ * Built for bf16 with d_k = d_v = 128 and chunk 16 (or 0); other
+ * combinations return KDA_ERR_UNSUPPORTED.  z and a_log may be NULL only
+ * when total_tokens is 0.  Under KDA_VALIDATE=1 only beta and cu_seqlens are
+ * checked (every z gives a g inside the bound).
+ */
+kda_status kda_prefill_fused(int32_t num_seqs, int64_t total_tokens,
+                             int32_t num_heads, int32_t d_k, int32_t d_v,
+                             int32_t qkv_dtype, int32_t chunk_size, float scale,
+                             const void *q, const void *k, const void *v,
+                             const void *z, const float *a_log,
+                             const float *beta, const float *initial_state,
+                             const int32_t *cu_seqlens, void *o,
+                             float *final_state, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /*
  * kda_decode_step -- one new token per sequence, state updated in place
  * (serving needs a dedicated decode kernel: "Kimi K3.1 and the Road From

@@ -13,6 +13,8 @@ from .kda import (  # noqa: F401
     kda_decode_supported,
     kda_prefill,
     kda_prefill_checkpointed,
+    kda_prefill_fused,
+    kda_prefill_fused_supported,
     kda_prefill_supported,
     kda_prefill_workspace_bytes,
 )

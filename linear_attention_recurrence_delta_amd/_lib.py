@@ -29,6 +29,9 @@ SIGNATURES = {
     "kda_prefill_checkpointed": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _i32, _vp, _i64, _vp, _sz, _vp]),
+    "kda_prefill_fused_supported": (_i32, [_i32, _i32, _i32, _i32]),
+    "kda_prefill_fused": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kda_decode_step": (_i32, [_i32, _i32, _i32, _i32, _i32, _f32,
                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }

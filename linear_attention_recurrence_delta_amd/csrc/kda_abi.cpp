@@ -57,16 +57,19 @@ int device_cu_count() {
 // the compute units (96 heads -> 2 slabs, 16 heads -> 8).  KDA_PREFILL_WAVES
 // (an integer) overrides the choice and KDA_PREFILL_KIND the kernel; results
 // are bitwise identical across slab widths.
-const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units) {
+const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units, bool fused) {
     int count = 0;
     const PrefillVariant* tab = variants(dtype, &count);
     int want_kind = 1;  // the wave-specialised pipeline where it is built
     if (const char* env = getenv("KDA_PREFILL_KIND")) want_kind = atoi(env);
+    if (fused) want_kind = 2;        // only the fused kernels read z and a_log
+    else if (want_kind == 2) want_kind = 1;
     bool have_kind = false;
     for (int i = 0; i < count; ++i)
         if (tab[i].D == D && tab[i].C == C && tab[i].kind == want_kind) have_kind = true;
+    if (fused && !have_kind) return nullptr;
     int want = D / 16;
-    if (have_kind && want_kind == 1) {
+    if (have_kind && (want_kind == 1 || want_kind == 2)) {
         const int64_t cus = device_cu_count();
         while (want > 1 && units * (D / (16 * want)) * 2 <= cus) want /= 2;
     }
@@ -81,6 +84,7 @@ const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t 
     for (int i = 0; i < count; ++i) {
         const PrefillVariant& v = tab[i];
         if (v.D != D || v.C != C) continue;
+        if ((v.kind == 2) != fused) continue;
         if (have_kind && v.kind != want_kind) continue;
         if (!smallest || v.nwc < smallest->nwc) smallest = &v;
         if (v.nwc <= want && (!best || v.nwc > best->nwc)) best = &v;
@@ -94,19 +98,24 @@ static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t n
                                const void* k, const void* v, const float* g, const float* beta,
                                const float* initial_state, const int32_t* cu_seqlens, void* o,
                                float* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                               int32_t ckpt_interval, float* checkpoints, int64_t ckpt_capacity) {
+                               int32_t ckpt_interval, float* checkpoints, int64_t ckpt_capacity,
+                               bool fused = false, const void* z = nullptr, const float* a_log = nullptr) {
     if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
     if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return KDA_ERR_UNSUPPORTED;
     if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0 && total_tokens > 0) return KDA_ERR_BAD_SHAPE;
     if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
     if (!kda_prefill_supported(dtype, d_k, d_v, chunk_size)) return KDA_ERR_UNSUPPORTED;
-    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL_POINTER;
-    const void* ptrs[] = {q, k, v, g, initial_state, o, final_state, workspace, checkpoints};
+    if (fused && !kda_prefill_fused_supported(dtype, d_k, d_v, chunk_size)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > 0 && (!q || !k || !v || !beta || !o)) return KDA_ERR_NULL_POINTER;
+    if (total_tokens > 0 && !fused && !g) return KDA_ERR_NULL_POINTER;
+    if (total_tokens > 0 && fused && (!z || !a_log)) return KDA_ERR_NULL_POINTER;
+    if (a_log && !aligned4(a_log)) return KDA_ERR_MISALIGNED;
+    const void* ptrs[] = {q, k, v, g, z, initial_state, o, final_state, workspace, checkpoints};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
     if ((beta && !aligned4(beta)) || (cu_seqlens && !aligned4(cu_seqlens))) return KDA_ERR_MISALIGNED;
-    if (o && (o == q || o == k || o == v || o == g || o == beta)) return KDA_ERR_BAD_SHAPE;
+    if (o && (o == q || o == k || o == v || o == g || o == beta || o == z)) return KDA_ERR_BAD_SHAPE;
     // Checkpoints (ckpt_interval 0: none).  The interval is a positive multiple
     // of the chunk in use; the buffer holds at least floor(T_total / interval)
     // states, which bounds the sum of floor(length / interval) over sequences.
@@ -131,7 +140,8 @@ static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t n
     if (validate_enabled()) {
         unsigned int bad = 0;
         const int64_t n_beta = total_tokens * num_heads;
-        if (kda::check_inputs(g, n_beta * d_k, beta, n_beta, cu_seqlens, num_seqs, total_tokens,
+        // (the fused gate maps any z into (-5, 0): there is no g to check)
+        if (kda::check_inputs(g, fused ? 0 : n_beta * d_k, beta, n_beta, cu_seqlens, num_seqs, total_tokens,
                               static_cast<hipStream_t>(stream), &bad) != hipSuccess)
             return KDA_ERR_HIP;
         if (bad) return KDA_ERR_DOMAIN;
@@ -139,7 +149,7 @@ static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t n
 
     const int C = resolve_chunk(dtype, chunk_size);
     const int64_t units = (int64_t)num_seqs * num_heads;
-    const PrefillVariant* var = pick_variant(dtype, d_k, C, units);
+    const PrefillVariant* var = pick_variant(dtype, d_k, C, units, fused);
     if (!var) return KDA_ERR_UNSUPPORTED;
     const int nslab = d_v / (16 * var->nwc);
     if ((units + 7) / 8 * 8 * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // padded grid
@@ -163,6 +173,8 @@ static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t n
     p.ckpt = (ckpt_interval > 0 && total_tokens / ckpt_interval > 0) ? checkpoints : nullptr;
     p.ckpt_cap = ckpt_capacity;
     p.ckpt_interval = ckpt_interval > 0 ? ckpt_interval : 1;
+    p.z = z;
+    p.a_log = a_log;
     const hipError_t err = var->launch(p, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -196,6 +208,16 @@ int32_t kda_prefill_supported(int32_t dtype, int32_t d_k, int32_t d_v, int32_t c
     return 0;
 }
 
+int32_t kda_prefill_fused_supported(int32_t dtype, int32_t d_k, int32_t d_v, int32_t chunk_size) {
+    if (d_k != d_v) return 0;
+    const int C = resolve_chunk(dtype, chunk_size);
+    int count = 0;
+    const PrefillVariant* tab = variants(dtype, &count);
+    for (int i = 0; i < count; ++i)
+        if (tab[i].kind == 2 && tab[i].D == d_k && tab[i].C == C) return 1;
+    return 0;
+}
+
 int32_t kda_decode_supported(int32_t dtype, int32_t d_k, int32_t d_v) {
     if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return 0;
     return d_k == d_v && kda::decode_d_supported(d_k) ? 1 : 0;
@@ -221,6 +243,16 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads
     return prefill_impl(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale, q, k, v, g, beta,
                         initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes, stream, 0, nullptr,
                         0);
+}
+
+kda_status kda_prefill_fused(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v,
+                             int32_t dtype, int32_t chunk_size, float scale, const void* q, const void* k,
+                             const void* v, const void* z, const float* a_log, const float* beta,
+                             const float* initial_state, const int32_t* cu_seqlens, void* o, float* final_state,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_impl(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale, q, k, v, nullptr,
+                        beta, initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes, stream, 0,
+                        nullptr, 0, true, z, a_log);
 }
 
 kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,

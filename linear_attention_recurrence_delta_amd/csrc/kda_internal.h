@@ -32,6 +32,11 @@ struct PrefillParams {
     float* ckpt;
     int64_t ckpt_cap;
     int32_t ckpt_interval;
+    // Fused gate and q/k norm (the kernels built for it): q and k arrive
+    // unnormalised, g is not read; z [T_total, H, d_k] (qkv dtype) and
+    // a_log [H] give g = -5 Sigmoid(exp(a_log[h]) z).
+    const void* z;
+    const float* a_log;
 };
 
 // Token range [*a, *b) of sequence n, with the bounds read from cu clamped to
@@ -81,7 +86,7 @@ struct DecodeParams {
 
 // One entry per built prefill kernel.
 struct PrefillVariant {
-    int kind;               // 0: chunk-staged kernel, 1: wave-specialised pipeline
+    int kind;               // 0: chunk-staged kernel, 1: wave-specialised pipeline, 2: the same, fused gate/norm
     int dtype;              // kda_dtype
     int D;                  // d_k = d_v
     int C;                  // chunk size

@@ -6,11 +6,16 @@
 namespace kda {
 
 static const PrefillVariant kBf16Variants[] = {
-    // wave-specialised pipeline: 4 consumer waves x 32 columns, 4 stage-A waves
+    // wave-specialised pipeline: NCW consumer waves x TPW 16 columns, 8 stage-A waves
     {1, 1, 128, 16, 8, WsCfg<4, 2, 8>::LDS, &launch_prefill_ws<4, 2, 8>},
     {1, 1, 128, 16, 4, WsCfg<2, 2, 8>::LDS, &launch_prefill_ws<2, 2, 8>},
     {1, 1, 128, 16, 2, WsCfg<1, 2, 8>::LDS, &launch_prefill_ws<1, 2, 8>},
     {1, 1, 128, 16, 1, WsCfg<1, 1, 8>::LDS, &launch_prefill_ws<1, 1, 8>},
+    // the same with the gate and the q/k L2 norm computed in the kernel
+    {2, 1, 128, 16, 8, WsCfg<4, 2, 8, true>::LDS, &launch_prefill_ws<4, 2, 8, true>},
+    {2, 1, 128, 16, 4, WsCfg<2, 2, 8, true>::LDS, &launch_prefill_ws<2, 2, 8, true>},
+    {2, 1, 128, 16, 2, WsCfg<1, 2, 8, true>::LDS, &launch_prefill_ws<1, 2, 8, true>},
+    {2, 1, 128, 16, 1, WsCfg<1, 1, 8, true>::LDS, &launch_prefill_ws<1, 1, 8, true>},
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 8),
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 4),
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 2),

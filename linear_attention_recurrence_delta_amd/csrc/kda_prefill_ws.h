@@ -57,7 +57,7 @@
 
 namespace kda {
 
-template <int NCW, int TPW, int NSA>
+template <int NCW, int TPW, int NSA, bool FUSED = false>
 struct WsCfg {
     static constexpr int D = 128;
     static constexpr int C = 16;
@@ -100,16 +100,21 @@ struct WsCfg {
     static constexpr size_t OFFP = OFF2 + 2 * S2;
     static constexpr size_t OFFT = OFFP + 3 * SP;
     static constexpr size_t OFFA = OFFT + 2 * SP;
-    // Raw q, k, g, beta of one chunk, row-major, assembled in LDS by the
-    // stage-A waves (2-deep).  A q or k load covers 4 token rows (1056 B of
-    // the tile at pitch PD), a g load 2 rows (1056 B at pitch PG): the same
-    // step, so every parking store has a constant offset.
+    // Raw q, k, g (or, fused, the gate input z), beta of one chunk, row-major,
+    // assembled in LDS by the stage-A waves (2-deep).  A q, k or z load covers
+    // 4 token rows (1056 B of the tile at pitch PD), a g load 2 rows (1056 B
+    // at pitch PG): the same step, so every parking store has a constant
+    // offset.  The fused kernel also parks the inverse L2 norms of the 16 q
+    // and 16 k rows.
     static constexpr int PG = D + 4;                 // fp32 pitch of the raw g tile
     static constexpr size_t R_Q = 0;
     static constexpr size_t R_K = R_Q + al16(2 * C * PD);
     static constexpr size_t R_G = R_K + al16(2 * C * PD);
-    static constexpr size_t R_B = R_G + al16(4 * C * PG);
-    static constexpr size_t SR = R_B + 4 * 64 * NSA;  // beta: 64 floats per stage-A wave
+    static constexpr size_t R_B = R_G + (FUSED ? al16(2 * C * PD) : al16(4 * C * PG));
+    static constexpr size_t R_N = R_B + 4 * 64 * NSA;  // beta: 64 floats per stage-A wave
+    static constexpr size_t R_X = R_N + (FUSED ? 4 * 2 * C : 0);    // parking area of waves without a raw load
+    static constexpr size_t SR = R_X + (FUSED ? (size_t)(16 / NSA - 1) * 4 * 2 * PD + 64 * 16 : 0);
+    static constexpr int NUNITS = FUSED ? 12 : 16;     // raw loads per chunk
     static constexpr int RAW_STEP = 4 * 2 * PD;      // LDS bytes per raw load
     static constexpr size_t OFFV = OFFA + 2 * SA;
     static constexpr size_t OFFR = OFFV + 2 * SV;
@@ -118,6 +123,7 @@ struct WsCfg {
     static_assert(DVW <= D && D % DVW == 0, "value slab");
     static constexpr int LPW = 16 / NSA;             // raw loads per stage-A wave and chunk
     static_assert(NSA == 4 || NSA == 8, "a stage-A wave's raw loads stay within one of q, k, g");
+    static_assert(!FUSED || NSA == 8, "the fused loads are laid out for eight stage-A waves");
     static_assert(2 * 4 * PG == RAW_STEP, "q/k and g raw loads step equally through LDS");
     static_assert(TPW == 1 || TPW == 2, "a consumer lane stores 4 TPW adjacent outputs");
     static_assert(NCB % NSA == 0, "stage-A waves split the channel blocks evenly");
@@ -141,9 +147,10 @@ struct LoadSet {
 // (16-channel block) one token x 4 channels of g, q, k per lane, plus beta.
 template <int IPW>
 struct RawSet {
-    f32x4 g[IPW];   // 4 channels of g
+    f32x4 g[IPW];   // 4 channels of g (fused: of the gate input z)
     u32x4 qk[IPW];  // 4 bf16 channels of q (words 0, 1) and of k (words 2, 3)
     float beta;
+    float rq, rk;   // fused: inverse L2 norms of the token's q and k
 };
 
 // V tile of one chunk held by the Gram wave between its load and its copy
@@ -161,9 +168,9 @@ __device__ __forceinline__ float row_bcast15(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
 }
 
-template <int NCW, int TPW, int NSA>
+template <int NCW, int TPW, int NSA, bool FUSED>
 __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
-    typedef WsCfg<NCW, TPW, NSA> Cfg;
+    typedef WsCfg<NCW, TPW, NSA, FUSED> Cfg;
     typedef Elem<bf16_t> E;
     typedef uint2 Frag;
     constexpr int D = Cfg::D, C = Cfg::C, NCB = Cfg::NCB, DVW = Cfg::DVW, IPW = Cfg::IPW;
@@ -195,6 +202,9 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     int64_t t_begin, t_end;
     seq_bounds(p, n, &t_begin, &t_end);
     const int64_t ntok = t_end - t_begin;
+    // fused gate: e^{A_h} log2(e) for this head (A_h = a_log[h], a per-head log-scale)
+    const float gate_ea_l2e =
+        (FUSED && ntok > 0) ? __builtin_amdgcn_exp2f(p.a_log[h] * 1.4426950408889634f) * 1.4426950408889634f : 0.f;
     const int nch = (int)((ntok + C - 1) / C);
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
 
@@ -241,22 +251,29 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     };
     // Raw q, k, g, beta of chunk c.  A chunk is 16 loads of 16 B per lane
     // over whole token rows: units 0-3 the q tile and 4-7 the k tile (4 rows
-    // of 256 B each), units 8-15 the g tile (2 rows of 512 B each).  Stage-A
+    // of 256 B each), units 8-15 the g tile (2 rows of 512 B each); fused,
+    // units 8-11 the bf16 gate input z (4 rows each) and no more.  Stage-A
     // wave sa issues units LPW sa .. LPW sa + LPW - 1 (all of one tensor) and
     // wave 0 also beta, so every cache line is requested by exactly one load
     // instruction.  The pieces are parked row-major in LDS and read back
-    // after a barrier in the layout stage A computes on.
+    // after a barrier in the layout stage A computes on.  A wave past the
+    // last unit still issues its loads, at an out-of-range offset (zeros, no
+    // memory request), and parks them in its own corner of LDS, so that no
+    // load or its use depends on the wave.
     constexpr int LPW = Cfg::LPW;
     const int ld_u0 = sa * LPW;
-    const bool ld_bf16 = ld_u0 < 8;
+    const bool ld_none = ld_u0 >= Cfg::NUNITS;
+    const bool ld_bf16 = FUSED || ld_u0 < 8;
     const int ld_lpr = ld_bf16 ? 16 : 32;  // lanes per token row
     const int ld_row = (ld_bf16 ? 4 * (ld_u0 & 3) : 2 * (ld_u0 - 8)) + lane / ld_lpr;
     const int ld_es = ld_bf16 ? 2 : 4;    // element bytes
     const char* ld_base = ld_u0 < 4 ? reinterpret_cast<const char*>(gq)
                         : ld_u0 < 8 ? reinterpret_cast<const char*>(gk)
+                        : FUSED     ? reinterpret_cast<const char*>(p.z)
                                     : reinterpret_cast<const char*>(p.g);
     const uint32_t ld_step = 8u * (uint32_t)(H * D);  // global bytes per load (4 bf16 or 2 fp32 rows)
-    const uint32_t ld_voff = (uint32_t)ld_row * (uint32_t)(H * D) * (uint32_t)ld_es + 16u * (uint32_t)(lane % ld_lpr);
+    const uint32_t ld_voff = ld_none ? 0x80000000u
+                                     : (uint32_t)ld_row * (uint32_t)(H * D) * (uint32_t)ld_es + 16u * (uint32_t)(lane % ld_lpr);
     // beta bytes; the other waves read out of range (zeros, no memory request)
     // so that the load and its use stay unconditional
     const uint32_t lb = sa == 0 ? (uint32_t)l16 * (uint32_t)H * 4u : 0x80000000u;
@@ -273,8 +290,10 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     };
     // Raw tile of chunk c (two slots in rotation).
     auto raw_slot = [&](int c) { return smem + Cfg::OFFR + (size_t)(c & 1) * Cfg::SR; };
-    const uint32_t park_off = (uint32_t)(ld_u0 < 4 ? Cfg::R_Q : ld_u0 < 8 ? Cfg::R_K : Cfg::R_G) +
-                              (uint32_t)ld_row * (uint32_t)(ld_bf16 ? 2 * PD : 4 * Cfg::PG) + 16u * (uint32_t)(lane % ld_lpr);
+    const uint32_t park_off =
+        ld_none ? (uint32_t)Cfg::R_X + 16u * (uint32_t)lane
+                : (uint32_t)(ld_u0 < 4 ? Cfg::R_Q : ld_u0 < 8 ? Cfg::R_K : Cfg::R_G) +
+                      (uint32_t)ld_row * (uint32_t)(ld_bf16 ? 2 * PD : 4 * Cfg::PG) + 16u * (uint32_t)(lane % ld_lpr);
     auto park_raw = [&](int c, const LoadSet<LPW>& R) {
         char* b = raw_slot(c) + park_off;
 #pragma unroll
@@ -284,6 +303,28 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             *reinterpret_cast<u32x2*>(b + i * Cfg::RAW_STEP + 8) = R.x[i].zw;
         }
         reinterpret_cast<float*>(raw_slot(c) + Cfg::R_B)[64 * sa + lane] = R.beta;  // wave 0's rows 0-15 are used
+        if constexpr (FUSED) {
+            if (ld_u0 < 8) {
+                // Inverse L2 norm of each loaded q or k row (L2Norm of the
+                // query and key, "Understanding Kimi K3's attention", symbol
+                // table): the 16 lanes of a DPP row hold one token row; the
+                // zero vector keeps norm factor 0.
+                float* rn = reinterpret_cast<float*>(raw_slot(c) + Cfg::R_N) + (ld_u0 < 4 ? 0 : C);
+#pragma unroll
+                for (int i = 0; i < LPW; ++i) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int w2 = 0; w2 < 4; ++w2) {
+                        const uint32_t wd = R.x[i][w2];
+                        const float lo = __uint_as_float(wd << 16), hi = __uint_as_float(wd & 0xffff0000u);
+                        ss += lo * lo;
+                        ss += hi * hi;
+                    }
+                    ss = row_inclusive_sum16(ss);
+                    if (l16 == 15) rn[ld_row + 4 * i] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
+                }
+            }
+        }
     };
     // Stage-A layout: token row l16, channels c0..c0+3 of each item.
     auto fetch_raw = [&](int c, RawSet<IPW>& R) {
@@ -291,12 +332,22 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 #pragma unroll
         for (int it = 0; it < IPW; ++it) {
             const int c0 = 16 * (IPW * sa + it) + 4 * g4;
-            R.g[it] = *reinterpret_cast<const f32x4*>(b + Cfg::R_G + (l16 * Cfg::PG + c0) * 4);
+            if constexpr (FUSED) {
+                const u32x2 zv = *reinterpret_cast<const u32x2*>(b + Cfg::R_G + (l16 * PD + c0) * 2);
+                R.g[it] = f32x4{__uint_as_float(zv.x << 16), __uint_as_float(zv.x & 0xffff0000u),
+                                __uint_as_float(zv.y << 16), __uint_as_float(zv.y & 0xffff0000u)};
+            } else {
+                R.g[it] = *reinterpret_cast<const f32x4*>(b + Cfg::R_G + (l16 * Cfg::PG + c0) * 4);
+            }
             const u32x2 qv = *reinterpret_cast<const u32x2*>(b + Cfg::R_Q + (l16 * PD + c0) * 2);
             const u32x2 kv = *reinterpret_cast<const u32x2*>(b + Cfg::R_K + (l16 * PD + c0) * 2);
             R.qk[it] = u32x4{qv.x, qv.y, kv.x, kv.y};
         }
         R.beta = reinterpret_cast<const float*>(b + Cfg::R_B)[l16];
+        if constexpr (FUSED) {
+            R.rq = reinterpret_cast<const float*>(b + Cfg::R_N)[l16];
+            R.rk = reinterpret_cast<const float*>(b + Cfg::R_N)[C + l16];
+        }
     };
 
     // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / VCPR,
@@ -355,14 +406,28 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         // Cumulative log-decay in base-2 units, all items and channels
         // interleaved so the dependent DPP steps of one scan overlap the others.
         // Rows past the end of the sequence get g = 0 through the same multiply.
-        const float lscale = ok ? LOG2E : 0.f;
         float L[IPW][4];
+        if constexpr (FUSED) {
+            // g = g_min Sigmoid(e^{A_h} z), g_min = -5 ("Understanding Kimi
+            // K3's attention", gate equation), in base-2 units:
+            // log2(e) g = -5 log2(e) / (1 + 2^{-log2(e) e^{A_h} z}).
+            const float gscale = ok ? -5.f * LOG2E : 0.f;
 #pragma unroll
-        for (int it = 0; it < IPW; ++it) {
-            L[it][0] = R.g[it][0] * lscale;
-            L[it][1] = R.g[it][1] * lscale;
-            L[it][2] = R.g[it][2] * lscale;
-            L[it][3] = R.g[it][3] * lscale;
+            for (int it = 0; it < IPW; ++it)
+#pragma unroll
+                for (int ch = 0; ch < 4; ++ch) {
+                    const float t = __builtin_amdgcn_exp2f(-gate_ea_l2e * R.g[it][ch]);
+                    L[it][ch] = gscale * __builtin_amdgcn_rcpf(1.f + t);
+                }
+        } else {
+            const float lscale = ok ? LOG2E : 0.f;
+#pragma unroll
+            for (int it = 0; it < IPW; ++it) {
+                L[it][0] = R.g[it][0] * lscale;
+                L[it][1] = R.g[it][1] * lscale;
+                L[it][2] = R.g[it][2] * lscale;
+                L[it][3] = R.g[it][3] * lscale;
+            }
         }
 #pragma unroll
         for (int it = 0; it < IPW; ++it)
@@ -389,8 +454,12 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                 e1[ch] = __builtin_amdgcn_exp2f(L[it][ch]);         // e^{L_r}  in [e^-80, 1]
                 const float e2 = __builtin_amdgcn_exp2f(-L[it][ch]);  // e^{-L_r} in [1, e^80]
                 const uint32_t qw = R.qk[it][ch >> 1], kw = R.qk[it][2 + (ch >> 1)];
-                const float qv = __uint_as_float((ch & 1) ? (qw & 0xffff0000u) : (qw << 16));
-                const float kv = __uint_as_float((ch & 1) ? (kw & 0xffff0000u) : (kw << 16));
+                float qv = __uint_as_float((ch & 1) ? (qw & 0xffff0000u) : (qw << 16));
+                float kv = __uint_as_float((ch & 1) ? (kw & 0xffff0000u) : (kw << 16));
+                if constexpr (FUSED) {  // L2-normalised query and key
+                    qv *= R.rq;
+                    kv *= R.rk;
+                }
                 qb[ch] = qv * e1[ch];
                 kb[ch] = kv * e1[ch];
                 kl[ch] = kv * e2;
@@ -741,11 +810,11 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     }
 }
 
-template <int NCW, int TPW, int NSA>
+template <int NCW, int TPW, int NSA, bool FUSED = false>
 hipError_t launch_prefill_ws(const PrefillParams& p, hipStream_t s) {
     const int64_t units = (int64_t)p.N * p.H;
     const int64_t blocks = (units + 7) / 8 * 8 * p.nslab;  // whole groups of 8 units
-    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA, FUSED>), dim3((unsigned)blocks),
                        dim3(64 * (NCW + 2 + NSA)), 0, s, p);
     return hipGetLastError();
 }

@@ -67,7 +67,8 @@ def kda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dty
                                                  _DTYPES.get(dtype, -1), chunk_size))
 
 
-def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state):
+def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state,
+                  g_dtype=torch.float32):
     """Shared argument handling of the prefill entry points (shapes, dtypes,
     output allocation).  Returns a dict of the marshalled arguments."""
     dense_batch = q.dim() == 4
@@ -85,7 +86,7 @@ def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, ou
     T, H, dk = q.shape
     _need(k, "k", qdt, 3)
     _need(v, "v", qdt, 3)
-    _need(g, "g", torch.float32, 3)
+    _need(g, "g" if g_dtype == torch.float32 else "z", g_dtype, 3)
     _need(beta, "beta", torch.float32, 2)
     dv = v.shape[-1]
     if k.shape != (T, H, dk) or g.shape != (T, H, dk) or v.shape[:2] != (T, H) or beta.shape != (T, H):
@@ -183,6 +184,36 @@ def kda_prefill_checkpointed(q, k, v, g, beta, initial_state=None, cu_seqlens=No
     if a["dense_batch"]:
         o = o.view(a["N"], a["T"] // max(a["N"], 1), a["H"], a["dv"])
     return o, a["fs"], ck, first_slot
+
+
+def kda_prefill_fused_supported(dtype: torch.dtype, d_k: int, d_v: int, chunk_size: int = 0) -> bool:
+    return bool(lib().kda_prefill_fused_supported(_DTYPES.get(dtype, -1), d_k, d_v, chunk_size))
+
+
+def kda_prefill_fused(q, k, v, z, a_log, beta, initial_state=None, cu_seqlens=None, *, chunk_size: int = 0,
+                      scale: float = 1.0, output_final_state: bool = True, num_seqs: int | None = None,
+                      out=None, final_state=None):
+    """kda_prefill with the gate and the q/k L2 norm computed in the kernel.
+
+    q, k: unnormalised [T, H, d_k] (bf16); z: decay logits [T, H, d_k] (same
+    dtype); a_log: fp32 [H] per-head log-scale.  g = -5 Sigmoid(exp(a_log) z)
+    is formed in the kernel (no g argument).  Returns (o, final_state)."""
+    # the shared marshalling checks shapes and dtypes; z takes g's place
+    a = _prefill_args(q, k, v, z, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state,
+                      final_state, g_dtype=q.dtype)
+    _need(a_log, "a_log", torch.float32, 1)
+    if a_log.shape[0] != a["H"]:
+        raise ValueError("a_log must have one entry per head")
+    ws, ws_bytes = _workspace(a, chunk_size)
+    with torch.cuda.device(a["dev"]):
+        _check(lib().kda_prefill_fused(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
+                                       _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a_log),
+                                       _ptr(a["beta"]), _ptr(initial_state), _ptr(cu_seqlens), _ptr(a["o"]),
+                                       _ptr(a["fs"]), _ptr(ws), ws_bytes, _stream(a["dev"])))
+    o = a["o"]
+    if a["dense_batch"]:
+        o = o.view(a["N"], a["T"] // max(a["N"], 1), a["H"], a["dv"])
+    return o, a["fs"]
 
 
 def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, out=None):

@@ -73,6 +73,29 @@ def token_inputs(T, H, dk, dv, dtype, seed, device, g_mode="k3", chunk_rows=1 <<
     return out["q"], out["k"], out["v"], g, beta, gen
 
 
+def fused_inputs(T, H, d, dtype, seed, device, a_log_std=0.3, chunk_rows=1 << 22):
+    """Inputs of the fused entry point: raw (unnormalised) q, k with norms that
+    vary per token (N(0, 1) rows times e^{N(0, 0.5)}), v ~ N(0, 1), decay
+    logits z ~ N(0, 1) (all in dtype), beta = sigmoid(N(0, 1)) and per-head
+    a_log ~ N(0, a_log_std^2) (fp32; a_log_std = 0 gives the same g
+    distribution as token_inputs).  Draw order: q, k, v, z, beta, a_log."""
+    gen = _gen(device, seed)
+    out = {}
+    rows = max(1, chunk_rows // max(1, H * d))
+    for name in ("q", "k", "v", "z"):
+        t = torch.empty((T, H, d), dtype=dtype, device=device)
+        for a in range(0, T, rows):
+            b = min(T, a + rows)
+            x = torch.randn((b - a, H, d), generator=gen, device=device, dtype=torch.float32)
+            if name in ("q", "k"):
+                x = x * torch.exp(0.5 * torch.randn((b - a, H, 1), generator=gen, device=device))
+            t[a:b] = x.to(dtype)
+        out[name] = t
+    beta = torch.sigmoid(torch.randn((T, H), generator=gen, device=device, dtype=torch.float32))
+    a_log = a_log_std * torch.randn((H,), generator=gen, device=device, dtype=torch.float32)
+    return out["q"], out["k"], out["v"], out["z"], a_log, beta, gen
+
+
 def initial_state(N, H, dk, dv, std, gen, device):
     return std * torch.randn((N, H, dk, dv), generator=gen, device=device, dtype=torch.float32)
 

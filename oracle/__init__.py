@@ -9,8 +9,11 @@ from .kda_oracle import (  # noqa: F401
     compile_source,
     build,
     decode_step,
+    gate,
+    l2norm,
     lib_path,
     max_threads,
     prefill,
     prefill_checkpoints,
+    prefill_fused,
 )

@@ -168,6 +168,35 @@ def prefill_checkpoints(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *
     return ck, first_slot
 
 
+def l2norm(x):
+    """L2Norm over the last axis (the head dimension) in fp64: each (token,
+    head) vector divided by its Euclidean norm; the zero vector stays zero
+    (the pages do not define L2Norm(0); this reading keeps a zero query or
+    key inert).  q_t and k_t are L2-normalised in the symbol table of
+    "Understanding Kimi K3's attention"."""
+    x = _f64(x)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return np.divide(x, n, out=np.zeros_like(x), where=n > 0)
+
+
+def gate(z, a_log, g_min: float = -5.0):
+    """Log-decay from the decay logits, in fp64: g = g_min Sigmoid(e^{A_h} z)
+    ("Understanding Kimi K3's attention", gate equation; g_min = -5, A_h a
+    per-head log-scale).  z [T, H, dk], a_log [H]."""
+    z = _f64(z)
+    a = np.exp(_f64(a_log))[None, :, None]
+    return g_min / (1.0 + np.exp(-a * z))
+
+
+def prefill_fused(q, k, v, z, a_log, beta, initial_state=None, cu_seqlens=None,
+                  scale: float = 1.0, nthreads: int = 0):
+    """The recurrence with its inputs prepared as the pages define them:
+    L2-normalised q and k and the gated log-decay from z (l2norm, gate
+    above), then prefill.  Returns (o, final_state)."""
+    return prefill(l2norm(q), l2norm(k), v, gate(z, a_log), beta, initial_state=initial_state,
+                   cu_seqlens=cu_seqlens, scale=scale, nthreads=nthreads)
+
+
 def decode_step(q, k, v, g, beta, state, scale: float = 1.0,
                 nthreads: int = 0, _lib=None):
     """One token per (n, h).  Returns (o [N, H, dv], new_state) without

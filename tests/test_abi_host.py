@@ -203,3 +203,30 @@ def test_prefill_checkpointed_validation(lib):
     assert _prefill_ck(lib, N=3) == BAD
     # no checkpoint fits: capacity 0 and a NULL buffer are fine (nothing launched for N = 0)
     assert _prefill_ck(lib, N=0, T=0, interval=16, ck=None, cap=0) == OK
+
+
+def _prefill_fused(lib, N=1, T=64, H=2, d=128, dt=BF16, C=0, q=FAKE, z=FAKE + 0x300000, a=FAKE + 0x500000,
+                   o=FAKE + 0x100000):
+    return lib.kda_prefill_fused(N, T, H, d, d, dt, C, 1.0, q, FAKE, FAKE, z, a, FAKE, None, None, o, None,
+                                 None, 0, None)
+
+
+def test_prefill_fused_supported_set(lib):
+    assert lib.kda_prefill_fused_supported(BF16, 128, 128, 0) == 1
+    assert lib.kda_prefill_fused_supported(BF16, 128, 128, 16) == 1
+    assert lib.kda_prefill_fused_supported(BF16, 128, 128, 64) == 0
+    assert lib.kda_prefill_fused_supported(F32, 128, 128, 16) == 0
+    assert lib.kda_prefill_fused_supported(BF16, 64, 64, 16) == 0
+
+
+def test_prefill_fused_validation(lib):
+    assert _prefill_fused(lib, z=None) == NULLP
+    assert _prefill_fused(lib, a=None) == NULLP
+    assert _prefill_fused(lib, z=FAKE + 0x300008) == MISAL
+    assert _prefill_fused(lib, a=FAKE + 0x500002) == MISAL
+    assert _prefill_fused(lib, o=FAKE + 0x300000) == BAD   # o == z
+    assert _prefill_fused(lib, dt=F32) == UNSUP
+    assert _prefill_fused(lib, C=64) == UNSUP
+    assert _prefill_fused(lib, d=64) == UNSUP
+    assert _prefill_fused(lib, N=3) == BAD
+    assert _prefill_fused(lib, N=0, T=0, q=None, z=None, a=None, o=None) == OK

@@ -358,3 +358,62 @@ def test_p11b_last_checkpoint_is_final_state(oracle_mod):
     assert list(first) == [0, 3, 5]
     np.testing.assert_array_equal(ck[2], S[0])
     np.testing.assert_array_equal(ck[4], S[1])
+
+
+# --------------------------------------------------------------------------
+# P12: the fused input preparation (Understanding Kimi K3's attention: q, k
+# L2-normalised in the symbol table; g = g_min Sigmoid(e^{A_h} z) with
+# g_min = -5 in the gate equation).  Special values of the logistic pin the
+# sign, the e^{A_h} factor and g_min; rescaling q and k per (token, head) by
+# positive factors must change nothing; the gate's inverse must give back a
+# chosen g through the already pinned recurrence.
+# --------------------------------------------------------------------------
+def test_p12a_gate_special_values(oracle_mod):
+    ln3 = np.log(3.0)
+    z = np.array([0.0, ln3, -ln3, ln3 / 2, 60.0, -60.0]).reshape(6, 1, 1)
+    a = np.array([0.0])
+    g = oracle_mod.gate(z, a)[:, 0, 0]
+    np.testing.assert_allclose(g[:4], [-2.5, -3.75, -1.25, -5.0 / (1 + 3 ** -0.5)], rtol=1e-15)
+    assert abs(g[4] + 5.0) <= 1e-20 and -1e-20 <= g[5] <= 0.0  # the limits g_min and 0
+    # e^{A_h}: A = ln 2 doubles the logit
+    g2 = oracle_mod.gate(np.full((1, 1, 1), ln3 / 2), np.array([np.log(2.0)]))
+    np.testing.assert_allclose(g2[0, 0, 0], -3.75, rtol=1e-15)
+    # one A per head, broadcast over tokens and channels
+    g3 = oracle_mod.gate(np.zeros((2, 3, 4)) + ln3, np.log(np.array([1.0, 2.0, 0.5])))
+    np.testing.assert_allclose(g3[:, 1, :], -5.0 / (1 + 1 / 9.0), rtol=1e-15)
+    np.testing.assert_allclose(g3[:, 2, :], -5.0 / (1 + 3 ** -0.5), rtol=1e-15)
+
+
+def test_p12b_l2norm_scale_invariance_and_zero(oracle_mod):
+    rng = np.random.default_rng(15)
+    T, H, dk, dv = 9, 2, 5, 3
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    v = rng.standard_normal((T, H, dv))
+    z = rng.standard_normal((T, H, dk))
+    a = rng.standard_normal(H) * 0.3
+    beta = rng.random((T, H))
+    o1, S1 = oracle_mod.prefill_fused(q, k, v, z, a, beta)
+    cq = np.exp(rng.standard_normal((T, H, 1)))
+    ck = np.exp(rng.standard_normal((T, H, 1)))
+    o2, S2 = oracle_mod.prefill_fused(q * cq, k * ck, v, z, a, beta)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S2, S1, rtol=1e-12, atol=1e-14)
+    n = np.linalg.norm(oracle_mod.l2norm(q), axis=-1)
+    np.testing.assert_allclose(n, 1.0, rtol=1e-15)
+    q0 = q.copy(); q0[4, 1] = 0.0
+    o3, _ = oracle_mod.prefill_fused(q0, k, v, z, a, beta)
+    assert np.all(o3[4, 1] == 0.0)
+
+
+def test_p12c_inverse_gate_matches_plain_prefill(oracle_mod):
+    rng = np.random.default_rng(16)
+    T, H, dk, dv = 11, 2, 4, 3
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv, g_scale=4.0)
+    g = np.clip(g, -4.99, -1e-3)
+    a = np.array([0.4, -0.7])
+    z = -np.log(-5.0 / g - 1.0) / np.exp(a)[None, :, None]   # Sigmoid^{-1}(g / g_min) / e^{A}
+    of, Sf = oracle_mod.prefill_fused(q, k, v, z, a, beta)
+    op, Sp = oracle_mod.prefill(q, k, v, g, beta)
+    np.testing.assert_allclose(of, op, rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(Sf, Sp, rtol=1e-10, atol=1e-13)
