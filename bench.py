@@ -260,6 +260,17 @@ def main():
             run_fused()
             fu_ms = time_launches(run_fused, args.steps, stream)
             del fq, fk, fv, fz, fa, fb
+        # the output gate on the dense output (Sigmoid(gate) * RMSNorm(o) * weight)
+        og_gate = torch.randn(o_d.shape, device=dev).to(o_d.dtype)
+        og_w = torch.ones(wd["d"], device=dev)
+        og_y = torch.empty_like(o_d)
+
+        def run_gate():
+            kda.kda_output_gate(o_d, og_gate, og_w, eps=1e-6, out=og_y)
+
+        run_gate()
+        og_ms = time_launches(run_gate, args.steps, stream)
+        del og_gate, og_y
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)
         log("dense prefill avg %.3f ms (min %.3f), varlen avg %.3f ms, wall %.3f s" %
@@ -295,6 +306,15 @@ def main():
                 "tokens_per_s": wd["T"] / (sum(fu_ms) / len(fu_ms) * 1e-3),
                 "hbm_gbs": FUSED_BYTES_PER_TOKEN_HEAD * token_heads / (sum(fu_ms) / len(fu_ms) * 1e-3) / 1e9,
                 "bytes_per_token_head": FUSED_BYTES_PER_TOKEN_HEAD,
+            },
+            "output_gate": {
+                "workload": "Sigmoid(gate) * RMSNorm(o) * weight over 32768 x 96 rows of 128 bf16",
+                "ms": sum(og_ms) / len(og_ms),
+                "roofline": {"bound": "hbm", "achieved": 3 * o_d.numel() * 2 / (sum(og_ms) / len(og_ms) * 1e-3) / 1e9,
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": 3 * o_d.numel() * 2 / (sum(og_ms) / len(og_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "kernel": "kda_output_gate_kernel<bf16, 128>",
+                             "bytes_per_launch": 3 * o_d.numel() * 2},
             },
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
@@ -386,8 +406,8 @@ def main():
                              "gbs": 2 * src.numel() * 4 / (min(copy_ms) * 1e-3) / 1e9,
                              "note": "best of 5 torch copy_ launches of 2 GiB (read + write bytes)"}
     del src, dst
-    for key in ("roofline", "mfma", "prefill_varlen", "prefill_checkpoints", "prefill_fused", "prefill_long_1m",
-                "decode", "device_copy"):
+    for key in ("roofline", "mfma", "prefill_varlen", "prefill_checkpoints", "prefill_fused", "output_gate",
+                "prefill_long_1m", "decode", "device_copy"):
         if key in result:
             line[key] = result[key]
 

@@ -255,6 +255,39 @@ kda_status kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t d_k,
                            const float *g, const float *beta, float *state,
                            void *o, void *stream);
 
+/* 1 if (qkv_dtype, d_v) has a built kda_output_gate kernel, else 0. */
+int32_t kda_output_gate_supported(int32_t qkv_dtype, int32_t d_v);
+
+/*
+ * kda_output_gate -- the gated output of a KDA layer before its output
+ * projection ("Understanding Kimi K3's attention", output equation:
+ * Sigmoid(W_g x_t) times RMSNorm of the ungated readout o~_t; W_g x_t is
+ * computed upstream and passed as `gate`, W_o stays outside).  Per (token,
+ * head) row of d_v channels:
+ *
+ *   y = Sigmoid(gate) * o / sqrt(mean over the row of o^2 + eps) * weight
+ *
+ *   total_tokens, num_heads  rows = total_tokens * num_heads
+ *   d_v         channels per row (see kda_output_gate_supported: 16, 32, 64
+ *               or 128)
+ *   qkv_dtype   dtype of o, gate and y (KDA_DTYPE_BF16 or KDA_DTYPE_F32);
+ *               arithmetic in fp32, y rounded to nearest even for bf16
+ *   eps         >= 0, added to the mean square (the pages give no value)
+ *   o, gate     [total_tokens, H, d_v] device buffers, 16-byte aligned
+ *   weight      [d_v] fp32, the per-channel RMSNorm weight, shared by heads
+ *   y           [total_tokens, H, d_v], written; may be the same buffer as
+ *               o or as gate (each element is read before it is written),
+ *               must not overlap them otherwise
+ *
+ * Errors: KDA_ERR_BAD_SHAPE (sizes, eps negative, NaN or huge, y == weight),
+ * KDA_ERR_UNSUPPORTED, KDA_ERR_NULL_POINTER, KDA_ERR_MISALIGNED, KDA_ERR_HIP.
+ * total_tokens = 0 is a valid no-op.
+ */
+kda_status kda_output_gate(int64_t total_tokens, int32_t num_heads,
+                           int32_t d_v, int32_t qkv_dtype, float eps,
+                           const void *o, const void *gate,
+                           const float *weight, void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

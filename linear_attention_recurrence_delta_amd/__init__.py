@@ -15,6 +15,8 @@ from .kda import (  # noqa: F401
     kda_prefill_checkpointed,
     kda_prefill_fused,
     kda_prefill_fused_supported,
+    kda_output_gate,
+    kda_output_gate_supported,
     kda_prefill_supported,
     kda_prefill_workspace_bytes,
 )

@@ -218,6 +218,33 @@ int32_t kda_prefill_fused_supported(int32_t dtype, int32_t d_k, int32_t d_v, int
     return 0;
 }
 
+int32_t kda_output_gate_supported(int32_t dtype, int32_t d_v) {
+    return (dtype == KDA_DTYPE_BF16 || dtype == KDA_DTYPE_F32) && kda::output_gate_d_supported(d_v) ? 1 : 0;
+}
+
+kda_status kda_output_gate(int64_t total_tokens, int32_t num_heads, int32_t d_v, int32_t dtype, float eps,
+                           const void* o, const void* gate, const float* weight, void* y, void* stream) {
+    if (total_tokens < 0 || num_heads < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
+    if (!(eps >= 0.f) || eps > 1e30f) return KDA_ERR_BAD_SHAPE;  // also rejects NaN
+    if (!kda_output_gate_supported(dtype, d_v)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > INT64_MAX / num_heads / d_v) return KDA_ERR_BAD_SHAPE;
+    if (total_tokens == 0) return KDA_OK;
+    if (!o || !gate || !weight || !y) return KDA_ERR_NULL_POINTER;
+    if (!aligned16(o) || !aligned16(gate) || !aligned16(y) || !aligned4(weight)) return KDA_ERR_MISALIGNED;
+    if (static_cast<const void*>(weight) == y) return KDA_ERR_BAD_SHAPE;
+    kda::OutputGateParams p;
+    p.o = o;
+    p.gate = gate;
+    p.weight = weight;
+    p.y = y;
+    p.rows = total_tokens * num_heads;
+    p.eps = eps;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t err = dtype == KDA_DTYPE_BF16 ? kda::launch_output_gate_bf16(d_v, p, device_cu_count(), s)
+                                                   : kda::launch_output_gate_f32(d_v, p, device_cu_count(), s);
+    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int32_t kda_decode_supported(int32_t dtype, int32_t d_k, int32_t d_v) {
     if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return 0;
     return d_k == d_v && kda::decode_d_supported(d_k) ? 1 : 0;

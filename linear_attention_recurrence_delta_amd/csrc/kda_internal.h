@@ -84,6 +84,15 @@ struct DecodeParams {
     float scale;
 };
 
+struct OutputGateParams {
+    const void* o;          // [rows, d_v] dtype
+    const void* gate;       // [rows, d_v] dtype
+    const float* weight;    // [d_v]
+    void* y;                // [rows, d_v] dtype
+    int64_t rows;           // T_total * H
+    float eps;
+};
+
 // One entry per built prefill kernel.
 struct PrefillVariant {
     int kind;               // 0: chunk-staged kernel, 1: wave-specialised pipeline, 2: the same, fused gate/norm
@@ -114,5 +123,11 @@ hipError_t check_inputs(const float* g, int64_t n_g, const float* beta, int64_t 
 hipError_t launch_decode_bf16(int D, const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_f32(int D, const DecodeParams& p, hipStream_t s);
 bool decode_d_supported(int D);
+
+// Output gate launchers (cus = compute units of the device); return
+// hipErrorInvalidValue for an unsupported d_v.
+hipError_t launch_output_gate_bf16(int DV, const OutputGateParams& p, int cus, hipStream_t s);
+hipError_t launch_output_gate_f32(int DV, const OutputGateParams& p, int cus, hipStream_t s);
+bool output_gate_d_supported(int DV);
 
 }  // namespace kda

@@ -216,6 +216,36 @@ def kda_prefill_fused(q, k, v, z, a_log, beta, initial_state=None, cu_seqlens=No
     return o, a["fs"]
 
 
+def kda_output_gate_supported(dtype: torch.dtype, d_v: int) -> bool:
+    return bool(lib().kda_output_gate_supported(_DTYPES.get(dtype, -1), d_v))
+
+
+def kda_output_gate(o, gate, weight, *, eps: float = 1e-6, out=None):
+    """y = sigmoid(gate) * RMSNorm(o) * weight over the last axis (d_v).
+
+    o, gate: [..., H, d_v] in bfloat16 or float32 (same dtype); weight: fp32
+    [d_v].  out may be o or gate (in place).  Returns y."""
+    if o.dtype not in _DTYPES or gate.dtype != o.dtype:
+        raise TypeError("o and gate must both be bfloat16 or both float32")
+    if o.dim() < 2 or gate.shape != o.shape:
+        raise ValueError("o and gate must have the same shape [..., H, d_v]")
+    _need(o, "o", o.dtype)
+    _need(gate, "gate", o.dtype)
+    _need(weight, "weight", torch.float32, 1)
+    H, dv = o.shape[-2], o.shape[-1]
+    if weight.shape[0] != dv:
+        raise ValueError("weight must have d_v entries")
+    T = o.numel() // max(1, H * dv)
+    y = out if out is not None else torch.empty_like(o)
+    _need(y, "out", o.dtype)
+    if y.shape != o.shape:
+        raise ValueError("out must have the shape of o")
+    with torch.cuda.device(o.device):
+        _check(lib().kda_output_gate(T, H, dv, _DTYPES[o.dtype], float(eps), _ptr(o), _ptr(gate), _ptr(weight),
+                                     _ptr(y), _stream(o.device)))
+    return y
+
+
 def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, out=None):
     """One token per sequence.  q, k, g: [N, H, d_k]; v: [N, H, d_v];
     beta: [N, H]; state: fp32 [N, H, d_k, d_v], updated in place.  Returns o."""

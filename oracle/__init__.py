@@ -13,6 +13,7 @@ from .kda_oracle import (  # noqa: F401
     l2norm,
     lib_path,
     max_threads,
+    output_gate,
     prefill,
     prefill_checkpoints,
     prefill_fused,

@@ -197,6 +197,18 @@ def prefill_fused(q, k, v, z, a_log, beta, initial_state=None, cu_seqlens=None,
                    cu_seqlens=cu_seqlens, scale=scale, nthreads=nthreads)
 
 
+def output_gate(o, gate, weight, eps: float):
+    """Gated output before the output projection, in fp64: Sigmoid(gate) times
+    RMSNorm(o) over the last axis, RMSNorm(x) = x / sqrt(mean(x^2) + eps) *
+    weight ("Understanding Kimi K3's attention", output equation; the pages
+    give no eps, so it is an argument).  o, gate [..., d_v], weight [d_v]."""
+    o = _f64(o)
+    gate = _f64(gate)
+    w = _f64(weight)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    return o / np.sqrt(ms + float(eps)) * w * (1.0 / (1.0 + np.exp(-gate)))
+
+
 def decode_step(q, k, v, g, beta, state, scale: float = 1.0,
                 nthreads: int = 0, _lib=None):
     """One token per (n, h).  Returns (o [N, H, dv], new_state) without

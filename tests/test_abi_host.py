@@ -230,3 +230,26 @@ def test_prefill_fused_validation(lib):
     assert _prefill_fused(lib, d=64) == UNSUP
     assert _prefill_fused(lib, N=3) == BAD
     assert _prefill_fused(lib, N=0, T=0, q=None, z=None, a=None, o=None) == OK
+
+
+def _gate(lib, T=10, H=2, dv=128, dt=BF16, eps=1e-6, o=FAKE, g=FAKE + 0x100000, w=FAKE + 0x200000,
+          y=FAKE + 0x300000):
+    return lib.kda_output_gate(T, H, dv, dt, eps, o, g, w, y, None)
+
+
+def test_output_gate_validation(lib):
+    for d in (16, 32, 64, 128):
+        assert lib.kda_output_gate_supported(BF16, d) == 1 and lib.kda_output_gate_supported(F32, d) == 1
+    assert lib.kda_output_gate_supported(BF16, 96) == 0 and lib.kda_output_gate_supported(5, 128) == 0
+    assert _gate(lib, T=-1) == BAD
+    assert _gate(lib, H=0) == BAD
+    assert _gate(lib, eps=-1.0) == BAD
+    assert _gate(lib, eps=float("nan")) == BAD
+    assert _gate(lib, dv=96) == UNSUP
+    assert _gate(lib, dt=7) == UNSUP
+    assert _gate(lib, o=None) == NULLP
+    assert _gate(lib, w=None) == NULLP
+    assert _gate(lib, y=FAKE + 0x300008) == MISAL
+    assert _gate(lib, w=FAKE + 0x200002) == MISAL
+    assert _gate(lib, y=FAKE + 0x200000) == BAD   # y == weight
+    assert _gate(lib, T=0, o=None, g=None, w=None, y=None) == OK

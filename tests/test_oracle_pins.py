@@ -417,3 +417,29 @@ def test_p12c_inverse_gate_matches_plain_prefill(oracle_mod):
     op, Sp = oracle_mod.prefill(q, k, v, g, beta)
     np.testing.assert_allclose(of, op, rtol=1e-10, atol=1e-13)
     np.testing.assert_allclose(Sf, Sp, rtol=1e-10, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# P13: the output gate Sigmoid(gate) * RMSNorm(o) (Understanding Kimi K3's
+# attention, output equation).  A constant row normalises to its sign; a
+# one-hot row of length d has RMS |a| / sqrt(d) (a sum in place of the mean
+# fails); Sigmoid(0) = 1/2 and Sigmoid(ln 3) = 3/4; the weight acts per
+# channel; eps enters under the root.
+# --------------------------------------------------------------------------
+def test_p13_output_gate_closed_forms(oracle_mod):
+    d = 8
+    w = np.arange(1, d + 1, dtype=np.float64) / 4.0
+    o = np.full((2, 1, d), -3.0)
+    gate = np.zeros((2, 1, d))
+    y = oracle_mod.output_gate(o, gate, w, 0.0)
+    np.testing.assert_allclose(y, np.broadcast_to(-0.5 * w, y.shape), rtol=1e-15)
+    oh = np.zeros((1, 1, d)); oh[0, 0, 3] = 2.5
+    g3 = np.full((1, 1, d), np.log(3.0))
+    y = oracle_mod.output_gate(oh, g3, w, 0.0)
+    expect = np.zeros(d); expect[3] = np.sqrt(d) * w[3] * 0.75
+    np.testing.assert_allclose(y[0, 0], expect, rtol=1e-14, atol=0)
+    # eps under the root: row (1, 1, ..., 1) with eps = 3 -> 1 / sqrt(1 + 3) = 1/2
+    y = oracle_mod.output_gate(np.ones((1, 1, d)), np.full((1, 1, d), 50.0), np.ones(d), 3.0)
+    np.testing.assert_allclose(y, 0.5, rtol=1e-15)
+    # zero row with eps > 0 stays zero
+    assert np.all(oracle_mod.output_gate(np.zeros((1, 1, d)), np.zeros((1, 1, d)), w, 1e-6) == 0.0)
