@@ -328,8 +328,8 @@ kda_status kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t d_k, int
     p.units = (int64_t)num_seqs * num_heads;
     p.scale = scale;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t err = dtype == KDA_DTYPE_BF16 ? kda::launch_decode_bf16(d_k, p, s)
-                                                   : kda::launch_decode_f32(d_k, p, s);
+    const hipError_t err = dtype == KDA_DTYPE_BF16 ? kda::launch_decode_bf16(d_k, p, device_cu_count(), s)
+                                                   : kda::launch_decode_f32(d_k, p, device_cu_count(), s);
     return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

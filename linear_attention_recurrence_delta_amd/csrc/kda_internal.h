@@ -120,8 +120,8 @@ hipError_t check_inputs(const float* g, int64_t n_g, const float* beta, int64_t 
                         int32_t n_seqs, int64_t total_tokens, hipStream_t s, unsigned int* violation);
 
 // Decode launchers; return hipErrorInvalidValue for an unsupported D.
-hipError_t launch_decode_bf16(int D, const DecodeParams& p, hipStream_t s);
-hipError_t launch_decode_f32(int D, const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_bf16(int D, const DecodeParams& p, int cus, hipStream_t s);
+hipError_t launch_decode_f32(int D, const DecodeParams& p, int cus, hipStream_t s);
 bool decode_d_supported(int D);
 
 // Output gate launchers (cus = compute units of the device); return
