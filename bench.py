@@ -60,6 +60,8 @@ KERNEL_SOURCES = {
     "kda_prefill_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
     "kda_prefill_k3_varlen_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
     "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
+    "kda_prefill_fused_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
+    "kda_output_gate_32k_x96": ("kda_output_gate.hip", "kda_device.h", "kda_internal.h"),
 }
 
 
@@ -306,6 +308,7 @@ def main():
                 "tokens_per_s": wd["T"] / (sum(fu_ms) / len(fu_ms) * 1e-3),
                 "hbm_gbs": FUSED_BYTES_PER_TOKEN_HEAD * token_heads / (sum(fu_ms) / len(fu_ms) * 1e-3) / 1e9,
                 "bytes_per_token_head": FUSED_BYTES_PER_TOKEN_HEAD,
+                "traffic": measured_traffic("kda_prefill_fused_k3_dense_32k"),
             },
             "output_gate": {
                 "workload": "Sigmoid(gate) * RMSNorm(o) * weight over 32768 x 96 rows of 128 bf16",
@@ -313,6 +316,7 @@ def main():
                 "roofline": {"bound": "hbm", "achieved": 3 * o_d.numel() * 2 / (sum(og_ms) / len(og_ms) * 1e-3) / 1e9,
                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": 3 * o_d.numel() * 2 / (sum(og_ms) / len(og_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "traffic": measured_traffic("kda_output_gate_32k_x96"),
                              "kernel": "kda_output_gate_kernel<bf16, 128>",
                              "bytes_per_launch": 3 * o_d.numel() * 2},
             },
