@@ -15,6 +15,7 @@ from .kda_oracle import (  # noqa: F401
     max_threads,
     output_gate,
     prefill,
+    prefill_backward,
     prefill_checkpoints,
     prefill_fused,
 )

@@ -35,6 +35,21 @@ int kda_oracle_decode_step_f64(int64_t N, int64_t H, int64_t dk, int64_t dv,
                                const double *beta, double *S, double *o,
                                int nthreads);
 
+/* Gradients of the prefill above (delta = 1) for a loss with output
+ * gradient dO [T_total,H,dv] and final-state gradient dS_T [N,H,dk,dv]
+ * (NULL = zeros): dq, dkey, dg [T_total,H,dk], dval [T_total,H,dv],
+ * dbeta [T_total,H], dS0 [N,H,dk,dv] (may be NULL).  S0 may be NULL (zeros).
+ * seg_len <= 0 selects 64: the forward states are kept at every seg_len-th
+ * token and each segment is recomputed from its start. */
+int kda_oracle_prefill_backward_f64(int64_t num_seqs, const int64_t *cu, int64_t H,
+                                    int64_t dk, int64_t dv, double scale,
+                                    const double *q, const double *k, const double *v,
+                                    const double *g, const double *beta,
+                                    const double *S0, const double *dO,
+                                    const double *dS_T, double *dq, double *dkey,
+                                    double *dval, double *dg, double *dbeta,
+                                    double *dS0, int64_t seg_len, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,10 @@ def _bind(path: str):
     lib.kda_oracle_decode_step_f64.argtypes = [
         i64, i64, i64, i64, dbl, vp, vp, vp, vp, vp, vp, vp, ip]
     lib.kda_oracle_decode_step_f64.restype = ip
+    lib.kda_oracle_prefill_backward_f64.argtypes = [
+        i64, vp, i64, i64, i64, dbl,
+        vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, ip]
+    lib.kda_oracle_prefill_backward_f64.restype = ip
     lib.kda_oracle_max_threads.restype = ip
     return lib
 
@@ -79,6 +83,9 @@ class OracleLib:
 
     def decode_step(self, *a, **kw):
         return decode_step(*a, _lib=self._l, **kw)
+
+    def prefill_backward(self, *a, **kw):
+        return prefill_backward(*a, _lib=self._l, **kw)
 
 
 def _f64(x) -> np.ndarray:
@@ -226,3 +233,44 @@ def decode_step(q, k, v, g, beta, state, scale: float = 1.0,
     if rc != 0:
         raise ValueError("kda_oracle_decode_step_f64 failed with %d" % rc)
     return o, S
+
+
+def prefill_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None,
+                     cu_seqlens=None, scale: float = 1.0, seg_len: int = 0,
+                     nthreads: int = 0, _lib=None):
+    """Gradients of prefill (delta = True) for a loss whose gradients with
+    respect to o and to the final states are d_o [T, H, dv] and d_final_state
+    [N, H, dk, dv] (None = zeros): the token recurrence differentiated in
+    reverse, in fp64 (kda_oracle.c).  Returns (dq, dk, dv, dg, dbeta, dS0)
+    with the shapes of q, k, v, g, beta and [N, H, dk, dv]."""
+    q, k, v, g, beta, d_o = (_f64(a) for a in (q, k, v, g, beta, d_o))
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int64))
+    N = cu.shape[0] - 1
+    assert k.shape == (T, H, dk) and g.shape == (T, H, dk)
+    assert v.shape == (T, H, dv) and beta.shape == (T, H) and d_o.shape == (T, H, dv)
+    assert int(cu[-1]) == T
+    S0 = None if initial_state is None else _f64(initial_state)
+    dST = None if d_final_state is None else _f64(d_final_state)
+    for x in (S0, dST):
+        if x is not None:
+            assert x.shape == (N, H, dk, dv)
+    dq = np.zeros((T, H, dk))
+    dkey = np.zeros((T, H, dk))
+    dval = np.zeros((T, H, dv))
+    dg = np.zeros((T, H, dk))
+    dbeta = np.zeros((T, H))
+    dS0 = np.zeros((N, H, dk, dv))
+    rc = (_lib or _load()).kda_oracle_prefill_backward_f64(
+        N, _ptr(cu), H, dk, dv, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(S0), _ptr(d_o), _ptr(dST), _ptr(dq), _ptr(dkey), _ptr(dval), _ptr(dg), _ptr(dbeta),
+        _ptr(dS0), int(seg_len), int(nthreads))
+    if rc != 0:
+        raise ValueError("kda_oracle_prefill_backward_f64 failed with %d" % rc)
+    return dq, dkey, dval, dg, dbeta, dS0

@@ -58,9 +58,25 @@ MUTANTS = {
     "readout_not_transposed": ("for (j = 0; j < dv; ++j) tmp[j] += row[j] * qi;",
                                "for (j = 0; j < dv; ++j) tmp[j] += (j < dk && i < dv ? S[j * dv + i] : 0.0) * qi;"),
     "readout_scale_dropped": ("o[j] = scale * tmp[j];", "o[j] = tmp[j];"),
-    "initial_state_ignored": ("if (S0) memcpy(", "if (0) memcpy("),
+    "initial_state_ignored": ("if (S0) memcpy(S, S0", "if (0) memcpy(S, S0"),
     "delta_always_on": ("if (delta) {", "if (1) {"),
     "delta_always_off": ("if (delta) {", "if (0) {"),
+    # backward (reverse-mode adjoint of the token recurrence)
+    "bwd_readout_gradient_dropped": ("for (j = 0; j < dv; ++j) dS[i * dv + j] += scale * q[i] * dout[j];",
+                                     "for (j = 0; j < dv; ++j) (void)dout[j];"),
+    "bwd_dq_scale_dropped": ("dq[i] = scale * acc;", "dq[i] = acc;"),
+    "bwd_dbeta_sign_flipped": ("*dbeta = acc;", "*dbeta = -acc;"),
+    "bwd_dv_sign_flipped": ("dval[j] = beta * w[j];", "dval[j] = -beta * w[j];"),
+    "bwd_dk_prediction_term_dropped": ("dkey[i] += acc;", "dkey[i] += 0.0 * acc;"),
+    "bwd_state_prediction_term_dropped": ("dS[i * dv + j] += k[i] * dp[j];   /* dS is now dD */",
+                                          "(void)dp[j];"),
+    "bwd_dg_from_undecayed_state": ("acc += D[i * dv + j] * dS[i * dv + j];",
+                                    "acc += S_prev[i * dv + j] * dS[i * dv + j];"),
+    "bwd_state_gradient_not_faded": ("for (j = 0; j < dv; ++j) dS[i * dv + j] *= alpha;", "(void)alpha;"),
+    "bwd_segment_recompute_off_by_one": ("const int64_t th = (a0 + t - 1) * H + h;",
+                                         "const int64_t th = (a0 + t) * H + h;"),
+    "bwd_final_state_gradient_ignored": ("if (dS_T) memcpy(dS, dS_T", "if (0) memcpy(dS, dS_T"),
+    "bwd_initial_state_ignored": ("if (S0) memcpy(dS, S0", "if (0) memcpy(dS, S0"),
 }
 
 
@@ -89,6 +105,8 @@ PIN_CALLS = [
     ("p6", lambda m: pins.test_p6_brute_force_unrolled_packed(m)),
     ("p7", lambda m: pins.test_p7_toy_demo_printed_errors(m)),
     ("p9", lambda m: pins.test_p9_superposition(m)),
+    ("p14", lambda m: pins.test_p14_backward_finite_differences(m, 2)),
+    ("p15", lambda m: pins.test_p15_backward_matches_autograd(m)),
 ]
 
 

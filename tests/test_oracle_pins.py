@@ -443,3 +443,85 @@ def test_p13_output_gate_closed_forms(oracle_mod):
     np.testing.assert_allclose(y, 0.5, rtol=1e-15)
     # zero row with eps > 0 stays zero
     assert np.all(oracle_mod.output_gate(np.zeros((1, 1, d)), np.zeros((1, 1, d)), w, 1e-6) == 0.0)
+
+
+# --------------------------------------------------------------------------
+# P14: the backward oracle against central finite differences of the forward
+# oracle (itself pinned by P1-P10), for every input of a tiny packed batch with
+# an initial state, an output gradient and a final-state gradient.  The
+# chunkwise form's gradients are checked against the token recurrence's
+# ("Hybrid Attention", section "But isn't a recurrent update sequential?");
+# these are the recurrence's.  seg_len = 2 makes the backward recompute the
+# forward from stored states at every other token.
+# --------------------------------------------------------------------------
+def _bwd_case(rng, lengths, H, dk, dv):
+    T = sum(lengths)
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv, g_scale=1.5)
+    N = len(lengths)
+    S0 = 0.5 * rng.standard_normal((N, H, dk, dv))
+    d_o = rng.standard_normal((T, H, dv))
+    dST = rng.standard_normal((N, H, dk, dv))
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return [q, k, v, g, beta, S0], d_o, dST, cu
+
+
+@pytest.mark.parametrize("seg_len", [2, 0])
+def test_p14_backward_finite_differences(oracle_mod, seg_len):
+    rng = np.random.default_rng(21)
+    inputs, d_o, dST, cu = _bwd_case(rng, [5, 0, 3], 2, 3, 2)
+    scale = 0.7
+
+    def loss(args):
+        o, S = oracle_mod.prefill(*args[:5], initial_state=args[5], cu_seqlens=cu, scale=scale)
+        return float(np.sum(d_o * o) + np.sum(dST * S))
+
+    grads = oracle_mod.prefill_backward(*inputs[:5], d_o, initial_state=inputs[5], d_final_state=dST,
+                                        cu_seqlens=cu, scale=scale, seg_len=seg_len)
+    h = 1e-6
+    for idx, (x, gx) in enumerate(zip(inputs, grads)):
+        fd = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            saved = x[pos]
+            x[pos] = saved + h
+            lp = loss(inputs)
+            x[pos] = saved - h
+            lm = loss(inputs)
+            x[pos] = saved
+            fd[pos] = (lp - lm) / (2 * h)
+        assert gx.shape == x.shape
+        np.testing.assert_allclose(gx, fd, rtol=0, atol=1e-7 * max(1.0, np.max(np.abs(fd)))), idx
+
+
+# --------------------------------------------------------------------------
+# P15: the same gradients by torch's fp64 autograd through a plain loop over
+# the product form S_t = (I - b k k^T) Diag(a) S_{t-1} + b k v^T, o = scale
+# S_t^T q (Understanding Kimi K3's attention, state-update and readout
+# equations), at lengths that cross the backward's 64-token segments, with
+# an empty sequence and a one-token one.
+# --------------------------------------------------------------------------
+def test_p15_backward_matches_autograd(oracle_mod):
+    import torch
+    rng = np.random.default_rng(22)
+    lengths = [150, 0, 70, 1]
+    H, dk, dv = 2, 6, 5
+    inputs, d_o, dST, cu = _bwd_case(rng, lengths, H, dk, dv)
+    scale = 0.9
+    ts = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in inputs]
+    q, k, v, g, beta, S0 = ts
+    eye = torch.eye(dk, dtype=torch.float64)
+    loss = torch.zeros((), dtype=torch.float64)
+    for n in range(len(lengths)):
+        for h in range(H):
+            S = S0[n, h]
+            for t in range(int(cu[n]), int(cu[n + 1])):
+                kk = k[t, h]
+                S = (eye - beta[t, h] * torch.outer(kk, kk)) @ (torch.exp(g[t, h])[:, None] * S) \
+                    + beta[t, h] * torch.outer(kk, v[t, h])
+                loss = loss + torch.dot(torch.tensor(d_o[t, h]), scale * (S.T @ q[t, h]))
+            loss = loss + torch.sum(torch.tensor(dST[n, h]) * S)
+    loss.backward()
+    grads = oracle_mod.prefill_backward(*inputs[:5], d_o, initial_state=inputs[5], d_final_state=dST,
+                                        cu_seqlens=cu, scale=scale)
+    for t, gx in zip(ts, grads):
+        ref = t.grad.numpy()
+        np.testing.assert_allclose(gx, ref, rtol=0, atol=1e-11 * max(1.0, np.max(np.abs(ref))))
