@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_DTYPE_F32 = 0,
@@ -287,6 +287,61 @@ kda_status kda_output_gate(int64_t total_tokens, int32_t num_heads,
                            int32_t d_v, int32_t qkv_dtype, float eps,
                            const void *o, const void *gate,
                            const float *weight, void *y, void *stream);
+
+/* 1 if kda_prefill_backward is built for (qkv_dtype, d_k, d_v): bf16 with
+ * d_k = d_v = 128. */
+int32_t kda_prefill_backward_supported(int32_t qkv_dtype, int32_t d_k,
+                                       int32_t d_v);
+
+/* Bytes of device workspace kda_prefill_backward needs: the state after
+ * every 16 tokens of each sequence, floor(total_tokens / 16) * num_heads *
+ * d_k * d_v fp32 values (0 for unsupported arguments). */
+size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs,
+                                            int64_t total_tokens,
+                                            int32_t num_heads, int32_t d_k,
+                                            int32_t d_v, int32_t qkv_dtype);
+
+/*
+ * kda_prefill_backward -- gradients of kda_prefill for training ("Hybrid
+ * Attention", kimi-k3.adriaflores.com, section "But isn't a recurrent update
+ * sequential?": the chunked form's outputs and gradients are checked against
+ * the token recurrence).  For a scalar loss with gradient d_o with respect to
+ * o and d_final_state with respect to the final states, it returns the
+ * gradients with respect to q, k, v, g, beta and the initial states.
+ *
+ * Computed in two launches on `stream`: the forward recurrence again (the
+ * same kernel as kda_prefill, chunk 16), keeping the state at every 16-token
+ * boundary in the workspace, then one workgroup per (sequence, head) that
+ * walks its chunks last to first and carries the state gradient.
+ *
+ * Arguments shared with kda_prefill (num_seqs, total_tokens, num_heads, d_k,
+ * d_v, qkv_dtype, scale, q, k, v, g, beta, initial_state, cu_seqlens) mean
+ * the same and follow the same rules; qkv_dtype must be KDA_DTYPE_BF16 and
+ * d_k = d_v = 128 (kda_prefill_backward_supported).  In addition, device
+ * memory, 16-byte aligned unless noted:
+ *   d_o              [T_total, H, d_v] bf16, read: gradient with respect to o.
+ *   d_final_state    [N, H, d_k, d_v] fp32 or NULL (zeros), read.
+ *   dq, dk           [T_total, H, d_k] bf16, written.
+ *   dv               [T_total, H, d_v] bf16, written.
+ *   dg               [T_total, H, d_k] fp32, written.
+ *   dbeta            [T_total, H] fp32 (4-byte aligned), written.
+ *   d_initial_state  [N, H, d_k, d_v] fp32 or NULL (not returned), written.
+ *   workspace        at least kda_prefill_backward_workspace_bytes, owned by
+ *                    the caller, contents undefined afterwards.
+ * Outputs must not alias inputs or each other.  Errors as kda_prefill
+ * (KDA_ERR_WORKSPACE for a short workspace); with KDA_VALIDATE=1, g, beta
+ * and cu_seqlens are checked as there.  Results are deterministic.
+ */
+kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens,
+                                int32_t num_heads, int32_t d_k, int32_t d_v,
+                                int32_t qkv_dtype, float scale, const void *q,
+                                const void *k, const void *v, const float *g,
+                                const float *beta, const float *initial_state,
+                                const int32_t *cu_seqlens, const void *d_o,
+                                const float *d_final_state, void *dq, void *dk,
+                                void *dv, float *dg, float *dbeta,
+                                float *d_initial_state, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

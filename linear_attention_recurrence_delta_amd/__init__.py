@@ -12,6 +12,8 @@ from .kda import (  # noqa: F401
     kda_decode_step,
     kda_decode_supported,
     kda_prefill,
+    kda_prefill_backward,
+    kda_prefill_backward_supported,
     kda_prefill_checkpointed,
     kda_prefill_fused,
     kda_prefill_fused_supported,

@@ -34,6 +34,11 @@ SIGNATURES = {
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kda_output_gate_supported": (_i32, [_i32, _i32]),
     "kda_output_gate": (_i32, [_i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp]),
+    "kda_prefill_backward_supported": (_i32, [_i32, _i32, _i32]),
+    "kda_prefill_backward_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
+    "kda_prefill_backward": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _f32,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "kda_decode_step": (_i32, [_i32, _i32, _i32, _i32, _i32, _f32,
                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }

@@ -295,6 +295,116 @@ kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int3
                         checkpoint_interval, checkpoints, checkpoint_capacity);
 }
 
+int32_t kda_prefill_backward_supported(int32_t dtype, int32_t d_k, int32_t d_v) {
+    return dtype == KDA_DTYPE_BF16 && d_k == 128 && d_v == 128 ? 1 : 0;
+}
+
+size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                                            int32_t d_k, int32_t d_v, int32_t dtype) {
+    (void)num_seqs;
+    if (!kda_prefill_backward_supported(dtype, d_k, d_v) || total_tokens < 0 || num_heads < 1) return 0;
+    // the state after every 16 tokens of each sequence: at most total_tokens / 16 states per head
+    return (size_t)(total_tokens / 16) * (size_t)num_heads * (size_t)d_k * (size_t)d_v * sizeof(float);
+}
+
+kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                                int32_t d_v, int32_t dtype, float scale, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta, const float* initial_state,
+                                const int32_t* cu_seqlens, const void* d_o, const float* d_final_state, void* dq,
+                                void* dk, void* dv, float* dg, float* dbeta, float* d_initial_state,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
+    if (!kda_prefill_backward_supported(dtype, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 && total_tokens > 0) return KDA_ERR_BAD_SHAPE;
+    if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
+    if ((int64_t)num_seqs * num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !d_o || !dq || !dk || !dv || !dg || !dbeta))
+        return KDA_ERR_NULL_POINTER;
+    const void* ptrs16[] = {q, k, v, g, d_o, initial_state, d_final_state, dq, dk, dv, dg, d_initial_state, workspace};
+    for (const void* ptr : ptrs16)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_MISALIGNED;
+    if ((beta && !aligned4(beta)) || (dbeta && !aligned4(dbeta)) || (cu_seqlens && !aligned4(cu_seqlens)))
+        return KDA_ERR_MISALIGNED;
+    // outputs alias neither the inputs nor each other
+    const void* ins[] = {q, k, v, g, beta, initial_state, d_o, d_final_state, cu_seqlens, workspace};
+    const void* outs[] = {dq, dk, dv, dg, dbeta, d_initial_state};
+    for (int a = 0; a < 6; ++a) {
+        if (!outs[a]) continue;
+        for (const void* in : ins)
+            if (outs[a] == in) return KDA_ERR_BAD_SHAPE;
+        for (int b = a + 1; b < 6; ++b)
+            if (outs[a] == outs[b]) return KDA_ERR_BAD_SHAPE;
+    }
+    const size_t need = kda_prefill_backward_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (num_seqs == 0) return KDA_OK;
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (validate_enabled()) {
+        unsigned int bad = 0;
+        const int64_t n_beta = total_tokens * num_heads;
+        if (kda::check_inputs(g, n_beta * d_k, beta, n_beta, cu_seqlens, num_seqs, total_tokens, s, &bad) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        if (bad) return KDA_ERR_DOMAIN;
+    }
+    const int64_t units = (int64_t)num_seqs * num_heads;
+    // 1. the forward pass again, for the state at every 16-token boundary (its o is not stored)
+    if (total_tokens / 16 > 0) {
+        const PrefillVariant* var = pick_variant(dtype, d_k, 16, units, false);
+        if (!var) return KDA_ERR_UNSUPPORTED;
+        const int nslab = d_v / (16 * var->nwc);
+        if ((units + 7) / 8 * 8 * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+        kda::PrefillParams fp;
+        fp.q = q;
+        fp.k = k;
+        fp.v = v;
+        fp.g = g;
+        fp.beta = beta;
+        fp.S0 = initial_state;
+        fp.cu = cu_seqlens;
+        fp.o = nullptr;
+        fp.Sout = nullptr;
+        fp.T_total = total_tokens;
+        fp.N = num_seqs;
+        fp.H = num_heads;
+        fp.seq_len = cu_seqlens ? 0 : (int32_t)(total_tokens / num_seqs);
+        fp.nslab = nslab;
+        fp.scale = scale;
+        fp.ckpt = static_cast<float*>(workspace);
+        fp.ckpt_cap = total_tokens / 16;
+        fp.ckpt_interval = 16;
+        fp.z = nullptr;
+        fp.a_log = nullptr;
+        if (var->launch(fp, s) != hipSuccess) return KDA_ERR_HIP;
+    }
+    // 2. the chunks in reverse
+    kda::BackwardParams bp;
+    bp.q = q;
+    bp.k = k;
+    bp.v = v;
+    bp.g = g;
+    bp.beta = beta;
+    bp.S0 = initial_state;
+    bp.cu = cu_seqlens;
+    bp.dO = d_o;
+    bp.dST = d_final_state;
+    bp.ckpt = static_cast<const float*>(workspace);
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.dg = dg;
+    bp.dbeta = dbeta;
+    bp.dS0 = d_initial_state;
+    bp.T_total = total_tokens;
+    bp.N = num_seqs;
+    bp.H = num_heads;
+    bp.seq_len = cu_seqlens ? 0 : (int32_t)(total_tokens / num_seqs);
+    bp.scale = scale;
+    return kda::launch_backward_bf16_d128(bp, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_decode_step(int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v, int32_t dtype,
                            float scale, const void* q, const void* k, const void* v, const float* g,
                            const float* beta, float* state, void* o, void* stream) {

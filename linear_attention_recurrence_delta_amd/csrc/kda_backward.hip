@@ -1,0 +1,511 @@
+// kda_backward.hip -- gradients of the KDA prefill in its chunked form.
+//
+// The forward pass over a chunk of C = 16 tokens starting from state S is
+// (relative log-decay Gamma = inclusive cumsum of g inside the chunk, gamma =
+// exp(Gamma at the chunk's last row)):
+//   Q~ = q e^Gamma, K~ = k e^Gamma, Ki = k e^-Gamma, Kb = k e^(Gamma_last - Gamma)
+//   M = K~ Ki^T (strictly lower part),  A = Diag(beta) M,  P = lower(Q~ Ki^T)
+//   T = (I + A)^-1,  W = T Diag(beta) K~,  U~ = T Diag(beta) V
+//   U = U~ - W S,    O = scale (Q~ S + P U),    S' = Diag(gamma) S + Kb^T U
+// which is the token recurrence of "Understanding Kimi K3's attention"
+// (state-update and readout equations) regrouped per chunk: the causal
+// dependencies inside a chunk go through a triangular solve and the state is
+// passed from chunk to chunk ("Hybrid Attention", section "But isn't a
+// recurrent update sequential?", whose tests compare the chunked form's
+// outputs and gradients with the recurrence).  With dO_s = scale dO and dS'
+// the gradient with respect to S', reverse mode gives per chunk
+//   dU  = P^T dO_s + Kb dS'                      dS  = Diag(gamma) dS' + Q~^T dO_s - W^T dU
+//   dQ~ = dO_s S^T + dP Ki                       dP  = lower(dO_s U^T)
+//   dW  = -dU S^T      dKb = U dS'^T             dgamma = rowsum(S * dS')
+//   dT  = dU (Diag(beta) V)^T + dW (Diag(beta) K~)^T,     dA = strict-lower(-T^T dT T^T)
+//   dV  = Diag(beta) T^T dU,   dK~ = Diag(beta) T^T dW + dM Ki,   dM = Diag(beta) dA
+//   dKi = dM^T K~ + dP^T Q~,   dbeta = rowsum(T^T dU * V) + rowsum(T^T dW * K~) + rowsum(dA * M)
+// then through the decay-scaled operands to q, k and Gamma, and from Gamma to
+// g by a reverse cumulative sum; Gamma_last, a sum of every g of the chunk,
+// adds dgamma * gamma and the Kb terms to all of them.
+//
+// Layout: one workgroup of 8 waves per (sequence, head), chunks last to
+// first.  Wave w owns value columns 16w..16w+15 in the column-separable
+// products (dU, U, the dS update, dV: dS stays in registers across chunks)
+// and key rows 16w..16w+15 in the products that sum over value columns
+// (dQ~, dW, dKb), with the full matrices staged in LDS between phases.  The
+// state at each chunk start comes from the forward kernel's checkpoints
+// (every 16 tokens) and enters the products as a bf16 operand, as in the
+// forward pass; dgamma uses its fp32 value.
+//
+// MFMA operand convention of kda_device.h: lane l (g = l / 16, i = l % 16)
+// supplies A[i][4g + p] and B[4g + p][i]; the accumulator holds C[4g + p][i].
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int BD = 128;        // d_k = d_v
+constexpr int BC = 16;         // chunk length
+constexpr int BNW = 8;         // waves
+constexpr int BNT = 64 * BNW;  // threads
+constexpr int PB = BD + 8;     // bf16 row pitch (elements) of the LDS matrices
+constexpr int PF = BD + 4;     // fp32 row pitch
+constexpr int P16 = 16;        // pitch of the 16 x 16 fp32 matrices
+
+// 4-value bf16 operand fragments from LDS: X[r][c..c+3] (one 8-byte read)
+// and X[r..r+3][c] (four reads).
+__device__ __forceinline__ uint2 frow(const uint16_t* X, int pitch, int r, int c) {
+    return *reinterpret_cast<const uint2*>(X + r * pitch + c);
+}
+__device__ __forceinline__ uint2 fcol(const uint16_t* X, int pitch, int r, int c) {
+    const uint32_t a = (uint32_t)X[r * pitch + c] | ((uint32_t)X[(r + 1) * pitch + c] << 16);
+    const uint32_t b = (uint32_t)X[(r + 2) * pitch + c] | ((uint32_t)X[(r + 3) * pitch + c] << 16);
+    return make_uint2(a, b);
+}
+// The same from fp32 LDS matrices, rounded to bf16.
+__device__ __forceinline__ uint2 frow32(const float* X, int pitch, int r, int c) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(X + r * pitch + c);
+    return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__device__ __forceinline__ uint2 fcol32(const float* X, int pitch, int r, int c) {
+    return make_uint2(pack_bf16x2(X[r * pitch + c], X[(r + 1) * pitch + c]),
+                      pack_bf16x2(X[(r + 2) * pitch + c], X[(r + 3) * pitch + c]));
+}
+// An accumulator, taken over its rows, as a B fragment.
+__device__ __forceinline__ uint2 fregs(const f32x4& a) {
+    return make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+}
+__device__ __forceinline__ uint2 fneg(uint2 a) { return make_uint2(a.x ^ 0x80008000u, a.y ^ 0x80008000u); }
+__device__ __forceinline__ uint2 fscale(uint2 a, float s) {
+    return make_uint2(pack_bf16x2(__uint_as_float(a.x << 16) * s, __uint_as_float(a.x & 0xffff0000u) * s),
+                      pack_bf16x2(__uint_as_float(a.y << 16) * s, __uint_as_float(a.y & 0xffff0000u) * s));
+}
+__device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Sum over the 16 lanes of a row group (lanes 16g .. 16g + 15).
+__device__ __forceinline__ float sum16(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    return x;
+}
+
+__global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
+    // S (bf16) of the chunk start; after its last use the fp32 staging of dq, dk and the dg terms
+    __shared__ __align__(16) uint16_t sS[BD * PB];
+    // dS' (bf16); after its last use the bf16 staging of dv
+    __shared__ __align__(16) uint16_t sdS[BD * PB];
+    __shared__ __align__(16) uint16_t sQr[BC * PB], sKr[BC * PB], sV[BC * PB], sdO[BC * PB];
+    __shared__ __align__(16) uint16_t sQt[BC * PB], sKt[BC * PB], sKi[BC * PB], sKb[BC * PB];
+    __shared__ __align__(16) uint16_t sU[BC * PB], sdU[BC * PB], sW[BC * PB];
+    __shared__ __align__(16) float sG[BC * PF];
+    __shared__ __align__(16) float sM[256], sP[256], sT[256], sdP[256], sdTv[256], sdM[256];
+    __shared__ __align__(16) float sdTk[BNW][256];
+    __shared__ float sBeta[BC], sGam[BD], sExt[BD], sdGam[BNW][BD], sdBv[BNW][BC], sdBk[BNW][BC], sdBa[BC];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, li = lane & 15;
+    const int col = 16 * w + li;  // value column (column owners) or key row (row owners)
+    const int64_t unit = blockIdx.x;
+    const int H = p.H;
+    const int n = (int)(unit / H), h = (int)(unit % H);
+
+    int64_t bos, L, slot0;
+    if (p.cu) {
+        bos = p.cu[n];
+        L = (int64_t)p.cu[n + 1] - bos;
+        // checkpoints of earlier sequences: sum of floor(length / 16), lanes split
+        int64_t part = 0;
+        for (int m = lane; m < n; m += 64) part += ((int64_t)p.cu[m + 1] - p.cu[m]) / BC;
+        for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+        slot0 = part;
+    } else {
+        bos = (int64_t)n * p.seq_len;
+        L = p.seq_len;
+        slot0 = (int64_t)n * (p.seq_len / BC);
+    }
+    const int64_t tok = (int64_t)H * BD;  // elements between tokens
+    const int64_t hoff = (int64_t)h * BD;
+    const uint16_t* gq_in = static_cast<const uint16_t*>(p.q);
+    const uint16_t* gk_in = static_cast<const uint16_t*>(p.k);
+    const uint16_t* gv_in = static_cast<const uint16_t*>(p.v);
+    const uint16_t* gdo_in = static_cast<const uint16_t*>(p.dO);
+    const float scale = p.scale;
+    const int nch = (int)((L + BC - 1) / BC);
+
+    float* fq = reinterpret_cast<float*>(sS);  // staging (aliases sS)
+    float* fk = fq + BC * PF;
+    float* fG = fk + BC * PF;
+    float* fB = fG + BC * PF;
+    uint16_t* sDv = sdS;                        // staging (aliases sdS)
+
+    // dS: gradient with respect to the state after the current chunk, rows
+    // 16r + 4gq + pp of column `col` in tile r.
+    f32x4 dSr[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp)
+            dSr[r][pp] = p.dST ? p.dST[unit * BD * BD + (16 * r + 4 * gq + pp) * BD + col] : 0.f;
+
+    for (int c = nch - 1; c >= 0; --c) {
+        const int64_t t0 = bos + (int64_t)c * BC;
+        const int nt = (int)((L - (int64_t)c * BC) < BC ? (L - (int64_t)c * BC) : BC);
+
+        // ---------------------------------------------- phase 0: chunk inputs
+        const float* Sc = c > 0 ? p.ckpt + ((slot0 + c - 1) * H + h) * (int64_t)(BD * BD)
+                                : (p.S0 ? p.S0 + unit * BD * BD : nullptr);
+        f32x4 Sr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int row = 16 * r + 4 * gq + pp;
+                Sr[r][pp] = Sc ? Sc[row * BD + col] : 0.f;
+                sS[row * PB + col] = f32_to_bf16(Sr[r][pp]);
+                sdS[row * PB + col] = f32_to_bf16(dSr[r][pp]);
+            }
+        if (tid < BD) {
+            // one key channel: Gamma over the chunk, the decay-scaled operands
+            const int ch = tid;
+            float G[BC];
+            float acc = 0.f;
+#pragma unroll
+            for (int t = 0; t < BC; ++t) {
+                acc += t < nt ? p.g[(t0 + t) * tok + hoff + ch] : 0.f;
+                G[t] = acc;
+                sG[t * PF + ch] = acc;
+            }
+            sGam[ch] = __expf(G[BC - 1]);
+#pragma unroll
+            for (int t = 0; t < BC; ++t) {
+                const uint16_t qb = t < nt ? gq_in[(t0 + t) * tok + hoff + ch] : (uint16_t)0;
+                const uint16_t kb = t < nt ? gk_in[(t0 + t) * tok + hoff + ch] : (uint16_t)0;
+                sQr[t * PB + ch] = qb;
+                sKr[t * PB + ch] = kb;
+                const float e = __expf(G[t]), ei = __expf(-G[t]), eb = __expf(G[BC - 1] - G[t]);
+                const float qf = bf(qb), kf = bf(kb);
+                sQt[t * PB + ch] = f32_to_bf16(qf * e);
+                sKt[t * PB + ch] = f32_to_bf16(kf * e);
+                sKi[t * PB + ch] = f32_to_bf16(kf * ei);
+                sKb[t * PB + ch] = f32_to_bf16(kf * eb);
+            }
+        } else {
+            // v and scale * dO rows (16-byte pieces), beta
+            constexpr int SEGS = BC * BD / 8;  // pieces per matrix
+            for (int s = tid - BD; s < 2 * SEGS; s += BNT - BD) {
+                const int which = s / SEGS, rem = s % SEGS, t = rem / (BD / 8), seg = rem % (BD / 8);
+                const uint16_t* src = which ? gdo_in : gv_in;
+                uint4 val = make_uint4(0u, 0u, 0u, 0u);
+                if (t < nt) val = *reinterpret_cast<const uint4*>(src + (t0 + t) * tok + hoff + 8 * seg);
+                if (which && scale != 1.f) {
+                    uint32_t wv[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        wv[e] = pack_bf16x2(__uint_as_float(wv[e] << 16) * scale,
+                                            __uint_as_float(wv[e] & 0xffff0000u) * scale);
+                    val = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                }
+                *reinterpret_cast<uint4*>((which ? sdO : sV) + t * PB + 8 * seg) = val;
+            }
+            if (tid - BD < BC) sBeta[tid - BD] = (tid - BD) < nt ? p.beta[(t0 + tid - BD) * H + h] : 0.f;
+        }
+        __syncthreads();  // B1
+
+        // ---------------------------------------------- phase 1: M, P; K-bar dS'; dgamma partials
+        if (w < 2) {
+            const uint16_t* X = w == 0 ? sKt : sQt;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < BD; kb += 32)
+                mma32(acc, frow(X, PB, li, kb + 4 * gq), frow(X, PB, li, kb + 16 + 4 * gq),
+                      frow(sKi, PB, li, kb + 4 * gq), frow(sKi, PB, li, kb + 16 + 4 * gq));
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int t = 4 * gq + pp, s = li;
+                if (w == 0) sM[t * P16 + s] = s < t ? acc[pp] : 0.f;
+                else sP[t * P16 + s] = s <= t ? acc[pp] : 0.f;
+            }
+        }
+        f32x4 dUa = zero4();  // (K-bar dS')[t][col]
+#pragma unroll
+        for (int r = 0; r < 8; r += 2)
+            mma32(dUa, frow(sKb, PB, li, 16 * r + 4 * gq), frow(sKb, PB, li, 16 * r + 16 + 4 * gq), fregs(dSr[r]),
+                  fregs(dSr[r + 1]));
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const float x = sum16(Sr[r][pp] * dSr[r][pp]);
+                if (li == 0) sdGam[w][16 * r + 4 * gq + pp] = x;
+            }
+        __syncthreads();  // B2
+
+        // ---------------------------------------------- phase 2: T; dU; dS without W
+        if (w == 0 && lane < BC) {
+            // column s of T = (I + A)^-1 by forward substitution, A = Diag(beta) M
+            const int s = lane;
+            float Tc[BC];
+#pragma unroll
+            for (int t = 0; t < BC; ++t) {
+                float acc = t == s ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < t; ++m) acc -= sBeta[t] * sM[t * P16 + m] * Tc[m];
+                Tc[t] = acc;
+                sT[t * P16 + s] = acc;
+            }
+        }
+        f32x4 dU;
+        {
+            f32x4 dUb = zero4();  // (P^T dO_s)[t][col]
+            mma16(dUb, fcol32(sP, P16, 4 * gq, li), fcol(sdO, PB, 4 * gq, col));
+            dU = dUa + dUb;
+        }
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) sdU[(4 * gq + pp) * PB + col] = f32_to_bf16(dU[pp]);
+        {
+            const uint2 bdo = fcol(sdO, PB, 4 * gq, col);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) dSr[r][pp] *= sGam[16 * r + 4 * gq + pp];
+                mma16(dSr[r], fcol(sQt, PB, 4 * gq, 16 * r + li), bdo);
+            }
+        }
+        __syncthreads();  // B3
+
+        // ---------------------------------------------- phase 3: W, U~, dV
+        f32x4 Ut, dvv;
+        {
+            // A = T Diag(beta): A[t][m] = T[t][m] beta_m
+            const f32x4 trow = *reinterpret_cast<const f32x4*>(&sT[li * P16 + 4 * gq]);
+            const uint2 aTb = make_uint2(pack_bf16x2(trow[0] * sBeta[4 * gq], trow[1] * sBeta[4 * gq + 1]),
+                                         pack_bf16x2(trow[2] * sBeta[4 * gq + 2], trow[3] * sBeta[4 * gq + 3]));
+            f32x4 Wt = zero4();
+            mma16(Wt, aTb, fcol(sKt, PB, 4 * gq, col));
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) sW[(4 * gq + pp) * PB + col] = f32_to_bf16(Wt[pp]);
+            Ut = zero4();
+            mma16(Ut, aTb, fcol(sV, PB, 4 * gq, col));
+            // dV = Diag(beta) T^T dU; beta partial rowsum(T^T dU * V)
+            f32x4 dBv = zero4();
+            mma16(dBv, fcol32(sT, P16, 4 * gq, li), fregs(dU));
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int m = 4 * gq + pp;
+                dvv[pp] = sBeta[m] * dBv[pp];
+                const float x = sum16(dBv[pp] * bf(sV[m * PB + col]));
+                if (li == 0) sdBv[w][m] = x;
+            }
+        }
+        __syncthreads();  // B4
+
+        // ---------------------------------------------- phase 4: U, dS -= W^T dU; row-owner products
+        {
+            f32x4 WS = zero4();
+#pragma unroll
+            for (int r = 0; r < 8; r += 2)
+                mma32(WS, frow(sW, PB, li, 16 * r + 4 * gq), frow(sW, PB, li, 16 * r + 16 + 4 * gq), fregs(Sr[r]),
+                      fregs(Sr[r + 1]));
+            const f32x4 U = Ut - WS;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) sU[(4 * gq + pp) * PB + col] = f32_to_bf16(U[pp]);
+            const uint2 bdu = fregs(dU);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) mma16(dSr[r], fneg(fcol(sW, PB, 4 * gq, 16 * r + li)), bdu);
+        }
+        // key rows R = 16w .. 16w + 15 (col): dQ~ = dO_s S^T, dW = -dU S^T, dW^T
+        f32x4 dQt = zero4(), dWt = zero4(), dWT = zero4();
+#pragma unroll
+        for (int cb = 0; cb < BD; cb += 32) {
+            const uint2 bS0 = frow(sS, PB, col, cb + 4 * gq), bS1 = frow(sS, PB, col, cb + 16 + 4 * gq);
+            const uint2 aU0 = frow(sdU, PB, li, cb + 4 * gq), aU1 = frow(sdU, PB, li, cb + 16 + 4 * gq);
+            mma32(dQt, frow(sdO, PB, li, cb + 4 * gq), frow(sdO, PB, li, cb + 16 + 4 * gq), bS0, bS1);
+            mma32(dWt, aU0, aU1, bS0, bS1);
+            mma32(dWT, bS0, bS1, aU0, aU1);
+        }
+        dWt = -dWt;  // dW[t][row]
+        dWT = -dWT;  // dW^T[row][t]
+        f32x4 dKt;   // dK~[t][row]
+        {
+            // from W = T Diag(beta) K~: Diag(beta) T^T dW; beta partial rowsum(T^T dW * K~)
+            f32x4 dBk = zero4();
+            mma16(dBk, fcol32(sT, P16, 4 * gq, li), fregs(dWt));
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int m = 4 * gq + pp;
+                dKt[pp] = sBeta[m] * dBk[pp];
+                const float ktf = bf(sKr[m * PB + col]) * __expf(sG[m * PF + col]);
+                const float x = sum16(dBk[pp] * ktf);
+                if (li == 0) sdBk[w][m] = x;
+            }
+            // this wave's share of dW (Diag(beta) K~)^T, as its transpose [s][t]
+            f32x4 dTk = zero4();
+            mma16(dTk, fscale(frow(sKt, PB, li, 16 * w + 4 * gq), sBeta[li]), fregs(dWT));
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) sdTk[w][(4 * gq + pp) * P16 + li] = dTk[pp];
+        }
+        if (w == 1) {
+            // dU (Diag(beta) V)^T
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int cb = 0; cb < BD; cb += 32)
+                mma32(acc, frow(sdU, PB, li, cb + 4 * gq), frow(sdU, PB, li, cb + 16 + 4 * gq),
+                      frow(sV, PB, li, cb + 4 * gq), frow(sV, PB, li, cb + 16 + 4 * gq));
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) sdTv[(4 * gq + pp) * P16 + li] = acc[pp] * sBeta[li];
+        }
+        __syncthreads();  // B5
+
+        // ---------------------------------------------- phase 5: dK-bar; dP; dA, dM
+        f32x4 dKb = zero4();
+#pragma unroll
+        for (int cb = 0; cb < BD; cb += 32)
+            mma32(dKb, frow(sU, PB, li, cb + 4 * gq), frow(sU, PB, li, cb + 16 + 4 * gq),
+                  frow(sdS, PB, col, cb + 4 * gq), frow(sdS, PB, col, cb + 16 + 4 * gq));
+        if (w == 0) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int cb = 0; cb < BD; cb += 32)
+                mma32(acc, frow(sdO, PB, li, cb + 4 * gq), frow(sdO, PB, li, cb + 16 + 4 * gq),
+                      frow(sU, PB, li, cb + 4 * gq), frow(sU, PB, li, cb + 16 + 4 * gq));
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int t = 4 * gq + pp, s = li;
+                sdP[t * P16 + s] = s <= t ? acc[pp] : 0.f;
+            }
+        } else if (w == 1) {
+            // dT[t][u] = dTv[t][u] + sum over waves of dTk^T; Z = dT T^T; dA = -T^T Z
+            uint2 adT;
+            {
+                float v4[4];
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int u = 4 * gq + pp;
+                    float acc = sdTv[li * P16 + u];
+#pragma unroll
+                    for (int ww = 0; ww < BNW; ++ww) acc += sdTk[ww][u * P16 + li];
+                    v4[pp] = acc;
+                }
+                adT = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+            }
+            f32x4 Z = zero4();
+            mma16(Z, adT, frow32(sT, P16, li, 4 * gq));
+            f32x4 dA = zero4();
+            mma16(dA, fcol32(sT, P16, 4 * gq, li), fregs(Z));
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int m = 4 * gq + pp, s = li;
+                const float da = s < m ? -dA[pp] : 0.f;
+                sdM[m * P16 + s] = sBeta[m] * da;
+                const float x = sum16(da * sM[m * P16 + s]);
+                if (li == 0) sdBa[m] = x;
+            }
+        }
+        __syncthreads();  // B6
+
+        // ---------------------------------------------- phase 6: dM, dP terms; q, k, Gamma gradients
+        {
+            f32x4 t1 = zero4(), t2 = zero4(), dKi = zero4();
+            const uint2 bKi = fcol(sKi, PB, 4 * gq, col);
+            mma16(t1, frow32(sdM, P16, li, 4 * gq), bKi);  // dM Ki
+            mma16(t2, frow32(sdP, P16, li, 4 * gq), bKi);  // dP Ki
+            mma32(dKi, fcol32(sdM, P16, 4 * gq, li), fcol32(sdP, P16, 4 * gq, li), fcol(sKt, PB, 4 * gq, col),
+                  fcol(sQt, PB, 4 * gq, col));          // dM^T K~ + dP^T Q~
+            const float eLg = sG[(BC - 1) * PF + col];
+        #pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int t = 4 * gq + pp;
+                const float G = sG[t * PF + col];
+                const float e = __expf(G), ei = __expf(-G), eb = __expf(eLg - G);
+                const float qf = bf(sQr[t * PB + col]), kf = bf(sKr[t * PB + col]);
+                const float Qt = qf * e, Kt = kf * e, Kb = kf * eb;
+                fq[t * PF + col] = (dQt[pp] + t2[pp]) * e;
+                fk[t * PF + col] = (dKt[pp] + t1[pp]) * e + dKi[pp] * ei + dKb[pp] * eb;
+                // The intra-chunk pair terms (through M and P) enter dGamma_t
+                // and dGamma_s with opposite signs and cancel exactly on the
+                // diagonal; both sides are formed from the bf16 operand values
+                // the products used, so they cancel to fp32 rounding.
+                // K-bar_t depends on Gamma_last - Gamma_t: its term enters
+                // dg_s for every s <= t through Gamma_t with a minus sign and
+                // for every s through Gamma_last with a plus sign, i.e. dg_s
+                // gets it for t < s only.  Kept apart and summed that way,
+                // the two large cancelling sums are never formed.
+                fG[t * PF + col] = dQt[pp] * Qt + t2[pp] * bf(sQt[t * PB + col]) + dKt[pp] * Kt +
+                                   t1[pp] * bf(sKt[t * PB + col]) - dKi[pp] * bf(sKi[t * PB + col]);
+                fB[t * PF + col] = dKb[pp] * Kb;
+                sDv[t * PB + col] = f32_to_bf16(dvv[pp]);
+            }
+            if (gq == 0) {
+                float dgam = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < BNW; ++ww) dgam += sdGam[ww][col];
+                sExt[col] = dgam * sGam[col];
+            }
+        }
+        __syncthreads();  // B7
+
+        // ---------------------------------------------- phase 7: stores
+        if (tid < BD) {
+            // dg_s = dgamma gamma + sum over t >= s of dGamma_t (the q, K~,
+            // Ki terms) + sum over t < s of the K-bar terms
+            const int ch = tid;
+            float pre[BC];
+            float a = 0.f;
+#pragma unroll
+            for (int t = 0; t < BC; ++t) {
+                pre[t] = a;
+                a += fB[t * PF + ch];
+            }
+            float acc = sExt[ch];
+#pragma unroll
+            for (int t = BC - 1; t >= 0; --t) {
+                acc += fG[t * PF + ch];
+                if (t < nt) p.dg[(t0 + t) * tok + hoff + ch] = acc + pre[t];
+            }
+        } else {
+            constexpr int SEGS = BC * BD / 8;
+            uint16_t* gdq = static_cast<uint16_t*>(p.dq);
+            uint16_t* gdk = static_cast<uint16_t*>(p.dk);
+            uint16_t* gdv = static_cast<uint16_t*>(p.dv);
+            for (int s = tid - BD; s < 3 * SEGS; s += BNT - BD) {
+                const int which = s / SEGS, rem = s % SEGS, t = rem / (BD / 8), seg = rem % (BD / 8);
+                if (t >= nt) continue;
+                const int64_t off = (t0 + t) * tok + hoff + 8 * seg;
+                if (which == 2) {
+                    *reinterpret_cast<uint4*>(gdv + off) = *reinterpret_cast<const uint4*>(sDv + t * PB + 8 * seg);
+                } else {
+                    const float* src = (which == 0 ? fq : fk) + t * PF + 8 * seg;
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+                    const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+                    *reinterpret_cast<uint4*>((which == 0 ? gdq : gdk) + off) =
+                        make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                                   pack_bf16x2(b[2], b[3]));
+                }
+            }
+            if (tid - BD < BC && tid - BD < nt) {
+                const int t = tid - BD;
+                float acc = sdBa[t];
+#pragma unroll
+                for (int ww = 0; ww < BNW; ++ww) acc += sdBv[ww][t] + sdBk[ww][t];
+                p.dbeta[(t0 + t) * H + h] = acc;
+            }
+        }
+        __syncthreads();  // B8: LDS reused by the next chunk
+    }
+    if (p.dS0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) p.dS0[unit * BD * BD + (16 * r + 4 * gq + pp) * BD + col] = dSr[r][pp];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward_bf16_d128(const BackwardParams& p, hipStream_t s) {
+    const int64_t units = (int64_t)p.N * p.H;
+    if (units <= 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_backward_kernel, dim3((unsigned)units), dim3(BNT), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -68,7 +68,7 @@ def kda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dty
 
 
 def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state,
-                  g_dtype=torch.float32):
+                  g_dtype=torch.float32, need_out=True):
     """Shared argument handling of the prefill entry points (shapes, dtypes,
     output allocation).  Returns a dict of the marshalled arguments."""
     dense_batch = q.dim() == 4
@@ -101,8 +101,10 @@ def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, ou
         if tuple(initial_state.shape) != (N, H, dk, dv):
             raise ValueError("initial_state must be [N, H, d_k, d_v]")
     dev = q.device
-    o = out if out is not None else torch.empty((T, H, dv), dtype=qdt, device=dev)
-    _need(o, "out", qdt, 3)
+    o = None
+    if need_out:
+        o = out if out is not None else torch.empty((T, H, dv), dtype=qdt, device=dev)
+        _need(o, "out", qdt, 3)
     fs = None
     if output_final_state:
         fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
@@ -244,6 +246,47 @@ def kda_output_gate(o, gate, weight, *, eps: float = 1e-6, out=None):
         _check(lib().kda_output_gate(T, H, dv, _DTYPES[o.dtype], float(eps), _ptr(o), _ptr(gate), _ptr(weight),
                                      _ptr(y), _stream(o.device)))
     return y
+
+
+def kda_prefill_backward_supported(dtype: torch.dtype, d_k: int, d_v: int) -> bool:
+    return bool(lib().kda_prefill_backward_supported(_DTYPES[dtype], d_k, d_v)) if dtype in _DTYPES else False
+
+
+def kda_prefill_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_state=None, cu_seqlens=None, *,
+                         scale: float = 1.0, num_seqs: int | None = None, need_d_initial_state: bool = True):
+    """Gradients of kda_prefill: for a loss with gradient d_o [T, H, d_v] with
+    respect to o and d_final_state [N, H, d_k, d_v] (or None) with respect to
+    the final states, returns (dq, dk, dv, dg, dbeta, d_initial_state) shaped
+    like q, k, v, g, beta and [N, H, d_k, d_v] (None if not requested).  q, k,
+    v and d_o are bf16 with d_k = d_v = 128; the other arguments are as in
+    kda_prefill (packed [T, H, d] layout)."""
+    if q.dim() != 3:
+        raise ValueError("kda_prefill_backward takes the packed [T, H, d] layout")
+    a = _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, None, False, None, need_out=False)
+    _need(d_o, "d_o", a["q"].dtype, 3)
+    if d_o.shape != (a["T"], a["H"], a["dv"]):
+        raise ValueError("d_o must be [T, H, d_v]")
+    if d_final_state is not None:
+        _need(d_final_state, "d_final_state", torch.float32, 4)
+        if tuple(d_final_state.shape) != (a["N"], a["H"], a["dk"], a["dv"]):
+            raise ValueError("d_final_state must be [N, H, d_k, d_v]")
+    dev = a["dev"]
+    dq = torch.empty_like(a["q"])
+    dk = torch.empty_like(a["k"])
+    dv = torch.empty_like(a["v"])
+    dg = torch.empty_like(a["g"])
+    dbeta = torch.empty_like(a["beta"])
+    dS0 = torch.empty((a["N"], a["H"], a["dk"], a["dv"]), dtype=torch.float32, device=dev) \
+        if need_d_initial_state else None
+    ws_bytes = int(lib().kda_prefill_backward_workspace_bytes(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"]))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    with torch.cuda.device(dev):
+        _check(lib().kda_prefill_backward(
+            a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], float(scale),
+            _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a["beta"]), _ptr(initial_state),
+            _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+            _ptr(dbeta), _ptr(dS0), _ptr(ws), ws_bytes, _stream(dev)))
+    return dq, dk, dv, dg, dbeta, dS0
 
 
 def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, out=None):

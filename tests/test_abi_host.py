@@ -56,7 +56,7 @@ def header_statuses():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     statuses = header_statuses()
     assert sorted(statuses) == list(range(8))
     for s, name in statuses.items():
@@ -253,3 +253,45 @@ def test_output_gate_validation(lib):
     assert _gate(lib, w=FAKE + 0x200002) == MISAL
     assert _gate(lib, y=FAKE + 0x200000) == BAD   # y == weight
     assert _gate(lib, T=0, o=None, g=None, w=None, y=None) == OK
+
+
+def _bwd(lib, N=1, T=32, H=2, d=128, dt=BF16, q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, g=FAKE + 0x300000,
+         b=FAKE + 0x400000, S0=None, cu=None, do=FAKE + 0x500000, dST=None, dq=FAKE + 0x600000,
+         dk=FAKE + 0x700000, dv=FAKE + 0x800000, dg=FAKE + 0x900000, db=FAKE + 0xa00000, dS0=None,
+         ws=FAKE + 0x1000000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.kda_prefill_backward_workspace_bytes(N, T, H, d, d, dt)
+    return lib.kda_prefill_backward(N, T, H, d, d, dt, 1.0, q, k, v, g, b, S0, cu, do, dST, dq, dk, dv, dg, db,
+                                    dS0, ws, ws_bytes, None)
+
+
+def test_prefill_backward_supported_set_and_workspace(lib):
+    assert lib.kda_prefill_backward_supported(BF16, 128, 128) == 1
+    assert lib.kda_prefill_backward_supported(F32, 128, 128) == 0
+    assert lib.kda_prefill_backward_supported(BF16, 64, 64) == 0
+    assert lib.kda_prefill_backward_supported(BF16, 128, 64) == 0
+    # one fp32 state per head for every full 16 tokens
+    assert lib.kda_prefill_backward_workspace_bytes(2, 100, 3, 128, 128, BF16) == (100 // 16) * 3 * 128 * 128 * 4
+    assert lib.kda_prefill_backward_workspace_bytes(1, 15, 3, 128, 128, BF16) == 0
+    assert lib.kda_prefill_backward_workspace_bytes(1, 64, 3, 128, 128, F32) == 0
+
+
+def test_prefill_backward_validation(lib):
+    assert _bwd(lib, T=-1) == BAD
+    assert _bwd(lib, H=0) == BAD
+    assert _bwd(lib, dt=F32) == UNSUP
+    assert _bwd(lib, d=64) == UNSUP
+    assert _bwd(lib, N=3) == BAD                        # 32 tokens do not split into 3 equal sequences
+    assert _bwd(lib, N=0) == BAD                        # tokens without sequences
+    for name in ("q", "k", "v", "g", "b", "do", "dq", "dk", "dv", "dg", "db"):
+        assert _bwd(lib, **{name: None}) == NULLP, name
+    assert _bwd(lib, dq=FAKE + 0x600008) == MISAL
+    assert _bwd(lib, db=FAKE + 0xa00002) == MISAL
+    assert _bwd(lib, dS0=FAKE + 0xb00008) == MISAL
+    assert _bwd(lib, dq=FAKE) == BAD                    # dq == q
+    assert _bwd(lib, dv=FAKE + 0x600000) == BAD         # dv == dq
+    assert _bwd(lib, dS0=FAKE + 0x1000000) == BAD       # d_initial_state == workspace
+    assert _bwd(lib, ws=None) == WS
+    assert _bwd(lib, ws_bytes=100) == WS
+    assert _bwd(lib, N=0, T=0, q=None, k=None, v=None, g=None, b=None, do=None, dq=None, dk=None, dv=None,
+                dg=None, db=None, ws=None, ws_bytes=0) == OK
