@@ -42,6 +42,13 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256
 # The fused entry reads bf16 decay logits z (256) instead of fp32 g.
 FUSED_BYTES_PER_TOKEN_HEAD = 3 * 256 + 256 + 4 + 256
+# Backward: each input and output once -- q, k, v, g, beta and d_o read (1540),
+# dq, dk, dv, dg and dbeta written (3 x 256 + 512 + 4).
+BWD_IO_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256 + 3 * 256 + 512 + 4
+# The same plus what this design adds: the forward read again (q, k, v, g,
+# beta) and an fp32 128 x 128 state per 16 tokens written by it and read by
+# the reverse kernel (65536 / 16 = 4096 each way).
+BWD_BYTES_PER_TOKEN_HEAD = BWD_IO_BYTES_PER_TOKEN_HEAD + (3 * 256 + 512 + 4) + 2 * 4096
 # Chunked flop count at the reference chunk C = 64, d = 128, causal tiles:
 # A, P, W, U~ and P U at C^2 d each, plus W S, Q~ S and Kbar^T U at 2 C d^2
 # each, per chunk of C tokens -> 5 C d + 6 d^2 per token-head.
@@ -273,6 +280,33 @@ def main():
         run_gate()
         og_ms = time_launches(run_gate, args.steps, stream)
         del og_gate, og_y
+        # the backward pass on the dense workload (forward again for its
+        # 16-token states, then the reverse chunk kernel), preallocated buffers
+        bw_ms = None
+        if kda.kda_prefill_backward_supported(torch.bfloat16, wd["d"], wd["d"]):
+            from linear_attention_recurrence_delta_amd._lib import lib as _kdalib
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(8)
+            b_do = torch.randn(wd["v"].shape, generator=gen, device=dev).to(torch.bfloat16)
+            b_dq, b_dk, b_dv = (torch.empty_like(wd[x]) for x in ("q", "k", "v"))
+            b_dg = torch.empty_like(wd["g"])
+            b_db = torch.empty_like(wd["beta"])
+            ws_b = int(_kdalib().kda_prefill_backward_workspace_bytes(wd["N"], wd["T"], wd["H"], wd["d"], wd["d"],
+                                                                      kda.KDA_DTYPE_BF16))
+            b_ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+            p_ = lambda t: t.data_ptr()
+
+            def run_bwd():
+                st = _kdalib().kda_prefill_backward(
+                    wd["N"], wd["T"], wd["H"], wd["d"], wd["d"], kda.KDA_DTYPE_BF16, 1.0,
+                    p_(wd["q"]), p_(wd["k"]), p_(wd["v"]), p_(wd["g"]), p_(wd["beta"]), None, None, p_(b_do), None,
+                    p_(b_dq), p_(b_dk), p_(b_dv), p_(b_dg), p_(b_db), None, p_(b_ws), ws_b, stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError("kda_prefill_backward failed: %d" % st)
+
+            run_bwd()
+            bw_ms = time_launches(run_bwd, args.steps, stream)
+            del b_do, b_dq, b_dk, b_dv, b_dg, b_db, b_ws
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)
         log("dense prefill avg %.3f ms (min %.3f), varlen avg %.3f ms, wall %.3f s" %
@@ -319,6 +353,16 @@ def main():
                              "traffic": measured_traffic("kda_output_gate_32k_x96"),
                              "kernel": "kda_output_gate_kernel<bf16, 128>",
                              "bytes_per_launch": 3 * o_d.numel() * 2},
+            },
+            "prefill_backward": None if bw_ms is None else {
+                "workload": "gradients of k3_dense_32k (dq, dk, dv, dg, dbeta) for a random bf16 d_o: the forward "
+                            "again keeping the state every 16 tokens, then the reverse chunk kernel",
+                "ms": sum(bw_ms) / len(bw_ms),
+                "tokens_per_s": wd["T"] / (sum(bw_ms) / len(bw_ms) * 1e-3),
+                "io_bytes_per_token_head": BWD_IO_BYTES_PER_TOKEN_HEAD,
+                "io_hbm_gbs": BWD_IO_BYTES_PER_TOKEN_HEAD * token_heads / (sum(bw_ms) / len(bw_ms) * 1e-3) / 1e9,
+                "bytes_per_token_head": BWD_BYTES_PER_TOKEN_HEAD,
+                "hbm_gbs": BWD_BYTES_PER_TOKEN_HEAD * token_heads / (sum(bw_ms) / len(bw_ms) * 1e-3) / 1e9,
             },
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
@@ -411,6 +455,7 @@ def main():
                              "note": "best of 5 torch copy_ launches of 2 GiB (read + write bytes)"}
     del src, dst
     for key in ("roofline", "mfma", "prefill_varlen", "prefill_checkpoints", "prefill_fused", "output_gate",
+                "prefill_backward",
                 "prefill_long_1m", "decode", "device_copy"):
         if key in result:
             line[key] = result[key]

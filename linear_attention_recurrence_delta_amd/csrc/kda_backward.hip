@@ -79,15 +79,6 @@ __device__ __forceinline__ uint2 fscale(uint2 a, float s) {
 }
 __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Sum over the 16 lanes of a row group (lanes 16g .. 16g + 15).
-__device__ __forceinline__ float sum16(float x) {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
-    return x;
-}
-
 __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     // S (bf16) of the chunk start; after its last use the fp32 staging of dq, dk and the dg terms
     __shared__ __align__(16) uint16_t sS[BD * PB];
@@ -151,62 +142,80 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         const int nt = (int)((L - (int64_t)c * BC) < BC ? (L - (int64_t)c * BC) : BC);
 
         // ---------------------------------------------- phase 0: chunk inputs
+        // Every global load of the chunk is issued before any is used, so
+        // the chunk pays one round trip to memory: the start state in the dS
+        // tile layout, and the token tiles as 16-byte pieces over all
+        // threads (g: one piece each; q, k, v, dO: two each).
         const float* Sc = c > 0 ? p.ckpt + ((slot0 + c - 1) * H + h) * (int64_t)(BD * BD)
                                 : (p.S0 ? p.S0 + unit * BD * BD : nullptr);
-        f32x4 Sr[8];
+        f32x4 sv[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r)
 #pragma unroll
+            for (int pp = 0; pp < 4; ++pp) sv[r][pp] = Sc ? Sc[(16 * r + 4 * gq + pp) * BD + col] : 0.f;
+        const int grow = tid >> 5, gseg = tid & 31;          // g piece: row, 4 floats
+        const int brow = (tid & 255) >> 4, bseg = tid & 15;  // bf16 piece: row, 8 values
+        f32x4 gv = zero4();
+        uint4 b0 = make_uint4(0u, 0u, 0u, 0u), b1 = b0;
+        if (grow < nt) gv = *reinterpret_cast<const f32x4*>(p.g + (t0 + grow) * tok + hoff + 4 * gseg);
+        if (brow < nt) {
+            const int64_t off = (t0 + brow) * tok + hoff + 8 * bseg;
+            b0 = *reinterpret_cast<const uint4*>((tid < 256 ? gq_in : gk_in) + off);
+            b1 = *reinterpret_cast<const uint4*>((tid < 256 ? gv_in : gdo_in) + off);
+        }
+        const float bet = tid < nt ? p.beta[(t0 + tid) * H + h] : 0.f;
+        *reinterpret_cast<f32x4*>(&sG[grow * PF + 4 * gseg]) = gv;  // g, summed in place below
+        *reinterpret_cast<uint4*>((tid < 256 ? sQr : sKr) + brow * PB + 8 * bseg) = b0;
+        if (tid >= 256 && scale != 1.f) {
+            uint32_t wv[4] = {b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                wv[e] = pack_bf16x2(__uint_as_float(wv[e] << 16) * scale, __uint_as_float(wv[e] & 0xffff0000u) * scale);
+            b1 = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        }
+        *reinterpret_cast<uint4*>((tid < 256 ? sV : sdO) + brow * PB + 8 * bseg) = b1;
+        if (tid < BC) sBeta[tid] = bet;
+        // S as bf16 B fragments for W S and in LDS; this wave's partial row
+        // sums of S * dS' (dgamma) from the fp32 values
+        uint2 Sb[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            Sb[r] = fregs(sv[r]);
+#pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int row = 16 * r + 4 * gq + pp;
-                Sr[r][pp] = Sc ? Sc[row * BD + col] : 0.f;
-                sS[row * PB + col] = f32_to_bf16(Sr[r][pp]);
+                sS[row * PB + col] = f32_to_bf16(sv[r][pp]);
                 sdS[row * PB + col] = f32_to_bf16(dSr[r][pp]);
+                const float x = row_inclusive_sum16(sv[r][pp] * dSr[r][pp]);  // total in lane 15 of the row
+                if (li == 15) sdGam[w][row] = x;
             }
+        }
+        __syncthreads();  // B0: raw tiles in LDS
         if (tid < BD) {
-            // one key channel: Gamma over the chunk, the decay-scaled operands
-            const int ch = tid;
-            float G[BC];
+            // Gamma: inclusive cumulative sum of g over the chunk, per key channel
+            float gc[BC];
+#pragma unroll
+            for (int t = 0; t < BC; ++t) gc[t] = sG[t * PF + tid];
             float acc = 0.f;
 #pragma unroll
             for (int t = 0; t < BC; ++t) {
-                acc += t < nt ? p.g[(t0 + t) * tok + hoff + ch] : 0.f;
-                G[t] = acc;
-                sG[t * PF + ch] = acc;
+                acc += gc[t];
+                sG[t * PF + tid] = acc;
             }
-            sGam[ch] = __expf(G[BC - 1]);
+            sGam[tid] = __expf(acc);
+        }
+        __syncthreads();  // B0b: Gamma
+        // the decay-scaled operands, four (token, channel) elements per thread
 #pragma unroll
-            for (int t = 0; t < BC; ++t) {
-                const uint16_t qb = t < nt ? gq_in[(t0 + t) * tok + hoff + ch] : (uint16_t)0;
-                const uint16_t kb = t < nt ? gk_in[(t0 + t) * tok + hoff + ch] : (uint16_t)0;
-                sQr[t * PB + ch] = qb;
-                sKr[t * PB + ch] = kb;
-                const float e = __expf(G[t]), ei = __expf(-G[t]), eb = __expf(G[BC - 1] - G[t]);
-                const float qf = bf(qb), kf = bf(kb);
-                sQt[t * PB + ch] = f32_to_bf16(qf * e);
-                sKt[t * PB + ch] = f32_to_bf16(kf * e);
-                sKi[t * PB + ch] = f32_to_bf16(kf * ei);
-                sKb[t * PB + ch] = f32_to_bf16(kf * eb);
-            }
-        } else {
-            // v and scale * dO rows (16-byte pieces), beta
-            constexpr int SEGS = BC * BD / 8;  // pieces per matrix
-            for (int s = tid - BD; s < 2 * SEGS; s += BNT - BD) {
-                const int which = s / SEGS, rem = s % SEGS, t = rem / (BD / 8), seg = rem % (BD / 8);
-                const uint16_t* src = which ? gdo_in : gv_in;
-                uint4 val = make_uint4(0u, 0u, 0u, 0u);
-                if (t < nt) val = *reinterpret_cast<const uint4*>(src + (t0 + t) * tok + hoff + 8 * seg);
-                if (which && scale != 1.f) {
-                    uint32_t wv[4] = {val.x, val.y, val.z, val.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        wv[e] = pack_bf16x2(__uint_as_float(wv[e] << 16) * scale,
-                                            __uint_as_float(wv[e] & 0xffff0000u) * scale);
-                    val = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                }
-                *reinterpret_cast<uint4*>((which ? sdO : sV) + t * PB + 8 * seg) = val;
-            }
-            if (tid - BD < BC) sBeta[tid - BD] = (tid - BD) < nt ? p.beta[(t0 + tid - BD) * H + h] : 0.f;
+        for (int e = tid; e < BC * BD; e += BNT) {
+            const int t = e / BD, ch = e % BD;
+            const float G = sG[t * PF + ch], GL = sG[(BC - 1) * PF + ch];
+            const float qf = bf(sQr[t * PB + ch]), kf = bf(sKr[t * PB + ch]);
+            const float ex = __expf(G), ei = __expf(-G), eb = __expf(GL - G);
+            sQt[t * PB + ch] = f32_to_bf16(qf * ex);
+            sKt[t * PB + ch] = f32_to_bf16(kf * ex);
+            sKi[t * PB + ch] = f32_to_bf16(kf * ei);
+            sKb[t * PB + ch] = f32_to_bf16(kf * eb);
         }
         __syncthreads();  // B1
 
@@ -230,27 +239,39 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         for (int r = 0; r < 8; r += 2)
             mma32(dUa, frow(sKb, PB, li, 16 * r + 4 * gq), frow(sKb, PB, li, 16 * r + 16 + 4 * gq), fregs(dSr[r]),
                   fregs(dSr[r + 1]));
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const float x = sum16(Sr[r][pp] * dSr[r][pp]);
-                if (li == 0) sdGam[w][16 * r + 4 * gq + pp] = x;
-            }
         __syncthreads();  // B2
 
         // ---------------------------------------------- phase 2: T; dU; dS without W
         if (w == 0 && lane < BC) {
-            // column s of T = (I + A)^-1 by forward substitution, A = Diag(beta) M
+            // column s of T = (I + A)^-1 by forward substitution, A = Diag(beta) M:
+            // T[t][s] = [t == s] - beta_t sum over m < t of M[t][m] T[m][s]
+            // (M is zero on and above the diagonal)
             const int s = lane;
             float Tc[BC];
+            f32x4 mr[4];
 #pragma unroll
+            for (int m = 0; m < BC; ++m) Tc[m] = 0.f;
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4) mr[m4] = *reinterpret_cast<const f32x4*>(&sM[4 * m4]);
+#pragma unroll 1
             for (int t = 0; t < BC; ++t) {
-                float acc = t == s ? 1.f : 0.f;
+                // the next row of M is requested while this one is used
+                f32x4 mn[4];
+                const int tn = t + 1 < BC ? t + 1 : t;
 #pragma unroll
-                for (int m = 0; m < t; ++m) acc -= sBeta[t] * sM[t * P16 + m] * Tc[m];
-                Tc[t] = acc;
-                sT[t * P16 + s] = acc;
+                for (int m4 = 0; m4 < 4; ++m4) mn[m4] = *reinterpret_cast<const f32x4*>(&sM[tn * P16 + 4 * m4]);
+                float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                for (int m = 0; m < BC; m += 2) {
+                    a0 += mr[m / 4][m % 4] * Tc[m];
+                    a1 += mr[m / 4][m % 4 + 1] * Tc[m + 1];
+                }
+                const float tv = (t == s ? 1.f : 0.f) - sBeta[t] * (a0 + a1);
+#pragma unroll
+                for (int m = 0; m < BC; ++m) Tc[m] = m == t ? tv : Tc[m];
+                sT[t * P16 + s] = tv;
+#pragma unroll
+                for (int m4 = 0; m4 < 4; ++m4) mr[m4] = mn[m4];
             }
         }
         f32x4 dU;
@@ -292,8 +313,8 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             for (int pp = 0; pp < 4; ++pp) {
                 const int m = 4 * gq + pp;
                 dvv[pp] = sBeta[m] * dBv[pp];
-                const float x = sum16(dBv[pp] * bf(sV[m * PB + col]));
-                if (li == 0) sdBv[w][m] = x;
+                const float x = row_inclusive_sum16(dBv[pp] * bf(sV[m * PB + col]));  // total in lane 15 of the row
+                if (li == 15) sdBv[w][m] = x;
             }
         }
         __syncthreads();  // B4
@@ -303,8 +324,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             f32x4 WS = zero4();
 #pragma unroll
             for (int r = 0; r < 8; r += 2)
-                mma32(WS, frow(sW, PB, li, 16 * r + 4 * gq), frow(sW, PB, li, 16 * r + 16 + 4 * gq), fregs(Sr[r]),
-                      fregs(Sr[r + 1]));
+                mma32(WS, frow(sW, PB, li, 16 * r + 4 * gq), frow(sW, PB, li, 16 * r + 16 + 4 * gq), Sb[r], Sb[r + 1]);
             const f32x4 U = Ut - WS;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) sU[(4 * gq + pp) * PB + col] = f32_to_bf16(U[pp]);
@@ -314,7 +334,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         }
         // key rows R = 16w .. 16w + 15 (col): dQ~ = dO_s S^T, dW = -dU S^T, dW^T
         f32x4 dQt = zero4(), dWt = zero4(), dWT = zero4();
-#pragma unroll
+#pragma unroll 1
         for (int cb = 0; cb < BD; cb += 32) {
             const uint2 bS0 = frow(sS, PB, col, cb + 4 * gq), bS1 = frow(sS, PB, col, cb + 16 + 4 * gq);
             const uint2 aU0 = frow(sdU, PB, li, cb + 4 * gq), aU1 = frow(sdU, PB, li, cb + 16 + 4 * gq);
@@ -334,8 +354,8 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 const int m = 4 * gq + pp;
                 dKt[pp] = sBeta[m] * dBk[pp];
                 const float ktf = bf(sKr[m * PB + col]) * __expf(sG[m * PF + col]);
-                const float x = sum16(dBk[pp] * ktf);
-                if (li == 0) sdBk[w][m] = x;
+                const float x = row_inclusive_sum16(dBk[pp] * ktf);  // total in lane 15 of the row
+                if (li == 15) sdBk[w][m] = x;
             }
             // this wave's share of dW (Diag(beta) K~)^T, as its transpose [s][t]
             f32x4 dTk = zero4();
@@ -346,7 +366,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         if (w == 1) {
             // dU (Diag(beta) V)^T
             f32x4 acc = zero4();
-#pragma unroll
+#pragma unroll 1
             for (int cb = 0; cb < BD; cb += 32)
                 mma32(acc, frow(sdU, PB, li, cb + 4 * gq), frow(sdU, PB, li, cb + 16 + 4 * gq),
                       frow(sV, PB, li, cb + 4 * gq), frow(sV, PB, li, cb + 16 + 4 * gq));
@@ -363,7 +383,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                   frow(sdS, PB, col, cb + 4 * gq), frow(sdS, PB, col, cb + 16 + 4 * gq));
         if (w == 0) {
             f32x4 acc = zero4();
-#pragma unroll
+#pragma unroll 1
             for (int cb = 0; cb < BD; cb += 32)
                 mma32(acc, frow(sdO, PB, li, cb + 4 * gq), frow(sdO, PB, li, cb + 16 + 4 * gq),
                       frow(sU, PB, li, cb + 4 * gq), frow(sU, PB, li, cb + 16 + 4 * gq));
@@ -396,8 +416,8 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 const int m = 4 * gq + pp, s = li;
                 const float da = s < m ? -dA[pp] : 0.f;
                 sdM[m * P16 + s] = sBeta[m] * da;
-                const float x = sum16(da * sM[m * P16 + s]);
-                if (li == 0) sdBa[m] = x;
+                const float x = row_inclusive_sum16(da * sM[m * P16 + s]);  // total in lane 15 of the row
+                if (li == 15) sdBa[m] = x;
             }
         }
         __syncthreads();  // B6
