@@ -295,7 +295,9 @@ int32_t kda_prefill_backward_supported(int32_t qkv_dtype, int32_t d_k,
 
 /* Bytes of device workspace kda_prefill_backward needs: the state after
  * every 16 tokens of each sequence, floor(total_tokens / 16) * num_heads *
- * d_k * d_v fp32 values (0 for unsupported arguments). */
+ * d_k * d_v fp32 values rounded up to 256 bytes, plus total_tokens *
+ * num_heads * d_v bf16 values for the forward run's output (0 for
+ * unsupported arguments). */
 size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs,
                                             int64_t total_tokens,
                                             int32_t num_heads, int32_t d_k,

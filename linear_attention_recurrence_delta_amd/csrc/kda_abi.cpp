@@ -10,6 +10,7 @@
 
 #include "kda.h"
 #include "kda_internal.h"
+#include "kda_backward.h"
 
 namespace {
 
@@ -295,6 +296,14 @@ kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int3
                         checkpoint_interval, checkpoints, checkpoint_capacity);
 }
 
+// Workspace of the backward: the state after every 16 tokens of each
+// sequence (at most total_tokens / 16 fp32 states per head), then the bf16 o
+// of the forward run that produces them, at a 256-byte aligned offset.
+static size_t backward_ckpt_bytes(int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v) {
+    const size_t b = (size_t)(total_tokens / 16) * (size_t)num_heads * (size_t)d_k * (size_t)d_v * sizeof(float);
+    return (b + 255) / 256 * 256;
+}
+
 int32_t kda_prefill_backward_supported(int32_t dtype, int32_t d_k, int32_t d_v) {
     return dtype == KDA_DTYPE_BF16 && d_k == 128 && d_v == 128 ? 1 : 0;
 }
@@ -303,8 +312,8 @@ size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs, int64_t total_toke
                                             int32_t d_k, int32_t d_v, int32_t dtype) {
     (void)num_seqs;
     if (!kda_prefill_backward_supported(dtype, d_k, d_v) || total_tokens < 0 || num_heads < 1) return 0;
-    // the state after every 16 tokens of each sequence: at most total_tokens / 16 states per head
-    return (size_t)(total_tokens / 16) * (size_t)num_heads * (size_t)d_k * (size_t)d_v * sizeof(float);
+    return backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) +
+           (size_t)total_tokens * (size_t)num_heads * (size_t)d_v * 2;  // the forward run's o (not returned)
 }
 
 kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
@@ -350,7 +359,7 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
         if (bad) return KDA_ERR_DOMAIN;
     }
     const int64_t units = (int64_t)num_seqs * num_heads;
-    // 1. the forward pass again, for the state at every 16-token boundary (its o is not stored)
+    // 1. the forward pass again, for the state at every 16-token boundary (its o goes to the workspace)
     if (total_tokens / 16 > 0) {
         const PrefillVariant* var = pick_variant(dtype, d_k, 16, units, false);
         if (!var) return KDA_ERR_UNSUPPORTED;
@@ -364,7 +373,7 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
         fp.beta = beta;
         fp.S0 = initial_state;
         fp.cu = cu_seqlens;
-        fp.o = nullptr;
+        fp.o = static_cast<char*>(workspace) + backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v);
         fp.Sout = nullptr;
         fp.T_total = total_tokens;
         fp.N = num_seqs;

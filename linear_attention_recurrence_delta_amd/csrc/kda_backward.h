@@ -1,0 +1,36 @@
+// kda_backward.h -- parameters and launcher of the prefill backward kernel
+// (kda_backward.hip), used by the C ABI in kda_abi.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Backward of the prefill (bf16 q/k/v/dO, d_k = d_v = 128, chunk 16): one
+// workgroup per (sequence, head) walks its chunks last to first.
+struct BackwardParams {
+    const void* q;          // [T, H, 128] bf16
+    const void* k;
+    const void* v;
+    const float* g;         // [T, H, 128]
+    const float* beta;      // [T, H]
+    const float* S0;        // [N, H, 128, 128] or nullptr (zeros)
+    const int32_t* cu;      // [N + 1] or nullptr (dense, seq_len each)
+    const void* dO;         // [T, H, 128] bf16: gradient with respect to o
+    const float* dST;       // [N, H, 128, 128] or nullptr: gradient with respect to the final state
+    const float* ckpt;      // state after every 16 tokens of each sequence (prefill checkpoints)
+    void* dq;               // [T, H, 128] bf16
+    void* dk;
+    void* dv;
+    float* dg;              // [T, H, 128]
+    float* dbeta;           // [T, H]
+    float* dS0;             // [N, H, 128, 128] or nullptr
+    int64_t T_total;
+    int32_t N, H, seq_len;
+    float scale;
+};
+
+hipError_t launch_backward_bf16_d128(const BackwardParams& p, hipStream_t s);
+
+}  // namespace kda

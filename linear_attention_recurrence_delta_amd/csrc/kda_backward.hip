@@ -37,6 +37,7 @@
 // supplies A[i][4g + p] and B[4g + p][i]; the accumulator holds C[4g + p][i].
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_backward.h"
 
 namespace kda {
 namespace {

@@ -84,30 +84,6 @@ struct DecodeParams {
     float scale;
 };
 
-// Backward of the prefill (bf16 q/k/v/dO, d_k = d_v = 128, chunk 16): one
-// workgroup per (sequence, head) walks its chunks last to first.
-struct BackwardParams {
-    const void* q;          // [T, H, 128] bf16
-    const void* k;
-    const void* v;
-    const float* g;         // [T, H, 128]
-    const float* beta;      // [T, H]
-    const float* S0;        // [N, H, 128, 128] or nullptr (zeros)
-    const int32_t* cu;      // [N + 1] or nullptr (dense, seq_len each)
-    const void* dO;         // [T, H, 128] bf16: gradient with respect to o
-    const float* dST;       // [N, H, 128, 128] or nullptr: gradient with respect to the final state
-    const float* ckpt;      // state after every 16 tokens of each sequence (prefill checkpoints)
-    void* dq;               // [T, H, 128] bf16
-    void* dk;
-    void* dv;
-    float* dg;              // [T, H, 128]
-    float* dbeta;           // [T, H]
-    float* dS0;             // [N, H, 128, 128] or nullptr
-    int64_t T_total;
-    int32_t N, H, seq_len;
-    float scale;
-};
-
 struct OutputGateParams {
     const void* o;          // [rows, d_v] dtype
     const void* gate;       // [rows, d_v] dtype
@@ -147,9 +123,6 @@ hipError_t check_inputs(const float* g, int64_t n_g, const float* beta, int64_t 
 hipError_t launch_decode_bf16(int D, const DecodeParams& p, int cus, hipStream_t s);
 hipError_t launch_decode_f32(int D, const DecodeParams& p, int cus, hipStream_t s);
 bool decode_d_supported(int D);
-
-// Backward launcher (one workgroup per (sequence, head)).
-hipError_t launch_backward_bf16_d128(const BackwardParams& p, hipStream_t s);
 
 // Output gate launchers (cus = compute units of the device); return
 // hipErrorInvalidValue for an unsupported d_v.

@@ -414,7 +414,7 @@ __global__ __launch_bounds__(64 * NWC) void kda_prefill_kernel(PrefillParams p) 
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int row = 16 * i + 4 * g4 + q4;
-                if (row < nv && go) go[((t0 + row) * H + h) * D + col0 + l16] = E::from_f32(p.scale * (QS[i][q4] + PU[q4]));
+                if (row < nv) go[((t0 + row) * H + h) * D + col0 + l16] = E::from_f32(p.scale * (QS[i][q4] + PU[q4]));
             }
         }
 #pragma unroll

@@ -658,10 +658,8 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             }
         // One store per lane; rows past the end of the sequence get an offset
         // beyond the buffer's range, and buffer stores out of range are dropped.
-        // o == nullptr (a run for its state checkpoints only): an empty range
-        // drops every store.
         const int64_t e0 = chunk_base(c);
-        const auto ro = go ? rsrc(go + e0, (n_tok_elems - e0) * 2) : rsrc(p.q, 0);
+        const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
         const uint32_t oo = l16 < nv ? o_voff : 0x80000000u;
         if constexpr (TPW == 2)
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
