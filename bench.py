@@ -45,10 +45,10 @@ FUSED_BYTES_PER_TOKEN_HEAD = 3 * 256 + 256 + 4 + 256
 # Backward: each input and output once -- q, k, v, g, beta and d_o read (1540),
 # dq, dk, dv, dg and dbeta written (3 x 256 + 512 + 4).
 BWD_IO_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256 + 3 * 256 + 512 + 4
-# The same plus what this design adds: the forward read again (q, k, v, g,
-# beta) and an fp32 128 x 128 state per 16 tokens written by it and read by
-# the reverse kernel (65536 / 16 = 4096 each way).
-BWD_BYTES_PER_TOKEN_HEAD = BWD_IO_BYTES_PER_TOKEN_HEAD + (3 * 256 + 512 + 4) + 2 * 4096
+# The reverse kernel: q, k, v, g, beta and d_o read, the five gradients
+# written, plus the fp32 128 x 128 state of every 16-token boundary read
+# (65536 / 16 = 4096), which the forward launch before it writes.
+BWD_REVERSE_BYTES_PER_TOKEN_HEAD = BWD_IO_BYTES_PER_TOKEN_HEAD + 4096
 # Chunked flop count at the reference chunk C = 64, d = 128, causal tiles:
 # A, P, W, U~ and P U at C^2 d each, plus W S, Q~ S and Kbar^T U at 2 C d^2
 # each, per chunk of C tokens -> 5 C d + 6 d^2 per token-head.
@@ -69,6 +69,7 @@ KERNEL_SOURCES = {
     "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
     "kda_prefill_fused_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
     "kda_output_gate_32k_x96": ("kda_output_gate.hip", "kda_device.h", "kda_internal.h"),
+    "kda_backward_k3_dense_32k": ("kda_backward.hip", "kda_backward.h", "kda_device.h"),
 }
 
 
@@ -114,6 +115,29 @@ def measured_mfma(kernel):
     simd_cycles = c["grbm_gui_active"] / c["xcds"] * c["simds"]
     return {"executed_bf16_flop_per_launch": c["mops_bf16"] * 512.0,
             "busy_frac_of_simd_cycles": c["busy_cycles"] / simd_cycles}
+
+
+def backward_entry(bw_ms, bwf_ms, token_heads, T):
+    """The backward call's timing: the whole call, its forward launch alone
+    (the checkpointed prefill, every 16 tokens) and the reverse kernel as the
+    difference, with the reverse kernel's HBM roofline."""
+    tot = sum(bw_ms) / len(bw_ms)
+    fwd = sum(bwf_ms) / len(bwf_ms)
+    rev = tot - fwd
+    rev_bytes = BWD_REVERSE_BYTES_PER_TOKEN_HEAD * token_heads
+    return {
+        "workload": "gradients of k3_dense_32k (dq, dk, dv, dg, dbeta) for a random bf16 d_o: the forward again "
+                    "keeping the state every 16 tokens, then the reverse chunk kernel",
+        "ms": tot, "tokens_per_s": T / (tot * 1e-3),
+        "forward_ckpt16_ms": fwd, "reverse_ms": rev,
+        "io_bytes_per_token_head": BWD_IO_BYTES_PER_TOKEN_HEAD,
+        "io_hbm_gbs": BWD_IO_BYTES_PER_TOKEN_HEAD * token_heads / (tot * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": rev_bytes / (rev * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": rev_bytes / (rev * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("kda_backward_k3_dense_32k"),
+                     "kernel": "kda_backward_kernel (reverse chunks; time = call - forward launch)",
+                     "bytes_per_launch": rev_bytes},
+    }
 
 
 def time_launches(fn, reps, stream):
@@ -306,7 +330,18 @@ def main():
 
             run_bwd()
             bw_ms = time_launches(run_bwd, args.steps, stream)
-            del b_do, b_dq, b_dk, b_dv, b_dg, b_db, b_ws
+            # its first launch alone: the forward keeping the state every 16 tokens
+            ck16 = b_ws[:(wd["T"] // 16) * wd["H"] * wd["d"] * wd["d"] * 4].view(torch.float32).view(
+                wd["T"] // 16, wd["H"], wd["d"], wd["d"])
+
+            def run_fwd16():
+                kda.kda_prefill_checkpointed(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"], None, None,
+                                             checkpoint_interval=16, chunk_size=C, out=o_d, final_state=s_d,
+                                             checkpoints=ck16)
+
+            run_fwd16()
+            bwf_ms = time_launches(run_fwd16, args.steps, stream)
+            del b_do, b_dq, b_dk, b_dv, b_dg, b_db, b_ws, ck16
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)
         log("dense prefill avg %.3f ms (min %.3f), varlen avg %.3f ms, wall %.3f s" %
@@ -354,16 +389,7 @@ def main():
                              "kernel": "kda_output_gate_kernel<bf16, 128>",
                              "bytes_per_launch": 3 * o_d.numel() * 2},
             },
-            "prefill_backward": None if bw_ms is None else {
-                "workload": "gradients of k3_dense_32k (dq, dk, dv, dg, dbeta) for a random bf16 d_o: the forward "
-                            "again keeping the state every 16 tokens, then the reverse chunk kernel",
-                "ms": sum(bw_ms) / len(bw_ms),
-                "tokens_per_s": wd["T"] / (sum(bw_ms) / len(bw_ms) * 1e-3),
-                "io_bytes_per_token_head": BWD_IO_BYTES_PER_TOKEN_HEAD,
-                "io_hbm_gbs": BWD_IO_BYTES_PER_TOKEN_HEAD * token_heads / (sum(bw_ms) / len(bw_ms) * 1e-3) / 1e9,
-                "bytes_per_token_head": BWD_BYTES_PER_TOKEN_HEAD,
-                "hbm_gbs": BWD_BYTES_PER_TOKEN_HEAD * token_heads / (sum(bw_ms) / len(bw_ms) * 1e-3) / 1e9,
-            },
+            "prefill_backward": None if bw_ms is None else backward_entry(bw_ms, bwf_ms, token_heads, wd["T"]),
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
                 "hbm_gbs": PREFILL_BYTES_PER_TOKEN_HEAD * wv["T"] * wv["H"] / (v_avg * 1e-3) / 1e9,
