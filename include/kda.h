@@ -293,11 +293,12 @@ kda_status kda_output_gate(int64_t total_tokens, int32_t num_heads,
 int32_t kda_prefill_backward_supported(int32_t qkv_dtype, int32_t d_k,
                                        int32_t d_v);
 
-/* Bytes of device workspace kda_prefill_backward needs: the state after
- * every 16 tokens of each sequence, floor(total_tokens / 16) * num_heads *
- * d_k * d_v fp32 values rounded up to 256 bytes, plus total_tokens *
- * num_heads * d_v bf16 values for the forward run's output (0 for
- * unsupported arguments). */
+/* Bytes of device workspace kda_prefill_backward needs (0 for unsupported
+ * arguments), three parts each rounded up to 256 bytes: the state after
+ * every 16 tokens of each sequence (floor(total_tokens / 16) * num_heads *
+ * d_k * d_v fp32), the forward run's output (total_tokens * num_heads * d_v
+ * bf16), and per half of the value columns the partial key-side gradients
+ * (2 * total_tokens * num_heads * (3 * d_k + 1) fp32). */
 size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs,
                                             int64_t total_tokens,
                                             int32_t num_heads, int32_t d_k,
@@ -311,10 +312,11 @@ size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs,
  * o and d_final_state with respect to the final states, it returns the
  * gradients with respect to q, k, v, g, beta and the initial states.
  *
- * Computed in two launches on `stream`: the forward recurrence again (the
+ * Computed in three launches on `stream`: the forward recurrence again (the
  * same kernel as kda_prefill, chunk 16), keeping the state at every 16-token
- * boundary in the workspace, then one workgroup per (sequence, head) that
- * walks its chunks last to first and carries the state gradient.
+ * boundary in the workspace; the reverse pass, two workgroups per (sequence,
+ * head), one per half of the value columns, walking the chunks last to first;
+ * and the sum of the two halves' key-side partials.
  *
  * Arguments shared with kda_prefill (num_seqs, total_tokens, num_heads, d_k,
  * d_v, qkv_dtype, scale, q, k, v, g, beta, initial_state, cu_seqlens) mean

@@ -296,12 +296,16 @@ kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int3
                         checkpoint_interval, checkpoints, checkpoint_capacity);
 }
 
-// Workspace of the backward: the state after every 16 tokens of each
-// sequence (at most total_tokens / 16 fp32 states per head), then the bf16 o
-// of the forward run that produces them, at a 256-byte aligned offset.
+// Workspace of the backward, each part at a 256-byte aligned offset: the
+// state after every 16 tokens of each sequence (at most total_tokens / 16
+// fp32 states per head), the bf16 o of the forward run that produces them,
+// and the reverse kernel's fp32 partials per half of the value columns.
+static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 static size_t backward_ckpt_bytes(int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v) {
-    const size_t b = (size_t)(total_tokens / 16) * (size_t)num_heads * (size_t)d_k * (size_t)d_v * sizeof(float);
-    return (b + 255) / 256 * 256;
+    return align256((size_t)(total_tokens / 16) * (size_t)num_heads * (size_t)d_k * (size_t)d_v * sizeof(float));
+}
+static size_t backward_o_bytes(int64_t total_tokens, int32_t num_heads, int32_t d_v) {
+    return align256((size_t)total_tokens * (size_t)num_heads * (size_t)d_v * 2);
 }
 
 int32_t kda_prefill_backward_supported(int32_t dtype, int32_t d_k, int32_t d_v) {
@@ -312,8 +316,8 @@ size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs, int64_t total_toke
                                             int32_t d_k, int32_t d_v, int32_t dtype) {
     (void)num_seqs;
     if (!kda_prefill_backward_supported(dtype, d_k, d_v) || total_tokens < 0 || num_heads < 1) return 0;
-    return backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) +
-           (size_t)total_tokens * (size_t)num_heads * (size_t)d_v * 2;  // the forward run's o (not returned)
+    return backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) + backward_o_bytes(total_tokens, num_heads, d_v) +
+           kda::backward_partial_bytes(total_tokens, num_heads);
 }
 
 kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
@@ -406,6 +410,8 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
     bp.dg = dg;
     bp.dbeta = dbeta;
     bp.dS0 = d_initial_state;
+    bp.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) +
+                                       backward_o_bytes(total_tokens, num_heads, d_v));
     bp.T_total = total_tokens;
     bp.N = num_seqs;
     bp.H = num_heads;

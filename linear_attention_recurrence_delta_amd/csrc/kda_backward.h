@@ -7,8 +7,9 @@
 
 namespace kda {
 
-// Backward of the prefill (bf16 q/k/v/dO, d_k = d_v = 128, chunk 16): one
-// workgroup per (sequence, head) walks its chunks last to first.
+// Backward of the prefill (bf16 q/k/v/dO, d_k = d_v = 128, chunk 16): two
+// workgroups per (sequence, head), one per half of the value columns, walk
+// the chunks last to first; a second kernel adds their key-side partials.
 struct BackwardParams {
     const void* q;          // [T, H, 128] bf16
     const void* k;
@@ -26,11 +27,15 @@ struct BackwardParams {
     float* dg;              // [T, H, 128]
     float* dbeta;           // [T, H]
     float* dS0;             // [N, H, 128, 128] or nullptr
+    float* part;            // per value half: dq, dk, dg [2][T, H, 128], then dbeta [2][T, H] (fp32)
     int64_t T_total;
     int32_t N, H, seq_len;
     float scale;
 };
 
+// Bytes of the partial buffer `part` for T_total tokens and H heads.
+size_t backward_partial_bytes(int64_t T_total, int32_t H);
+// Both kernels, in order, on stream s.
 hipError_t launch_backward_bf16_d128(const BackwardParams& p, hipStream_t s);
 
 }  // namespace kda

@@ -24,14 +24,24 @@
 // g by a reverse cumulative sum; Gamma_last, a sum of every g of the chunk,
 // adds dgamma * gamma and the Kb terms to all of them.
 //
-// Layout: one workgroup of 8 waves per (sequence, head), chunks last to
-// first.  Wave w owns value columns 16w..16w+15 in the column-separable
-// products (dU, U, the dS update, dV: dS stays in registers across chunks)
-// and key rows 16w..16w+15 in the products that sum over value columns
-// (dQ~, dW, dKb), with the full matrices staged in LDS between phases.  The
-// state at each chunk start comes from the forward kernel's checkpoints
-// (every 16 tokens) and enters the products as a bf16 operand, as in the
-// forward pass; dgamma uses its fp32 value.
+// Value columns never mix in the reverse pass (dS, dU, U, dV keep them
+// apart), and every key-side gradient (dq, dk, dg, dbeta) is linear in
+// column sums (dO_s S^T, dU S^T, U dS'^T, dO_s U^T, dU V^T, rowsum(S * dS')).
+// So two workgroups per (sequence, head), one per half of the value columns,
+// run the reverse pass independently: each writes dV and d(initial state)
+// for its columns and fp32 partials of dq, dk, dg and dbeta over its columns,
+// and a second kernel adds the two partials (in a fixed order).
+//
+// Layout of the reverse kernel: 4 waves per workgroup.  Wave w owns the 16
+// value columns 16w..16w+15 of its half in the column products (dU, U, the
+// dS update, dV; dS stays in registers across chunks) and key rows
+// 32w..32w+31 (two 16-row tiles) in the products that sum over the half's
+// value columns (dQ~, dW and its transpose, dKb), with full operands staged
+// in LDS between phases.  The state at each chunk start comes from the
+// forward kernel's checkpoints (every 16 tokens) and enters the products as a
+// bf16 operand, as in the forward pass; dgamma uses its fp32 value.  All
+// global loads of the next chunk are issued while the current one is
+// processed (one wave per SIMD leaves the registers for them).
 //
 // MFMA operand convention of kda_device.h: lane l (g = l / 16, i = l % 16)
 // supplies A[i][4g + p] and B[4g + p][i]; the accumulator holds C[4g + p][i].
@@ -44,11 +54,16 @@ namespace {
 
 constexpr int BD = 128;        // d_k = d_v
 constexpr int BC = 16;         // chunk length
-constexpr int BNW = 8;         // waves
+constexpr int NSL = 2;         // value halves (workgroups per (sequence, head))
+constexpr int CW = BD / NSL;   // value columns per workgroup
+constexpr int BNW = CW / 16;   // waves
 constexpr int BNT = 64 * BNW;  // threads
-constexpr int PB = BD + 8;     // bf16 row pitch (elements) of the LDS matrices
+constexpr int RT = BD / 16 / BNW;  // key-row tiles per wave
+constexpr int PB = BD + 8;     // bf16 row pitch (elements) of 128-wide LDS matrices
+constexpr int PS = CW + 8;     // bf16 row pitch of the value-half matrices
 constexpr int PF = BD + 4;     // fp32 row pitch
 constexpr int P16 = 16;        // pitch of the 16 x 16 fp32 matrices
+static_assert(RT == 2 && BNT == 256, "layout below assumes 4 waves and two key-row tiles per wave");
 
 // 4-value bf16 operand fragments from LDS: X[r][c..c+3] (one 8-byte read)
 // and X[r..r+3][c] (four reads).
@@ -80,24 +95,49 @@ __device__ __forceinline__ uint2 fscale(uint2 a, float s) {
 }
 __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// The global inputs of one chunk, held in registers until the chunk's turn.
+struct ChunkLoads {
+    f32x4 S[8];    // start state, rows 16r + 4gq + p of this lane's value column
+    f32x4 g[2];    // g tile pieces (4 floats each)
+    uint4 q, k;    // raw q, k pieces (8 bf16 each)
+    uint2 v, dO;   // this half's v, dO pieces (4 bf16 each)
+    float beta;
+};
+
 __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
-    // S (bf16) of the chunk start; after its last use the fp32 staging of dq, dk and the dg terms
-    __shared__ __align__(16) uint16_t sS[BD * PB];
-    // dS' (bf16); after its last use the bf16 staging of dv
-    __shared__ __align__(16) uint16_t sdS[BD * PB];
-    __shared__ __align__(16) uint16_t sQr[BC * PB], sKr[BC * PB], sV[BC * PB], sdO[BC * PB];
-    __shared__ __align__(16) uint16_t sQt[BC * PB], sKt[BC * PB], sKi[BC * PB], sKb[BC * PB];
-    __shared__ __align__(16) uint16_t sU[BC * PB], sdU[BC * PB], sW[BC * PB];
+    // S and dS' of this half (bf16); after their last use, the fp32 staging of
+    // the key-side partials (dq, dk and the two dg term sets)
+    __shared__ __align__(16) uint16_t sSS[2 * BD * PS];
+    __shared__ __align__(16) uint16_t sQr[BC * PB], sKr[BC * PB], sQt[BC * PB], sKt[BC * PB], sKi[BC * PB],
+        sKb[BC * PB], sW[BC * PB];
+    // this half's v, scale * dO (after its last use, the dv staging), U, dU
+    __shared__ __align__(16) uint16_t sV[BC * PS], sdO[BC * PS], sU[BC * PS], sdU[BC * PS];
     __shared__ __align__(16) float sG[BC * PF];
-    __shared__ __align__(16) float sM[256], sP[256], sT[256], sdP[256], sdTv[256], sdM[256];
+    __shared__ __align__(16) float sM[256], sP[256], sT[256], sdP[256], sdTv[256], sdM[256], sIA[256];
     __shared__ __align__(16) float sdTk[BNW][256];
     __shared__ float sBeta[BC], sGam[BD], sExt[BD], sdGam[BNW][BD], sdBv[BNW][BC], sdBk[BNW][BC], sdBa[BC];
+    static_assert(4 * BC * PF * sizeof(float) <= sizeof(sSS), "staging fits in the S / dS' area");
+    uint16_t* sS = sSS;
+    uint16_t* sdS = sSS + BD * PS;
+    float* fq = reinterpret_cast<float*>(sSS);
+    float* fk = fq + BC * PF;
+    float* fG = fk + BC * PF;
+    float* fB = fG + BC * PF;
+    uint16_t* sDv = sdO;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, gq = lane >> 4, li = lane & 15;
-    const int col = 16 * w + li;  // value column (column owners) or key row (row owners)
-    const int64_t unit = blockIdx.x;
     const int H = p.H;
+    const int64_t units = (int64_t)p.N * H;
+    // workgroup -> (unit, half): the two halves of a unit on one XCD (their
+    // q, k, g, beta and dO reads can share its L2)
+    const int64_t b = blockIdx.x;
+    const int64_t unit = ((b / 8) >> 1) * 8 + (b % 8);
+    const int half = (int)((b / 8) & 1);
+    if (unit >= units) return;
+    const int c0 = half * CW;         // first value column of this half
+    const int cl = 16 * w + li;       // this lane's column within the half
+    const int col = c0 + cl;          // ... and among all value columns
     const int n = (int)(unit / H), h = (int)(unit % H);
 
     int64_t bos, L, slot0;
@@ -108,7 +148,10 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         int64_t part = 0;
         for (int m = lane; m < n; m += 64) part += ((int64_t)p.cu[m + 1] - p.cu[m]) / BC;
         for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-        slot0 = part;
+        // the same in every lane: made wave-uniform so that the buffer
+        // descriptors built from it stay in scalar registers
+        slot0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(part >> 32)) << 32) |
+                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(part & 0xffffffff)));
     } else {
         bos = (int64_t)n * p.seq_len;
         L = p.seq_len;
@@ -122,15 +165,60 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     const uint16_t* gdo_in = static_cast<const uint16_t*>(p.dO);
     const float scale = p.scale;
     const int nch = (int)((L + BC - 1) / BC);
+    const int64_t nel = p.T_total * tok;  // elements of one [T, H, 128] tensor
+    float* pdq = p.part + (int64_t)half * nel;
+    float* pdk = p.part + (int64_t)(NSL + half) * nel;
+    float* pdg = p.part + (int64_t)(2 * NSL + half) * nel;
+    float* pdb = p.part + (int64_t)(3 * NSL) * nel + (int64_t)half * p.T_total * H;
 
-    float* fq = reinterpret_cast<float*>(sS);  // staging (aliases sS)
-    float* fk = fq + BC * PF;
-    float* fG = fk + BC * PF;
-    float* fB = fG + BC * PF;
-    uint16_t* sDv = sdS;                        // staging (aliases sdS)
+    // piece of each token tile this thread loads: g (2 x 4 floats), q and k
+    // (8 bf16 each) over rows x 128 channels; v and dO (4 bf16 each) over rows
+    // x this half's 64 columns
+    const int qrow = tid >> 4, qseg = tid & 15;
+
+    // Buffer ranges over the rows of one chunk: rows past the end of the
+    // sequence read zeros and their stores are dropped, so every load and
+    // store below is unconditional (a fixed count of memory operations per
+    // chunk, which keeps the compiler's waits on the prefetched loads from
+    // draining the previous chunk's stores).
+    auto rows_rsrc = [](const void* base, int nt, int64_t row_bytes, int row_len) {
+        return buffer_rsrc(base, nt > 0 ? (int)((int64_t)(nt - 1) * row_bytes + row_len) : 0);
+    };
+    constexpr int OOB = 0x40000000;  // an offset past every range
+
+    auto issue_loads = [&](int c, ChunkLoads& ld) {
+        const int64_t t0 = bos + (int64_t)c * BC;
+        const int nt = (int)((L - (int64_t)c * BC) < BC ? (L - (int64_t)c * BC) : BC);
+        const float* Sc = c > 0 ? p.ckpt + ((slot0 + c - 1) * H + h) * (int64_t)(BD * BD)
+                                : (p.S0 ? p.S0 + unit * BD * BD : nullptr);
+        const auto rS = buffer_rsrc(Sc ? Sc : p.g, Sc ? BD * BD * 4 : 0);
+        const int sv0 = (4 * gq * BD + col) * 4;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp)
+                ld.S[r][pp] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rS, sv0, (16 * r + pp) * BD * 4, 0));
+        const auto rg = rows_rsrc(p.g + t0 * tok + hoff, nt, tok * 4, BD * 4);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int pi = tid + BNT * j, row = pi >> 5, seg = pi & 31;
+            ld.g[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, (int)(row * tok * 4) + 16 * seg, 0, 0));
+        }
+        const int qoff = (int)(qrow * tok * 2);
+        ld.q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rows_rsrc(gq_in + t0 * tok + hoff, nt, tok * 2, BD * 2), qoff + 16 * qseg, 0, 0));
+        ld.k = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rows_rsrc(gk_in + t0 * tok + hoff, nt, tok * 2, BD * 2), qoff + 16 * qseg, 0, 0));
+        ld.v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rows_rsrc(gv_in + t0 * tok + hoff + c0, nt, tok * 2, CW * 2), qoff + 8 * qseg, 0, 0));
+        ld.dO = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                              rows_rsrc(gdo_in + t0 * tok + hoff + c0, nt, tok * 2, CW * 2), qoff + 8 * qseg, 0, 0));
+        ld.beta = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rows_rsrc(p.beta + t0 * H + h, nt, H * 4, 4),
+                                                                      tid < BC ? tid * H * 4 : OOB, 0, 0));
+    };
 
     // dS: gradient with respect to the state after the current chunk, rows
-    // 16r + 4gq + pp of column `col` in tile r.
+    // 16r + 4gq + pp of value column `col` in tile r.
     f32x4 dSr[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r)
@@ -138,59 +226,47 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         for (int pp = 0; pp < 4; ++pp)
             dSr[r][pp] = p.dST ? p.dST[unit * BD * BD + (16 * r + 4 * gq + pp) * BD + col] : 0.f;
 
+    ChunkLoads ld;
+    if (nch > 0) issue_loads(nch - 1, ld);
+
     for (int c = nch - 1; c >= 0; --c) {
         const int64_t t0 = bos + (int64_t)c * BC;
         const int nt = (int)((L - (int64_t)c * BC) < BC ? (L - (int64_t)c * BC) : BC);
 
-        // ---------------------------------------------- phase 0: chunk inputs
-        // Every global load of the chunk is issued before any is used, so
-        // the chunk pays one round trip to memory: the start state in the dS
-        // tile layout, and the token tiles as 16-byte pieces over all
-        // threads (g: one piece each; q, k, v, dO: two each).
-        const float* Sc = c > 0 ? p.ckpt + ((slot0 + c - 1) * H + h) * (int64_t)(BD * BD)
-                                : (p.S0 ? p.S0 + unit * BD * BD : nullptr);
-        f32x4 sv[8];
+        // ---------------------------------------------- phase 0: this chunk's loads into LDS
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) sv[r][pp] = Sc ? Sc[(16 * r + 4 * gq + pp) * BD + col] : 0.f;
-        const int grow = tid >> 5, gseg = tid & 31;          // g piece: row, 4 floats
-        const int brow = (tid & 255) >> 4, bseg = tid & 15;  // bf16 piece: row, 8 values
-        f32x4 gv = zero4();
-        uint4 b0 = make_uint4(0u, 0u, 0u, 0u), b1 = b0;
-        if (grow < nt) gv = *reinterpret_cast<const f32x4*>(p.g + (t0 + grow) * tok + hoff + 4 * gseg);
-        if (brow < nt) {
-            const int64_t off = (t0 + brow) * tok + hoff + 8 * bseg;
-            b0 = *reinterpret_cast<const uint4*>((tid < 256 ? gq_in : gk_in) + off);
-            b1 = *reinterpret_cast<const uint4*>((tid < 256 ? gv_in : gdo_in) + off);
+        for (int j = 0; j < 2; ++j) {
+            const int pi = tid + BNT * j, row = pi >> 5, seg = pi & 31;
+            *reinterpret_cast<f32x4*>(&sG[row * PF + 4 * seg]) = ld.g[j];  // g, summed in place below
         }
-        const float bet = tid < nt ? p.beta[(t0 + tid) * H + h] : 0.f;
-        *reinterpret_cast<f32x4*>(&sG[grow * PF + 4 * gseg]) = gv;  // g, summed in place below
-        *reinterpret_cast<uint4*>((tid < 256 ? sQr : sKr) + brow * PB + 8 * bseg) = b0;
-        if (tid >= 256 && scale != 1.f) {
-            uint32_t wv[4] = {b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                wv[e] = pack_bf16x2(__uint_as_float(wv[e] << 16) * scale, __uint_as_float(wv[e] & 0xffff0000u) * scale);
-            b1 = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+        *reinterpret_cast<uint4*>(sQr + qrow * PB + 8 * qseg) = ld.q;
+        *reinterpret_cast<uint4*>(sKr + qrow * PB + 8 * qseg) = ld.k;
+        *reinterpret_cast<uint2*>(sV + qrow * PS + 4 * qseg) = ld.v;
+        {
+            uint2 d = ld.dO;
+            if (scale != 1.f)
+                d = make_uint2(pack_bf16x2(__uint_as_float(d.x << 16) * scale, __uint_as_float(d.x & 0xffff0000u) * scale),
+                               pack_bf16x2(__uint_as_float(d.y << 16) * scale, __uint_as_float(d.y & 0xffff0000u) * scale));
+            *reinterpret_cast<uint2*>(sdO + qrow * PS + 4 * qseg) = d;
         }
-        *reinterpret_cast<uint4*>((tid < 256 ? sV : sdO) + brow * PB + 8 * bseg) = b1;
-        if (tid < BC) sBeta[tid] = bet;
+        if (tid < BC) sBeta[tid] = ld.beta;
         // S as bf16 B fragments for W S and in LDS; this wave's partial row
         // sums of S * dS' (dgamma) from the fp32 values
         uint2 Sb[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            Sb[r] = fregs(sv[r]);
+            Sb[r] = fregs(ld.S[r]);
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int row = 16 * r + 4 * gq + pp;
-                sS[row * PB + col] = f32_to_bf16(sv[r][pp]);
-                sdS[row * PB + col] = f32_to_bf16(dSr[r][pp]);
-                const float x = row_inclusive_sum16(sv[r][pp] * dSr[r][pp]);  // total in lane 15 of the row
+                sS[row * PS + cl] = f32_to_bf16(ld.S[r][pp]);
+                sdS[row * PS + cl] = f32_to_bf16(dSr[r][pp]);
+                const float x = row_inclusive_sum16(ld.S[r][pp] * dSr[r][pp]);  // total in lane 15 of the row
                 if (li == 15) sdGam[w][row] = x;
             }
         }
+        // the next chunk's loads, in flight while this one is processed
+        if (c > 0) issue_loads(c - 1, ld);
         __syncthreads();  // B0: raw tiles in LDS
         if (tid < BD) {
             // Gamma: inclusive cumulative sum of g over the chunk, per key channel
@@ -206,7 +282,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             sGam[tid] = __expf(acc);
         }
         __syncthreads();  // B0b: Gamma
-        // the decay-scaled operands, four (token, channel) elements per thread
+        // the decay-scaled operands, eight (token, channel) elements per thread
 #pragma unroll
         for (int e = tid; e < BC * BD; e += BNT) {
             const int t = e / BD, ch = e % BD;
@@ -220,7 +296,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         }
         __syncthreads();  // B1
 
-        // ---------------------------------------------- phase 1: M, P; K-bar dS'; dgamma partials
+        // ---------------------------------------------- phase 1: M, P; K-bar dS'
         if (w < 2) {
             const uint16_t* X = w == 0 ? sKt : sQt;
             f32x4 acc = zero4();
@@ -243,48 +319,58 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         __syncthreads();  // B2
 
         // ---------------------------------------------- phase 2: T; dU; dS without W
-        if (w == 0 && lane < BC) {
-            // column s of T = (I + A)^-1 by forward substitution, A = Diag(beta) M:
-            // T[t][s] = [t == s] - beta_t sum over m < t of M[t][m] T[m][s]
-            // (M is zero on and above the diagonal)
-            const int s = lane;
-            float Tc[BC];
-            f32x4 mr[4];
+        if (w == 0) {
+            // T = (I + A)^-1, A = Diag(beta) M, by Newton-Schulz steps
+            // T <- T + T (I - (I + A) T) from T = I - A: the residual
+            // I - (I + A) T squares each step (A^2, A^4, A^8) and A^16 = 0
+            // (A is strictly lower triangular), so three steps give T up to
+            // fp32 rounding.  fp32 matrix products on this wave; lane
+            // (gq, li) holds entries (4gq + pp, li).
+            f32x4 Tacc;
 #pragma unroll
-            for (int m = 0; m < BC; ++m) Tc[m] = 0.f;
+            for (int pp = 0; pp < 4; ++pp) {
+                const int r = 4 * gq + pp;
+                const float a = sBeta[r] * sM[r * P16 + li];
+                const float id = r == li ? 1.f : 0.f;
+                Tacc[pp] = id - a;
+                sIA[r * P16 + li] = id + a;
+                sT[r * P16 + li] = id - a;
+            }
 #pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) mr[m4] = *reinterpret_cast<const f32x4*>(&sM[4 * m4]);
-#pragma unroll 1
-            for (int t = 0; t < BC; ++t) {
-                // the next row of M is requested while this one is used
-                f32x4 mn[4];
-                const int tn = t + 1 < BC ? t + 1 : t;
+            for (int it = 0; it < 3; ++it) {
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                // X = (I + A) T; R = I - X
+                const f32x4 ia = *reinterpret_cast<const f32x4*>(&sIA[li * P16 + 4 * gq]);
+                const float4 bt = make_float4(sT[(4 * gq) * P16 + li], sT[(4 * gq + 1) * P16 + li],
+                                              sT[(4 * gq + 2) * P16 + li], sT[(4 * gq + 3) * P16 + li]);
+                const float4 at = make_float4(sT[li * P16 + 4 * gq], sT[li * P16 + 4 * gq + 1],
+                                              sT[li * P16 + 4 * gq + 2], sT[li * P16 + 4 * gq + 3]);
+                f32x4 X = zero4();
+                mma16(X, make_float4(ia[0], ia[1], ia[2], ia[3]), bt);
+                float4 R;
+                R.x = (4 * gq == li ? 1.f : 0.f) - X[0];
+                R.y = (4 * gq + 1 == li ? 1.f : 0.f) - X[1];
+                R.z = (4 * gq + 2 == li ? 1.f : 0.f) - X[2];
+                R.w = (4 * gq + 3 == li ? 1.f : 0.f) - X[3];
+                // T <- T + T R
+                mma16(Tacc, at, R);
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int m4 = 0; m4 < 4; ++m4) mn[m4] = *reinterpret_cast<const f32x4*>(&sM[tn * P16 + 4 * m4]);
-                float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-                for (int m = 0; m < BC; m += 2) {
-                    a0 += mr[m / 4][m % 4] * Tc[m];
-                    a1 += mr[m / 4][m % 4 + 1] * Tc[m + 1];
-                }
-                const float tv = (t == s ? 1.f : 0.f) - sBeta[t] * (a0 + a1);
-#pragma unroll
-                for (int m = 0; m < BC; ++m) Tc[m] = m == t ? tv : Tc[m];
-                sT[t * P16 + s] = tv;
-#pragma unroll
-                for (int m4 = 0; m4 < 4; ++m4) mr[m4] = mn[m4];
+                for (int pp = 0; pp < 4; ++pp) sT[(4 * gq + pp) * P16 + li] = Tacc[pp];
             }
         }
         f32x4 dU;
         {
             f32x4 dUb = zero4();  // (P^T dO_s)[t][col]
-            mma16(dUb, fcol32(sP, P16, 4 * gq, li), fcol(sdO, PB, 4 * gq, col));
+            mma16(dUb, fcol32(sP, P16, 4 * gq, li), fcol(sdO, PS, 4 * gq, cl));
             dU = dUa + dUb;
         }
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) sdU[(4 * gq + pp) * PB + col] = f32_to_bf16(dU[pp]);
+        for (int pp = 0; pp < 4; ++pp) sdU[(4 * gq + pp) * PS + cl] = f32_to_bf16(dU[pp]);
         {
-            const uint2 bdo = fcol(sdO, PB, 4 * gq, col);
+            const uint2 bdo = fcol(sdO, PS, 4 * gq, cl);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
 #pragma unroll
@@ -301,12 +387,16 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             const f32x4 trow = *reinterpret_cast<const f32x4*>(&sT[li * P16 + 4 * gq]);
             const uint2 aTb = make_uint2(pack_bf16x2(trow[0] * sBeta[4 * gq], trow[1] * sBeta[4 * gq + 1]),
                                          pack_bf16x2(trow[2] * sBeta[4 * gq + 2], trow[3] * sBeta[4 * gq + 3]));
-            f32x4 Wt = zero4();
-            mma16(Wt, aTb, fcol(sKt, PB, 4 * gq, col));
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) sW[(4 * gq + pp) * PB + col] = f32_to_bf16(Wt[pp]);
+            for (int rr = 0; rr < RT; ++rr) {
+                const int kc = 32 * w + 16 * rr + li;  // key channel of this W column
+                f32x4 Wt = zero4();
+                mma16(Wt, aTb, fcol(sKt, PB, 4 * gq, kc));
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) sW[(4 * gq + pp) * PB + kc] = f32_to_bf16(Wt[pp]);
+            }
             Ut = zero4();
-            mma16(Ut, aTb, fcol(sV, PB, 4 * gq, col));
+            mma16(Ut, aTb, fcol(sV, PS, 4 * gq, cl));
             // dV = Diag(beta) T^T dU; beta partial rowsum(T^T dU * V)
             f32x4 dBv = zero4();
             mma16(dBv, fcol32(sT, P16, 4 * gq, li), fregs(dU));
@@ -314,13 +404,13 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             for (int pp = 0; pp < 4; ++pp) {
                 const int m = 4 * gq + pp;
                 dvv[pp] = sBeta[m] * dBv[pp];
-                const float x = row_inclusive_sum16(dBv[pp] * bf(sV[m * PB + col]));  // total in lane 15 of the row
+                const float x = row_inclusive_sum16(dBv[pp] * bf(sV[m * PS + cl]));  // total in lane 15 of the row
                 if (li == 15) sdBv[w][m] = x;
             }
         }
         __syncthreads();  // B4
 
-        // ---------------------------------------------- phase 4: U, dS -= W^T dU; row-owner products
+        // ---------------------------------------------- phase 4: U, dS -= W^T dU; key-row products
         {
             f32x4 WS = zero4();
 #pragma unroll
@@ -328,66 +418,78 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 mma32(WS, frow(sW, PB, li, 16 * r + 4 * gq), frow(sW, PB, li, 16 * r + 16 + 4 * gq), Sb[r], Sb[r + 1]);
             const f32x4 U = Ut - WS;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) sU[(4 * gq + pp) * PB + col] = f32_to_bf16(U[pp]);
+            for (int pp = 0; pp < 4; ++pp) sU[(4 * gq + pp) * PS + cl] = f32_to_bf16(U[pp]);
             const uint2 bdu = fregs(dU);
 #pragma unroll
             for (int r = 0; r < 8; ++r) mma16(dSr[r], fneg(fcol(sW, PB, 4 * gq, 16 * r + li)), bdu);
         }
-        // key rows R = 16w .. 16w + 15 (col): dQ~ = dO_s S^T, dW = -dU S^T, dW^T
-        f32x4 dQt = zero4(), dWt = zero4(), dWT = zero4();
-#pragma unroll 1
-        for (int cb = 0; cb < BD; cb += 32) {
-            const uint2 bS0 = frow(sS, PB, col, cb + 4 * gq), bS1 = frow(sS, PB, col, cb + 16 + 4 * gq);
-            const uint2 aU0 = frow(sdU, PB, li, cb + 4 * gq), aU1 = frow(sdU, PB, li, cb + 16 + 4 * gq);
-            mma32(dQt, frow(sdO, PB, li, cb + 4 * gq), frow(sdO, PB, li, cb + 16 + 4 * gq), bS0, bS1);
-            mma32(dWt, aU0, aU1, bS0, bS1);
-            mma32(dWT, bS0, bS1, aU0, aU1);
-        }
-        dWt = -dWt;  // dW[t][row]
-        dWT = -dWT;  // dW^T[row][t]
-        f32x4 dKt;   // dK~[t][row]
-        {
+        // key rows kr = 32w + 16rr + li: dQ~ = dO_s S^T, dW = -dU S^T and dW^T,
+        // over this half's value columns
+        f32x4 dQt[RT], dKt[RT];
+        f32x4 dTk = zero4();
+        float bk[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rr = 0; rr < RT; ++rr) {
+            const int kr0 = 32 * w + 16 * rr;
+            f32x4 dWt = zero4(), dWT = zero4();
+            dQt[rr] = zero4();
+#pragma unroll
+            for (int cb = 0; cb < CW; cb += 32) {
+                const uint2 bS0 = frow(sS, PS, kr0 + li, cb + 4 * gq), bS1 = frow(sS, PS, kr0 + li, cb + 16 + 4 * gq);
+                const uint2 aU0 = frow(sdU, PS, li, cb + 4 * gq), aU1 = frow(sdU, PS, li, cb + 16 + 4 * gq);
+                mma32(dQt[rr], frow(sdO, PS, li, cb + 4 * gq), frow(sdO, PS, li, cb + 16 + 4 * gq), bS0, bS1);
+                mma32(dWt, aU0, aU1, bS0, bS1);
+                mma32(dWT, bS0, bS1, aU0, aU1);
+            }
+            dWt = -dWt;  // dW[t][row]
+            dWT = -dWT;  // dW^T[row][t]
             // from W = T Diag(beta) K~: Diag(beta) T^T dW; beta partial rowsum(T^T dW * K~)
             f32x4 dBk = zero4();
             mma16(dBk, fcol32(sT, P16, 4 * gq, li), fregs(dWt));
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int m = 4 * gq + pp;
-                dKt[pp] = sBeta[m] * dBk[pp];
-                const float ktf = bf(sKr[m * PB + col]) * __expf(sG[m * PF + col]);
-                const float x = row_inclusive_sum16(dBk[pp] * ktf);  // total in lane 15 of the row
-                if (li == 15) sdBk[w][m] = x;
+                dKt[rr][pp] = sBeta[m] * dBk[pp];
+                bk[pp] += dBk[pp] * bf(sKr[m * PB + kr0 + li]) * __expf(sG[m * PF + kr0 + li]);
             }
             // this wave's share of dW (Diag(beta) K~)^T, as its transpose [s][t]
-            f32x4 dTk = zero4();
-            mma16(dTk, fscale(frow(sKt, PB, li, 16 * w + 4 * gq), sBeta[li]), fregs(dWT));
+            mma16(dTk, fscale(frow(sKt, PB, li, kr0 + 4 * gq), sBeta[li]), fregs(dWT));
+        }
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) sdTk[w][(4 * gq + pp) * P16 + li] = dTk[pp];
+        for (int pp = 0; pp < 4; ++pp) {
+            const float x = row_inclusive_sum16(bk[pp]);  // total in lane 15 of the row
+            if (li == 15) sdBk[w][4 * gq + pp] = x;
+            sdTk[w][(4 * gq + pp) * P16 + li] = dTk[pp];
         }
         if (w == 1) {
-            // dU (Diag(beta) V)^T
+            // dU (Diag(beta) V)^T over this half's columns
             f32x4 acc = zero4();
-#pragma unroll 1
-            for (int cb = 0; cb < BD; cb += 32)
-                mma32(acc, frow(sdU, PB, li, cb + 4 * gq), frow(sdU, PB, li, cb + 16 + 4 * gq),
-                      frow(sV, PB, li, cb + 4 * gq), frow(sV, PB, li, cb + 16 + 4 * gq));
+#pragma unroll
+            for (int cb = 0; cb < CW; cb += 32)
+                mma32(acc, frow(sdU, PS, li, cb + 4 * gq), frow(sdU, PS, li, cb + 16 + 4 * gq),
+                      frow(sV, PS, li, cb + 4 * gq), frow(sV, PS, li, cb + 16 + 4 * gq));
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) sdTv[(4 * gq + pp) * P16 + li] = acc[pp] * sBeta[li];
         }
         __syncthreads();  // B5
 
         // ---------------------------------------------- phase 5: dK-bar; dP; dA, dM
-        f32x4 dKb = zero4();
+        f32x4 dKb[RT];
 #pragma unroll
-        for (int cb = 0; cb < BD; cb += 32)
-            mma32(dKb, frow(sU, PB, li, cb + 4 * gq), frow(sU, PB, li, cb + 16 + 4 * gq),
-                  frow(sdS, PB, col, cb + 4 * gq), frow(sdS, PB, col, cb + 16 + 4 * gq));
+        for (int rr = 0; rr < RT; ++rr) {
+            const int kr0 = 32 * w + 16 * rr;
+            dKb[rr] = zero4();
+#pragma unroll
+            for (int cb = 0; cb < CW; cb += 32)
+                mma32(dKb[rr], frow(sU, PS, li, cb + 4 * gq), frow(sU, PS, li, cb + 16 + 4 * gq),
+                      frow(sdS, PS, kr0 + li, cb + 4 * gq), frow(sdS, PS, kr0 + li, cb + 16 + 4 * gq));
+        }
         if (w == 0) {
             f32x4 acc = zero4();
-#pragma unroll 1
-            for (int cb = 0; cb < BD; cb += 32)
-                mma32(acc, frow(sdO, PB, li, cb + 4 * gq), frow(sdO, PB, li, cb + 16 + 4 * gq),
-                      frow(sU, PB, li, cb + 4 * gq), frow(sU, PB, li, cb + 16 + 4 * gq));
+#pragma unroll
+            for (int cb = 0; cb < CW; cb += 32)
+                mma32(acc, frow(sdO, PS, li, cb + 4 * gq), frow(sdO, PS, li, cb + 16 + 4 * gq),
+                      frow(sU, PS, li, cb + 4 * gq), frow(sU, PS, li, cb + 16 + 4 * gq));
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int t = 4 * gq + pp, s = li;
@@ -423,24 +525,26 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         }
         __syncthreads();  // B6
 
-        // ---------------------------------------------- phase 6: dM, dP terms; q, k, Gamma gradients
-        {
+        // ---------------------------------------------- phase 6: dM, dP terms; q, k, Gamma partials
+#pragma unroll
+        for (int rr = 0; rr < RT; ++rr) {
+            const int kc = 32 * w + 16 * rr + li;  // key channel of this lane
             f32x4 t1 = zero4(), t2 = zero4(), dKi = zero4();
-            const uint2 bKi = fcol(sKi, PB, 4 * gq, col);
+            const uint2 bKi = fcol(sKi, PB, 4 * gq, kc);
             mma16(t1, frow32(sdM, P16, li, 4 * gq), bKi);  // dM Ki
             mma16(t2, frow32(sdP, P16, li, 4 * gq), bKi);  // dP Ki
-            mma32(dKi, fcol32(sdM, P16, 4 * gq, li), fcol32(sdP, P16, 4 * gq, li), fcol(sKt, PB, 4 * gq, col),
-                  fcol(sQt, PB, 4 * gq, col));          // dM^T K~ + dP^T Q~
-            const float eLg = sG[(BC - 1) * PF + col];
-        #pragma unroll
+            mma32(dKi, fcol32(sdM, P16, 4 * gq, li), fcol32(sdP, P16, 4 * gq, li), fcol(sKt, PB, 4 * gq, kc),
+                  fcol(sQt, PB, 4 * gq, kc));           // dM^T K~ + dP^T Q~
+            const float eLg = sG[(BC - 1) * PF + kc];
+#pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int t = 4 * gq + pp;
-                const float G = sG[t * PF + col];
+                const float G = sG[t * PF + kc];
                 const float e = __expf(G), ei = __expf(-G), eb = __expf(eLg - G);
-                const float qf = bf(sQr[t * PB + col]), kf = bf(sKr[t * PB + col]);
+                const float qf = bf(sQr[t * PB + kc]), kf = bf(sKr[t * PB + kc]);
                 const float Qt = qf * e, Kt = kf * e, Kb = kf * eb;
-                fq[t * PF + col] = (dQt[pp] + t2[pp]) * e;
-                fk[t * PF + col] = (dKt[pp] + t1[pp]) * e + dKi[pp] * ei + dKb[pp] * eb;
+                fq[t * PF + kc] = (dQt[rr][pp] + t2[pp]) * e;
+                fk[t * PF + kc] = (dKt[rr][pp] + t1[pp]) * e + dKi[pp] * ei + dKb[rr][pp] * eb;
                 // The intra-chunk pair terms (through M and P) enter dGamma_t
                 // and dGamma_s with opposite signs and cancel exactly on the
                 // diagonal; both sides are formed from the bf16 operand values
@@ -450,24 +554,25 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 // for every s through Gamma_last with a plus sign, i.e. dg_s
                 // gets it for t < s only.  Kept apart and summed that way,
                 // the two large cancelling sums are never formed.
-                fG[t * PF + col] = dQt[pp] * Qt + t2[pp] * bf(sQt[t * PB + col]) + dKt[pp] * Kt +
-                                   t1[pp] * bf(sKt[t * PB + col]) - dKi[pp] * bf(sKi[t * PB + col]);
-                fB[t * PF + col] = dKb[pp] * Kb;
-                sDv[t * PB + col] = f32_to_bf16(dvv[pp]);
+                fG[t * PF + kc] = dQt[rr][pp] * Qt + t2[pp] * bf(sQt[t * PB + kc]) + dKt[rr][pp] * Kt +
+                                  t1[pp] * bf(sKt[t * PB + kc]) - dKi[pp] * bf(sKi[t * PB + kc]);
+                fB[t * PF + kc] = dKb[rr][pp] * Kb;
             }
             if (gq == 0) {
                 float dgam = 0.f;
 #pragma unroll
-                for (int ww = 0; ww < BNW; ++ww) dgam += sdGam[ww][col];
-                sExt[col] = dgam * sGam[col];
+                for (int ww = 0; ww < BNW; ++ww) dgam += sdGam[ww][kc];
+                sExt[kc] = dgam * sGam[kc];
             }
         }
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) sDv[(4 * gq + pp) * PS + cl] = f32_to_bf16(dvv[pp]);
         __syncthreads();  // B7
 
-        // ---------------------------------------------- phase 7: stores
+        // ---------------------------------------------- phase 7: stores (this half's partials, dV)
         if (tid < BD) {
             // dg_s = dgamma gamma + sum over t >= s of dGamma_t (the q, K~,
-            // Ki terms) + sum over t < s of the K-bar terms
+            // Ki terms) + sum over t < s of the K-bar terms, in place of dGamma
             const int ch = tid;
             float pre[BC];
             float a = 0.f;
@@ -480,34 +585,39 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
 #pragma unroll
             for (int t = BC - 1; t >= 0; --t) {
                 acc += fG[t * PF + ch];
-                if (t < nt) p.dg[(t0 + t) * tok + hoff + ch] = acc + pre[t];
+                fG[t * PF + ch] = acc + pre[t];
             }
-        } else {
-            constexpr int SEGS = BC * BD / 8;
-            uint16_t* gdq = static_cast<uint16_t*>(p.dq);
-            uint16_t* gdk = static_cast<uint16_t*>(p.dk);
-            uint16_t* gdv = static_cast<uint16_t*>(p.dv);
-            for (int s = tid - BD; s < 3 * SEGS; s += BNT - BD) {
-                const int which = s / SEGS, rem = s % SEGS, t = rem / (BD / 8), seg = rem % (BD / 8);
-                if (t >= nt) continue;
-                const int64_t off = (t0 + t) * tok + hoff + 8 * seg;
-                if (which == 2) {
-                    *reinterpret_cast<uint4*>(gdv + off) = *reinterpret_cast<const uint4*>(sDv + t * PB + 8 * seg);
-                } else {
-                    const float* src = (which == 0 ? fq : fk) + t * PF + 8 * seg;
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-                    const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-                    *reinterpret_cast<uint4*>((which == 0 ? gdq : gdk) + off) =
-                        make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                                   pack_bf16x2(b[2], b[3]));
-                }
+        }
+        __syncthreads();  // B7b
+        {
+            const auto rq = rows_rsrc(pdq + t0 * tok + hoff, nt, tok * 4, BD * 4);
+            const auto rk = rows_rsrc(pdk + t0 * tok + hoff, nt, tok * 4, BD * 4);
+            const auto rgd = rows_rsrc(pdg + t0 * tok + hoff, nt, tok * 4, BD * 4);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int pi = tid + BNT * j, t = pi >> 5, seg = pi & 31;
+                const int vo = (int)(t * tok * 4) + 16 * seg;
+                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4v*>(fq + t * PF + 4 * seg), rq, vo, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4v*>(fk + t * PF + 4 * seg), rk, vo, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4v*>(fG + t * PF + 4 * seg), rgd, vo, 0, 0);
             }
-            if (tid - BD < BC && tid - BD < nt) {
-                const int t = tid - BD;
+            // dV of this half: 128 pieces of 8 bf16 (threads 0..127)
+            {
+                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+                const int t = (tid & 127) >> 3, seg = tid & 7;
+                const auto rv = rows_rsrc(static_cast<uint16_t*>(p.dv) + t0 * tok + hoff + c0, nt, tok * 2, CW * 2);
+                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4v*>(sDv + t * PS + 8 * seg), rv,
+                                                       tid < 128 ? (int)(t * tok * 2) + 16 * seg : OOB, 0, 0);
+            }
+            // dbeta partial (threads 0..15)
+            {
+                const int t = tid & (BC - 1);
                 float acc = sdBa[t];
 #pragma unroll
                 for (int ww = 0; ww < BNW; ++ww) acc += sdBv[ww][t] + sdBk[ww][t];
-                p.dbeta[(t0 + t) * H + h] = acc;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rows_rsrc(pdb + t0 * H + h, nt, H * 4, 4),
+                                                      tid < BC ? t * H * 4 : OOB, 0, 0);
             }
         }
         __syncthreads();  // B8: LDS reused by the next chunk
@@ -520,13 +630,46 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     }
 }
 
+// dq, dk (bf16), dg, dbeta (fp32) = partial of the first value half + that of
+// the second, per element; 32 threads per (token, head) row, 4 channels each.
+__global__ __launch_bounds__(256) void kda_backward_sum_kernel(BackwardParams p) {
+    const int64_t rows = p.T_total * p.H;
+    const int64_t nel = rows * BD;
+    const int64_t row = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+    const int seg = threadIdx.x & 31;
+    if (row >= rows) return;
+    const int64_t e = row * BD + 4 * seg;
+    const f32x4 q = *reinterpret_cast<const f32x4*>(p.part + e) + *reinterpret_cast<const f32x4*>(p.part + nel + e);
+    const f32x4 k =
+        *reinterpret_cast<const f32x4*>(p.part + 2 * nel + e) + *reinterpret_cast<const f32x4*>(p.part + 3 * nel + e);
+    const f32x4 g =
+        *reinterpret_cast<const f32x4*>(p.part + 4 * nel + e) + *reinterpret_cast<const f32x4*>(p.part + 5 * nel + e);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.dq) + e) = make_uint2(pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3]));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.dk) + e) = make_uint2(pack_bf16x2(k[0], k[1]), pack_bf16x2(k[2], k[3]));
+    *reinterpret_cast<f32x4*>(p.dg + e) = g;
+    if (seg == 0) p.dbeta[row] = p.part[6 * nel + row] + p.part[6 * nel + rows + row];
+}
+
 }  // namespace
+
+size_t backward_partial_bytes(int64_t T_total, int32_t H) {
+    const int64_t rows = T_total * H;
+    return (size_t)(3 * NSL * rows * BD + NSL * rows) * sizeof(float);
+}
 
 hipError_t launch_backward_bf16_d128(const BackwardParams& p, hipStream_t s) {
     const int64_t units = (int64_t)p.N * p.H;
     if (units <= 0) return hipSuccess;
-    hipLaunchKernelGGL(kda_backward_kernel, dim3((unsigned)units), dim3(BNT), 0, s, p);
-    return hipGetLastError();
+    const int64_t wgs = (units + 7) / 8 * 8 * NSL;
+    hipLaunchKernelGGL(kda_backward_kernel, dim3((unsigned)wgs), dim3(BNT), 0, s, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t rows = p.T_total * p.H;
+    if (rows > 0) {
+        hipLaunchKernelGGL(kda_backward_sum_kernel, dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, s, p);
+        err = hipGetLastError();
+    }
+    return err;
 }
 
 }  // namespace kda

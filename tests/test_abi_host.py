@@ -270,10 +270,12 @@ def test_prefill_backward_supported_set_and_workspace(lib):
     assert lib.kda_prefill_backward_supported(F32, 128, 128) == 0
     assert lib.kda_prefill_backward_supported(BF16, 64, 64) == 0
     assert lib.kda_prefill_backward_supported(BF16, 128, 64) == 0
-    # one fp32 state per head for every full 16 tokens, then the forward run's bf16 o
-    ck = lambda T, H: -(-(T // 16) * H * 128 * 128 * 4 // 256) * 256
-    assert lib.kda_prefill_backward_workspace_bytes(2, 100, 3, 128, 128, BF16) == ck(100, 3) + 100 * 3 * 128 * 2
-    assert lib.kda_prefill_backward_workspace_bytes(1, 15, 3, 128, 128, BF16) == 15 * 3 * 128 * 2
+    # one fp32 state per head for every full 16 tokens, the forward run's bf16 o,
+    # the two value halves' fp32 partials of dq, dk, dg and dbeta
+    r256 = lambda b: -(-b // 256) * 256
+    want = lambda T, H: (r256((T // 16) * H * 128 * 128 * 4) + r256(T * H * 128 * 2) + 2 * T * H * (3 * 128 + 1) * 4)
+    assert lib.kda_prefill_backward_workspace_bytes(2, 100, 3, 128, 128, BF16) == want(100, 3)
+    assert lib.kda_prefill_backward_workspace_bytes(1, 15, 3, 128, 128, BF16) == want(15, 3)
     assert lib.kda_prefill_backward_workspace_bytes(1, 64, 3, 128, 128, F32) == 0
 
 
