@@ -208,6 +208,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "long"], default="all")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward timing (counter runs of the prefill kernels: the backward's forward "
+                         "launch is the same kernel)")
     ap.add_argument("--no-checkpoints", action="store_true",
                     help="skip the checkpointed prefill timing (counter runs per kernel launch)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -307,7 +310,7 @@ def main():
         # the backward pass on the dense workload (forward again for its
         # 16-token states, then the reverse chunk kernel), preallocated buffers
         bw_ms = None
-        if kda.kda_prefill_backward_supported(torch.bfloat16, wd["d"], wd["d"]):
+        if not args.no_backward and kda.kda_prefill_backward_supported(torch.bfloat16, wd["d"], wd["d"]):
             from linear_attention_recurrence_delta_amd._lib import lib as _kdalib
             gen = torch.Generator(device=dev)
             gen.manual_seed(8)
