@@ -174,3 +174,30 @@ def test_k3_dense_32k_checkpoints(kda, oracle_mod):
     e_s = (S_r - S).abs().max().item() / S.abs().max().item()
     say("  resumed from checkpoint 3: rel err o=%.3e S=%.3e" % (e_o, e_s))
     assert e_o <= 1e-6 and e_s <= 1e-6
+
+
+def test_k3_varlen_32k_backward_sampled_units(kda, oracle_mod):
+    """The backward on the 16-sequence K3 varlen batch (1536 (sequence, head)
+    units, 3072 workgroups): the longest and the shortest sequence on two
+    heads each against the oracle, with the gradient tensors restricted to
+    those tokens and heads."""
+    from linear_attention_recurrence_delta_amd import synth
+    w = synth.workload_inputs("k3_varlen_32k", DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(708)
+    d_o = torch.randn(w["v"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    say("CASE backward k3 varlen 32K x 96")
+    got = kda.kda_prefill_backward(w["q"], w["k"], w["v"], w["g"], w["beta"], d_o, cu_seqlens=w["cu"])
+    torch.cuda.synchronize()
+    lengths = w["lengths"]
+    cu = [0] + [int(x) for x in np.cumsum(lengths)]
+    picks = [int(np.argmax(lengths)), int(np.argmin(lengths))]
+    heads = torch.tensor([3, 77], device=DEV)
+    for n in picks:
+        a, b = cu[n], cu[n + 1]
+        sl = lambda x: f64(x[a:b].index_select(1, heads))
+        ref = oracle_mod.prefill_backward(sl(w["q"]), sl(w["k"]), sl(w["v"]), sl(w["g"]), sl(w["beta"]), sl(d_o))
+        errs = [rel_err(sl(x), r) for x, r in zip(got[:5], ref[:5])]
+        errs.append(rel_err(f64(got[5][n].index_select(0, heads)), ref[5][0]))
+        say("  sequence %d (%d tokens): " % (n, b - a) + " ".join("%.2e" % e for e in errs))
+        assert max(errs) <= TOL[torch.bfloat16]
