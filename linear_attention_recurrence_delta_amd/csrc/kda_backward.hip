@@ -36,12 +36,14 @@
 // value columns 16w..16w+15 of its half in the column products (dU, U, the
 // dS update, dV; dS stays in registers across chunks) and key rows
 // 32w..32w+31 (two 16-row tiles) in the products that sum over the half's
-// value columns (dQ~, dW and its transpose, dKb), with full operands staged
-// in LDS between phases.  The state at each chunk start comes from the
+// value columns (dQ~, dW and its transpose, dKb, dgamma), with full operands
+// staged in LDS between phases.  The state at each chunk start comes from the
 // forward kernel's checkpoints (every 16 tokens) and enters the products as a
-// bf16 operand, as in the forward pass; dgamma uses its fp32 value.  All
-// global loads of the next chunk are issued while the current one is
-// processed (one wave per SIMD leaves the registers for them).
+// bf16 operand, as in the forward pass; dgamma is the diagonal of S dS'^T
+// formed from the same bf16 operands.  e^Gamma and e^-Gamma are computed once
+// per chunk and kept in LDS for the gradient formulas.  All global loads of
+// the next chunk are issued while the current one is processed (one wave per
+// SIMD leaves the registers for them).
 //
 // MFMA operand convention of kda_device.h: lane l (g = l / 16, i = l % 16)
 // supplies A[i][4g + p] and B[4g + p][i]; the accumulator holds C[4g + p][i].
@@ -106,23 +108,24 @@ struct ChunkLoads {
 
 __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     // S and dS' of this half (bf16); after their last use, the fp32 staging of
-    // the key-side partials (dq, dk and the two dg term sets)
+    // the key-side partials (dq, dk, dg)
     __shared__ __align__(16) uint16_t sSS[2 * BD * PS];
     __shared__ __align__(16) uint16_t sQr[BC * PB], sKr[BC * PB], sQt[BC * PB], sKt[BC * PB], sKi[BC * PB],
         sKb[BC * PB], sW[BC * PB];
     // this half's v, scale * dO (after its last use, the dv staging), U, dU
     __shared__ __align__(16) uint16_t sV[BC * PS], sdO[BC * PS], sU[BC * PS], sdU[BC * PS];
-    __shared__ __align__(16) float sG[BC * PF];
-    __shared__ __align__(16) float sM[256], sP[256], sT[256], sdP[256], sdTv[256], sdM[256], sIA[256];
+    // Gamma, then e^Gamma and e^-Gamma (fp32)
+    __shared__ __align__(16) float sG[BC * PF], sE[BC * PF], sEi[BC * PF];
+    __shared__ __align__(16) float sM[256], sP[256], sT[256], sdP[256], sdTv[256], sdM[256];
     __shared__ __align__(16) float sdTk[BNW][256];
-    __shared__ float sBeta[BC], sGam[BD], sExt[BD], sdGam[BNW][BD], sdBv[BNW][BC], sdBk[BNW][BC], sdBa[BC];
-    static_assert(4 * BC * PF * sizeof(float) <= sizeof(sSS), "staging fits in the S / dS' area");
+    __shared__ __align__(16) float sGam[BD];
+    __shared__ float sBeta[BC], sExt[BD], sdBv[BNW][BC], sdBk[BNW][BC], sdBa[BC];
+    static_assert(3 * BC * PF * sizeof(float) <= sizeof(sSS), "staging fits in the S / dS' area");
     uint16_t* sS = sSS;
     uint16_t* sdS = sSS + BD * PS;
     float* fq = reinterpret_cast<float*>(sSS);
     float* fk = fq + BC * PF;
     float* fG = fk + BC * PF;
-    float* fB = fG + BC * PF;
     uint16_t* sDv = sdO;
 
     const int tid = threadIdx.x;
@@ -226,6 +229,10 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         for (int pp = 0; pp < 4; ++pp)
             dSr[r][pp] = p.dST ? p.dST[unit * BD * BD + (16 * r + 4 * gq + pp) * BD + col] : 0.f;
 
+    // B fragment of the 16 x 16 identity (bf16 1.0 = 0x3f80)
+    const uint2 eye = make_uint2((4 * gq == li ? 0x3f80u : 0u) | (4 * gq + 1 == li ? 0x3f800000u : 0u),
+                                 (4 * gq + 2 == li ? 0x3f80u : 0u) | (4 * gq + 3 == li ? 0x3f800000u : 0u));
+
     ChunkLoads ld;
     if (nch > 0) issue_loads(nch - 1, ld);
 
@@ -250,20 +257,19 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             *reinterpret_cast<uint2*>(sdO + qrow * PS + 4 * qseg) = d;
         }
         if (tid < BC) sBeta[tid] = ld.beta;
-        // S as bf16 B fragments for W S and in LDS; this wave's partial row
-        // sums of S * dS' (dgamma) from the fp32 values
+        // S as bf16 B fragments for W S, and S, dS' as bf16 in LDS: a tile
+        // times the identity with the tile as the A operand gives its
+        // transpose, so each lane then holds 4 adjacent columns of one row
+        // (one 8-byte LDS write)
         uint2 Sb[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             Sb[r] = fregs(ld.S[r]);
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const int row = 16 * r + 4 * gq + pp;
-                sS[row * PS + cl] = f32_to_bf16(ld.S[r][pp]);
-                sdS[row * PS + cl] = f32_to_bf16(dSr[r][pp]);
-                const float x = row_inclusive_sum16(ld.S[r][pp] * dSr[r][pp]);  // total in lane 15 of the row
-                if (li == 15) sdGam[w][row] = x;
-            }
+            f32x4 tS = zero4(), tD = zero4();
+            mma16(tS, Sb[r], eye);
+            mma16(tD, fregs(dSr[r]), eye);
+            *reinterpret_cast<uint2*>(sS + (16 * r + li) * PS + 16 * w + 4 * gq) = fregs(tS);
+            *reinterpret_cast<uint2*>(sdS + (16 * r + li) * PS + 16 * w + 4 * gq) = fregs(tD);
         }
         // the next chunk's loads, in flight while this one is processed
         if (c > 0) issue_loads(c - 1, ld);
@@ -282,17 +288,37 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             sGam[tid] = __expf(acc);
         }
         __syncthreads();  // B0b: Gamma
-        // the decay-scaled operands, eight (token, channel) elements per thread
+        // the decay factors e^Gamma, e^-Gamma (kept for the gradients) and
+        // e^(Gamma_last - Gamma) = gamma e^-Gamma, and the decay-scaled
+        // operands: two pieces of 4 channels of one token row per thread
 #pragma unroll
-        for (int e = tid; e < BC * BD; e += BNT) {
-            const int t = e / BD, ch = e % BD;
-            const float G = sG[t * PF + ch], GL = sG[(BC - 1) * PF + ch];
-            const float qf = bf(sQr[t * PB + ch]), kf = bf(sKr[t * PB + ch]);
-            const float ex = __expf(G), ei = __expf(-G), eb = __expf(GL - G);
-            sQt[t * PB + ch] = f32_to_bf16(qf * ex);
-            sKt[t * PB + ch] = f32_to_bf16(kf * ex);
-            sKi[t * PB + ch] = f32_to_bf16(kf * ei);
-            sKb[t * PB + ch] = f32_to_bf16(kf * eb);
+        for (int j = 0; j < 2; ++j) {
+            const int pi = tid + BNT * j, t = pi >> 5, c4 = 4 * (pi & 31);
+            const f32x4 G = *reinterpret_cast<const f32x4*>(&sG[t * PF + c4]);
+            const f32x4 gam = *reinterpret_cast<const f32x4*>(&sGam[c4]);
+            const uint2 qr = *reinterpret_cast<const uint2*>(sQr + t * PB + c4);
+            const uint2 kr = *reinterpret_cast<const uint2*>(sKr + t * PB + c4);
+            const float qf[4] = {__uint_as_float(qr.x << 16), __uint_as_float(qr.x & 0xffff0000u),
+                                 __uint_as_float(qr.y << 16), __uint_as_float(qr.y & 0xffff0000u)};
+            const float kf[4] = {__uint_as_float(kr.x << 16), __uint_as_float(kr.x & 0xffff0000u),
+                                 __uint_as_float(kr.y << 16), __uint_as_float(kr.y & 0xffff0000u)};
+            f32x4 ex, ei;
+            float vq[4], vk[4], vi[4], vb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ex[u] = __expf(G[u]);
+                ei[u] = __expf(-G[u]);
+                vq[u] = qf[u] * ex[u];
+                vk[u] = kf[u] * ex[u];
+                vi[u] = kf[u] * ei[u];
+                vb[u] = kf[u] * (gam[u] * ei[u]);
+            }
+            *reinterpret_cast<f32x4*>(&sE[t * PF + c4]) = ex;
+            *reinterpret_cast<f32x4*>(&sEi[t * PF + c4]) = ei;
+            *reinterpret_cast<uint2*>(sQt + t * PB + c4) = make_uint2(pack_bf16x2(vq[0], vq[1]), pack_bf16x2(vq[2], vq[3]));
+            *reinterpret_cast<uint2*>(sKt + t * PB + c4) = make_uint2(pack_bf16x2(vk[0], vk[1]), pack_bf16x2(vk[2], vk[3]));
+            *reinterpret_cast<uint2*>(sKi + t * PB + c4) = make_uint2(pack_bf16x2(vi[0], vi[1]), pack_bf16x2(vi[2], vi[3]));
+            *reinterpret_cast<uint2*>(sKb + t * PB + c4) = make_uint2(pack_bf16x2(vb[0], vb[1]), pack_bf16x2(vb[2], vb[3]));
         }
         __syncthreads();  // B1
 
@@ -324,42 +350,50 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             // T <- T + T (I - (I + A) T) from T = I - A: the residual
             // I - (I + A) T squares each step (A^2, A^4, A^8) and A^16 = 0
             // (A is strictly lower triangular), so three steps give T up to
-            // fp32 rounding.  fp32 matrix products on this wave; lane
-            // (gq, li) holds entries (4gq + pp, li).
-            f32x4 Tacc;
+            // fp32 rounding.  fp32 matrix products on this wave, all operands
+            // in registers: every iterate is a polynomial in A, so T, R and
+            // I + A commute, and the wave keeps T and T^T as accumulators
+            // (lane (gq, li) holds entries (4gq + pp, li)).  An accumulator
+            // of X is the B fragment of X and the A fragment of X^T; row li
+            // of I + A is its A fragment and the B fragment of its transpose.
+            //   R = I - (I + A) T,   R^T = I - T^T (I + A)^T,
+            //   T <- T + T R,        T^T <- T^T + T^T R^T
+            const f32x4 mrow = *reinterpret_cast<const f32x4*>(&sM[li * P16 + 4 * gq]);
+            const float bl = sBeta[li];
+            float4 ia;
+            ia.x = (4 * gq == li ? 1.f : 0.f) + bl * mrow[0];
+            ia.y = (4 * gq + 1 == li ? 1.f : 0.f) + bl * mrow[1];
+            ia.z = (4 * gq + 2 == li ? 1.f : 0.f) + bl * mrow[2];
+            ia.w = (4 * gq + 3 == li ? 1.f : 0.f) + bl * mrow[3];
+            f32x4 Tc, Ttc;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int r = 4 * gq + pp;
-                const float a = sBeta[r] * sM[r * P16 + li];
                 const float id = r == li ? 1.f : 0.f;
-                Tacc[pp] = id - a;
-                sIA[r * P16 + li] = id + a;
-                sT[r * P16 + li] = id - a;
+                Tc[pp] = id - sBeta[r] * sM[r * P16 + li];
+                Ttc[pp] = id - bl * mrow[pp];
             }
 #pragma unroll
             for (int it = 0; it < 3; ++it) {
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                // X = (I + A) T; R = I - X
-                const f32x4 ia = *reinterpret_cast<const f32x4*>(&sIA[li * P16 + 4 * gq]);
-                const float4 bt = make_float4(sT[(4 * gq) * P16 + li], sT[(4 * gq + 1) * P16 + li],
-                                              sT[(4 * gq + 2) * P16 + li], sT[(4 * gq + 3) * P16 + li]);
-                const float4 at = make_float4(sT[li * P16 + 4 * gq], sT[li * P16 + 4 * gq + 1],
-                                              sT[li * P16 + 4 * gq + 2], sT[li * P16 + 4 * gq + 3]);
-                f32x4 X = zero4();
-                mma16(X, make_float4(ia[0], ia[1], ia[2], ia[3]), bt);
-                float4 R;
+                const float4 Tf = make_float4(Tc[0], Tc[1], Tc[2], Tc[3]);
+                const float4 Ttf = make_float4(Ttc[0], Ttc[1], Ttc[2], Ttc[3]);
+                f32x4 X = zero4(), Xt = zero4();
+                mma16(X, ia, Tf);
+                mma16(Xt, Tf, ia);
+                float4 R, Rt;
                 R.x = (4 * gq == li ? 1.f : 0.f) - X[0];
                 R.y = (4 * gq + 1 == li ? 1.f : 0.f) - X[1];
                 R.z = (4 * gq + 2 == li ? 1.f : 0.f) - X[2];
                 R.w = (4 * gq + 3 == li ? 1.f : 0.f) - X[3];
-                // T <- T + T R
-                mma16(Tacc, at, R);
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int pp = 0; pp < 4; ++pp) sT[(4 * gq + pp) * P16 + li] = Tacc[pp];
+                Rt.x = (4 * gq == li ? 1.f : 0.f) - Xt[0];
+                Rt.y = (4 * gq + 1 == li ? 1.f : 0.f) - Xt[1];
+                Rt.z = (4 * gq + 2 == li ? 1.f : 0.f) - Xt[2];
+                Rt.w = (4 * gq + 3 == li ? 1.f : 0.f) - Xt[3];
+                mma16(Tc, Ttf, R);
+                mma16(Ttc, Tf, Rt);
             }
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) sT[(4 * gq + pp) * P16 + li] = Tc[pp];
         }
         f32x4 dU;
         {
@@ -450,7 +484,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             for (int pp = 0; pp < 4; ++pp) {
                 const int m = 4 * gq + pp;
                 dKt[rr][pp] = sBeta[m] * dBk[pp];
-                bk[pp] += dBk[pp] * bf(sKr[m * PB + kr0 + li]) * __expf(sG[m * PF + kr0 + li]);
+                bk[pp] += dBk[pp] * bf(sKr[m * PB + kr0 + li]) * sE[m * PF + kr0 + li];
             }
             // this wave's share of dW (Diag(beta) K~)^T, as its transpose [s][t]
             mma16(dTk, fscale(frow(sKt, PB, li, kr0 + 4 * gq), sBeta[li]), fregs(dWT));
@@ -473,16 +507,25 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         }
         __syncthreads();  // B5
 
-        // ---------------------------------------------- phase 5: dK-bar; dP; dA, dM
+        // ---------------------------------------------- phase 5: dK-bar, dgamma; dP; dA, dM
+        // dgamma = rowsum(S * dS') over this half's columns: the diagonal of
+        // the 16 x 16 diagonal blocks of S dS'^T, from the bf16 operand values
         f32x4 dKb[RT];
 #pragma unroll
         for (int rr = 0; rr < RT; ++rr) {
             const int kr0 = 32 * w + 16 * rr;
+            f32x4 dd = zero4();
             dKb[rr] = zero4();
 #pragma unroll
-            for (int cb = 0; cb < CW; cb += 32)
-                mma32(dKb[rr], frow(sU, PS, li, cb + 4 * gq), frow(sU, PS, li, cb + 16 + 4 * gq),
-                      frow(sdS, PS, kr0 + li, cb + 4 * gq), frow(sdS, PS, kr0 + li, cb + 16 + 4 * gq));
+            for (int cb = 0; cb < CW; cb += 32) {
+                const uint2 bd0 = frow(sdS, PS, kr0 + li, cb + 4 * gq), bd1 = frow(sdS, PS, kr0 + li, cb + 16 + 4 * gq);
+                mma32(dKb[rr], frow(sU, PS, li, cb + 4 * gq), frow(sU, PS, li, cb + 16 + 4 * gq), bd0, bd1);
+                mma32(dd, frow(sS, PS, kr0 + li, cb + 4 * gq), frow(sS, PS, kr0 + li, cb + 16 + 4 * gq), bd0, bd1);
+            }
+            // entry (li, li) sits in lane group li / 4, register li % 4
+            const int dp = li & 3;
+            const float dg = dp == 0 ? dd[0] : dp == 1 ? dd[1] : dp == 2 ? dd[2] : dd[3];
+            if ((li >> 2) == gq) sExt[kr0 + li] = dg * sGam[kr0 + li];
         }
         if (w == 0) {
             f32x4 acc = zero4();
@@ -535,12 +578,12 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             mma16(t2, frow32(sdP, P16, li, 4 * gq), bKi);  // dP Ki
             mma32(dKi, fcol32(sdM, P16, 4 * gq, li), fcol32(sdP, P16, 4 * gq, li), fcol(sKt, PB, 4 * gq, kc),
                   fcol(sQt, PB, 4 * gq, kc));           // dM^T K~ + dP^T Q~
-            const float eLg = sG[(BC - 1) * PF + kc];
+            const float gmk = sGam[kc];
+            float ga[4], gb[4];
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int t = 4 * gq + pp;
-                const float G = sG[t * PF + kc];
-                const float e = __expf(G), ei = __expf(-G), eb = __expf(eLg - G);
+                const float e = sE[t * PF + kc], ei = sEi[t * PF + kc], eb = gmk * ei;
                 const float qf = bf(sQr[t * PB + kc]), kf = bf(sKr[t * PB + kc]);
                 const float Qt = qf * e, Kt = kf * e, Kb = kf * eb;
                 fq[t * PF + kc] = (dQt[rr][pp] + t2[pp]) * e;
@@ -554,41 +597,44 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 // for every s through Gamma_last with a plus sign, i.e. dg_s
                 // gets it for t < s only.  Kept apart and summed that way,
                 // the two large cancelling sums are never formed.
-                fG[t * PF + kc] = dQt[rr][pp] * Qt + t2[pp] * bf(sQt[t * PB + kc]) + dKt[rr][pp] * Kt +
-                                  t1[pp] * bf(sKt[t * PB + kc]) - dKi[pp] * bf(sKi[t * PB + kc]);
-                fB[t * PF + kc] = dKb[rr][pp] * Kb;
+                ga[pp] = dQt[rr][pp] * Qt + t2[pp] * bf(sQt[t * PB + kc]) + dKt[rr][pp] * Kt +
+                         t1[pp] * bf(sKt[t * PB + kc]) - dKi[pp] * bf(sKi[t * PB + kc]);
+                gb[pp] = dKb[rr][pp] * Kb;
             }
-            if (gq == 0) {
-                float dgam = 0.f;
+            // dg_s = dgamma gamma + sum over t >= s of dGamma_t (the q, K~, Ki
+            // terms) + sum over t < s of the K-bar terms.  This lane holds
+            // tokens 4gq..4gq+3 of channel kc; the other token groups' totals
+            // come from the lanes 16 apart.
+            float sa[4], pb[4];
+            sa[3] = ga[3];
+            sa[2] = ga[2] + sa[3];
+            sa[1] = ga[1] + sa[2];
+            sa[0] = ga[0] + sa[1];
+            pb[0] = 0.f;
+            pb[1] = gb[0];
+            pb[2] = pb[1] + gb[1];
+            pb[3] = pb[2] + gb[2];
+            const float totA = sa[0], totB = pb[3] + gb[3];
+            float sufA = 0.f, preB = 0.f;
 #pragma unroll
-                for (int ww = 0; ww < BNW; ++ww) dgam += sdGam[ww][kc];
-                sExt[kc] = dgam * sGam[kc];
+            for (int g2 = 3; g2 >= 0; --g2) {
+                const float x = __shfl(totA, 16 * g2 + li, 64);
+                sufA += g2 > gq ? x : 0.f;
             }
+#pragma unroll
+            for (int g2 = 0; g2 < 4; ++g2) {
+                const float x = __shfl(totB, 16 * g2 + li, 64);
+                preB += g2 < gq ? x : 0.f;
+            }
+            const float ext = sExt[kc] + sufA;
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) fG[(4 * gq + pp) * PF + kc] = (ext + sa[pp]) + (preB + pb[pp]);
         }
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) sDv[(4 * gq + pp) * PS + cl] = f32_to_bf16(dvv[pp]);
         __syncthreads();  // B7
 
         // ---------------------------------------------- phase 7: stores (this half's partials, dV)
-        if (tid < BD) {
-            // dg_s = dgamma gamma + sum over t >= s of dGamma_t (the q, K~,
-            // Ki terms) + sum over t < s of the K-bar terms, in place of dGamma
-            const int ch = tid;
-            float pre[BC];
-            float a = 0.f;
-#pragma unroll
-            for (int t = 0; t < BC; ++t) {
-                pre[t] = a;
-                a += fB[t * PF + ch];
-            }
-            float acc = sExt[ch];
-#pragma unroll
-            for (int t = BC - 1; t >= 0; --t) {
-                acc += fG[t * PF + ch];
-                fG[t * PF + ch] = acc + pre[t];
-            }
-        }
-        __syncthreads();  // B7b
         {
             const auto rq = rows_rsrc(pdq + t0 * tok + hoff, nt, tok * 4, BD * 4);
             const auto rk = rows_rsrc(pdk + t0 * tok + hoff, nt, tok * 4, BD * 4);
