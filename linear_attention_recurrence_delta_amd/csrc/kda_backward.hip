@@ -65,6 +65,7 @@ constexpr int PB = BD + 8;     // bf16 row pitch (elements) of 128-wide LDS matr
 constexpr int PS = CW + 8;     // bf16 row pitch of the value-half matrices
 constexpr int PF = BD + 4;     // fp32 row pitch
 constexpr int P16 = 16;        // pitch of the 16 x 16 fp32 matrices
+constexpr int PT = BC + 4;     // row pitch of the channel-major [128][16] copies (bf16 and fp32)
 static_assert(RT == 2 && BNT == 256, "layout below assumes 4 waves and two key-row tiles per wave");
 
 // 4-value bf16 operand fragments from LDS: X[r][c..c+3] (one 8-byte read)
@@ -112,11 +113,17 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     __shared__ __align__(16) uint16_t sSS[2 * BD * PS];
     __shared__ __align__(16) uint16_t sQr[BC * PB], sKr[BC * PB], sQt[BC * PB], sKt[BC * PB], sKi[BC * PB],
         sKb[BC * PB], sW[BC * PB];
+    // channel-major copies [channel][token] of Q~, K~, Ki, W and raw q, k: the
+    // 4 tokens of a fragment taken down a column become one 8-byte read
+    __shared__ __align__(16) uint16_t sQtT[BD * PT], sKtT[BD * PT], sKiT[BD * PT], sWT[BD * PT], sQrT[BD * PT],
+        sKrT[BD * PT];
     // this half's v, scale * dO (after its last use, the dv staging), U, dU
     __shared__ __align__(16) uint16_t sV[BC * PS], sdO[BC * PS], sU[BC * PS], sdU[BC * PS];
-    // Gamma, then e^Gamma and e^-Gamma (fp32)
-    __shared__ __align__(16) float sG[BC * PF], sE[BC * PF], sEi[BC * PF];
-    __shared__ __align__(16) float sM[256], sP[256], sT[256], sdP[256], sdTv[256], sdM[256];
+    // Gamma; e^Gamma and e^-Gamma (fp32, channel-major)
+    __shared__ __align__(16) float sG[BC * PF], sET[BD * PT], sEiT[BD * PT];
+    // 16 x 16 fp32 matrices; the ...T arrays hold transposes
+    __shared__ __align__(16) float sM[256], sPT[256], sT[256], sTT[256], sdP[256], sdPT[256], sdTv[256], sdM[256],
+        sdMT[256];
     __shared__ __align__(16) float sdTk[BNW][256];
     __shared__ __align__(16) float sGam[BD];
     __shared__ float sBeta[BC], sExt[BD], sdBv[BNW][BC], sdBk[BNW][BC], sdBa[BC];
@@ -290,10 +297,13 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         __syncthreads();  // B0b: Gamma
         // the decay factors e^Gamma, e^-Gamma (kept for the gradients) and
         // e^(Gamma_last - Gamma) = gamma e^-Gamma, and the decay-scaled
-        // operands: two pieces of 4 channels of one token row per thread
+        // operands.  Wave w takes channel tiles 2w and 2w + 1; lane (gq, li)
+        // token li and channels 4gq..4gq+3 of the tile, i.e. its A fragment,
+        // which times the identity gives the channel-major copy (4 tokens of
+        // one channel per lane)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int pi = tid + BNT * j, t = pi >> 5, c4 = 4 * (pi & 31);
+            const int c16 = 16 * (2 * w + j), t = li, c4 = c16 + 4 * gq;
             const f32x4 G = *reinterpret_cast<const f32x4*>(&sG[t * PF + c4]);
             const f32x4 gam = *reinterpret_cast<const f32x4*>(&sGam[c4]);
             const uint2 qr = *reinterpret_cast<const uint2*>(sQr + t * PB + c4);
@@ -313,11 +323,29 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 vi[u] = kf[u] * ei[u];
                 vb[u] = kf[u] * (gam[u] * ei[u]);
             }
-            *reinterpret_cast<f32x4*>(&sE[t * PF + c4]) = ex;
-            *reinterpret_cast<f32x4*>(&sEi[t * PF + c4]) = ei;
-            *reinterpret_cast<uint2*>(sQt + t * PB + c4) = make_uint2(pack_bf16x2(vq[0], vq[1]), pack_bf16x2(vq[2], vq[3]));
-            *reinterpret_cast<uint2*>(sKt + t * PB + c4) = make_uint2(pack_bf16x2(vk[0], vk[1]), pack_bf16x2(vk[2], vk[3]));
-            *reinterpret_cast<uint2*>(sKi + t * PB + c4) = make_uint2(pack_bf16x2(vi[0], vi[1]), pack_bf16x2(vi[2], vi[3]));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                sET[(c4 + u) * PT + t] = ex[u];
+                sEiT[(c4 + u) * PT + t] = ei[u];
+            }
+            const uint2 uq = make_uint2(pack_bf16x2(vq[0], vq[1]), pack_bf16x2(vq[2], vq[3]));
+            const uint2 uk = make_uint2(pack_bf16x2(vk[0], vk[1]), pack_bf16x2(vk[2], vk[3]));
+            const uint2 ui = make_uint2(pack_bf16x2(vi[0], vi[1]), pack_bf16x2(vi[2], vi[3]));
+            *reinterpret_cast<uint2*>(sQt + t * PB + c4) = uq;
+            *reinterpret_cast<uint2*>(sKt + t * PB + c4) = uk;
+            *reinterpret_cast<uint2*>(sKi + t * PB + c4) = ui;
+            f32x4 xq = zero4(), xk = zero4(), xi = zero4(), xqr = zero4(), xkr = zero4();
+            mma16(xq, uq, eye);
+            mma16(xk, uk, eye);
+            mma16(xi, ui, eye);
+            mma16(xqr, qr, eye);
+            mma16(xkr, kr, eye);
+            const int ct = (c16 + li) * PT + 4 * gq;
+            *reinterpret_cast<uint2*>(sQtT + ct) = fregs(xq);
+            *reinterpret_cast<uint2*>(sKtT + ct) = fregs(xk);
+            *reinterpret_cast<uint2*>(sKiT + ct) = fregs(xi);
+            *reinterpret_cast<uint2*>(sQrT + ct) = fregs(xqr);
+            *reinterpret_cast<uint2*>(sKrT + ct) = fregs(xkr);
             *reinterpret_cast<uint2*>(sKb + t * PB + c4) = make_uint2(pack_bf16x2(vb[0], vb[1]), pack_bf16x2(vb[2], vb[3]));
         }
         __syncthreads();  // B1
@@ -330,11 +358,18 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             for (int kb = 0; kb < BD; kb += 32)
                 mma32(acc, frow(X, PB, li, kb + 4 * gq), frow(X, PB, li, kb + 16 + 4 * gq),
                       frow(sKi, PB, li, kb + 4 * gq), frow(sKi, PB, li, kb + 16 + 4 * gq));
+            if (w == 0) {
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const int t = 4 * gq + pp, s = li;
-                if (w == 0) sM[t * P16 + s] = s < t ? acc[pp] : 0.f;
-                else sP[t * P16 + s] = s <= t ? acc[pp] : 0.f;
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int t = 4 * gq + pp, s = li;
+                    sM[t * P16 + s] = s < t ? acc[pp] : 0.f;
+                }
+            } else {
+                // P^T[s][t] for s = li, t = 4gq..4gq+3
+                f32x4 pt;
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) pt[pp] = li <= 4 * gq + pp ? acc[pp] : 0.f;
+                *reinterpret_cast<f32x4*>(&sPT[li * P16 + 4 * gq]) = pt;
             }
         }
         f32x4 dUa = zero4();  // (K-bar dS')[t][col]
@@ -392,13 +427,14 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 mma16(Tc, Ttf, R);
                 mma16(Ttc, Tf, Rt);
             }
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) sT[(4 * gq + pp) * P16 + li] = Tc[pp];
+            // row li of T is column li of T^T (the T^T accumulator), and vice versa
+            *reinterpret_cast<f32x4*>(&sT[li * P16 + 4 * gq]) = Ttc;
+            *reinterpret_cast<f32x4*>(&sTT[li * P16 + 4 * gq]) = Tc;
         }
         f32x4 dU;
         {
             f32x4 dUb = zero4();  // (P^T dO_s)[t][col]
-            mma16(dUb, fcol32(sP, P16, 4 * gq, li), fcol(sdO, PS, 4 * gq, cl));
+            mma16(dUb, frow32(sPT, P16, li, 4 * gq), fcol(sdO, PS, 4 * gq, cl));
             dU = dUa + dUb;
         }
 #pragma unroll
@@ -409,7 +445,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             for (int r = 0; r < 8; ++r) {
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) dSr[r][pp] *= sGam[16 * r + 4 * gq + pp];
-                mma16(dSr[r], fcol(sQt, PB, 4 * gq, 16 * r + li), bdo);
+                mma16(dSr[r], frow(sQtT, PT, 16 * r + li, 4 * gq), bdo);
             }
         }
         __syncthreads();  // B3
@@ -425,15 +461,16 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             for (int rr = 0; rr < RT; ++rr) {
                 const int kc = 32 * w + 16 * rr + li;  // key channel of this W column
                 f32x4 Wt = zero4();
-                mma16(Wt, aTb, fcol(sKt, PB, 4 * gq, kc));
+                mma16(Wt, aTb, frow(sKtT, PT, kc, 4 * gq));
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) sW[(4 * gq + pp) * PB + kc] = f32_to_bf16(Wt[pp]);
+                *reinterpret_cast<uint2*>(sWT + kc * PT + 4 * gq) = fregs(Wt);
             }
             Ut = zero4();
             mma16(Ut, aTb, fcol(sV, PS, 4 * gq, cl));
             // dV = Diag(beta) T^T dU; beta partial rowsum(T^T dU * V)
             f32x4 dBv = zero4();
-            mma16(dBv, fcol32(sT, P16, 4 * gq, li), fregs(dU));
+            mma16(dBv, frow32(sTT, P16, li, 4 * gq), fregs(dU));
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int m = 4 * gq + pp;
@@ -455,7 +492,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             for (int pp = 0; pp < 4; ++pp) sU[(4 * gq + pp) * PS + cl] = f32_to_bf16(U[pp]);
             const uint2 bdu = fregs(dU);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) mma16(dSr[r], fneg(fcol(sW, PB, 4 * gq, 16 * r + li)), bdu);
+            for (int r = 0; r < 8; ++r) mma16(dSr[r], fneg(frow(sWT, PT, 16 * r + li, 4 * gq)), bdu);
         }
         // key rows kr = 32w + 16rr + li: dQ~ = dO_s S^T, dW = -dU S^T and dW^T,
         // over this half's value columns
@@ -479,12 +516,17 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             dWT = -dWT;  // dW^T[row][t]
             // from W = T Diag(beta) K~: Diag(beta) T^T dW; beta partial rowsum(T^T dW * K~)
             f32x4 dBk = zero4();
-            mma16(dBk, fcol32(sT, P16, 4 * gq, li), fregs(dWt));
+            mma16(dBk, frow32(sTT, P16, li, 4 * gq), fregs(dWt));
+            // fp32 K~ = k e^Gamma at tokens 4gq..4gq+3 of channel kr0 + li
+            const uint2 kr4 = frow(sKrT, PT, kr0 + li, 4 * gq);
+            const f32x4 e4 = *reinterpret_cast<const f32x4*>(&sET[(kr0 + li) * PT + 4 * gq]);
+            const float kt4[4] = {__uint_as_float(kr4.x << 16) * e4[0], __uint_as_float(kr4.x & 0xffff0000u) * e4[1],
+                                  __uint_as_float(kr4.y << 16) * e4[2], __uint_as_float(kr4.y & 0xffff0000u) * e4[3]};
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int m = 4 * gq + pp;
                 dKt[rr][pp] = sBeta[m] * dBk[pp];
-                bk[pp] += dBk[pp] * bf(sKr[m * PB + kr0 + li]) * sE[m * PF + kr0 + li];
+                bk[pp] += dBk[pp] * kt4[pp];
             }
             // this wave's share of dW (Diag(beta) K~)^T, as its transpose [s][t]
             mma16(dTk, fscale(frow(sKt, PB, li, kr0 + 4 * gq), sBeta[li]), fregs(dWT));
@@ -533,11 +575,14 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             for (int cb = 0; cb < CW; cb += 32)
                 mma32(acc, frow(sdO, PS, li, cb + 4 * gq), frow(sdO, PS, li, cb + 16 + 4 * gq),
                       frow(sU, PS, li, cb + 4 * gq), frow(sU, PS, li, cb + 16 + 4 * gq));
+            f32x4 pt;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int t = 4 * gq + pp, s = li;
-                sdP[t * P16 + s] = s <= t ? acc[pp] : 0.f;
+                pt[pp] = s <= t ? acc[pp] : 0.f;
+                sdP[t * P16 + s] = pt[pp];
             }
+            *reinterpret_cast<f32x4*>(&sdPT[li * P16 + 4 * gq]) = pt;
         } else if (w == 1) {
             // dT[t][u] = dTv[t][u] + sum over waves of dTk^T; Z = dT T^T; dA = -T^T Z
             uint2 adT;
@@ -556,15 +601,18 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             f32x4 Z = zero4();
             mma16(Z, adT, frow32(sT, P16, li, 4 * gq));
             f32x4 dA = zero4();
-            mma16(dA, fcol32(sT, P16, 4 * gq, li), fregs(Z));
+            mma16(dA, frow32(sTT, P16, li, 4 * gq), fregs(Z));
+            f32x4 mt;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int m = 4 * gq + pp, s = li;
                 const float da = s < m ? -dA[pp] : 0.f;
-                sdM[m * P16 + s] = sBeta[m] * da;
+                mt[pp] = sBeta[m] * da;
+                sdM[m * P16 + s] = mt[pp];
                 const float x = row_inclusive_sum16(da * sM[m * P16 + s]);  // total in lane 15 of the row
                 if (li == 15) sdBa[m] = x;
             }
+            *reinterpret_cast<f32x4*>(&sdMT[li * P16 + 4 * gq]) = mt;
         }
         __syncthreads();  // B6
 
@@ -573,18 +621,32 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         for (int rr = 0; rr < RT; ++rr) {
             const int kc = 32 * w + 16 * rr + li;  // key channel of this lane
             f32x4 t1 = zero4(), t2 = zero4(), dKi = zero4();
-            const uint2 bKi = fcol(sKi, PB, 4 * gq, kc);
+            // tokens 4gq..4gq+3 of channel kc of Ki, K~, Q~ (B fragments)
+            const uint2 bKi = frow(sKiT, PT, kc, 4 * gq), bKt = frow(sKtT, PT, kc, 4 * gq),
+                        bQt = frow(sQtT, PT, kc, 4 * gq);
             mma16(t1, frow32(sdM, P16, li, 4 * gq), bKi);  // dM Ki
             mma16(t2, frow32(sdP, P16, li, 4 * gq), bKi);  // dP Ki
-            mma32(dKi, fcol32(sdM, P16, 4 * gq, li), fcol32(sdP, P16, 4 * gq, li), fcol(sKt, PB, 4 * gq, kc),
-                  fcol(sQt, PB, 4 * gq, kc));           // dM^T K~ + dP^T Q~
+            mma32(dKi, frow32(sdMT, P16, li, 4 * gq), frow32(sdPT, P16, li, 4 * gq), bKt, bQt);  // dM^T K~ + dP^T Q~
+            const float qtv[4] = {__uint_as_float(bQt.x << 16), __uint_as_float(bQt.x & 0xffff0000u),
+                                  __uint_as_float(bQt.y << 16), __uint_as_float(bQt.y & 0xffff0000u)};
+            const float ktv[4] = {__uint_as_float(bKt.x << 16), __uint_as_float(bKt.x & 0xffff0000u),
+                                  __uint_as_float(bKt.y << 16), __uint_as_float(bKt.y & 0xffff0000u)};
+            const float kiv[4] = {__uint_as_float(bKi.x << 16), __uint_as_float(bKi.x & 0xffff0000u),
+                                  __uint_as_float(bKi.y << 16), __uint_as_float(bKi.y & 0xffff0000u)};
             const float gmk = sGam[kc];
+            const f32x4 e4 = *reinterpret_cast<const f32x4*>(&sET[kc * PT + 4 * gq]);
+            const f32x4 ei4 = *reinterpret_cast<const f32x4*>(&sEiT[kc * PT + 4 * gq]);
+            const uint2 qr4 = frow(sQrT, PT, kc, 4 * gq), kr4 = frow(sKrT, PT, kc, 4 * gq);
+            const float qrv[4] = {__uint_as_float(qr4.x << 16), __uint_as_float(qr4.x & 0xffff0000u),
+                                  __uint_as_float(qr4.y << 16), __uint_as_float(qr4.y & 0xffff0000u)};
+            const float krv[4] = {__uint_as_float(kr4.x << 16), __uint_as_float(kr4.x & 0xffff0000u),
+                                  __uint_as_float(kr4.y << 16), __uint_as_float(kr4.y & 0xffff0000u)};
             float ga[4], gb[4];
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int t = 4 * gq + pp;
-                const float e = sE[t * PF + kc], ei = sEi[t * PF + kc], eb = gmk * ei;
-                const float qf = bf(sQr[t * PB + kc]), kf = bf(sKr[t * PB + kc]);
+                const float e = e4[pp], ei = ei4[pp], eb = gmk * ei;
+                const float qf = qrv[pp], kf = krv[pp];
                 const float Qt = qf * e, Kt = kf * e, Kb = kf * eb;
                 fq[t * PF + kc] = (dQt[rr][pp] + t2[pp]) * e;
                 fk[t * PF + kc] = (dKt[rr][pp] + t1[pp]) * e + dKi[pp] * ei + dKb[rr][pp] * eb;
@@ -597,8 +659,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 // for every s through Gamma_last with a plus sign, i.e. dg_s
                 // gets it for t < s only.  Kept apart and summed that way,
                 // the two large cancelling sums are never formed.
-                ga[pp] = dQt[rr][pp] * Qt + t2[pp] * bf(sQt[t * PB + kc]) + dKt[rr][pp] * Kt +
-                         t1[pp] * bf(sKt[t * PB + kc]) - dKi[pp] * bf(sKi[t * PB + kc]);
+                ga[pp] = dQt[rr][pp] * Qt + t2[pp] * qtv[pp] + dKt[rr][pp] * Kt + t1[pp] * ktv[pp] - dKi[pp] * kiv[pp];
                 gb[pp] = dKb[rr][pp] * Kb;
             }
             // dg_s = dgamma gamma + sum over t >= s of dGamma_t (the q, K~, Ki
