@@ -381,55 +381,39 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
 
         // ---------------------------------------------- phase 2: T; dU; dS without W
         if (w == 0) {
-            // T = (I + A)^-1, A = Diag(beta) M, by Newton-Schulz steps
-            // T <- T + T (I - (I + A) T) from T = I - A: the residual
-            // I - (I + A) T squares each step (A^2, A^4, A^8) and A^16 = 0
-            // (A is strictly lower triangular), so three steps give T up to
-            // fp32 rounding.  fp32 matrix products on this wave, all operands
-            // in registers: every iterate is a polynomial in A, so T, R and
-            // I + A commute, and the wave keeps T and T^T as accumulators
-            // (lane (gq, li) holds entries (4gq + pp, li)).  An accumulator
-            // of X is the B fragment of X and the A fragment of X^T; row li
-            // of I + A is its A fragment and the B fragment of its transpose.
-            //   R = I - (I + A) T,   R^T = I - T^T (I + A)^T,
-            //   T <- T + T R,        T^T <- T^T + T^T R^T
+            // T = (I + A)^-1, A = Diag(beta) M strictly lower triangular, so
+            // A^16 = 0 and T = (I - A)(I + A^2)(I + A^4)(I + A^8): three
+            // squarings and three products, fp32 on this wave with every
+            // operand in registers.  The factors are polynomials in A and
+            // commute, so each product is taken as A^(2^k) T.  Lane (gq, li)
+            // holds entries (4gq + pp, li) of each accumulator; the
+            // accumulator of X is the B fragment of X and the A fragment of
+            // X^T, so the wave keeps A^(2^k) and its transpose.
             const f32x4 mrow = *reinterpret_cast<const f32x4*>(&sM[li * P16 + 4 * gq]);
             const float bl = sBeta[li];
-            float4 ia;
-            ia.x = (4 * gq == li ? 1.f : 0.f) + bl * mrow[0];
-            ia.y = (4 * gq + 1 == li ? 1.f : 0.f) + bl * mrow[1];
-            ia.z = (4 * gq + 2 == li ? 1.f : 0.f) + bl * mrow[2];
-            ia.w = (4 * gq + 3 == li ? 1.f : 0.f) + bl * mrow[3];
-            f32x4 Tc, Ttc;
+            f32x4 Aa, At, Tc;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
                 const int r = 4 * gq + pp;
-                const float id = r == li ? 1.f : 0.f;
-                Tc[pp] = id - sBeta[r] * sM[r * P16 + li];
-                Ttc[pp] = id - bl * mrow[pp];
+                Aa[pp] = sBeta[r] * sM[r * P16 + li];  // A[r][li]
+                At[pp] = bl * mrow[pp];                 // A[li][r]
+                Tc[pp] = (r == li ? 1.f : 0.f) - Aa[pp];
             }
+            auto f4 = [](const f32x4& x) { return make_float4(x[0], x[1], x[2], x[3]); };
+            f32x4 A2 = zero4(), A2t = zero4();
+            mma16(A2, f4(At), f4(Aa));
+            mma16(A2t, f4(Aa), f4(At));
+            mma16(Tc, f4(A2t), f4(Tc));  // (I + A^2)(I - A)
+            f32x4 A4 = zero4(), A4t = zero4();
+            mma16(A4, f4(A2t), f4(A2));
+            mma16(A4t, f4(A2), f4(A2t));
+            mma16(Tc, f4(A4t), f4(Tc));  // (I + A^4) ...
+            f32x4 A8t = zero4();
+            mma16(A8t, f4(A4), f4(A4t));
+            mma16(Tc, f4(A8t), f4(Tc));  // (I + A^8) ...
 #pragma unroll
-            for (int it = 0; it < 3; ++it) {
-                const float4 Tf = make_float4(Tc[0], Tc[1], Tc[2], Tc[3]);
-                const float4 Ttf = make_float4(Ttc[0], Ttc[1], Ttc[2], Ttc[3]);
-                f32x4 X = zero4(), Xt = zero4();
-                mma16(X, ia, Tf);
-                mma16(Xt, Tf, ia);
-                float4 R, Rt;
-                R.x = (4 * gq == li ? 1.f : 0.f) - X[0];
-                R.y = (4 * gq + 1 == li ? 1.f : 0.f) - X[1];
-                R.z = (4 * gq + 2 == li ? 1.f : 0.f) - X[2];
-                R.w = (4 * gq + 3 == li ? 1.f : 0.f) - X[3];
-                Rt.x = (4 * gq == li ? 1.f : 0.f) - Xt[0];
-                Rt.y = (4 * gq + 1 == li ? 1.f : 0.f) - Xt[1];
-                Rt.z = (4 * gq + 2 == li ? 1.f : 0.f) - Xt[2];
-                Rt.w = (4 * gq + 3 == li ? 1.f : 0.f) - Xt[3];
-                mma16(Tc, Ttf, R);
-                mma16(Ttc, Tf, Rt);
-            }
-            // row li of T is column li of T^T (the T^T accumulator), and vice versa
-            *reinterpret_cast<f32x4*>(&sT[li * P16 + 4 * gq]) = Ttc;
-            *reinterpret_cast<f32x4*>(&sTT[li * P16 + 4 * gq]) = Tc;
+            for (int pp = 0; pp < 4; ++pp) sT[(4 * gq + pp) * P16 + li] = Tc[pp];
+            *reinterpret_cast<f32x4*>(&sTT[li * P16 + 4 * gq]) = Tc;  // column li of T is row li of T^T
         }
         f32x4 dU;
         {
