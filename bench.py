@@ -45,10 +45,6 @@ FUSED_BYTES_PER_TOKEN_HEAD = 3 * 256 + 256 + 4 + 256
 # Backward: each input and output once -- q, k, v, g, beta and d_o read (1540),
 # dq, dk, dv, dg and dbeta written (3 x 256 + 512 + 4).
 BWD_IO_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256 + 3 * 256 + 512 + 4
-# The reverse kernel: q, k, v, g, beta and d_o read, the five gradients
-# written, plus the fp32 128 x 128 state of every 16-token boundary read
-# (65536 / 16 = 4096), which the forward launch before it writes.
-BWD_REVERSE_BYTES_PER_TOKEN_HEAD = BWD_IO_BYTES_PER_TOKEN_HEAD + 4096
 # Chunked flop count at the reference chunk C = 64, d = 128, causal tiles:
 # A, P, W, U~ and P U at C^2 d each, plus W S, Q~ S and Kbar^T U at 2 C d^2
 # each, per chunk of C tokens -> 5 C d + 6 d^2 per token-head.
@@ -69,7 +65,7 @@ KERNEL_SOURCES = {
     "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
     "kda_prefill_fused_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
     "kda_output_gate_32k_x96": ("kda_output_gate.hip", "kda_device.h", "kda_internal.h"),
-    "kda_backward_k3_dense_32k": ("kda_backward.hip", "kda_backward.h", "kda_device.h"),
+    "kda_backward_k3_dense_32k": ("kda_backward.hip", "kda_backward.h", "kda_device.h", "kda_prefill_ws.h"),
 }
 
 
@@ -117,26 +113,24 @@ def measured_mfma(kernel):
             "busy_frac_of_simd_cycles": c["busy_cycles"] / simd_cycles}
 
 
-def backward_entry(bw_ms, bwf_ms, token_heads, T):
-    """The backward call's timing: the whole call, its forward launch alone
-    (the checkpointed prefill, every 16 tokens) and the reverse kernel as the
-    difference, with the reverse kernel's HBM roofline."""
+def backward_entry(bw_ms, token_heads, T):
+    """The backward call's timing (its three launches: the forward again with
+    a bf16 state every 16 tokens, the reverse chunk kernel, the sum of the two
+    value halves) and its HBM roofline over the whole call: the gradients'
+    inputs and outputs are the algorithmic bytes (the states are the call's
+    own intermediate data); traffic is what the three kernels move."""
     tot = sum(bw_ms) / len(bw_ms)
-    fwd = sum(bwf_ms) / len(bwf_ms)
-    rev = tot - fwd
-    rev_bytes = BWD_REVERSE_BYTES_PER_TOKEN_HEAD * token_heads
+    io_bytes = BWD_IO_BYTES_PER_TOKEN_HEAD * token_heads
     return {
         "workload": "gradients of k3_dense_32k (dq, dk, dv, dg, dbeta) for a random bf16 d_o: the forward again "
-                    "keeping the state every 16 tokens, then the reverse chunk kernel",
+                    "keeping the state every 16 tokens, then the reverse chunk kernel and the sum of its halves",
         "ms": tot, "tokens_per_s": T / (tot * 1e-3),
-        "forward_ckpt16_ms": fwd, "reverse_ms": rev,
         "io_bytes_per_token_head": BWD_IO_BYTES_PER_TOKEN_HEAD,
-        "io_hbm_gbs": BWD_IO_BYTES_PER_TOKEN_HEAD * token_heads / (tot * 1e-3) / 1e9,
-        "roofline": {"bound": "hbm", "achieved": rev_bytes / (rev * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": rev_bytes / (rev * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": io_bytes / (tot * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": io_bytes / (tot * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "traffic": measured_traffic("kda_backward_k3_dense_32k"),
-                     "kernel": "kda_backward_kernel (reverse chunks; time = call - forward launch)",
-                     "bytes_per_launch": rev_bytes},
+                     "kernel": "kda_prefill_backward (forward with 16-token states + reverse + sum)",
+                     "bytes_per_launch": io_bytes},
     }
 
 
@@ -209,8 +203,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "long"], default="all")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the backward timing (counter runs of the prefill kernels: the backward's forward "
-                         "launch is the same kernel)")
+                    help="skip the backward timing (counter runs of the prefill kernels alone; the backward's forward "
+                         "launch is a variant of the same kernel)")
     ap.add_argument("--no-checkpoints", action="store_true",
                     help="skip the checkpointed prefill timing (counter runs per kernel launch)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -333,18 +327,7 @@ def main():
 
             run_bwd()
             bw_ms = time_launches(run_bwd, args.steps, stream)
-            # its first launch alone: the forward keeping the state every 16 tokens
-            ck16 = b_ws[:(wd["T"] // 16) * wd["H"] * wd["d"] * wd["d"] * 4].view(torch.float32).view(
-                wd["T"] // 16, wd["H"], wd["d"], wd["d"])
-
-            def run_fwd16():
-                kda.kda_prefill_checkpointed(wd["q"], wd["k"], wd["v"], wd["g"], wd["beta"], None, None,
-                                             checkpoint_interval=16, chunk_size=C, out=o_d, final_state=s_d,
-                                             checkpoints=ck16)
-
-            run_fwd16()
-            bwf_ms = time_launches(run_fwd16, args.steps, stream)
-            del b_do, b_dq, b_dk, b_dv, b_dg, b_db, b_ws, ck16
+            del b_do, b_dq, b_dk, b_dv, b_dg, b_db, b_ws
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)
         log("dense prefill avg %.3f ms (min %.3f), varlen avg %.3f ms, wall %.3f s" %
@@ -392,7 +375,7 @@ def main():
                              "kernel": "kda_output_gate_kernel<bf16, 128>",
                              "bytes_per_launch": 3 * o_d.numel() * 2},
             },
-            "prefill_backward": None if bw_ms is None else backward_entry(bw_ms, bwf_ms, token_heads, wd["T"]),
+            "prefill_backward": None if bw_ms is None else backward_entry(bw_ms, token_heads, wd["T"]),
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
                 "hbm_gbs": PREFILL_BYTES_PER_TOKEN_HEAD * wv["T"] * wv["H"] / (v_avg * 1e-3) / 1e9,

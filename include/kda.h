@@ -294,11 +294,13 @@ int32_t kda_prefill_backward_supported(int32_t qkv_dtype, int32_t d_k,
                                        int32_t d_v);
 
 /* Bytes of device workspace kda_prefill_backward needs (0 for unsupported
- * arguments), three parts each rounded up to 256 bytes: the state after
- * every 16 tokens of each sequence (floor(total_tokens / 16) * num_heads *
- * d_k * d_v fp32), the forward run's output (total_tokens * num_heads * d_v
- * bf16), and per half of the value columns the partial key-side gradients
- * (2 * total_tokens * num_heads * (3 * d_k + 1) fp32). */
+ * arguments), four parts each rounded up to 256 bytes: the state after every
+ * 16 tokens of each sequence (floor(total_tokens / 16) * num_heads * d_k *
+ * d_v, rounded to bf16: the reverse pass uses the states only as bf16 matrix
+ * operands), the forward run's output (total_tokens * num_heads * d_v bf16),
+ * per half of the value columns the partial key-side gradients (2 *
+ * total_tokens * num_heads * (3 * d_k + 1) fp32), and the initial states
+ * rounded to bf16 (num_seqs * num_heads * d_k * d_v). */
 size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs,
                                             int64_t total_tokens,
                                             int32_t num_heads, int32_t d_k,
@@ -312,11 +314,12 @@ size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs,
  * o and d_final_state with respect to the final states, it returns the
  * gradients with respect to q, k, v, g, beta and the initial states.
  *
- * Computed in three launches on `stream`: the forward recurrence again (the
- * same kernel as kda_prefill, chunk 16), keeping the state at every 16-token
- * boundary in the workspace; the reverse pass, two workgroups per (sequence,
- * head), one per half of the value columns, walking the chunks last to first;
- * and the sum of the two halves' key-side partials.
+ * Computed in three launches on `stream` (four with initial states): the
+ * forward recurrence again (the kernel of kda_prefill, chunk 16), keeping the
+ * state at every 16-token boundary in the workspace; the initial states
+ * rounded into the same form; the reverse pass, two workgroups per
+ * (sequence, head), one per half of the value columns, walking the chunks
+ * last to first; and the sum of the two halves' key-side partials.
  *
  * Arguments shared with kda_prefill (num_seqs, total_tokens, num_heads, d_k,
  * d_v, qkv_dtype, scale, q, k, v, g, beta, initial_state, cu_seqlens) mean

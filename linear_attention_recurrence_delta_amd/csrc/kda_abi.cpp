@@ -58,19 +58,22 @@ int device_cu_count() {
 // the compute units (96 heads -> 2 slabs, 16 heads -> 8).  KDA_PREFILL_WAVES
 // (an integer) overrides the choice and KDA_PREFILL_KIND the kernel; results
 // are bitwise identical across slab widths.
-const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units, bool fused) {
+// ckb: the backward's forward run, whose kernels write bf16 checkpoints in the
+// backward kernel's blocked layout (kind 3); no other call may get those.
+const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units, bool fused, bool ckb = false) {
     int count = 0;
     const PrefillVariant* tab = variants(dtype, &count);
     int want_kind = 1;  // the wave-specialised pipeline where it is built
     if (const char* env = getenv("KDA_PREFILL_KIND")) want_kind = atoi(env);
     if (fused) want_kind = 2;        // only the fused kernels read z and a_log
-    else if (want_kind == 2) want_kind = 1;
+    else if (ckb) want_kind = 3;
+    else if (want_kind == 2 || want_kind == 3) want_kind = 1;
     bool have_kind = false;
     for (int i = 0; i < count; ++i)
         if (tab[i].D == D && tab[i].C == C && tab[i].kind == want_kind) have_kind = true;
-    if (fused && !have_kind) return nullptr;
+    if ((fused || ckb) && !have_kind) return nullptr;
     int want = D / 16;
-    if (have_kind && (want_kind == 1 || want_kind == 2)) {
+    if (have_kind && want_kind >= 1) {
         const int64_t cus = device_cu_count();
         while (want > 1 && units * (D / (16 * want)) * 2 <= cus) want /= 2;
     }
@@ -85,7 +88,7 @@ const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t 
     for (int i = 0; i < count; ++i) {
         const PrefillVariant& v = tab[i];
         if (v.D != D || v.C != C) continue;
-        if ((v.kind == 2) != fused) continue;
+        if ((v.kind == 2) != fused || (v.kind == 3) != ckb) continue;
         if (have_kind && v.kind != want_kind) continue;
         if (!smallest || v.nwc < smallest->nwc) smallest = &v;
         if (v.nwc <= want && (!best || v.nwc > best->nwc)) best = &v;
@@ -298,11 +301,15 @@ kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int3
 
 // Workspace of the backward, each part at a 256-byte aligned offset: the
 // state after every 16 tokens of each sequence (at most total_tokens / 16
-// fp32 states per head), the bf16 o of the forward run that produces them,
-// and the reverse kernel's fp32 partials per half of the value columns.
+// states per head, bf16 in the backward kernel's blocked layout), the bf16 o
+// of the forward run that produces them, the reverse kernel's fp32 partials
+// per half of the value columns, and the initial states in the blocked layout.
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 static size_t backward_ckpt_bytes(int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v) {
-    return align256((size_t)(total_tokens / 16) * (size_t)num_heads * (size_t)d_k * (size_t)d_v * sizeof(float));
+    return align256((size_t)(total_tokens / 16) * (size_t)num_heads * (size_t)d_k * (size_t)d_v * 2);
+}
+static size_t backward_s0_bytes(int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v) {
+    return align256((size_t)num_seqs * (size_t)num_heads * (size_t)d_k * (size_t)d_v * 2);
 }
 static size_t backward_o_bytes(int64_t total_tokens, int32_t num_heads, int32_t d_v) {
     return align256((size_t)total_tokens * (size_t)num_heads * (size_t)d_v * 2);
@@ -314,10 +321,11 @@ int32_t kda_prefill_backward_supported(int32_t dtype, int32_t d_k, int32_t d_v) 
 
 size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                                             int32_t d_k, int32_t d_v, int32_t dtype) {
-    (void)num_seqs;
-    if (!kda_prefill_backward_supported(dtype, d_k, d_v) || total_tokens < 0 || num_heads < 1) return 0;
+    if (!kda_prefill_backward_supported(dtype, d_k, d_v) || total_tokens < 0 || num_heads < 1 || num_seqs < 0)
+        return 0;
     return backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) + backward_o_bytes(total_tokens, num_heads, d_v) +
-           kda::backward_partial_bytes(total_tokens, num_heads);
+           align256(kda::backward_partial_bytes(total_tokens, num_heads)) +
+           backward_s0_bytes(num_seqs, num_heads, d_k, d_v);
 }
 
 kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
@@ -365,7 +373,7 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
     const int64_t units = (int64_t)num_seqs * num_heads;
     // 1. the forward pass again, for the state at every 16-token boundary (its o goes to the workspace)
     if (total_tokens / 16 > 0) {
-        const PrefillVariant* var = pick_variant(dtype, d_k, 16, units, false);
+        const PrefillVariant* var = pick_variant(dtype, d_k, 16, units, false, true);
         if (!var) return KDA_ERR_UNSUPPORTED;
         const int nslab = d_v / (16 * var->nwc);
         if ((units + 7) / 8 * 8 * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;
@@ -385,7 +393,7 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
         fp.seq_len = cu_seqlens ? 0 : (int32_t)(total_tokens / num_seqs);
         fp.nslab = nslab;
         fp.scale = scale;
-        fp.ckpt = static_cast<float*>(workspace);
+        fp.ckpt = static_cast<float*>(workspace);  // bf16 blocked states (kind 3 kernels)
         fp.ckpt_cap = total_tokens / 16;
         fp.ckpt_interval = 16;
         fp.z = nullptr;
@@ -403,15 +411,18 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
     bp.cu = cu_seqlens;
     bp.dO = d_o;
     bp.dST = d_final_state;
-    bp.ckpt = static_cast<const float*>(workspace);
+    bp.ckpt = workspace;
     bp.dq = dq;
     bp.dk = dk;
     bp.dv = dv;
     bp.dg = dg;
     bp.dbeta = dbeta;
     bp.dS0 = d_initial_state;
-    bp.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) +
-                                       backward_o_bytes(total_tokens, num_heads, d_v));
+    const size_t part_off = backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) + backward_o_bytes(total_tokens, num_heads, d_v);
+    bp.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_off);
+    bp.S0b = initial_state ? static_cast<char*>(workspace) + part_off +
+                                 align256(kda::backward_partial_bytes(total_tokens, num_heads))
+                           : nullptr;
     bp.T_total = total_tokens;
     bp.N = num_seqs;
     bp.H = num_heads;

@@ -38,8 +38,12 @@
 // 32w..32w+31 (two 16-row tiles) in the products that sum over the half's
 // value columns (dQ~, dW and its transpose, dKb, dgamma), with full operands
 // staged in LDS between phases.  The state at each chunk start comes from the
-// forward kernel's checkpoints (every 16 tokens) and enters the products as a
-// bf16 operand, as in the forward pass; dgamma is the diagonal of S dS'^T
+// forward kernel's checkpoints (every 16 tokens), which it writes rounded to
+// bf16 in a blocked layout (a lane's fragment is one 8-byte load): the state
+// only enters the products as a bf16 operand, as in the forward pass, and
+// rounding it once there gives the values the reverse pass would form from
+// fp32 states (the initial state goes through the same rounding in a first
+// small kernel).  dgamma is the diagonal of S dS'^T
 // formed from the same bf16 operands.  e^Gamma and e^-Gamma are computed once
 // per chunk and kept in LDS for the gradient formulas.  All global loads of
 // the next chunk are issued while the current one is processed (one wave per
@@ -100,7 +104,7 @@ __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32
 
 // The global inputs of one chunk, held in registers until the chunk's turn.
 struct ChunkLoads {
-    f32x4 S[8];    // start state, rows 16r + 4gq + p of this lane's value column
+    uint2 S[8];    // start state (bf16), rows 16r + 4gq + p of this lane's value column
     f32x4 g[2];    // g tile pieces (4 floats each)
     uint4 q, k;    // raw q, k pieces (8 bf16 each)
     uint2 v, dO;   // this half's v, dO pieces (4 bf16 each)
@@ -199,15 +203,14 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     auto issue_loads = [&](int c, ChunkLoads& ld) {
         const int64_t t0 = bos + (int64_t)c * BC;
         const int nt = (int)((L - (int64_t)c * BC) < BC ? (L - (int64_t)c * BC) : BC);
-        const float* Sc = c > 0 ? p.ckpt + ((slot0 + c - 1) * H + h) * (int64_t)(BD * BD)
-                                : (p.S0 ? p.S0 + unit * BD * BD : nullptr);
-        const auto rS = buffer_rsrc(Sc ? Sc : p.g, Sc ? BD * BD * 4 : 0);
-        const int sv0 = (4 * gq * BD + col) * 4;
+        // bf16 blocked states (rows 16r + 4gq .. + 3 of column col: 8 bytes)
+        const uint16_t* Sc = c > 0 ? static_cast<const uint16_t*>(p.ckpt) + ((slot0 + c - 1) * H + h) * (int64_t)(BD * BD)
+                                   : (p.S0 ? static_cast<const uint16_t*>(p.S0b) + unit * BD * BD : nullptr);
+        const auto rS = buffer_rsrc(Sc ? static_cast<const void*>(Sc) : static_cast<const void*>(p.g), Sc ? BD * BD * 2 : 0);
+        const int sv0 = (gq * BD + col) * 8;
 #pragma unroll
         for (int r = 0; r < 8; ++r)
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp)
-                ld.S[r][pp] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rS, sv0, (16 * r + pp) * BD * 4, 0));
+            ld.S[r] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rS, sv0, r * 4 * BD * 8, 0));
         const auto rg = rows_rsrc(p.g + t0 * tok + hoff, nt, tok * 4, BD * 4);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         uint2 Sb[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            Sb[r] = fregs(ld.S[r]);
+            Sb[r] = ld.S[r];
             f32x4 tS = zero4(), tD = zero4();
             mma16(tS, Sb[r], eye);
             mma16(tD, fregs(dSr[r]), eye);
@@ -721,6 +724,19 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     }
 }
 
+// S0 (fp32 row-major) -> the bf16 blocked layout of the checkpoints; one
+// thread per (state, row quad, column).
+__global__ __launch_bounds__(256) void kda_backward_s0_kernel(BackwardParams p) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t units = (int64_t)p.N * p.H;
+    if (i >= units * (BD / 4) * BD) return;
+    const int64_t u = i / ((BD / 4) * BD);
+    const int rq = (int)((i / BD) % (BD / 4)), col = (int)(i % BD);
+    const float* src = p.S0 + u * BD * BD + (4 * rq) * BD + col;
+    const uint2 v = make_uint2(pack_bf16x2(src[0], src[BD]), pack_bf16x2(src[2 * BD], src[3 * BD]));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.S0b) + u * BD * BD + ((int64_t)rq * BD + col) * 4) = v;
+}
+
 // dq, dk (bf16), dg, dbeta (fp32) = partial of the first value half + that of
 // the second, per element; 32 threads per (token, head) row, 4 channels each.
 __global__ __launch_bounds__(256) void kda_backward_sum_kernel(BackwardParams p) {
@@ -751,9 +767,16 @@ size_t backward_partial_bytes(int64_t T_total, int32_t H) {
 hipError_t launch_backward_bf16_d128(const BackwardParams& p, hipStream_t s) {
     const int64_t units = (int64_t)p.N * p.H;
     if (units <= 0) return hipSuccess;
+    hipError_t err;
+    if (p.S0) {
+        if (!p.S0b) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(kda_backward_s0_kernel, dim3((unsigned)((units * (BD / 4) * BD + 255) / 256)), dim3(256), 0, s, p);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     const int64_t wgs = (units + 7) / 8 * 8 * NSL;
     hipLaunchKernelGGL(kda_backward_kernel, dim3((unsigned)wgs), dim3(BNT), 0, s, p);
-    hipError_t err = hipGetLastError();
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t rows = p.T_total * p.H;
     if (rows > 0) {

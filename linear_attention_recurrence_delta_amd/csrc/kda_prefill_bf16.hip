@@ -16,6 +16,12 @@ static const PrefillVariant kBf16Variants[] = {
     {2, 1, 128, 16, 4, WsCfg<2, 2, 8, true>::LDS, &launch_prefill_ws<2, 2, 8, true>},
     {2, 1, 128, 16, 2, WsCfg<1, 2, 8, true>::LDS, &launch_prefill_ws<1, 2, 8, true>},
     {2, 1, 128, 16, 1, WsCfg<1, 1, 8, true>::LDS, &launch_prefill_ws<1, 1, 8, true>},
+    // kind 3: the plain pipeline writing its checkpoints as bf16 in the blocked
+    // layout of the backward kernel (only the backward launches these)
+    {3, 1, 128, 16, 8, WsCfg<4, 2, 8>::LDS, &launch_prefill_ws<4, 2, 8, false, true>},
+    {3, 1, 128, 16, 4, WsCfg<2, 2, 8>::LDS, &launch_prefill_ws<2, 2, 8, false, true>},
+    {3, 1, 128, 16, 2, WsCfg<1, 2, 8>::LDS, &launch_prefill_ws<1, 2, 8, false, true>},
+    {3, 1, 128, 16, 1, WsCfg<1, 1, 8>::LDS, &launch_prefill_ws<1, 1, 8, false, true>},
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 8),
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 4),
     KDA_PREFILL_VARIANT(1, bf16_t, 128, 4, 2),

@@ -168,7 +168,11 @@ __device__ __forceinline__ float row_bcast15(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
 }
 
-template <int NCW, int TPW, int NSA, bool FUSED>
+// CKB: checkpoints as bf16 in the blocked layout the backward kernel reads
+// ([row / 4][column][row % 4] per state: the 4 rows a lane holds of one
+// column are 8 adjacent bytes), instead of the fp32 row-major states of the
+// public checkpoint call.
+template <int NCW, int TPW, int NSA, bool FUSED, bool CKB>
 __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
     typedef WsCfg<NCW, TPW, NSA, FUSED> Cfg;
     typedef Elem<bf16_t> E;
@@ -771,17 +775,33 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                     if (p.ckpt && (c + 1) % ck_chunks == 0 && (int64_t)(c + 1) * C <= ntok) {
                         const int64_t slot = (int64_t)ck0 + (c + 1) / ck_chunks - 1;
                         if (slot < p.ckpt_cap) {
-                            // one per-lane offset; rows as wave-uniform offsets
-                            const auto rc = buffer_rsrc(p.ckpt + (slot * H + h) * D * D, D * D * 4);
+                            if constexpr (CKB) {
+                                // rows 16ct + 4g4 .. + 3 of a column: one 8-byte store
+                                const auto rc = buffer_rsrc(reinterpret_cast<uint16_t*>(p.ckpt) + (slot * H + h) * D * D,
+                                                            D * D * 2);
+                                const uint32_t b_voff = (uint32_t)(g4 * D + col_base + vcol(0, l16)) * 8u;
 #pragma unroll
-                            for (int t = 0; t < TPW; ++t)
+                                for (int t = 0; t < TPW; ++t)
 #pragma unroll
-                                for (int ct = 0; ct < NCB; ++ct)
+                                    for (int ct = 0; ct < NCB; ++ct) {
+                                        u32x2 pk;
+                                        pk[0] = pack_bf16x2(Sm[t][ct][0], Sm[t][ct][1]);
+                                        pk[1] = pack_bf16x2(Sm[t][ct][2], Sm[t][ct][3]);
+                                        __builtin_amdgcn_raw_buffer_store_b64(pk, rc, b_voff + 32 * t, ct * 4 * D * 8, 0);
+                                    }
+                            } else {
+                                // one per-lane offset; rows as wave-uniform offsets
+                                const auto rc = buffer_rsrc(p.ckpt + (slot * H + h) * D * D, D * D * 4);
 #pragma unroll
-                                    for (int pp = 0; pp < 4; ++pp)
-                                        __builtin_amdgcn_raw_buffer_store_b32(
-                                            __float_as_uint(Sm[t][ct][pp]), rc, s_voff + 16 * t,
-                                            (16 * ct + pp) * D * 4, 0);
+                                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                                    for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                                        for (int pp = 0; pp < 4; ++pp)
+                                            __builtin_amdgcn_raw_buffer_store_b32(
+                                                __float_as_uint(Sm[t][ct][pp]), rc, s_voff + 16 * t,
+                                                (16 * ct + pp) * D * 4, 0);
+                            }
                         }
                     }
                 }
@@ -810,11 +830,11 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     }
 }
 
-template <int NCW, int TPW, int NSA, bool FUSED = false>
+template <int NCW, int TPW, int NSA, bool FUSED = false, bool CKB = false>
 hipError_t launch_prefill_ws(const PrefillParams& p, hipStream_t s) {
     const int64_t units = (int64_t)p.N * p.H;
     const int64_t blocks = (units + 7) / 8 * 8 * p.nslab;  // whole groups of 8 units
-    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA, FUSED>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA, FUSED, CKB>), dim3((unsigned)blocks),
                        dim3(64 * (NCW + 2 + NSA)), 0, s, p);
     return hipGetLastError();
 }

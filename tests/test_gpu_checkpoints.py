@@ -81,6 +81,15 @@ def test_bf16_chunk_staged_kernel(kda, oracle_mod, monkeypatch, chunk, interval)
            init_std=0.05, kind="0", monkeypatch=monkeypatch)
 
 
+@pytest.mark.parametrize("kind", ["2", "3"])
+def test_bf16_internal_kernel_kinds_not_selectable(kda, oracle_mod, monkeypatch, kind):
+    """Kind 2 (fused gate) and kind 3 (the backward's bf16 blocked
+    checkpoints) are never picked for the public call: KDA_PREFILL_KIND asking
+    for them falls back to the plain pipeline, fp32 row-major checkpoints."""
+    _check(kda, oracle_mod, [37, 0, 64, 1, 130, 200, 16], 2, 128, torch.bfloat16, 16, 0, 305, init_std=0.05,
+           kind=kind, monkeypatch=monkeypatch)
+
+
 @pytest.mark.parametrize("d,chunk", [(16, 16), (64, 32), (128, 16)])
 def test_fp32(kda, oracle_mod, d, chunk):
     _check(kda, oracle_mod, [33, 48, 0, 70], 2, d, torch.float32, 2 * chunk, chunk, 304, init_std=0.3)
