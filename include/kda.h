@@ -294,11 +294,10 @@ int32_t kda_prefill_backward_supported(int32_t qkv_dtype, int32_t d_k,
                                        int32_t d_v);
 
 /* Bytes of device workspace kda_prefill_backward needs (0 for unsupported
- * arguments), four parts each rounded up to 256 bytes: the state after every
+ * arguments), three parts each rounded up to 256 bytes: the state after every
  * 16 tokens of each sequence (floor(total_tokens / 16) * num_heads * d_k *
  * d_v, rounded to bf16: the reverse pass uses the states only as bf16 matrix
- * operands), the forward run's output (total_tokens * num_heads * d_v bf16),
- * per half of the value columns the partial key-side gradients (2 *
+ * operands), per half of the value columns the partial key-side gradients (2 *
  * total_tokens * num_heads * (3 * d_k + 1) fp32), and the initial states
  * rounded to bf16 (num_seqs * num_heads * d_k * d_v). */
 size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs,
@@ -315,8 +314,9 @@ size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs,
  * gradients with respect to q, k, v, g, beta and the initial states.
  *
  * Computed in three launches on `stream` (four with initial states): the
- * forward recurrence again (the kernel of kda_prefill, chunk 16), keeping the
- * state at every 16-token boundary in the workspace; the initial states
+ * forward recurrence again (the kernel of kda_prefill, chunk 16, without its
+ * output), keeping the state at every 16-token boundary in the workspace; the
+ * initial states
  * rounded into the same form; the reverse pass, two workgroups per
  * (sequence, head), one per half of the value columns, walking the chunks
  * last to first; and the sum of the two halves' key-side partials.

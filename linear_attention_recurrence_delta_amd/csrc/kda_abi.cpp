@@ -301,18 +301,15 @@ kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int3
 
 // Workspace of the backward, each part at a 256-byte aligned offset: the
 // state after every 16 tokens of each sequence (at most total_tokens / 16
-// states per head, bf16 in the backward kernel's blocked layout), the bf16 o
-// of the forward run that produces them, the reverse kernel's fp32 partials
-// per half of the value columns, and the initial states in the blocked layout.
+// states per head, bf16 in the backward kernel's blocked layout), the reverse
+// kernel's fp32 partials per half of the value columns, and the initial
+// states in the blocked layout.
 static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 static size_t backward_ckpt_bytes(int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v) {
     return align256((size_t)(total_tokens / 16) * (size_t)num_heads * (size_t)d_k * (size_t)d_v * 2);
 }
 static size_t backward_s0_bytes(int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v) {
     return align256((size_t)num_seqs * (size_t)num_heads * (size_t)d_k * (size_t)d_v * 2);
-}
-static size_t backward_o_bytes(int64_t total_tokens, int32_t num_heads, int32_t d_v) {
-    return align256((size_t)total_tokens * (size_t)num_heads * (size_t)d_v * 2);
 }
 
 int32_t kda_prefill_backward_supported(int32_t dtype, int32_t d_k, int32_t d_v) {
@@ -323,7 +320,7 @@ size_t kda_prefill_backward_workspace_bytes(int32_t num_seqs, int64_t total_toke
                                             int32_t d_k, int32_t d_v, int32_t dtype) {
     if (!kda_prefill_backward_supported(dtype, d_k, d_v) || total_tokens < 0 || num_heads < 1 || num_seqs < 0)
         return 0;
-    return backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) + backward_o_bytes(total_tokens, num_heads, d_v) +
+    return backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) +
            align256(kda::backward_partial_bytes(total_tokens, num_heads)) +
            backward_s0_bytes(num_seqs, num_heads, d_k, d_v);
 }
@@ -371,7 +368,7 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
         if (bad) return KDA_ERR_DOMAIN;
     }
     const int64_t units = (int64_t)num_seqs * num_heads;
-    // 1. the forward pass again, for the state at every 16-token boundary (its o goes to the workspace)
+    // 1. the forward pass again, for the state at every 16-token boundary (no o)
     if (total_tokens / 16 > 0) {
         const PrefillVariant* var = pick_variant(dtype, d_k, 16, units, false, true);
         if (!var) return KDA_ERR_UNSUPPORTED;
@@ -385,7 +382,7 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
         fp.beta = beta;
         fp.S0 = initial_state;
         fp.cu = cu_seqlens;
-        fp.o = static_cast<char*>(workspace) + backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v);
+        fp.o = nullptr;  // not read by the kind 3 kernels
         fp.Sout = nullptr;
         fp.T_total = total_tokens;
         fp.N = num_seqs;
@@ -418,7 +415,7 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
     bp.dg = dg;
     bp.dbeta = dbeta;
     bp.dS0 = d_initial_state;
-    const size_t part_off = backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v) + backward_o_bytes(total_tokens, num_heads, d_v);
+    const size_t part_off = backward_ckpt_bytes(total_tokens, num_heads, d_k, d_v);
     bp.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_off);
     bp.S0b = initial_state ? static_cast<char*>(workspace) + part_off +
                                  align256(kda::backward_partial_bytes(total_tokens, num_heads))

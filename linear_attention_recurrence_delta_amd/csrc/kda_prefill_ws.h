@@ -168,10 +168,11 @@ __device__ __forceinline__ float row_bcast15(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
 }
 
-// CKB: checkpoints as bf16 in the blocked layout the backward kernel reads
-// ([row / 4][column][row % 4] per state: the 4 rows a lane holds of one
-// column are 8 adjacent bytes), instead of the fp32 row-major states of the
-// public checkpoint call.
+// CKB: the backward's forward run.  Checkpoints as bf16 in the blocked layout
+// the backward kernel reads ([row / 4][column][row % 4] per state: the 4 rows
+// a lane holds of one column are 8 adjacent bytes) instead of the fp32
+// row-major states of the public checkpoint call, and no output o (p.o is not
+// read): the readout products Q~ S and P U and the P tile are skipped.
 template <int NCW, int TPW, int NSA, bool FUSED, bool CKB>
 __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
     typedef WsCfg<NCW, TPW, NSA, FUSED> Cfg;
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                 kl[ch] = kv * e2;
             }
             const Frag klf = E::make(kl[0], kl[1], kl[2], kl[3]);
-            st_frag(QB + l16 * PD + c0, E::make(qb[0], qb[1], qb[2], qb[3]));
+            if constexpr (!CKB) st_frag(QB + l16 * PD + c0, E::make(qb[0], qb[1], qb[2], qb[3]));
             st_frag(KB + l16 * PD + c0, E::make(kb[0], kb[1], kb[2], kb[3]));
             st_frag(KL + l16 * PD + c0, klf);
             uint16_t* klt = reinterpret_cast<uint16_t*>(KLT) + l16;
@@ -496,18 +497,22 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             const int c0 = 16 * kb + 4 * g4;
             const Frag a0 = ld_frag(KL + l16 * PD + c0), a1 = ld_frag(KL + l16 * PD + c0 + 16);
             const Frag k0 = ld_frag(KB + l16 * PD + c0), k1 = ld_frag(KB + l16 * PD + c0 + 16);
-            const Frag q0 = ld_frag(QB + l16 * PD + c0), q1 = ld_frag(QB + l16 * PD + c0 + 16);
             mma32(accA, a0, a1, k0, k1);
-            mma32(accP, a0, a1, q0, q1);
+            if constexpr (!CKB) {
+                const Frag q0 = ld_frag(QB + l16 * PD + c0), q1 = ld_frag(QB + l16 * PD + c0 + 16);
+                mma32(accP, a0, a1, q0, q1);
+            }
         }
         // acc[pp] = M[s = 4 g4 + pp][r = l16] = sum_c KL[s][c] X[r][c]
         bf16_t* P = reinterpret_cast<bf16_t*>(slotP(c));
         float* AT = reinterpret_cast<float*>(slotA(c));
         const int r = l16;
-        f32x4 pv;
+        if constexpr (!CKB) {
+            f32x4 pv;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? accP[pp] : 0.f;
-        st_frag(P + r * PK + 4 * g4, E::make(pv));
+            for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? accP[pp] : 0.f;
+            st_frag(P + r * PK + 4 * g4, E::make(pv));
+        }
         const float br = BETA[r];
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) {
@@ -566,7 +571,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     // ------------------------------------------------------------ consumers
     const uint32_t o_voff = (uint32_t)l16 * (uint32_t)(H * D) * 2u + (uint32_t)(col_base + 4 * TPW * g4) * 2u;
     auto consume = [&](int c, f32x4 (&Sm)[TPW][NCB]) {
-        const int nv = rows_valid(c);
+        [[maybe_unused]] const int nv = rows_valid(c);
         char* s4 = slot4(c);
         const bf16_t* QB = reinterpret_cast<const bf16_t*>(s4 + Cfg::S4_QB);
         const bf16_t* KB = reinterpret_cast<const bf16_t*>(s4 + Cfg::S4_KB);
@@ -579,14 +584,16 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 
         // Every LDS operand of this step is requested up front, so their
         // latency overlaps the state conversion and the X / QS products.
+        // (CKB: the backward's run needs only the states, not o: no Q~ S, P U)
         Frag kf[NCB], qf[NCB];
 #pragma unroll
         for (int kb = 0; kb < NCB; ++kb) {
             kf[kb] = ld_frag(KB + l16 * PD + 16 * kb + 4 * g4);
-            qf[kb] = ld_frag(QB + l16 * PD + 16 * kb + 4 * g4);
+            if constexpr (!CKB) qf[kb] = ld_frag(QB + l16 * PD + 16 * kb + 4 * g4);
         }
         const Frag Tf = ld_frag(T + l16 * PK + 4 * g4);
-        const Frag Pf = ld_frag(P + l16 * PK + 4 * g4);
+        Frag Pf;
+        if constexpr (!CKB) Pf = ld_frag(P + l16 * PK + 4 * g4);
         const float4 b4 = *reinterpret_cast<const float4*>(BETA + 4 * g4);
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
         float vv[TPW][4];
@@ -620,7 +627,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 mma32(X[t], kf[kb], kf[kb + 1], Sop[t][kb], Sop[t][kb + 1]);
-                mma32(QS[t], Sop[t][kb], Sop[t][kb + 1], qf[kb], qf[kb + 1]);
+                if constexpr (!CKB) mma32(QS[t], Sop[t][kb], Sop[t][kb + 1], qf[kb], qf[kb + 1]);
             }
         // U = T diag(beta) (V - X), all tiles side by side.
         Frag Uf[TPW];
@@ -641,15 +648,17 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             for (int t = 0; t < TPW; ++t) mma16(Sm[t][ct], ktf[ct], Uf[t]);  // S + KL^T U
         // O^T = (Qt S)^T + U^T P^T: lane (g4, l16) holds token l16 at the
         // value columns vcol(t, 4 g4 + pp) = 4 TPW g4 + 4 t + pp, adjacent.
-        uint32_t ov[TPW][2];
+        [[maybe_unused]] uint32_t ov[TPW][2];
+        if constexpr (!CKB) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            // (P U)^T in its own accumulator, added to the 32-deep QS
-            // product by VALU (kda_device.h: no SrcC chain across shapes)
-            f32x4 PU = zero4();
-            mma16(PU, Uf[t], Pf);
-            ov[t][0] = pack_bf16x2(p.scale * (QS[t][0] + PU[0]), p.scale * (QS[t][1] + PU[1]));
-            ov[t][1] = pack_bf16x2(p.scale * (QS[t][2] + PU[2]), p.scale * (QS[t][3] + PU[3]));
+            for (int t = 0; t < TPW; ++t) {
+                // (P U)^T in its own accumulator, added to the 32-deep QS
+                // product by VALU (kda_device.h: no SrcC chain across shapes)
+                f32x4 PU = zero4();
+                mma16(PU, Uf[t], Pf);
+                ov[t][0] = pack_bf16x2(p.scale * (QS[t][0] + PU[0]), p.scale * (QS[t][1] + PU[1]));
+                ov[t][1] = pack_bf16x2(p.scale * (QS[t][2] + PU[2]), p.scale * (QS[t][3] + PU[3]));
+            }
         }
 #pragma unroll
         for (int ct = 0; ct < NCB; ++ct)
@@ -662,13 +671,15 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             }
         // One store per lane; rows past the end of the sequence get an offset
         // beyond the buffer's range, and buffer stores out of range are dropped.
-        const int64_t e0 = chunk_base(c);
-        const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
-        const uint32_t oo = l16 < nv ? o_voff : 0x80000000u;
-        if constexpr (TPW == 2)
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
-        else
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{ov[0][0], ov[0][1]}, ro, oo, 0, 0);
+        if constexpr (!CKB) {
+            const int64_t e0 = chunk_base(c);
+            const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
+            const uint32_t oo = l16 < nv ? o_voff : 0x80000000u;
+            if constexpr (TPW == 2)
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{ov[0][0], ov[0][1]}, ro, oo, 0, 0);
+        }
     };
 
     // ------------------------------------------------------------ pipeline

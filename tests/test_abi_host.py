@@ -270,12 +270,11 @@ def test_prefill_backward_supported_set_and_workspace(lib):
     assert lib.kda_prefill_backward_supported(F32, 128, 128) == 0
     assert lib.kda_prefill_backward_supported(BF16, 64, 64) == 0
     assert lib.kda_prefill_backward_supported(BF16, 128, 64) == 0
-    # one bf16 state per head for every full 16 tokens, the forward run's bf16 o,
-    # the two value halves' fp32 partials of dq, dk, dg and dbeta, the bf16
-    # initial states
+    # one bf16 state per head for every full 16 tokens, the two value halves'
+    # fp32 partials of dq, dk, dg and dbeta, the bf16 initial states
     r256 = lambda b: -(-b // 256) * 256
-    want = lambda N, T, H: (r256((T // 16) * H * 128 * 128 * 2) + r256(T * H * 128 * 2) +
-                            r256(2 * T * H * (3 * 128 + 1) * 4) + r256(N * H * 128 * 128 * 2))
+    want = lambda N, T, H: (r256((T // 16) * H * 128 * 128 * 2) + r256(2 * T * H * (3 * 128 + 1) * 4) +
+                            r256(N * H * 128 * 128 * 2))
     assert lib.kda_prefill_backward_workspace_bytes(2, 100, 3, 128, 128, BF16) == want(2, 100, 3)
     assert lib.kda_prefill_backward_workspace_bytes(1, 15, 3, 128, 128, BF16) == want(1, 15, 3)
     assert lib.kda_prefill_backward_workspace_bytes(0, 0, 3, 128, 128, BF16) == want(0, 0, 3)
