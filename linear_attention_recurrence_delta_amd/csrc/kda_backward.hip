@@ -36,7 +36,7 @@
 // value columns 16w..16w+15 of its half in the column products (dU, U, the
 // dS update, dV; dS stays in registers across chunks) and key rows
 // 32w..32w+31 (two 16-row tiles) in the products that sum over the half's
-// value columns (dQ~, dW and its transpose, dKb, dgamma), with full operands
+// value columns (dQ~, dW and its transpose, dKb), with full operands
 // staged in LDS between phases.  The state at each chunk start comes from the
 // forward kernel's checkpoints (every 16 tokens), which it writes rounded to
 // bf16 in a blocked layout (a lane's fragment is one 8-byte load): the state
@@ -91,6 +91,11 @@ __device__ __forceinline__ uint2 fcol32(const float* X, int pitch, int r, int c)
     return make_uint2(pack_bf16x2(X[r * pitch + c], X[(r + 1) * pitch + c]),
                       pack_bf16x2(X[(r + 2) * pitch + c], X[(r + 3) * pitch + c]));
 }
+// Lane 15 of each 16-lane row, broadcast to the row (ds_swizzle bit mode:
+// and-mask 0x10, or-mask 0x0f).
+__device__ __forceinline__ float row_lane15(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
+}
 // An accumulator, taken over its rows, as a B fragment.
 __device__ __forceinline__ uint2 fregs(const f32x4& a) {
     return make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         sKrT[BD * PT];
     // this half's v, scale * dO (after its last use, the dv staging), U, dU
     __shared__ __align__(16) uint16_t sV[BC * PS], sdO[BC * PS], sU[BC * PS], sdU[BC * PS];
-    // Gamma; e^Gamma and e^-Gamma (fp32, channel-major)
+    // raw g; e^Gamma and e^-Gamma (fp32, channel-major)
     __shared__ __align__(16) float sG[BC * PF], sET[BD * PT], sEiT[BD * PT];
     // 16 x 16 fp32 matrices; the ...T arrays hold transposes
     __shared__ __align__(16) float sM[256], sPT[256], sT[256], sTT[256], sdP[256], sdPT[256], sdTv[256], sdM[256],
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int pi = tid + BNT * j, row = pi >> 5, seg = pi & 31;
-            *reinterpret_cast<f32x4*>(&sG[row * PF + 4 * seg]) = ld.g[j];  // g, summed in place below
+            *reinterpret_cast<f32x4*>(&sG[row * PF + 4 * seg]) = ld.g[j];
         }
         *reinterpret_cast<uint4*>(sQr + qrow * PB + 8 * qseg) = ld.q;
         *reinterpret_cast<uint4*>(sKr + qrow * PB + 8 * qseg) = ld.k;
@@ -284,31 +289,25 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         // the next chunk's loads, in flight while this one is processed
         if (c > 0) issue_loads(c - 1, ld);
         __syncthreads();  // B0: raw tiles in LDS
-        if (tid < BD) {
-            // Gamma: inclusive cumulative sum of g over the chunk, per key channel
-            float gc[BC];
-#pragma unroll
-            for (int t = 0; t < BC; ++t) gc[t] = sG[t * PF + tid];
-            float acc = 0.f;
-#pragma unroll
-            for (int t = 0; t < BC; ++t) {
-                acc += gc[t];
-                sG[t * PF + tid] = acc;
-            }
-            sGam[tid] = __expf(acc);
-        }
-        __syncthreads();  // B0b: Gamma
-        // the decay factors e^Gamma, e^-Gamma (kept for the gradients) and
+        // Gamma (inclusive cumulative sum of g over the chunk's tokens), the
+        // decay factors e^Gamma, e^-Gamma (kept for the gradients) and
         // e^(Gamma_last - Gamma) = gamma e^-Gamma, and the decay-scaled
         // operands.  Wave w takes channel tiles 2w and 2w + 1; lane (gq, li)
         // token li and channels 4gq..4gq+3 of the tile, i.e. its A fragment,
         // which times the identity gives the channel-major copy (4 tokens of
-        // one channel per lane)
+        // one channel per lane).  The 16 tokens of a channel are the 16 lanes
+        // of a DPP row: Gamma is a row scan, Gamma_last the row's lane 15.
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c16 = 16 * (2 * w + j), t = li, c4 = c16 + 4 * gq;
-            const f32x4 G = *reinterpret_cast<const f32x4*>(&sG[t * PF + c4]);
-            const f32x4 gam = *reinterpret_cast<const f32x4*>(&sGam[c4]);
+            f32x4 G = *reinterpret_cast<const f32x4*>(&sG[t * PF + c4]);  // raw g
+            f32x4 gam;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                G[u] = row_inclusive_sum16(G[u]);
+                gam[u] = __expf(row_lane15(G[u]));
+            }
+            if (li == 15) *reinterpret_cast<f32x4*>(&sGam[c4]) = gam;
             const uint2 qr = *reinterpret_cast<const uint2*>(sQr + t * PB + c4);
             const uint2 kr = *reinterpret_cast<const uint2*>(sKr + t * PB + c4);
             const float qf[4] = {__uint_as_float(qr.x << 16), __uint_as_float(qr.x & 0xffff0000u),
@@ -353,26 +352,84 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         }
         __syncthreads();  // B1
 
-        // ---------------------------------------------- phase 1: M, P; K-bar dS'
-        if (w < 2) {
-            const uint16_t* X = w == 0 ? sKt : sQt;
+        // ---------------------------------------------- phase 1: M and T, P, dgamma; K-bar dS'
+        if (w == 1 || w == 2) {
+            const uint16_t* X = w == 2 ? sKt : sQt;
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb = 0; kb < BD; kb += 32)
                 mma32(acc, frow(X, PB, li, kb + 4 * gq), frow(X, PB, li, kb + 16 + 4 * gq),
                       frow(sKi, PB, li, kb + 4 * gq), frow(sKi, PB, li, kb + 16 + 4 * gq));
-            if (w == 0) {
+            if (w == 2) {
+                // M, and T from it on this wave (waves 0 and 3 have no other
+                // work here; the next phase then has none of the inverse)
+                f32x4 Aa;
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
                     const int t = 4 * gq + pp, s = li;
-                    sM[t * P16 + s] = s < t ? acc[pp] : 0.f;
+                    const float m = s < t ? acc[pp] : 0.f;
+                    sM[t * P16 + s] = m;
+                    Aa[pp] = sBeta[t] * m;  // A[t][li]
                 }
+                // T = (I + A)^-1, A = Diag(beta) M strictly lower triangular,
+                // so A^16 = 0 and T = (I - A)(I + A^2)(I + A^4)(I + A^8): three
+                // squarings and three products, fp32, every operand in
+                // registers.  The factors are polynomials in A and commute, so
+                // each product is taken as A^(2^k) T.  Lane (gq, li) holds
+                // entries (4gq + pp, li) of each accumulator; the accumulator
+                // of X is the B fragment of X and the A fragment of X^T, so
+                // the wave keeps A^(2^k) and its transpose.  A^T comes from
+                // the rows of M just written (this wave's own LDS writes).
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                const f32x4 mrow = *reinterpret_cast<const f32x4*>(&sM[li * P16 + 4 * gq]);
+                const float bl = sBeta[li];
+                f32x4 At, Tc;
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) {
+                    const int r = 4 * gq + pp;
+                    At[pp] = bl * mrow[pp];  // A[li][r]
+                    Tc[pp] = (r == li ? 1.f : 0.f) - Aa[pp];
+                }
+                auto f4 = [](const f32x4& x) { return make_float4(x[0], x[1], x[2], x[3]); };
+                f32x4 A2 = zero4(), A2t = zero4();
+                mma16(A2, f4(At), f4(Aa));
+                mma16(A2t, f4(Aa), f4(At));
+                mma16(Tc, f4(A2t), f4(Tc));  // (I + A^2)(I - A)
+                f32x4 A4 = zero4(), A4t = zero4();
+                mma16(A4, f4(A2t), f4(A2));
+                mma16(A4t, f4(A2), f4(A2t));
+                mma16(Tc, f4(A4t), f4(Tc));  // (I + A^4) ...
+                f32x4 A8t = zero4();
+                mma16(A8t, f4(A4), f4(A4t));
+                mma16(Tc, f4(A8t), f4(Tc));  // (I + A^8) ...
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) sT[(4 * gq + pp) * P16 + li] = Tc[pp];
+                *reinterpret_cast<f32x4*>(&sTT[li * P16 + 4 * gq]) = Tc;  // column li of T is row li of T^T
             } else {
                 // P^T[s][t] for s = li, t = 4gq..4gq+3
                 f32x4 pt;
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) pt[pp] = li <= 4 * gq + pp ? acc[pp] : 0.f;
                 *reinterpret_cast<f32x4*>(&sPT[li * P16 + 4 * gq]) = pt;
+            }
+        } else {
+            // dgamma = rowsum(S * dS') over this half's columns, as dgamma *
+            // gamma for the dg formula: the diagonal of the 16 x 16 diagonal
+            // blocks of S dS'^T, from the bf16 operand values the other
+            // products use; waves 0 and 3 take 4 row tiles each
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int kr0 = 16 * ((w == 0 ? 0 : 4) + q);
+                f32x4 dd = zero4();
+#pragma unroll
+                for (int cb = 0; cb < CW; cb += 32)
+                    mma32(dd, frow(sS, PS, kr0 + li, cb + 4 * gq), frow(sS, PS, kr0 + li, cb + 16 + 4 * gq),
+                          frow(sdS, PS, kr0 + li, cb + 4 * gq), frow(sdS, PS, kr0 + li, cb + 16 + 4 * gq));
+                // entry (li, li) sits in lane group li / 4, register li % 4
+                const int dp = li & 3;
+                const float dg = dp == 0 ? dd[0] : dp == 1 ? dd[1] : dp == 2 ? dd[2] : dd[3];
+                if ((li >> 2) == gq) sExt[kr0 + li] = dg * sGam[kr0 + li];
             }
         }
         f32x4 dUa = zero4();  // (K-bar dS')[t][col]
@@ -382,42 +439,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                   fregs(dSr[r + 1]));
         __syncthreads();  // B2
 
-        // ---------------------------------------------- phase 2: T; dU; dS without W
-        if (w == 0) {
-            // T = (I + A)^-1, A = Diag(beta) M strictly lower triangular, so
-            // A^16 = 0 and T = (I - A)(I + A^2)(I + A^4)(I + A^8): three
-            // squarings and three products, fp32 on this wave with every
-            // operand in registers.  The factors are polynomials in A and
-            // commute, so each product is taken as A^(2^k) T.  Lane (gq, li)
-            // holds entries (4gq + pp, li) of each accumulator; the
-            // accumulator of X is the B fragment of X and the A fragment of
-            // X^T, so the wave keeps A^(2^k) and its transpose.
-            const f32x4 mrow = *reinterpret_cast<const f32x4*>(&sM[li * P16 + 4 * gq]);
-            const float bl = sBeta[li];
-            f32x4 Aa, At, Tc;
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const int r = 4 * gq + pp;
-                Aa[pp] = sBeta[r] * sM[r * P16 + li];  // A[r][li]
-                At[pp] = bl * mrow[pp];                 // A[li][r]
-                Tc[pp] = (r == li ? 1.f : 0.f) - Aa[pp];
-            }
-            auto f4 = [](const f32x4& x) { return make_float4(x[0], x[1], x[2], x[3]); };
-            f32x4 A2 = zero4(), A2t = zero4();
-            mma16(A2, f4(At), f4(Aa));
-            mma16(A2t, f4(Aa), f4(At));
-            mma16(Tc, f4(A2t), f4(Tc));  // (I + A^2)(I - A)
-            f32x4 A4 = zero4(), A4t = zero4();
-            mma16(A4, f4(A2t), f4(A2));
-            mma16(A4t, f4(A2), f4(A2t));
-            mma16(Tc, f4(A4t), f4(Tc));  // (I + A^4) ...
-            f32x4 A8t = zero4();
-            mma16(A8t, f4(A4), f4(A4t));
-            mma16(Tc, f4(A8t), f4(Tc));  // (I + A^8) ...
-#pragma unroll
-            for (int pp = 0; pp < 4; ++pp) sT[(4 * gq + pp) * P16 + li] = Tc[pp];
-            *reinterpret_cast<f32x4*>(&sTT[li * P16 + 4 * gq]) = Tc;  // column li of T is row li of T^T
-        }
+        // ---------------------------------------------- phase 2: dU; dS without W
         f32x4 dU;
         {
             f32x4 dUb = zero4();  // (P^T dO_s)[t][col]
@@ -536,25 +558,16 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         }
         __syncthreads();  // B5
 
-        // ---------------------------------------------- phase 5: dK-bar, dgamma; dP; dA, dM
-        // dgamma = rowsum(S * dS') over this half's columns: the diagonal of
-        // the 16 x 16 diagonal blocks of S dS'^T, from the bf16 operand values
+        // ---------------------------------------------- phase 5: dK-bar; dP; dA, dM
         f32x4 dKb[RT];
 #pragma unroll
         for (int rr = 0; rr < RT; ++rr) {
             const int kr0 = 32 * w + 16 * rr;
-            f32x4 dd = zero4();
             dKb[rr] = zero4();
 #pragma unroll
-            for (int cb = 0; cb < CW; cb += 32) {
-                const uint2 bd0 = frow(sdS, PS, kr0 + li, cb + 4 * gq), bd1 = frow(sdS, PS, kr0 + li, cb + 16 + 4 * gq);
-                mma32(dKb[rr], frow(sU, PS, li, cb + 4 * gq), frow(sU, PS, li, cb + 16 + 4 * gq), bd0, bd1);
-                mma32(dd, frow(sS, PS, kr0 + li, cb + 4 * gq), frow(sS, PS, kr0 + li, cb + 16 + 4 * gq), bd0, bd1);
-            }
-            // entry (li, li) sits in lane group li / 4, register li % 4
-            const int dp = li & 3;
-            const float dg = dp == 0 ? dd[0] : dp == 1 ? dd[1] : dp == 2 ? dd[2] : dd[3];
-            if ((li >> 2) == gq) sExt[kr0 + li] = dg * sGam[kr0 + li];
+            for (int cb = 0; cb < CW; cb += 32)
+                mma32(dKb[rr], frow(sU, PS, li, cb + 4 * gq), frow(sU, PS, li, cb + 16 + 4 * gq),
+                      frow(sdS, PS, kr0 + li, cb + 4 * gq), frow(sdS, PS, kr0 + li, cb + 16 + 4 * gq));
         }
         if (w == 0) {
             f32x4 acc = zero4();
