@@ -20,6 +20,9 @@
 //   dT  = dU (Diag(beta) V)^T + dW (Diag(beta) K~)^T,     dA = strict-lower(-T^T dT T^T)
 //   dV  = Diag(beta) T^T dU,   dK~ = Diag(beta) T^T dW + dM Ki,   dM = Diag(beta) dA
 //   dKi = dM^T K~ + dP^T Q~,   dbeta = rowsum(T^T dU * V) + rowsum(T^T dW * K~) + rowsum(dA * M)
+// where the first two sums are the column sums of T * (dU V^T + dW K~^T), the
+// matrix dT is made from (so they take one 16 x 16 pass instead of sums over
+// all value columns and key rows);
 // then through the decay-scaled operands to q, k and Gamma, and from Gamma to
 // g by a reverse cumulative sum; Gamma_last, a sum of every g of the chunk,
 // adds dgamma * gamma and the Kb terms to all of them.
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         sdMT[256];
     __shared__ __align__(16) float sdTk[BNW][256];
     __shared__ __align__(16) float sGam[BD];
-    __shared__ float sBeta[BC], sExt[BD], sdBv[BNW][BC], sdBk[BNW][BC], sdBa[BC];
+    __shared__ float sBeta[BC], sExt[BD], sdBa[BC];
     static_assert(3 * BC * PF * sizeof(float) <= sizeof(sSS), "staging fits in the S / dS' area");
     uint16_t* sS = sSS;
     uint16_t* sdS = sSS + BD * PS;
@@ -477,16 +480,11 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             }
             Ut = zero4();
             mma16(Ut, aTb, fcol(sV, PS, 4 * gq, cl));
-            // dV = Diag(beta) T^T dU; beta partial rowsum(T^T dU * V)
+            // dV = Diag(beta) T^T dU
             f32x4 dBv = zero4();
             mma16(dBv, frow32(sTT, P16, li, 4 * gq), fregs(dU));
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const int m = 4 * gq + pp;
-                dvv[pp] = sBeta[m] * dBv[pp];
-                const float x = row_inclusive_sum16(dBv[pp] * bf(sV[m * PS + cl]));  // total in lane 15 of the row
-                if (li == 15) sdBv[w][m] = x;
-            }
+            for (int pp = 0; pp < 4; ++pp) dvv[pp] = sBeta[4 * gq + pp] * dBv[pp];
         }
         __syncthreads();  // B4
 
@@ -507,7 +505,6 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         // over this half's value columns
         f32x4 dQt[RT], dKt[RT];
         f32x4 dTk = zero4();
-        float bk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rr = 0; rr < RT; ++rr) {
             const int kr0 = 32 * w + 16 * rr;
@@ -523,38 +520,25 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             }
             dWt = -dWt;  // dW[t][row]
             dWT = -dWT;  // dW^T[row][t]
-            // from W = T Diag(beta) K~: Diag(beta) T^T dW; beta partial rowsum(T^T dW * K~)
+            // from W = T Diag(beta) K~: Diag(beta) T^T dW
             f32x4 dBk = zero4();
             mma16(dBk, frow32(sTT, P16, li, 4 * gq), fregs(dWt));
-            // fp32 K~ = k e^Gamma at tokens 4gq..4gq+3 of channel kr0 + li
-            const uint2 kr4 = frow(sKrT, PT, kr0 + li, 4 * gq);
-            const f32x4 e4 = *reinterpret_cast<const f32x4*>(&sET[(kr0 + li) * PT + 4 * gq]);
-            const float kt4[4] = {__uint_as_float(kr4.x << 16) * e4[0], __uint_as_float(kr4.x & 0xffff0000u) * e4[1],
-                                  __uint_as_float(kr4.y << 16) * e4[2], __uint_as_float(kr4.y & 0xffff0000u) * e4[3]};
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) {
-                const int m = 4 * gq + pp;
-                dKt[rr][pp] = sBeta[m] * dBk[pp];
-                bk[pp] += dBk[pp] * kt4[pp];
-            }
-            // this wave's share of dW (Diag(beta) K~)^T, as its transpose [s][t]
-            mma16(dTk, fscale(frow(sKt, PB, li, kr0 + 4 * gq), sBeta[li]), fregs(dWT));
+            for (int pp = 0; pp < 4; ++pp) dKt[rr][pp] = sBeta[4 * gq + pp] * dBk[pp];
+            // this wave's share of H = dW K~^T, as its transpose [s][t]
+            mma16(dTk, frow(sKt, PB, li, kr0 + 4 * gq), fregs(dWT));
         }
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-            const float x = row_inclusive_sum16(bk[pp]);  // total in lane 15 of the row
-            if (li == 15) sdBk[w][4 * gq + pp] = x;
-            sdTk[w][(4 * gq + pp) * P16 + li] = dTk[pp];
-        }
+        for (int pp = 0; pp < 4; ++pp) sdTk[w][(4 * gq + pp) * P16 + li] = dTk[pp];
         if (w == 1) {
-            // dU (Diag(beta) V)^T over this half's columns
+            // G = dU V^T over this half's columns
             f32x4 acc = zero4();
 #pragma unroll
             for (int cb = 0; cb < CW; cb += 32)
                 mma32(acc, frow(sdU, PS, li, cb + 4 * gq), frow(sdU, PS, li, cb + 16 + 4 * gq),
                       frow(sV, PS, li, cb + 4 * gq), frow(sV, PS, li, cb + 16 + 4 * gq));
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) sdTv[(4 * gq + pp) * P16 + li] = acc[pp] * sBeta[li];
+            for (int pp = 0; pp < 4; ++pp) sdTv[(4 * gq + pp) * P16 + li] = acc[pp];
         }
         __syncthreads();  // B5
 
@@ -584,9 +568,16 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             }
             *reinterpret_cast<f32x4*>(&sdPT[li * P16 + 4 * gq]) = pt;
         } else if (w == 1) {
-            // dT[t][u] = dTv[t][u] + sum over waves of dTk^T; Z = dT T^T; dA = -T^T Z
+            // dT[t][u] = (G + H)[t][u] beta_u, with G = dU V^T and H = dW K~^T
+            // (the W and U~ products, W = T Diag(beta) K~, U~ = T Diag(beta)
+            // V); Z = dT T^T; dA = -T^T Z.  The same G + H gives the beta
+            // partial of those two products, sum over i of T[i][t] (G + H)[i][t]:
+            // lane (gq, li) holds (G + H)[li][4gq + pp], summed over the lanes
+            // of its row with the dA * M terms below.
             uint2 adT;
+            float xb[4];
             {
+                const f32x4 trow = *reinterpret_cast<const f32x4*>(&sT[li * P16 + 4 * gq]);
                 float v4[4];
 #pragma unroll
                 for (int pp = 0; pp < 4; ++pp) {
@@ -594,7 +585,8 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                     float acc = sdTv[li * P16 + u];
 #pragma unroll
                     for (int ww = 0; ww < BNW; ++ww) acc += sdTk[ww][u * P16 + li];
-                    v4[pp] = acc;
+                    v4[pp] = acc * sBeta[u];
+                    xb[pp] = trow[pp] * acc;
                 }
                 adT = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
             }
@@ -609,7 +601,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 const float da = s < m ? -dA[pp] : 0.f;
                 mt[pp] = sBeta[m] * da;
                 sdM[m * P16 + s] = mt[pp];
-                const float x = row_inclusive_sum16(da * sM[m * P16 + s]);  // total in lane 15 of the row
+                const float x = row_inclusive_sum16(xb[pp] + da * sM[m * P16 + s]);  // total in lane 15 of the row
                 if (li == 15) sdBa[m] = x;
             }
             *reinterpret_cast<f32x4*>(&sdMT[li * P16 + 4 * gq]) = mt;
@@ -720,10 +712,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             // dbeta partial (threads 0..15)
             {
                 const int t = tid & (BC - 1);
-                float acc = sdBa[t];
-#pragma unroll
-                for (int ww = 0; ww < BNW; ++ww) acc += sdBv[ww][t] + sdBk[ww][t];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc), rows_rsrc(pdb + t0 * H + h, nt, H * 4, 4),
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sdBa[t]), rows_rsrc(pdb + t0 * H + h, nt, H * 4, 4),
                                                       tid < BC ? t * H * 4 : OOB, 0, 0);
             }
         }
