@@ -120,8 +120,7 @@ struct ChunkLoads {
 };
 
 __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
-    // S and dS' of this half (bf16); after their last use, the fp32 staging of
-    // the key-side partials (dq, dk, dg)
+    // S and dS' of this half (bf16)
     __shared__ __align__(16) uint16_t sSS[2 * BD * PS];
     __shared__ __align__(16) uint16_t sQr[BC * PB], sKr[BC * PB], sQt[BC * PB], sKt[BC * PB], sKi[BC * PB],
         sKb[BC * PB], sW[BC * PB];
@@ -139,12 +138,8 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     __shared__ __align__(16) float sdTk[BNW][256];
     __shared__ __align__(16) float sGam[BD];
     __shared__ float sBeta[BC], sExt[BD], sdBa[BC];
-    static_assert(3 * BC * PF * sizeof(float) <= sizeof(sSS), "staging fits in the S / dS' area");
     uint16_t* sS = sSS;
     uint16_t* sdS = sSS + BD * PS;
-    float* fq = reinterpret_cast<float*>(sSS);
-    float* fk = fq + BC * PF;
-    float* fG = fk + BC * PF;
     uint16_t* sDv = sdO;
 
     const int tid = threadIdx.x;
@@ -609,9 +604,16 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         __syncthreads();  // B6
 
         // ---------------------------------------------- phase 6: dM, dP terms; q, k, Gamma partials
+        // this half's partials go straight from registers to memory: a lane
+        // holds tokens 4gq..4gq+3 of one channel (4-byte stores, token rows
+        // as wave-uniform offsets; rows past the sequence end are dropped)
+        const auto rq = rows_rsrc(pdq + t0 * tok + hoff, nt, tok * 4, BD * 4);
+        const auto rk = rows_rsrc(pdk + t0 * tok + hoff, nt, tok * 4, BD * 4);
+        const auto rgd = rows_rsrc(pdg + t0 * tok + hoff, nt, tok * 4, BD * 4);
 #pragma unroll
         for (int rr = 0; rr < RT; ++rr) {
             const int kc = 32 * w + 16 * rr + li;  // key channel of this lane
+            const int vo = (int)((4 * gq * tok + kc) * 4);
             f32x4 t1 = zero4(), t2 = zero4(), dKi = zero4();
             // tokens 4gq..4gq+3 of channel kc of Ki, K~, Q~ (B fragments)
             const uint2 bKi = frow(sKiT, PT, kc, 4 * gq), bKt = frow(sKtT, PT, kc, 4 * gq),
@@ -640,8 +642,11 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
                 const float e = e4[pp], ei = ei4[pp], eb = gmk * ei;
                 const float qf = qrv[pp], kf = krv[pp];
                 const float Qt = qf * e, Kt = kf * e, Kb = kf * eb;
-                fq[t * PF + kc] = (dQt[rr][pp] + t2[pp]) * e;
-                fk[t * PF + kc] = (dKt[rr][pp] + t1[pp]) * e + dKi[pp] * ei + dKb[rr][pp] * eb;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((dQt[rr][pp] + t2[pp]) * e), rq, vo,
+                                                      (int)(pp * tok * 4), 0);
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __float_as_uint((dKt[rr][pp] + t1[pp]) * e + dKi[pp] * ei + dKb[rr][pp] * eb), rk, vo,
+                    (int)(pp * tok * 4), 0);
                 // The intra-chunk pair terms (through M and P) enter dGamma_t
                 // and dGamma_s with opposite signs and cancel exactly on the
                 // diagonal; both sides are formed from the bf16 operand values
@@ -681,26 +686,16 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
             }
             const float ext = sExt[kc] + sufA;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) fG[(4 * gq + pp) * PF + kc] = (ext + sa[pp]) + (preB + pb[pp]);
+            for (int pp = 0; pp < 4; ++pp)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((ext + sa[pp]) + (preB + pb[pp])), rgd, vo,
+                                                      (int)(pp * tok * 4), 0);
         }
 #pragma unroll
         for (int pp = 0; pp < 4; ++pp) sDv[(4 * gq + pp) * PS + cl] = f32_to_bf16(dvv[pp]);
         __syncthreads();  // B7
 
-        // ---------------------------------------------- phase 7: stores (this half's partials, dV)
+        // ---------------------------------------------- phase 7: stores (dV, dbeta partial)
         {
-            const auto rq = rows_rsrc(pdq + t0 * tok + hoff, nt, tok * 4, BD * 4);
-            const auto rk = rows_rsrc(pdk + t0 * tok + hoff, nt, tok * 4, BD * 4);
-            const auto rgd = rows_rsrc(pdg + t0 * tok + hoff, nt, tok * 4, BD * 4);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int pi = tid + BNT * j, t = pi >> 5, seg = pi & 31;
-                const int vo = (int)(t * tok * 4) + 16 * seg;
-                typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4v*>(fq + t * PF + 4 * seg), rq, vo, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4v*>(fk + t * PF + 4 * seg), rk, vo, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4v*>(fG + t * PF + 4 * seg), rgd, vo, 0, 0);
-            }
             // dV of this half: 128 pieces of 8 bf16 (threads 0..127)
             {
                 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
