@@ -59,13 +59,14 @@ def log(*a):
 
 # Sources each measured kernel is compiled from; a counter record is used only
 # while these files are unchanged.
-KERNEL_SOURCES = {
-    "kda_prefill_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
-    "kda_prefill_k3_varlen_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
+KERNEL_SOURCES = {  # csrc/ files, and the build script where it sets per-file compiler flags
+    "kda_prefill_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "../build_lib.py"),
+    "kda_prefill_k3_varlen_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "../build_lib.py"),
     "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
-    "kda_prefill_fused_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h"),
+    "kda_prefill_fused_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "../build_lib.py"),
     "kda_output_gate_32k_x96": ("kda_output_gate.hip", "kda_device.h", "kda_internal.h"),
-    "kda_backward_k3_dense_32k": ("kda_backward.hip", "kda_backward.h", "kda_device.h", "kda_prefill_ws.h"),
+    "kda_backward_k3_dense_32k": ("kda_backward.hip", "kda_backward.h", "kda_device.h", "kda_prefill_ws.h",
+                                  "../build_lib.py"),
 }
 
 

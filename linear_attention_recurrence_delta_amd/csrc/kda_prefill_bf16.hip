@@ -5,6 +5,17 @@
 
 namespace kda {
 
+// instantiated in kda_prefill_ws_ilp.hip (built with another scheduler)
+extern template hipError_t launch_prefill_ws<2, 2, 8, false, false>(const PrefillParams&, hipStream_t);
+extern template hipError_t launch_prefill_ws<1, 2, 8, false, false>(const PrefillParams&, hipStream_t);
+extern template hipError_t launch_prefill_ws<1, 1, 8, false, false>(const PrefillParams&, hipStream_t);
+extern template hipError_t launch_prefill_ws<2, 2, 8, true, false>(const PrefillParams&, hipStream_t);
+extern template hipError_t launch_prefill_ws<1, 2, 8, true, false>(const PrefillParams&, hipStream_t);
+extern template hipError_t launch_prefill_ws<1, 1, 8, true, false>(const PrefillParams&, hipStream_t);
+extern template hipError_t launch_prefill_ws<2, 2, 8, false, true>(const PrefillParams&, hipStream_t);
+extern template hipError_t launch_prefill_ws<1, 2, 8, false, true>(const PrefillParams&, hipStream_t);
+extern template hipError_t launch_prefill_ws<1, 1, 8, false, true>(const PrefillParams&, hipStream_t);
+
 static const PrefillVariant kBf16Variants[] = {
     // wave-specialised pipeline: NCW consumer waves x TPW 16 columns, 8 stage-A waves
     {1, 1, 128, 16, 8, WsCfg<4, 2, 8>::LDS, &launch_prefill_ws<4, 2, 8>},
