@@ -59,22 +59,29 @@ def log(*a):
 
 # Sources each measured kernel is compiled from; a counter record is used only
 # while these files are unchanged.
-KERNEL_SOURCES = {  # csrc/ files, and the build script where it sets per-file compiler flags
-    "kda_prefill_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "../build_lib.py"),
-    "kda_prefill_k3_varlen_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "../build_lib.py"),
-    "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
-    "kda_prefill_fused_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "../build_lib.py"),
+# csrc/ files a record depends on; "flags:<file>" stands for the extra compiler
+# flags build_lib.py gives that translation unit.
+KERNEL_SOURCES = {
+    "kda_prefill_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "flags:kda_prefill_ws_ilp.hip"),
+    "kda_prefill_k3_varlen_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "flags:kda_prefill_bf16.hip"),
+    "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h", "flags:kda_decode.hip"),
+    "kda_prefill_fused_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h",
+                                       "flags:kda_prefill_ws_ilp.hip"),
     "kda_output_gate_32k_x96": ("kda_output_gate.hip", "kda_device.h", "kda_internal.h"),
     "kda_backward_k3_dense_32k": ("kda_backward.hip", "kda_backward.h", "kda_device.h", "kda_prefill_ws.h",
-                                  "../build_lib.py"),
+                                  "flags:kda_backward.hip", "flags:kda_prefill_ws_ilp.hip"),
 }
 
 
 def kernel_source_digest(kernel):
+    from linear_attention_recurrence_delta_amd import build_lib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_recurrence_delta_amd", "csrc")
     for f in KERNEL_SOURCES[kernel]:
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        if f.startswith("flags:"):
+            h.update(repr(build_lib.PER_FILE.get(f[len("flags:"):], [])).encode())
+        else:
+            h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
