@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_DTYPE_F32 = 0,
@@ -96,7 +96,13 @@ int32_t kda_decode_supported(int32_t qkv_dtype, int32_t d_k, int32_t d_v);
 /*
  * Bytes of device workspace kda_prefill needs for these sizes (0 = none;
  * then workspace may be NULL).  Returns 0 as well for unsupported or invalid
- * sizes, which kda_prefill itself rejects.
+ * sizes, which kda_prefill itself rejects.  The figure is for a dense batch
+ * (cu_seqlens NULL) on the current device; a call with cu_seqlens needs no
+ * workspace.  The only user is the sequence-segment scan (see
+ * kda_prefill_desc.segments), which the library picks for dense batches with
+ * few (sequence, head) recurrences per compute unit: about (G - 1) * 128 KiB
+ * per (sequence, head) for G segments per sequence (32 MiB for one
+ * 1,048,576-token sequence of 16 heads on 256 compute units).
  */
 size_t kda_prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens,
                                    int32_t num_heads, int32_t d_k, int32_t d_v,
@@ -149,6 +155,83 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens,
                        const float *initial_state, const int32_t *cu_seqlens,
                        void *o, float *final_state,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill_ex -- the prefill entry points in one call, with the kernel
+ * plan explicit: for measurements and tests that compare kernels, and for
+ * callers that want to fix the plan.  kda_prefill, kda_prefill_fused and
+ * kda_prefill_checkpointed are this call with a zero plan (the library's
+ * choice, which depends only on the sizes and the device's compute-unit
+ * count).  No plan changes what is computed; kernels and slab widths change
+ * the rounding order at most (results stay deterministic for a given plan;
+ * slab widths of one kernel are bitwise identical).
+ *
+ * Sequence-segment scan.  A dense batch whose (sequence, head) recurrences
+ * are too few to fill the device is cut into G segments per sequence.  The
+ * state update is affine in the state ("Understanding Kimi K3's attention",
+ * state-update equation), so each segment g is one map S_end = M_g S_start +
+ * B_g.  Three launches: segment 0 runs from the initial state while the maps
+ * of segments 1 .. G-2 are computed in parallel (M_g from the identity with
+ * v = 0, B_g from zero: two 128-column state runs each); a short combine
+ * chains start(g + 1) = M_g start(g) + B_g in fp32; segments 1 .. G-1 run
+ * again from their start states with outputs.  This is the pages' state
+ * passing between chunks ("Inside Kimi K3", section "Sequence mixing")
+ * applied between segments, in parallel over segments instead of one chain.
+ */
+#define KDA_KERNEL_AUTO 0          /* the library's choice                          */
+#define KDA_KERNEL_PIPELINED 1     /* wave-specialised pipeline: bf16, d = 128, chunk 16 */
+#define KDA_KERNEL_CHUNK_STAGED 2  /* one chunk at a time by all waves: every built
+                                      (dtype, d, chunk)                              */
+
+typedef struct {
+    int32_t num_seqs;             /* as kda_prefill                                   */
+    int64_t total_tokens;
+    int32_t num_heads;
+    int32_t d_k;
+    int32_t d_v;
+    int32_t qkv_dtype;
+    int32_t chunk_size;           /* 16, 32, 64 or 0 (default 16)                     */
+    float scale;
+    int32_t fused;                /* 1: kda_prefill_fused semantics (raw q, k; z and   */
+                                  /*    a_log instead of g), else 0                   */
+    int32_t checkpoint_interval;  /* 0: none; else as kda_prefill_checkpointed        */
+    int64_t checkpoint_capacity;
+    int32_t kernel;               /* KDA_KERNEL_*                                     */
+    int32_t slab_columns;         /* value columns per workgroup: 0 = library choice,  */
+                                  /* else one the kernel is built with (pipelined:    */
+                                  /* 16, 32, 64, 128; chunk-staged d = 128: 32, 64,   */
+                                  /* 128 by chunk)                                    */
+    int32_t segments;             /* segment scan: 0 = library choice, 1 = off,        */
+                                  /* 2 .. 256 = segments per sequence (dense batches,  */
+                                  /* pipelined kernel, no fused gate or checkpoints,  */
+                                  /* at least segments + 1 chunks per sequence)        */
+} kda_prefill_desc;
+
+typedef struct {
+    const void *q, *k, *v;        /* as kda_prefill (fused: raw q and k)              */
+    const float *g;               /* NULL when fused                                  */
+    const void *z;                /* fused only: decay logits                          */
+    const float *a_log;           /* fused only                                       */
+    const float *beta;
+    const float *initial_state;
+    const int32_t *cu_seqlens;
+    void *o;
+    float *final_state;
+    float *checkpoints;           /* with checkpoint_interval > 0                      */
+} kda_prefill_tensors;
+
+/* Workspace bytes of kda_prefill_ex for this description, for a dense batch
+ * (cu_seqlens NULL) on the current device; 0 for invalid or unsupported
+ * descriptions and whenever no segment scan runs. */
+size_t kda_prefill_ex_workspace_bytes(const kda_prefill_desc *desc);
+
+/* Errors as the flat entry points; KDA_ERR_NULL_POINTER for a NULL desc or
+ * tensors; KDA_ERR_UNSUPPORTED for a kernel, slab width or segment count
+ * that is not built or not applicable to the call (e.g. segments >= 2 with
+ * cu_seqlens); KDA_ERR_BAD_SHAPE for negative plan fields or a workspace
+ * equal to a tensor pointer. */
+kda_status kda_prefill_ex(const kda_prefill_desc *desc, const kda_prefill_tensors *tensors, void *workspace,
+                          size_t workspace_bytes, void *stream);
 
 /*
  * kda_prefill_checkpointed -- kda_prefill that also emits the state at every

@@ -7,6 +7,9 @@ from ._lib import LIB_PATH, LibraryMissing  # noqa: F401
 from .kda import (  # noqa: F401
     KDA_DTYPE_BF16,
     KDA_DTYPE_F32,
+    KDA_KERNEL_AUTO,
+    KDA_KERNEL_CHUNK_STAGED,
+    KDA_KERNEL_PIPELINED,
     KdaError,
     kda_abi_version,
     kda_decode_step,
@@ -15,6 +18,7 @@ from .kda import (  # noqa: F401
     kda_prefill_backward,
     kda_prefill_backward_supported,
     kda_prefill_checkpointed,
+    kda_prefill_ex_workspace_bytes,
     kda_prefill_fused,
     kda_prefill_fused_supported,
     kda_output_gate,

@@ -18,6 +18,23 @@ _lib = None
 # name -> (restype, argtypes)
 _i32, _i64, _f32, _sz, _vp = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                               ctypes.c_size_t, ctypes.c_void_p)
+
+
+class PrefillDesc(ctypes.Structure):
+    """kda_prefill_desc (include/kda.h), same field order and C layout."""
+    _fields_ = [("num_seqs", _i32), ("total_tokens", _i64), ("num_heads", _i32), ("d_k", _i32),
+                ("d_v", _i32), ("qkv_dtype", _i32), ("chunk_size", _i32), ("scale", _f32), ("fused", _i32),
+                ("checkpoint_interval", _i32), ("checkpoint_capacity", _i64), ("kernel", _i32),
+                ("slab_columns", _i32), ("segments", _i32)]
+
+
+class PrefillTensors(ctypes.Structure):
+    """kda_prefill_tensors (include/kda.h): device pointers."""
+    _fields_ = [(n, _vp) for n in ("q", "k", "v", "g", "z", "a_log", "beta", "initial_state", "cu_seqlens",
+                                   "o", "final_state", "checkpoints")]
+
+
+_pdesc, _ptens = ctypes.POINTER(PrefillDesc), ctypes.POINTER(PrefillTensors)
 SIGNATURES = {
     "kda_abi_version": (_i32, []),
     "kda_status_string": (ctypes.c_char_p, [_i32]),
@@ -29,6 +46,8 @@ SIGNATURES = {
     "kda_prefill_checkpointed": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                         _i32, _vp, _i64, _vp, _sz, _vp]),
+    "kda_prefill_ex_workspace_bytes": (_sz, [_pdesc]),
+    "kda_prefill_ex": (_i32, [_pdesc, _ptens, _vp, _sz, _vp]),
     "kda_prefill_fused_supported": (_i32, [_i32, _i32, _i32, _i32]),
     "kda_prefill_fused": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

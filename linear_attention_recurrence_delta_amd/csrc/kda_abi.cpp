@@ -48,6 +48,29 @@ int device_cu_count() {
     return n;
 }
 
+bool kind_built(int32_t dtype, int32_t D, int32_t C, int kind) {
+    int count = 0;
+    const PrefillVariant* tab = variants(dtype, &count);
+    for (int i = 0; i < count; ++i)
+        if (tab[i].D == D && tab[i].C == C && tab[i].kind == kind) return true;
+    return false;
+}
+
+// Kernel kind a call runs: 3 for the backward's forward run (bf16 blocked
+// checkpoints, no o), 2 for the fused gate / norm, else the plan's kernel
+// (the pipeline where it is built when the plan leaves it to the library).
+// -1 when the combination is not built.
+int plan_kind(int32_t dtype, int32_t D, int32_t C, bool fused, bool ckb, int32_t kernel) {
+    int kind;
+    if (ckb) kind = 3;
+    else if (fused) kind = kernel == KDA_KERNEL_CHUNK_STAGED ? -1 : 2;
+    else if (kernel == KDA_KERNEL_PIPELINED) kind = 1;
+    else if (kernel == KDA_KERNEL_CHUNK_STAGED) kind = 0;
+    else if (kernel == KDA_KERNEL_AUTO) kind = kind_built(dtype, D, C, 1) ? 1 : 0;
+    else kind = -1;
+    return kind >= 0 && kind_built(dtype, D, C, kind) ? kind : -1;
+}
+
 // Value columns per workgroup, in 16-column waves.  Fewer columns per
 // (sequence, head) means more workgroups (d_v slabs): that fills more compute
 // units when there are few (sequence, head) recurrences, and each workgroup's
@@ -55,62 +78,163 @@ int device_cu_count() {
 // work (decay, Gram, solve).  The chunk-staged kernel keeps whole heads (8
 // waves, fastest on MI355X for the K3 shapes at every batch size tried).  The
 // pipelined kernel halves the slab while the grid still fits in one pass over
-// the compute units (96 heads -> 2 slabs, 16 heads -> 8).  KDA_PREFILL_WAVES
-// (an integer) overrides the choice and KDA_PREFILL_KIND the kernel; results
-// are bitwise identical across slab widths.
-// ckb: the backward's forward run, whose kernels write bf16 checkpoints in the
-// backward kernel's blocked layout (kind 3); no other call may get those.
-const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units, bool fused, bool ckb = false) {
+// the compute units (96 heads -> 2 slabs, 16 heads -> 8); the segment scan
+// runs whole heads (its items already fill the device).  An explicit slab
+// width must be built for the kernel.  Results are bitwise identical across
+// slab widths.
+const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t units, int kind, int32_t slab_cols,
+                                   bool whole_heads) {
     int count = 0;
     const PrefillVariant* tab = variants(dtype, &count);
-    int want_kind = 1;  // the wave-specialised pipeline where it is built
-    if (const char* env = getenv("KDA_PREFILL_KIND")) want_kind = atoi(env);
-    if (fused) want_kind = 2;        // only the fused kernels read z and a_log
-    else if (ckb) want_kind = 3;
-    else if (want_kind == 2 || want_kind == 3) want_kind = 1;
-    bool have_kind = false;
-    for (int i = 0; i < count; ++i)
-        if (tab[i].D == D && tab[i].C == C && tab[i].kind == want_kind) have_kind = true;
-    if ((fused || ckb) && !have_kind) return nullptr;
     int want = D / 16;
-    if (have_kind && want_kind >= 1) {
+    if (slab_cols > 0) {
+        if (slab_cols % 16 != 0) return nullptr;
+        want = slab_cols / 16;
+    } else if (kind >= 1 && !whole_heads) {
         const int64_t cus = device_cu_count();
         while (want > 1 && units * (D / (16 * want)) * 2 <= cus) want /= 2;
     }
-    if (const char* env = getenv("KDA_PREFILL_WAVES")) {
-        const int e = atoi(env);
-        if (e > 0) want = e;
-    }
-    // Among (D, C) matches: the wanted kind if built; then the largest wave
-    // count not above the wanted one, else the smallest built.
     const PrefillVariant* best = nullptr;
     const PrefillVariant* smallest = nullptr;
     for (int i = 0; i < count; ++i) {
         const PrefillVariant& v = tab[i];
-        if (v.D != D || v.C != C) continue;
-        if ((v.kind == 2) != fused || (v.kind == 3) != ckb) continue;
-        if (have_kind && v.kind != want_kind) continue;
+        if (v.D != D || v.C != C || v.kind != kind) continue;
+        if (slab_cols > 0) {
+            if (v.nwc == want) return &v;
+            continue;
+        }
         if (!smallest || v.nwc < smallest->nwc) smallest = &v;
         if (v.nwc <= want && (!best || v.nwc > best->nwc)) best = &v;
     }
+    if (slab_cols > 0) return nullptr;
     return best ? best : smallest;
+}
+
+// Sequence-segment scan plan (kda_internal.h, PrefillParams::seg_*): G
+// segments per sequence, segments 1 .. G-1 of Lc chunks each and segment 0
+// the rest (at least 2 Lc - 1 chunks: it runs alone while the maps of two
+// segments run one after the other on another compute unit).
+struct SegPlan {
+    int G = 1;
+    int64_t len0 = 0, len = 0;  // tokens
+};
+
+constexpr int kMaxSegments = 256;
+
+// The library's choice: with P = compute units per (sequence, head) unit,
+// phase 1 runs segment 0 and 2 (G - 2) maps, phase 3 the G - 1 other
+// segments, so G = P + 1 fills the device with a chain of about 3 / (G + 1)
+// of the sequence (against the whole sequence for the direct chain).  Worth
+// it from P = 4 on, with segments of at least 64 chunks.
+int auto_segments(int64_t units, int64_t t_seq) {
+    if (units <= 0) return 1;
+    const int64_t P = device_cu_count() / units;
+    if (P < 4) return 1;
+    const int G = (int)(P < 32 ? P : 32) + 1;
+    const int64_t chunks = (t_seq + 15) / 16;
+    return chunks >= 64 * (int64_t)(G + 1) ? G : 1;
+}
+
+SegPlan seg_plan(int G, int64_t t_seq) {
+    SegPlan sp;
+    sp.G = G;
+    if (G < 2) return sp;
+    const int64_t chunks = (t_seq + 15) / 16;
+    const int64_t lc = chunks / (G + 1);
+    sp.len = 16 * lc;
+    sp.len0 = t_seq - (int64_t)(G - 1) * sp.len;
+    return sp;
+}
+
+size_t seg_workspace_bytes(int64_t units, int G, int D) {
+    return G < 2 ? 0 : (size_t)units * (size_t)(G - 1) * 2 * (size_t)D * (size_t)D * sizeof(float);
+}
+
+// Segment count a call uses: 1 (direct) unless the plan asks for the scan or
+// leaves it to the library, and the call is one it supports: a dense batch
+// (no cu_seqlens) on the plain pipelined kernel (bf16, d = 128, chunk 16),
+// without checkpoints.  0 when the plan asks for a scan the call cannot run.
+int plan_segments(const kda_prefill_desc& d, bool dense, int kind) {
+    const bool eligible = dense && kind == 1 && !d.fused && d.checkpoint_interval == 0 && d.num_seqs > 0 &&
+                          d.total_tokens > 0 && d.d_k == 128 && d.d_v == 128;
+    const int64_t units = (int64_t)d.num_seqs * d.num_heads;
+    const int64_t t_seq = d.num_seqs > 0 ? d.total_tokens / d.num_seqs : 0;
+    if (d.segments == 1) return 1;
+    if (d.segments == 0) return eligible ? auto_segments(units, t_seq) : 1;
+    if (!eligible || d.segments > kMaxSegments) return 0;
+    const int64_t chunks = (t_seq + 15) / 16;
+    if (chunks < d.segments + 1) return 0;  // every segment needs a chunk
+    return d.segments;
+}
+
+// Workspace a call needs; the segment scan is the only user.  kind and
+// segments as the call resolves them.
+size_t plan_workspace(const kda_prefill_desc& d, int segments) {
+    return seg_workspace_bytes((int64_t)d.num_seqs * d.num_heads, segments, d.d_k);
+}
+
+kda_prefill_desc flat_desc(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v,
+                           int32_t dtype, int32_t chunk_size, float scale) {
+    kda_prefill_desc d;
+    d.num_seqs = num_seqs;
+    d.total_tokens = total_tokens;
+    d.num_heads = num_heads;
+    d.d_k = d_k;
+    d.d_v = d_v;
+    d.qkv_dtype = dtype;
+    d.chunk_size = chunk_size;
+    d.scale = scale;
+    d.fused = 0;
+    d.checkpoint_interval = 0;
+    d.checkpoint_capacity = 0;
+    d.kernel = KDA_KERNEL_AUTO;
+    d.slab_columns = 0;
+    d.segments = 0;
+    return d;
+}
+
+bool sizes_valid(const kda_prefill_desc& d) {
+    return d.num_seqs >= 0 && d.total_tokens >= 0 && d.num_heads >= 1 && d.d_k >= 1 && d.d_v >= 1;
+}
+
+// Workspace bytes of a call described by d (dense tells whether cu_seqlens
+// is absent); 0 for invalid or unsupported descriptions, which the call
+// itself rejects.
+size_t desc_workspace_bytes(const kda_prefill_desc& d, bool dense) {
+    if (!sizes_valid(d) || d.total_tokens > INT32_MAX) return 0;
+    if (d.qkv_dtype != KDA_DTYPE_BF16 && d.qkv_dtype != KDA_DTYPE_F32) return 0;
+    if (d.d_k != d.d_v) return 0;
+    const int C = resolve_chunk(d.qkv_dtype, d.chunk_size);
+    const int kind = plan_kind(d.qkv_dtype, d.d_k, C, d.fused != 0, false, d.kernel);
+    if (kind < 0) return 0;
+    if (dense && d.num_seqs > 0 && d.total_tokens % d.num_seqs != 0) return 0;
+    const int G = plan_segments(d, dense, kind);
+    return G >= 2 ? plan_workspace(d, G) : 0;
 }
 }  // namespace
 
-static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
-                               int32_t d_v, int32_t dtype, int32_t chunk_size, float scale, const void* q,
-                               const void* k, const void* v, const float* g, const float* beta,
-                               const float* initial_state, const int32_t* cu_seqlens, void* o,
-                               float* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                               int32_t ckpt_interval, float* checkpoints, int64_t ckpt_capacity,
-                               bool fused = false, const void* z = nullptr, const float* a_log = nullptr) {
-    if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
+static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tensors& t, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    const int32_t num_seqs = d.num_seqs, num_heads = d.num_heads, d_k = d.d_k, d_v = d.d_v, dtype = d.qkv_dtype;
+    const int64_t total_tokens = d.total_tokens;
+    const bool fused = d.fused != 0;
+    const int32_t ckpt_interval = d.checkpoint_interval;
+    const int64_t ckpt_capacity = d.checkpoint_capacity;
+    const void *q = t.q, *k = t.k, *v = t.v, *z = t.z;
+    const float *g = t.g, *beta = t.beta, *a_log = t.a_log, *initial_state = t.initial_state;
+    const int32_t* cu_seqlens = t.cu_seqlens;
+    void* o = t.o;
+    float *final_state = t.final_state, *checkpoints = t.checkpoints;
+
+    if (!sizes_valid(d)) return KDA_ERR_BAD_SHAPE;
     if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return KDA_ERR_UNSUPPORTED;
     if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0 && total_tokens > 0) return KDA_ERR_BAD_SHAPE;
     if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
-    if (!kda_prefill_supported(dtype, d_k, d_v, chunk_size)) return KDA_ERR_UNSUPPORTED;
-    if (fused && !kda_prefill_fused_supported(dtype, d_k, d_v, chunk_size)) return KDA_ERR_UNSUPPORTED;
+    if (d.kernel < KDA_KERNEL_AUTO || d.kernel > KDA_KERNEL_CHUNK_STAGED || d.slab_columns < 0 || d.segments < 0)
+        return KDA_ERR_BAD_SHAPE;
+    if (!kda_prefill_supported(dtype, d_k, d_v, d.chunk_size)) return KDA_ERR_UNSUPPORTED;
+    if (fused && !kda_prefill_fused_supported(dtype, d_k, d_v, d.chunk_size)) return KDA_ERR_UNSUPPORTED;
     if (total_tokens > 0 && (!q || !k || !v || !beta || !o)) return KDA_ERR_NULL_POINTER;
     if (total_tokens > 0 && !fused && !g) return KDA_ERR_NULL_POINTER;
     if (total_tokens > 0 && fused && (!z || !a_log)) return KDA_ERR_NULL_POINTER;
@@ -123,10 +247,10 @@ static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t n
     // Checkpoints (ckpt_interval 0: none).  The interval is a positive multiple
     // of the chunk in use; the buffer holds at least floor(T_total / interval)
     // states, which bounds the sum of floor(length / interval) over sequences.
-    const int C_use = resolve_chunk(dtype, chunk_size);
+    const int C = resolve_chunk(dtype, d.chunk_size);
     if (ckpt_interval < 0 || ckpt_capacity < 0) return KDA_ERR_BAD_SHAPE;
     if (ckpt_interval > 0) {
-        if (ckpt_interval % C_use != 0) return KDA_ERR_BAD_SHAPE;
+        if (ckpt_interval % C != 0) return KDA_ERR_BAD_SHAPE;
         if (ckpt_capacity < total_tokens / ckpt_interval) return KDA_ERR_BAD_SHAPE;
         if (ckpt_capacity > 0 && !checkpoints) return KDA_ERR_NULL_POINTER;
         if ((int64_t)num_heads * d_k * d_v > INT64_MAX / (ckpt_capacity > 0 ? ckpt_capacity : 1))
@@ -135,8 +259,17 @@ static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t n
         for (const void* ptr : ins)
             if (checkpoints && ptr == checkpoints) return KDA_ERR_BAD_SHAPE;
     }
-    const size_t need = kda_prefill_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size);
+    const int kind = plan_kind(dtype, d_k, C, fused, false, d.kernel);
+    if (kind < 0) return KDA_ERR_UNSUPPORTED;
+    const int G = plan_segments(d, cu_seqlens == nullptr, kind);
+    if (G == 0) return KDA_ERR_UNSUPPORTED;
+    const size_t need = G >= 2 ? plan_workspace(d, G) : 0;
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (need > 0) {
+        const void* io[] = {q, k, v, g, beta, initial_state, o, final_state};
+        for (const void* ptr : io)
+            if (ptr == workspace) return KDA_ERR_BAD_SHAPE;
+    }
 
     if (num_seqs == 0) return KDA_OK;
     if (total_tokens == 0 && !final_state) return KDA_OK;
@@ -151,12 +284,10 @@ static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t n
         if (bad) return KDA_ERR_DOMAIN;
     }
 
-    const int C = resolve_chunk(dtype, chunk_size);
     const int64_t units = (int64_t)num_seqs * num_heads;
-    const PrefillVariant* var = pick_variant(dtype, d_k, C, units, fused);
+    const PrefillVariant* var = pick_variant(dtype, d_k, C, units, kind, d.slab_columns, G >= 2);
     if (!var) return KDA_ERR_UNSUPPORTED;
     const int nslab = d_v / (16 * var->nwc);
-    if ((units + 7) / 8 * 8 * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;  // padded grid
 
     kda::PrefillParams p;
     p.q = q;
@@ -173,14 +304,33 @@ static kda_status prefill_impl(int32_t num_seqs, int64_t total_tokens, int32_t n
     p.H = num_heads;
     p.seq_len = cu_seqlens ? 0 : (int32_t)(total_tokens / num_seqs);
     p.nslab = nslab;
-    p.scale = scale;
+    p.scale = d.scale;
     p.ckpt = (ckpt_interval > 0 && total_tokens / ckpt_interval > 0) ? checkpoints : nullptr;
     p.ckpt_cap = ckpt_capacity;
     p.ckpt_interval = ckpt_interval > 0 ? ckpt_interval : 1;
     p.z = z;
     p.a_log = a_log;
-    const hipError_t err = var->launch(p, static_cast<hipStream_t>(stream));
-    return err == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (G < 2) {
+        if (kda::ws_grid_blocks(p) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+        return var->launch(p, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    // Segment scan: maps (phase 1), their chain (phase 2), re-runs (phase 3).
+    if (!var->launch_seg) return KDA_ERR_UNSUPPORTED;
+    const SegPlan sp = seg_plan(G, p.seq_len);
+    p.seg_G = sp.G;
+    p.seg_len0 = (int32_t)sp.len0;
+    p.seg_len = (int32_t)sp.len;
+    p.seg_ws = static_cast<float*>(workspace);
+    p.seg_phase = 1;
+    const int64_t b1 = kda::ws_grid_blocks(p);
+    p.seg_phase = 3;
+    if (b1 > INT32_MAX || kda::ws_grid_blocks(p) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    p.seg_phase = 1;
+    if (var->launch_seg(p, s) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_segment_combine(p, s) != hipSuccess) return KDA_ERR_HIP;
+    p.seg_phase = 3;
+    return var->launch_seg(p, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 
@@ -256,14 +406,37 @@ int32_t kda_decode_supported(int32_t dtype, int32_t d_k, int32_t d_v) {
 
 size_t kda_prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
                                    int32_t d_v, int32_t dtype, int32_t chunk_size) {
-    (void)num_seqs;
-    (void)total_tokens;
-    (void)num_heads;
-    (void)d_k;
-    (void)d_v;
-    (void)dtype;
-    (void)chunk_size;
-    return 0;  // the fused chunk kernel keeps everything on chip
+    // the dense layout's need; packed batches (cu_seqlens) need none
+    return desc_workspace_bytes(flat_desc(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, 1.f), true);
+}
+
+size_t kda_prefill_ex_workspace_bytes(const kda_prefill_desc* desc) {
+    return desc ? desc_workspace_bytes(*desc, true) : 0;
+}
+
+kda_status kda_prefill_ex(const kda_prefill_desc* desc, const kda_prefill_tensors* tensors, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (!desc || !tensors) return KDA_ERR_NULL_POINTER;
+    return prefill_impl(*desc, *tensors, workspace, workspace_bytes, stream);
+}
+
+static kda_prefill_tensors flat_tensors(const void* q, const void* k, const void* v, const float* g,
+                                        const float* beta, const float* initial_state, const int32_t* cu_seqlens,
+                                        void* o, float* final_state) {
+    kda_prefill_tensors t;
+    t.q = q;
+    t.k = k;
+    t.v = v;
+    t.g = g;
+    t.z = nullptr;
+    t.a_log = nullptr;
+    t.beta = beta;
+    t.initial_state = initial_state;
+    t.cu_seqlens = cu_seqlens;
+    t.o = o;
+    t.final_state = final_state;
+    t.checkpoints = nullptr;
+    return t;
 }
 
 kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v,
@@ -271,9 +444,9 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads
                        const void* v, const float* g, const float* beta, const float* initial_state,
                        const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
                        size_t workspace_bytes, void* stream) {
-    return prefill_impl(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale, q, k, v, g, beta,
-                        initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes, stream, 0, nullptr,
-                        0);
+    const kda_prefill_desc d = flat_desc(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale);
+    const kda_prefill_tensors t = flat_tensors(q, k, v, g, beta, initial_state, cu_seqlens, o, final_state);
+    return prefill_impl(d, t, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_prefill_fused(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v,
@@ -281,9 +454,12 @@ kda_status kda_prefill_fused(int32_t num_seqs, int64_t total_tokens, int32_t num
                              const void* v, const void* z, const float* a_log, const float* beta,
                              const float* initial_state, const int32_t* cu_seqlens, void* o, float* final_state,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    return prefill_impl(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale, q, k, v, nullptr,
-                        beta, initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes, stream, 0,
-                        nullptr, 0, true, z, a_log);
+    kda_prefill_desc d = flat_desc(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale);
+    d.fused = 1;
+    kda_prefill_tensors t = flat_tensors(q, k, v, nullptr, beta, initial_state, cu_seqlens, o, final_state);
+    t.z = z;
+    t.a_log = a_log;
+    return prefill_impl(d, t, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
@@ -294,9 +470,12 @@ kda_status kda_prefill_checkpointed(int32_t num_seqs, int64_t total_tokens, int3
                                     int64_t checkpoint_capacity, void* workspace, size_t workspace_bytes,
                                     void* stream) {
     if (checkpoint_interval < 1) return KDA_ERR_BAD_SHAPE;
-    return prefill_impl(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale, q, k, v, g, beta,
-                        initial_state, cu_seqlens, o, final_state, workspace, workspace_bytes, stream,
-                        checkpoint_interval, checkpoints, checkpoint_capacity);
+    kda_prefill_desc d = flat_desc(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale);
+    d.checkpoint_interval = checkpoint_interval;
+    d.checkpoint_capacity = checkpoint_capacity;
+    kda_prefill_tensors t = flat_tensors(q, k, v, g, beta, initial_state, cu_seqlens, o, final_state);
+    t.checkpoints = checkpoints;
+    return prefill_impl(d, t, workspace, workspace_bytes, stream);
 }
 
 // Workspace of the backward, each part at a 256-byte aligned offset: the
@@ -370,10 +549,10 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
     const int64_t units = (int64_t)num_seqs * num_heads;
     // 1. the forward pass again, for the state at every 16-token boundary (no o)
     if (total_tokens / 16 > 0) {
-        const PrefillVariant* var = pick_variant(dtype, d_k, 16, units, false, true);
+        const PrefillVariant* var = pick_variant(dtype, d_k, 16, units, 3, 0, false);
         if (!var) return KDA_ERR_UNSUPPORTED;
         const int nslab = d_v / (16 * var->nwc);
-        if ((units + 7) / 8 * 8 * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+        if (kda::ws_pad8(units) * nslab > INT32_MAX) return KDA_ERR_UNSUPPORTED;
         kda::PrefillParams fp;
         fp.q = q;
         fp.k = k;

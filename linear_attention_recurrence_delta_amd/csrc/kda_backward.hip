@@ -159,11 +159,16 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
 
     int64_t bos, L, slot0;
     if (p.cu) {
-        bos = p.cu[n];
-        L = (int64_t)p.cu[n + 1] - bos;
+        // the forward kernels' rule: bounds clamped to [0, T_total], end >= start
+        const SeqRange r = clamp_seq(p.cu[n], p.cu[n + 1], p.T_total);
+        bos = r.a;
+        L = r.b - r.a;
         // checkpoints of earlier sequences: sum of floor(length / 16), lanes split
         int64_t part = 0;
-        for (int m = lane; m < n; m += 64) part += ((int64_t)p.cu[m + 1] - p.cu[m]) / BC;
+        for (int m = lane; m < n; m += 64) {
+            const SeqRange rm = clamp_seq(p.cu[m], p.cu[m + 1], p.T_total);
+            part += (rm.b - rm.a) / BC;
+        }
         for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
         // the same in every lane: made wave-uniform so that the buffer
         // descriptors built from it stay in scalar registers
@@ -182,6 +187,7 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
     const uint16_t* gdo_in = static_cast<const uint16_t*>(p.dO);
     const float scale = p.scale;
     const int nch = (int)((L + BC - 1) / BC);
+    const int64_t ckpt_cap = p.T_total / BC;  // states the forward run keeps
     const int64_t nel = p.T_total * tok;  // elements of one [T, H, 128] tensor
     float* pdq = p.part + (int64_t)half * nel;
     float* pdk = p.part + (int64_t)(NSL + half) * nel;
@@ -207,7 +213,12 @@ __global__ __launch_bounds__(BNT) void kda_backward_kernel(BackwardParams p) {
         const int64_t t0 = bos + (int64_t)c * BC;
         const int nt = (int)((L - (int64_t)c * BC) < BC ? (L - (int64_t)c * BC) : BC);
         // bf16 blocked states (rows 16r + 4gq .. + 3 of column col: 8 bytes)
-        const uint16_t* Sc = c > 0 ? static_cast<const uint16_t*>(p.ckpt) + ((slot0 + c - 1) * H + h) * (int64_t)(BD * BD)
+        // Slots past the forward run's T_total / 16 (reachable only when
+        // malformed offsets make sequences overlap) were never written: they
+        // read as zeros through an empty range.
+        const uint16_t* Sc = c > 0 ? ((slot0 + c - 1) < ckpt_cap
+                                          ? static_cast<const uint16_t*>(p.ckpt) + ((slot0 + c - 1) * H + h) * (int64_t)(BD * BD)
+                                          : nullptr)
                                    : (p.S0 ? static_cast<const uint16_t*>(p.S0b) + unit * BD * BD : nullptr);
         const auto rS = buffer_rsrc(Sc ? static_cast<const void*>(Sc) : static_cast<const void*>(p.g), Sc ? BD * BD * 2 : 0);
         const int sv0 = (gq * BD + col) * 8;

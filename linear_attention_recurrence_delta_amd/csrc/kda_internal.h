@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_bounds.h"
+
 namespace kda {
 
 // Everything a prefill launch needs; pointers are device pointers.
@@ -37,18 +39,45 @@ struct PrefillParams {
     // a_log [H] give g = -5 Sigmoid(exp(a_log[h]) z).
     const void* z;
     const float* a_log;
+    // Sequence-segment scan (dense batches, pipelined kernel).  seg_phase 0:
+    // off, one workgroup chain per (sequence, head, slab) walks the whole
+    // sequence.  Otherwise each sequence is cut into seg_G segments: segment 0
+    // holds tokens [0, seg_len0), segment g >= 1 tokens [seg_len0 + (g - 1)
+    // seg_len, + seg_len).  Phase 1 runs segment 0 from the initial state (its
+    // outputs stored, its end state kept) and, for g = 1 .. seg_G - 2, the
+    // affine map of segment g: S_end = M_g S_start + B_g, with M_g the run
+    // from the identity with v = 0 and B_g the run from zero with the real v.
+    // A combine kernel turns the maps into every segment's start state; phase
+    // 3 runs segments 1 .. seg_G - 1 from those states with outputs.
+    // seg_ws holds [N H][seg_G - 1][2][D][D] fp32: (M_g, B_g), the B slot
+    // replaced by the start state of segment g + 1 (slot 0: segment 0's end).
+    int32_t seg_phase = 0;  // 0, 1 or 3
+    int32_t seg_G = 1;
+    int32_t seg_len0 = 0;
+    int32_t seg_len = 0;
+    float* seg_ws = nullptr;
 };
+
+// Workgroups of a pipelined-kernel launch: units are padded to whole groups
+// of 8 (one per XCD), each unit or segment item with nslab slabs (segment maps
+// with 2 nslab: the M columns, then the B columns).
+inline int64_t ws_pad8(int64_t x) { return (x + 7) / 8 * 8; }
+inline int64_t ws_grid_blocks(const PrefillParams& p) {
+    const int64_t units = (int64_t)p.N * p.H;
+    if (p.seg_phase == 1)
+        return ws_pad8(units) * p.nslab + ws_pad8(units * (p.seg_G - 2)) * 2 * p.nslab;
+    if (p.seg_phase == 3) return ws_pad8(units * (p.seg_G - 1)) * p.nslab;
+    return ws_pad8(units) * p.nslab;
+}
 
 // Token range [*a, *b) of sequence n, with the bounds read from cu clamped to
 // [0, T_total] and b >= a (malformed offsets change the numbers, never the
 // memory touched).  Every prefill kernel uses these bounds.
 __device__ inline void seq_bounds(const PrefillParams& p, int n, int64_t* a, int64_t* b) {
     if (p.cu) {
-        int64_t x = p.cu[n], y = p.cu[n + 1];
-        x = x < 0 ? 0 : (x > p.T_total ? p.T_total : x);
-        y = y < x ? x : (y > p.T_total ? p.T_total : y);
-        *a = x;
-        *b = y;
+        const SeqRange r = clamp_seq(p.cu[n], p.cu[n + 1], p.T_total);
+        *a = r.a;
+        *b = r.b;
     } else {
         *a = (int64_t)n * p.seq_len;
         *b = *a + p.seq_len;
@@ -93,6 +122,11 @@ struct OutputGateParams {
     float eps;
 };
 
+// Phase 2 of the segment scan: for g = 1 .. seg_G - 2, start(g + 1) =
+// M_g start(g) + B_g in fp32, in place of B_g, per (sequence, head) and
+// 16-column group.
+hipError_t launch_segment_combine(const PrefillParams& p, hipStream_t s);
+
 // One entry per built prefill kernel.
 struct PrefillVariant {
     int kind;               // 0: chunk-staged kernel, 1: wave-specialised pipeline, 2: the same, fused gate/norm
@@ -102,6 +136,8 @@ struct PrefillVariant {
     int nwc;                // column waves per workgroup (16 d_v columns each)
     size_t lds_bytes;
     hipError_t (*launch)(const PrefillParams&, hipStream_t);
+    // the same kernel built with the segment-scan phases, or nullptr
+    hipError_t (*launch_seg)(const PrefillParams&, hipStream_t) = nullptr;
 };
 
 // Tables defined in the kernel translation units.

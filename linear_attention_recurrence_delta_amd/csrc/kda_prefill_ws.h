@@ -168,12 +168,124 @@ __device__ __forceinline__ float row_bcast15(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x1F0));
 }
 
+// A wave-uniform 64-bit value moved into scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// What one workgroup of a pipelined launch works on: the token range of its
+// sequence or segment, the head, the value slab, where its state starts and
+// ends, and whether it stores outputs and reads v.
+struct WsWork {
+    int64_t t_begin, t_end;
+    int n, h, z;
+    const float* s_in;  // start state [D][D] of the (sequence, head), or nullptr (zeros)
+    bool s_identity;    // start from the identity (segment map M): s_in unused
+    float* s_out;       // end state [D][D], or nullptr
+    bool store_o;
+    bool v_zero;        // v read as zeros (segment map M)
+};
+
+// Block -> work.  The dispatcher deals consecutive workgroups to the 8 XCDs
+// in turn, so block b runs on XCD b % 8.  All slabs of one item get the same
+// b % 8 and neighbouring b / 8, so they run on one XCD at the same pace and
+// the q, k, g and beta they all read come from that XCD's L2 after the first
+// slab's miss.  Items are padded to whole groups of 8; padding blocks get no
+// work.  Segment-scan launches (seg_phase 1 and 3) list their items the same
+// way: phase 1 first the segment-0 runs (slabs 0 .. nslab - 1), then the
+// segment maps (slabs 0 .. nslab - 1 for M, nslab .. 2 nslab - 1 for B, so
+// the two halves of one map share an XCD); phase 3 the runs of segments 1 ..
+// seg_G - 1.
+template <int D, bool SEG>
+__device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
+    const int units = p.N * p.H;
+    const int xcd = bid & 7;
+    const int64_t sdd = (int64_t)D * D;
+    auto map_slot = [&](int uh, int g, int part) {
+        return p.seg_ws + (((int64_t)uh * (p.seg_G - 1) + g) * 2 + part) * sdd;
+    };
+    auto seg_range = [&](int n, int g) {
+        const int64_t s0 = (int64_t)n * p.seq_len;
+        if (g == 0) {
+            w.t_begin = s0;
+            w.t_end = s0 + p.seg_len0;
+        } else {
+            w.t_begin = s0 + p.seg_len0 + (int64_t)(g - 1) * p.seg_len;
+            w.t_end = w.t_begin + p.seg_len;
+        }
+    };
+    w.s_identity = false;
+    w.v_zero = false;
+    w.store_o = true;
+    if (!SEG || p.seg_phase == 0) {
+        const int rest = bid >> 3;
+        w.z = rest % p.nslab;
+        const int uh = (rest / p.nslab) * 8 + xcd;
+        if (uh >= units) return false;
+        w.h = uh % p.H;
+        w.n = uh / p.H;
+        seq_bounds(p, w.n, &w.t_begin, &w.t_end);
+        w.s_in = p.S0 ? p.S0 + (int64_t)uh * sdd : nullptr;
+        w.s_out = p.Sout ? p.Sout + (int64_t)uh * sdd : nullptr;
+        return true;
+    }
+    if (p.seg_phase == 1) {
+        const int ra = (units + 7) / 8 * 8 * p.nslab;
+        if (bid < ra) {  // segment 0 from the initial state; its end state goes to slot (0, B)
+            const int rest = bid >> 3;
+            w.z = rest % p.nslab;
+            const int uh = (rest / p.nslab) * 8 + xcd;
+            if (uh >= units) return false;
+            w.h = uh % p.H;
+            w.n = uh / p.H;
+            seg_range(w.n, 0);
+            w.s_in = p.S0 ? p.S0 + (int64_t)uh * sdd : nullptr;
+            w.s_out = map_slot(uh, 0, 1);
+            return true;
+        }
+        const int rest = (bid - ra) >> 3;  // ra is a multiple of 8: same XCD rule
+        const int zz = rest % (2 * p.nslab);
+        const int item = (rest / (2 * p.nslab)) * 8 + xcd;
+        if (item >= units * (p.seg_G - 2)) return false;
+        const int uh = item / (p.seg_G - 2), g = 1 + item % (p.seg_G - 2);
+        const int part = zz / p.nslab;  // 0: M (identity start, v = 0), 1: B (zero start, real v)
+        w.z = zz % p.nslab;
+        w.h = uh % p.H;
+        w.n = uh / p.H;
+        seg_range(w.n, g);
+        w.s_in = nullptr;
+        w.s_identity = part == 0;
+        w.v_zero = part == 0;
+        w.s_out = map_slot(uh, g, part);
+        w.store_o = false;
+        return true;
+    }
+    // phase 3: segment g >= 1 from the start state the combine left in slot (g - 1, B)
+    const int rest = bid >> 3;
+    w.z = rest % p.nslab;
+    const int item = (rest / p.nslab) * 8 + xcd;
+    if (item >= units * (p.seg_G - 1)) return false;
+    const int uh = item / (p.seg_G - 1), g = 1 + item % (p.seg_G - 1);
+    w.h = uh % p.H;
+    w.n = uh / p.H;
+    seg_range(w.n, g);
+    if (g == p.seg_G - 1) w.t_end = (int64_t)(w.n + 1) * p.seq_len;  // the last segment ends the sequence
+    w.s_in = map_slot(uh, g - 1, 1);
+    w.s_out = (g == p.seg_G - 1 && p.Sout) ? p.Sout + (int64_t)uh * sdd : nullptr;
+    return true;
+}
+
 // CKB: the backward's forward run.  Checkpoints as bf16 in the blocked layout
 // the backward kernel reads ([row / 4][column][row % 4] per state: the 4 rows
 // a lane holds of one column are 8 adjacent bytes) instead of the fp32
 // row-major states of the public checkpoint call, and no output o (p.o is not
 // read): the readout products Q~ S and P U and the P tile are skipped.
-template <int NCW, int TPW, int NSA, bool FUSED, bool CKB>
+//
+// SEG: the variant that also runs the segment-scan phases (PrefillParams::
+// seg_phase 1 and 3); the plain kernels are compiled without that code.
+template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG>
 __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
     typedef WsCfg<NCW, TPW, NSA, FUSED> Cfg;
     typedef Elem<bf16_t> E;
@@ -189,29 +301,32 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     const int g4 = lane >> 4;
     const int l16 = lane & 15;
 
-    // XCD-aware block order: the dispatcher deals consecutive workgroups to the
-    // 8 XCDs in turn, so block b runs on XCD b % 8.  All slabs of one (sequence,
-    // head) get the same b % 8 and neighbouring b / 8, so they run on one XCD
-    // at the same pace and the q, k, g and beta they all read come from that
-    // XCD's L2 after the first slab's miss.  The grid is padded to whole groups
-    // of 8 units; padding blocks exit at once.
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7;
-    const int rest = bid >> 3;
-    const int z = rest % p.nslab;
-    const int uh = (rest / p.nslab) * 8 + xcd;
-    if (uh >= p.N * p.H) return;
-    const int h = uh % p.H;
-    const int n = uh / p.H;
+    // XCD-aware block order (ws_resolve); padding blocks exit at once.  The
+    // work description is uniform: pinned to scalar registers (integer
+    // divisions by run-time values leave their results in vector registers).
+    WsWork wk;
+    if (!ws_resolve<D, SEG>(p, blockIdx.x, wk)) return;
+    wk.t_begin = uniform_i64(wk.t_begin);
+    wk.t_end = uniform_i64(wk.t_end);
+    wk.n = __builtin_amdgcn_readfirstlane(wk.n);
+    wk.h = __builtin_amdgcn_readfirstlane(wk.h);
+    wk.z = __builtin_amdgcn_readfirstlane(wk.z);
+    wk.s_in = reinterpret_cast<const float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_in)));
+    wk.s_out = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_out)));
+    // segment-map flags: compile-time false / true in the plain kernels
+    const bool w_identity = SEG && __builtin_amdgcn_readfirstlane((int)wk.s_identity) != 0;
+    const bool w_store_o = !SEG || __builtin_amdgcn_readfirstlane((int)wk.store_o) != 0;
+    const bool w_v_zero = SEG && __builtin_amdgcn_readfirstlane((int)wk.v_zero) != 0;
+    const int z = wk.z;
+    const int h = wk.h;
+    const int n = wk.n;
     const int H = p.H;
-    int64_t t_begin, t_end;
-    seq_bounds(p, n, &t_begin, &t_end);
+    const int64_t t_begin = wk.t_begin, t_end = wk.t_end;
     const int64_t ntok = t_end - t_begin;
     // fused gate: e^{A_h} log2(e) for this head (A_h = a_log[h], a per-head log-scale)
     const float gate_ea_l2e =
         (FUSED && ntok > 0) ? __builtin_amdgcn_exp2f(p.a_log[h] * 1.4426950408889634f) * 1.4426950408889634f : 0.f;
     const int nch = (int)((ntok + C - 1) / C);
-    const int64_t sbase = ((int64_t)n * H + h) * D * D;
 
     const bf16_t* gq = static_cast<const bf16_t*>(p.q);
     const bf16_t* gk = static_cast<const bf16_t*>(p.k);
@@ -368,7 +483,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     auto v_load = [&](int c, int i) -> VChunk {
         const int cc = c < 0 ? 0 : (c < nch ? c : nch - 1);
         const int64_t base = chunk_base(cc) + z * DVW;
-        const auto rv = rsrc(gv + base, (n_tok_elems - base) * 2);
+        const auto rv = rsrc(gv + base, w_v_zero ? 0 : (n_tok_elems - base) * 2);
         if constexpr (Cfg::VCB == 16)
             return __builtin_bit_cast(VChunk, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off(i), 0, 0));
         else
@@ -674,7 +789,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         if constexpr (!CKB) {
             const int64_t e0 = chunk_base(c);
             const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
-            const uint32_t oo = l16 < nv ? o_voff : 0x80000000u;
+            const uint32_t oo = (w_store_o && l16 < nv) ? o_voff : 0x80000000u;
             if constexpr (TPW == 2)
                 __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
             else
@@ -760,8 +875,17 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             // Without an initial state the range is empty and the loads read 0.
             const uint32_t s_voff = (uint32_t)(4 * g4 * D + col_base + vcol(0, l16)) * 4u;
             f32x4 Sm[TPW][NCB];
-            {
-                const auto rs = p.S0 ? buffer_rsrc(p.S0 + sbase, D * D * 4) : buffer_rsrc(p.g, 0);
+            if (w_identity) {
+                // segment map M: the run from the identity (row == column)
+#pragma unroll
+                for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                    for (int ct = 0; ct < NCB; ++ct)
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp)
+                            Sm[t][ct][pp] = (16 * ct + 4 * g4 + pp == col_base + vcol(t, l16)) ? 1.f : 0.f;
+            } else {
+                const auto rs = wk.s_in ? buffer_rsrc(wk.s_in, D * D * 4) : buffer_rsrc(p.g, 0);
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -818,8 +942,8 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                 }
                 __syncthreads();
             }
-            if (p.Sout) {
-                const auto rs = buffer_rsrc(p.Sout + sbase, D * D * 4);
+            if (wk.s_out) {
+                const auto rs = buffer_rsrc(wk.s_out, D * D * 4);
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -830,22 +954,23 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                                                                   s_voff + 16 * t, (16 * ct + pp) * D * 4, 0);
             }
         }
-    } else if (is_cons && p.Sout) {
+    } else if (is_cons && wk.s_out) {
         // empty sequence: the final state is the initial state
         for (int t = 0; t < TPW; ++t)
             for (int ct = 0; ct < NCB; ++ct)
                 for (int pp = 0; pp < 4; ++pp) {
-                    const int64_t off = sbase + (int64_t)(16 * ct + 4 * g4 + pp) * D + col_base + 16 * t + l16;
-                    p.Sout[off] = p.S0 ? p.S0[off] : 0.f;
+                    const int row = 16 * ct + 4 * g4 + pp, col = col_base + 16 * t + l16;
+                    const int64_t off = (int64_t)row * D + col;
+                    wk.s_out[off] = w_identity ? (row == col ? 1.f : 0.f) : (wk.s_in ? wk.s_in[off] : 0.f);
                 }
     }
 }
 
-template <int NCW, int TPW, int NSA, bool FUSED = false, bool CKB = false>
+template <int NCW, int TPW, int NSA, bool FUSED = false, bool CKB = false, bool SEG = false>
 hipError_t launch_prefill_ws(const PrefillParams& p, hipStream_t s) {
-    const int64_t units = (int64_t)p.N * p.H;
-    const int64_t blocks = (units + 7) / 8 * 8 * p.nslab;  // whole groups of 8 units
-    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA, FUSED, CKB>), dim3((unsigned)blocks),
+    if (!SEG && p.seg_phase != 0) return hipErrorInvalidValue;
+    const int64_t blocks = ws_grid_blocks(p);  // whole groups of 8 items
+    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA, FUSED, CKB, SEG>), dim3((unsigned)blocks),
                        dim3(64 * (NCW + 2 + NSA)), 0, s, p);
     return hipGetLastError();
 }

@@ -9,11 +9,16 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import lib
+from ._lib import PrefillDesc, PrefillTensors, lib
 
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 _DTYPES = {torch.float32: KDA_DTYPE_F32, torch.bfloat16: KDA_DTYPE_BF16}
+
+# Kernel plans (kda_prefill_desc.kernel in include/kda.h)
+KDA_KERNEL_AUTO = 0
+KDA_KERNEL_PIPELINED = 1
+KDA_KERNEL_CHUNK_STAGED = 2
 
 
 class KdaError(RuntimeError):
@@ -101,42 +106,98 @@ def _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, ou
         if tuple(initial_state.shape) != (N, H, dk, dv):
             raise ValueError("initial_state must be [N, H, d_k, d_v]")
     dev = q.device
+    for name, t in (("k", k), ("v", v), ("g" if g_dtype == torch.float32 else "z", g), ("beta", beta),
+                    ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)):
+        if t is not None and t.device != dev:
+            raise ValueError("%s must be on q's device (%s), got %s" % (name, dev, t.device))
     o = None
     if need_out:
         o = out if out is not None else torch.empty((T, H, dv), dtype=qdt, device=dev)
-        _need(o, "out", qdt, 3)
+        _need(o, "out", qdt)
+        if tuple(o.shape) != (T, H, dv) and not (dense_batch and o.numel() == T * H * dv and o.dim() == 4
+                                                 and tuple(o.shape) == (num_seqs, T // max(num_seqs, 1), H, dv)):
+            raise ValueError("out must be [T, H, d_v] = %s, got %s" % ((T, H, dv), tuple(o.shape)))
+        if o.device != dev:
+            raise ValueError("out must be on q's device")
+        o = o.view(T, H, dv)
     fs = None
     if output_final_state:
         fs = final_state if final_state is not None else torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
         _need(fs, "final_state", torch.float32, 4)
+        if tuple(fs.shape) != (N, H, dk, dv):
+            raise ValueError("final_state must be [N, H, d_k, d_v] = %s, got %s" % ((N, H, dk, dv), tuple(fs.shape)))
+        if fs.device != dev:
+            raise ValueError("final_state must be on q's device")
     return dict(dense_batch=dense_batch, q=q, k=k, v=v, g=g, beta=beta, T=T, H=H, dk=dk, dv=dv, N=N, dev=dev,
                 o=o, fs=fs, dt=_DTYPES[qdt])
 
 
-def _workspace(a, chunk_size):
-    ws_bytes = int(lib().kda_prefill_workspace_bytes(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size))
+def _desc(a, chunk_size, scale, fused=False, interval=0, capacity=0, plan=None):
+    plan = plan or {}
+    unknown = set(plan) - {"kernel", "slab_columns", "segments"}
+    if unknown:
+        raise ValueError("unknown plan keys %s" % sorted(unknown))
+    return PrefillDesc(num_seqs=a["N"], total_tokens=a["T"], num_heads=a["H"], d_k=a["dk"], d_v=a["dv"],
+                       qkv_dtype=a["dt"], chunk_size=int(chunk_size), scale=float(scale), fused=int(fused),
+                       checkpoint_interval=int(interval), checkpoint_capacity=int(capacity),
+                       kernel=int(plan.get("kernel", 0)), slab_columns=int(plan.get("slab_columns", 0)),
+                       segments=int(plan.get("segments", 0)))
+
+
+def _workspace(a, desc, packed):
+    """Workspace of the call (the segment scan's maps; packed batches need none)."""
+    if packed:
+        ws_bytes = 0
+    else:
+        with torch.cuda.device(a["dev"]):  # the plan depends on the device's compute units
+            ws_bytes = int(lib().kda_prefill_ex_workspace_bytes(desc))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=a["dev"]) if ws_bytes else None
     return ws, ws_bytes
 
 
+def _run_ex(a, desc, initial_state, cu_seqlens, z=None, a_log=None, checkpoints=None):
+    """kda_prefill_ex with the marshalled arguments."""
+    t = PrefillTensors(q=_ptr(a["q"]), k=_ptr(a["k"]), v=_ptr(a["v"]), g=None if z is not None else _ptr(a["g"]),
+                       z=_ptr(z), a_log=_ptr(a_log), beta=_ptr(a["beta"]), initial_state=_ptr(initial_state),
+                       cu_seqlens=_ptr(cu_seqlens), o=_ptr(a["o"]), final_state=_ptr(a["fs"]),
+                       checkpoints=_ptr(checkpoints))
+    ws, ws_bytes = _workspace(a, desc, cu_seqlens is not None)
+    with torch.cuda.device(a["dev"]):
+        _check(lib().kda_prefill_ex(desc, t, _ptr(ws), ws_bytes, _stream(a["dev"])))
+
+
+def kda_prefill_ex_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size=0, *,
+                                   fused=False, checkpoint_interval=0, checkpoint_capacity=0, plan=None) -> int:
+    a = dict(N=num_seqs, T=total_tokens, H=num_heads, dk=d_k, dv=d_v, dt=_DTYPES.get(dtype, -1))
+    return int(lib().kda_prefill_ex_workspace_bytes(_desc(a, chunk_size, 1.0, fused, checkpoint_interval,
+                                                          checkpoint_capacity, plan)))
+
+
 def kda_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_size: int = 0,
                 scale: float = 1.0, output_final_state: bool = True, num_seqs: int | None = None,
-                out=None, final_state=None):
+                out=None, final_state=None, plan=None):
     """Chunked KDA prefill over a packed batch.
 
     q, k, g: [T, H, d_k]; v: [T, H, d_v]; beta: [T, H].  A dense batch may be
     passed as [B, T, H, d] (and beta [B, T, H]); it is the packed layout with
     B equal-length sequences.  cu_seqlens: int32 device tensor [N + 1] or None.
     initial_state: fp32 [N, H, d_k, d_v] or None (zeros).
+    plan: None (the library's choice, through kda_prefill) or a dict with
+    any of kernel (KDA_KERNEL_*), slab_columns, segments (through
+    kda_prefill_ex; include/kda.h describes the fields).
     Returns (o, final_state); final_state is None if output_final_state is False.
     """
     a = _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state)
-    ws, ws_bytes = _workspace(a, chunk_size)
-    with torch.cuda.device(a["dev"]):
-        _check(lib().kda_prefill(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
-                                 _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a["beta"]),
-                                 _ptr(initial_state), _ptr(cu_seqlens), _ptr(a["o"]), _ptr(a["fs"]),
-                                 _ptr(ws), ws_bytes, _stream(a["dev"])))
+    desc = _desc(a, chunk_size, scale, plan=plan)
+    if plan is not None:
+        _run_ex(a, desc, initial_state, cu_seqlens)
+    else:
+        ws, ws_bytes = _workspace(a, desc, cu_seqlens is not None)
+        with torch.cuda.device(a["dev"]):
+            _check(lib().kda_prefill(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
+                                     _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a["beta"]),
+                                     _ptr(initial_state), _ptr(cu_seqlens), _ptr(a["o"]), _ptr(a["fs"]),
+                                     _ptr(ws), ws_bytes, _stream(a["dev"])))
     o = a["o"]
     if a["dense_batch"]:
         o = o.view(a["N"], a["T"] // max(a["N"], 1), a["H"], a["dv"])
@@ -145,7 +206,8 @@ def kda_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_
 
 def kda_prefill_checkpointed(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, checkpoint_interval: int,
                              chunk_size: int = 0, scale: float = 1.0, output_final_state: bool = True,
-                             num_seqs: int | None = None, out=None, final_state=None, checkpoints=None):
+                             num_seqs: int | None = None, out=None, final_state=None, checkpoints=None,
+                             plan=None):
     """kda_prefill that also returns the state after every checkpoint_interval
     tokens of each sequence (a multiple of the chunk size in use).
 
@@ -174,14 +236,20 @@ def kda_prefill_checkpointed(q, k, v, g, beta, initial_state=None, cu_seqlens=No
     first_slot = torch.zeros(a["N"] + 1, dtype=torch.int64, device=a["dev"])
     if a["N"] > 0:
         first_slot[1:] = torch.cumsum(counts, 0)
-    ws, ws_bytes = _workspace(a, chunk_size)
-    with torch.cuda.device(a["dev"]):
-        _check(lib().kda_prefill_checkpointed(
-            a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
-            _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a["beta"]),
-            _ptr(initial_state), _ptr(cu_seqlens), _ptr(a["o"]), _ptr(a["fs"]),
-            interval, _ptr(ck) if ck.numel() else None, int(ck.shape[0]),
-            _ptr(ws), ws_bytes, _stream(a["dev"])))
+    if ck.device != a["dev"]:
+        raise ValueError("checkpoints must be on q's device")
+    desc = _desc(a, chunk_size, scale, interval=interval, capacity=int(ck.shape[0]), plan=plan)
+    if plan is not None:
+        _run_ex(a, desc, initial_state, cu_seqlens, checkpoints=ck if ck.numel() else None)
+    else:
+        ws, ws_bytes = _workspace(a, desc, cu_seqlens is not None)
+        with torch.cuda.device(a["dev"]):
+            _check(lib().kda_prefill_checkpointed(
+                a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
+                _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a["beta"]),
+                _ptr(initial_state), _ptr(cu_seqlens), _ptr(a["o"]), _ptr(a["fs"]),
+                interval, _ptr(ck) if ck.numel() else None, int(ck.shape[0]),
+                _ptr(ws), ws_bytes, _stream(a["dev"])))
     o = a["o"]
     if a["dense_batch"]:
         o = o.view(a["N"], a["T"] // max(a["N"], 1), a["H"], a["dv"])
@@ -194,7 +262,7 @@ def kda_prefill_fused_supported(dtype: torch.dtype, d_k: int, d_v: int, chunk_si
 
 def kda_prefill_fused(q, k, v, z, a_log, beta, initial_state=None, cu_seqlens=None, *, chunk_size: int = 0,
                       scale: float = 1.0, output_final_state: bool = True, num_seqs: int | None = None,
-                      out=None, final_state=None):
+                      out=None, final_state=None, plan=None):
     """kda_prefill with the gate and the q/k L2 norm computed in the kernel.
 
     q, k: unnormalised [T, H, d_k] (bf16); z: decay logits [T, H, d_k] (same
@@ -206,12 +274,18 @@ def kda_prefill_fused(q, k, v, z, a_log, beta, initial_state=None, cu_seqlens=No
     _need(a_log, "a_log", torch.float32, 1)
     if a_log.shape[0] != a["H"]:
         raise ValueError("a_log must have one entry per head")
-    ws, ws_bytes = _workspace(a, chunk_size)
-    with torch.cuda.device(a["dev"]):
-        _check(lib().kda_prefill_fused(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
-                                       _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a_log),
-                                       _ptr(a["beta"]), _ptr(initial_state), _ptr(cu_seqlens), _ptr(a["o"]),
-                                       _ptr(a["fs"]), _ptr(ws), ws_bytes, _stream(a["dev"])))
+    if a_log.device != a["dev"]:
+        raise ValueError("a_log must be on q's device")
+    desc = _desc(a, chunk_size, scale, fused=True, plan=plan)
+    if plan is not None:
+        _run_ex(a, desc, initial_state, cu_seqlens, z=a["g"], a_log=a_log)
+    else:
+        ws, ws_bytes = _workspace(a, desc, cu_seqlens is not None)
+        with torch.cuda.device(a["dev"]):
+            _check(lib().kda_prefill_fused(a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size,
+                                           float(scale), _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]),
+                                           _ptr(a_log), _ptr(a["beta"]), _ptr(initial_state), _ptr(cu_seqlens),
+                                           _ptr(a["o"]), _ptr(a["fs"]), _ptr(ws), ws_bytes, _stream(a["dev"])))
     o = a["o"]
     if a["dense_batch"]:
         o = o.view(a["N"], a["T"] // max(a["N"], 1), a["H"], a["dv"])
@@ -264,12 +338,12 @@ def kda_prefill_backward(q, k, v, g, beta, d_o, initial_state=None, d_final_stat
         raise ValueError("kda_prefill_backward takes the packed [T, H, d] layout")
     a = _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, None, False, None, need_out=False)
     _need(d_o, "d_o", a["q"].dtype, 3)
-    if d_o.shape != (a["T"], a["H"], a["dv"]):
-        raise ValueError("d_o must be [T, H, d_v]")
+    if d_o.shape != (a["T"], a["H"], a["dv"]) or d_o.device != a["dev"]:
+        raise ValueError("d_o must be [T, H, d_v] on q's device")
     if d_final_state is not None:
         _need(d_final_state, "d_final_state", torch.float32, 4)
-        if tuple(d_final_state.shape) != (a["N"], a["H"], a["dk"], a["dv"]):
-            raise ValueError("d_final_state must be [N, H, d_k, d_v]")
+        if tuple(d_final_state.shape) != (a["N"], a["H"], a["dk"], a["dv"]) or d_final_state.device != a["dev"]:
+            raise ValueError("d_final_state must be [N, H, d_k, d_v] on q's device")
     dev = a["dev"]
     dq = torch.empty_like(a["q"])
     dk = torch.empty_like(a["k"])
@@ -307,8 +381,13 @@ def kda_decode_step(q, k, v, g, beta, state, *, scale: float = 1.0, out=None):
             tuple(state.shape) != (N, H, dk, dv):
         raise ValueError("inconsistent decode shapes")
     dev = q.device
+    for name, t in (("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state)):
+        if t.device != dev:
+            raise ValueError("%s must be on q's device (%s), got %s" % (name, dev, t.device))
     o = out if out is not None else torch.empty((N, H, dv), dtype=qdt, device=dev)
     _need(o, "out", qdt, 3)
+    if tuple(o.shape) != (N, H, dv) or o.device != dev:
+        raise ValueError("out must be [N, H, d_v] = %s on q's device, got %s" % ((N, H, dv), tuple(o.shape)))
     with torch.cuda.device(dev):
         _check(lib().kda_decode_step(N, H, dk, dv, _DTYPES[qdt], float(scale),
                                      _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),

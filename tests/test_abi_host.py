@@ -56,7 +56,7 @@ def header_statuses():
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     statuses = header_statuses()
     assert sorted(statuses) == list(range(8))
     for s, name in statuses.items():
@@ -125,6 +125,113 @@ def test_prefill_validation(lib):
 
 def test_workspace_query(lib):
     assert lib.kda_prefill_workspace_bytes(1, 4096, 8, 128, 128, BF16, 64) == 0
+    # direct chains: many (sequence, head) units, or short sequences
+    assert lib.kda_prefill_workspace_bytes(1, 32768, 96, 128, 128, BF16, 0) == 0
+    assert lib.kda_prefill_workspace_bytes(1, 4096, 8, 128, 128, BF16, 0) == 0
+    assert lib.kda_prefill_workspace_bytes(1, 1 << 20, 16, 128, 128, F32, 0) == 0  # no pipeline for fp32
+
+
+def _desc(**kw):
+    from linear_attention_recurrence_delta_amd._lib import PrefillDesc
+    base = dict(num_seqs=1, total_tokens=1 << 20, num_heads=16, d_k=128, d_v=128, qkv_dtype=BF16, chunk_size=0,
+                scale=1.0, fused=0, checkpoint_interval=0, checkpoint_capacity=0, kernel=0, slab_columns=0,
+                segments=0)
+    base.update(kw)
+    return PrefillDesc(**base)
+
+
+def test_desc_layout_matches_header():
+    # the ctypes mirror of kda_prefill_desc has the C layout (int64 fields
+    # 8-byte aligned): 72 bytes, total_tokens at 8, checkpoint_capacity at 48
+    from linear_attention_recurrence_delta_amd._lib import PrefillDesc, PrefillTensors
+    import ctypes as ct
+    assert ct.sizeof(PrefillDesc) == 72
+    assert PrefillDesc.total_tokens.offset == 8 and PrefillDesc.checkpoint_capacity.offset == 48
+    assert ct.sizeof(PrefillTensors) == 12 * 8
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} kda_prefill_desc;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    assert re.findall(r"(\w+);", body) == [f[0] for f in PrefillDesc._fields_]
+    body = re.search(r"typedef struct \{(.*?)\} kda_prefill_tensors;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"\*\s*(\w+)", body)
+    assert names == [f[0] for f in PrefillTensors._fields_]
+
+
+def test_segment_scan_workspace(lib):
+    # One 1,048,576-token sequence of 16 heads on a 256-CU device (the count
+    # used when no device answers): 17 segments, 16 maps of 2 x 64 KiB per
+    # head.  Packed or checkpointed or fp32 calls need none.
+    import ctypes as ct
+    ex = lambda **kw: lib.kda_prefill_ex_workspace_bytes(ct.byref(_desc(**kw)))
+    assert ex() == 16 * 16 * 2 * 128 * 128 * 4
+    assert ex(segments=1) == 0
+    assert ex(segments=5) == 16 * 4 * 2 * 128 * 128 * 4
+    assert ex(segments=300) == 0                      # beyond the built maximum
+    assert ex(checkpoint_interval=1024, checkpoint_capacity=1024) == 0
+    assert ex(fused=1) == 0
+    assert ex(qkv_dtype=F32) == 0
+    assert ex(kernel=2) == 0                          # chunk-staged: no scan
+    assert ex(num_heads=96, total_tokens=32768) == 0  # 96 units: no room
+    assert lib.kda_prefill_ex_workspace_bytes(None) == 0
+
+
+def test_prefill_ex_validation(lib):
+    import ctypes as ct
+    from linear_attention_recurrence_delta_amd._lib import PrefillTensors
+    t = PrefillTensors(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE + 0x100000)
+    run = lambda d, tens=t, ws=None, wsb=0: lib.kda_prefill_ex(ct.byref(d), ct.byref(tens), ws, wsb, None)
+    small = dict(total_tokens=4096, num_heads=2)
+    assert lib.kda_prefill_ex(None, ct.byref(t), None, 0, None) == NULLP
+    assert lib.kda_prefill_ex(ct.byref(_desc()), None, None, 0, None) == NULLP
+    assert run(_desc(kernel=3, **small)) == BAD
+    assert run(_desc(slab_columns=-1, **small)) == BAD
+    assert run(_desc(segments=-2, **small)) == BAD
+    assert run(_desc(slab_columns=48, segments=1, num_seqs=0, total_tokens=0)) == OK  # nothing to run
+    assert run(_desc(kernel=1, chunk_size=32, **small)) == UNSUP     # the pipeline is chunk 16 only
+    tf = PrefillTensors(q=FAKE, k=FAKE, v=FAKE, z=FAKE, a_log=FAKE, beta=FAKE, o=FAKE + 0x100000)
+    assert run(_desc(kernel=2, fused=1, **small), tf) == UNSUP       # the fused gate is pipelined only
+    assert run(_desc(kernel=1, fused=1, **small)) == NULLP           # fused without z / a_log
+    assert run(_desc(segments=4, **small), PrefillTensors(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
+                                                          cu_seqlens=FAKE, o=FAKE + 0x100000)) == UNSUP
+    assert run(_desc(segments=4, qkv_dtype=F32, **small)) == UNSUP
+    assert run(_desc(segments=300, **small)) == UNSUP
+    assert run(_desc(segments=300, num_seqs=1, total_tokens=64, num_heads=2)) == UNSUP  # 4 chunks < 301
+    assert run(_desc(segments=4, **small)) == WS                     # the maps need a workspace
+    assert run(_desc(segments=4, **small), ws=FAKE, wsb=1 << 40) == BAD  # workspace == q
+
+
+def test_offset_clamp_rule(tmp_path):
+    """kda_bounds.h, the rule every kernel applies to cu_seqlens offsets,
+    compiled with g++ and driven over well-formed and malformed offsets:
+    ranges stay inside [0, T] with end >= start, and well-formed offsets
+    pass unchanged."""
+    src = tmp_path / "clamp.cpp"
+    src.write_text(r"""
+#include "kda_bounds.h"
+#include <cstdio>
+#include <cstdlib>
+int main() {
+    unsigned s = 12345;
+    auto rnd = [&]() { s = s * 1103515245u + 12345u; return (int64_t)((s >> 8) % 4001) - 2000; };
+    for (int i = 0; i < 200000; ++i) {
+        const int64_t T = (rnd() + 2000) / 2, x = rnd(), y = rnd();
+        const kda::SeqRange r = kda::clamp_seq(x, y, T);
+        if (!(0 <= r.a && r.a <= r.b && r.b <= T)) { std::puts("bad"); return 1; }
+        if (0 <= x && x <= y && y <= T && (r.a != x || r.b != y)) { std::puts("changed"); return 1; }
+    }
+    static_assert(kda::clamp_seq(-3, 5, 4).a == 0 && kda::clamp_seq(-3, 5, 4).b == 4, "");
+    static_assert(kda::clamp_seq(3, 1, 10).a == 3 && kda::clamp_seq(3, 1, 10).b == 3, "");
+    std::puts("ok");
+    return 0;
+}
+""")
+    import subprocess
+    exe = tmp_path / "clamp"
+    csrc = os.path.join(ROOT, "linear_attention_recurrence_delta_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", csrc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
 
 
 def _decode(lib, N=4, H=2, d=128, dt=BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,

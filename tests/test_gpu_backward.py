@@ -125,3 +125,45 @@ def test_dense_k3_sampled_heads(kda, oracle_mod):
     say("  dense: " + " ".join("%s=%.2e" % kv for kv in errs.items()))
     for name, e in errs.items():
         assert e <= TOL[BF16], (name, e)
+
+
+@pytest.mark.parametrize("cu_list", [[0, 500, 100, 300], [-50, 200, 10000], [0, 300, 0, 300]])
+def test_malformed_offsets_stay_in_bounds(kda, monkeypatch, cu_list):
+    """Malformed cu_seqlens without KDA_VALIDATE: the backward clamps each
+    sequence to [0, T_total] as the forward kernels do, so it changes numbers
+    but touches no memory outside its buffers.  Each output and the
+    workspace sit inside a larger allocation whose guard tail must come back
+    untouched.  ([0, 300, 0, 300]: overlapping sequences whose 16-token
+    state slots add up past the workspace's T_total / 16.)"""
+    import ctypes as ct
+    from linear_attention_recurrence_delta_amd._lib import lib
+    from linear_attention_recurrence_delta_amd import synth
+    monkeypatch.delenv("KDA_VALIDATE", raising=False)
+    T, H, N = 300, 2, len(cu_list) - 1
+    say("CASE backward malformed cu_seqlens %s" % cu_list)
+    q, k, v, g, beta, gen = synth.token_inputs(T, H, 128, 128, BF16, 880, DEV)
+    d_o = torch.randn((T, H, 128), generator=gen, device=DEV).to(BF16)
+    cu = torch.tensor(cu_list, dtype=torch.int32, device=DEV)
+    GUARD = 4096
+
+    def guarded(n, dtype):
+        buf = torch.full((n + GUARD,), 7, dtype=dtype, device=DEV)
+        return buf, buf[:n]
+
+    outs = {}
+    for name, n, dt in (("dq", T * H * 128, BF16), ("dk", T * H * 128, BF16), ("dv", T * H * 128, BF16),
+                        ("dg", T * H * 128, torch.float32), ("dbeta", T * H, torch.float32),
+                        ("dS0", N * H * 128 * 128, torch.float32)):
+        outs[name] = guarded(n, dt)
+    wsb = int(lib().kda_prefill_backward_workspace_bytes(N, T, H, 128, 128, 1))
+    ws_buf, ws = guarded(wsb, torch.uint8)
+    p = lambda t: t.data_ptr()
+    st = lib().kda_prefill_backward(N, T, H, 128, 128, 1, 1.0, p(q), p(k), p(v), p(g), p(beta), None, p(cu),
+                                    p(d_o), None, p(outs["dq"][1]), p(outs["dk"][1]), p(outs["dv"][1]),
+                                    p(outs["dg"][1]), p(outs["dbeta"][1]), p(outs["dS0"][1]), p(ws), wsb,
+                                    torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    for name, (buf, _) in outs.items():
+        assert bool((buf[-GUARD:] == 7).all()), name
+    assert bool((ws_buf[-GUARD:] == 7).all())

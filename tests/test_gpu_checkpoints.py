@@ -33,19 +33,16 @@ def _inputs(lengths, H, d, dtype, seed, init_std=None):
     return q, k, v, g, beta, S0, cu, cu_list
 
 
-def _check(kda, oracle_mod, lengths, H, d, dtype, interval, chunk, seed, init_std=None, kind=None,
-           monkeypatch=None):
-    if kind is not None:
-        monkeypatch.setenv("KDA_PREFILL_KIND", kind)
-    say("CASE checkpoints lengths=%s H=%d d=%d %s interval=%d chunk=%d kind=%s S0=%s"
-        % (lengths, H, d, dtype, interval, chunk, kind, init_std))
+def _check(kda, oracle_mod, lengths, H, d, dtype, interval, chunk, seed, init_std=None, plan=None):
+    say("CASE checkpoints lengths=%s H=%d d=%d %s interval=%d chunk=%d plan=%s S0=%s"
+        % (lengths, H, d, dtype, interval, chunk, plan, init_std))
     q, k, v, g, beta, S0, cu, cu_list = _inputs(lengths, H, d, dtype, seed, init_std)
     T = sum(lengths)
     cap = T // interval
     ck = torch.full((cap + 2, H, d, d), float("nan"), dtype=torch.float32, device=DEV)  # 2 spare slots
     o, S, ck, first = kda.kda_prefill_checkpointed(q, k, v, g, beta, S0, cu, checkpoint_interval=interval,
-                                                   chunk_size=chunk, checkpoints=ck)
-    o_ref, S_ref = kda.kda_prefill(q, k, v, g, beta, S0, cu, chunk_size=chunk)
+                                                   chunk_size=chunk, checkpoints=ck, plan=plan)
+    o_ref, S_ref = kda.kda_prefill(q, k, v, g, beta, S0, cu, chunk_size=chunk, plan=plan)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
     exp_ck, exp_first = oracle_mod.prefill_checkpoints(f64(q), f64(k), f64(v), f64(g), f64(beta),
@@ -76,18 +73,29 @@ def test_bf16_initial_state_and_many_heads(kda, oracle_mod):
 
 
 @pytest.mark.parametrize("chunk,interval", [(16, 16), (32, 32), (64, 64), (64, 128)])
-def test_bf16_chunk_staged_kernel(kda, oracle_mod, monkeypatch, chunk, interval):
+def test_bf16_chunk_staged_kernel(kda, oracle_mod, chunk, interval):
     _check(kda, oracle_mod, [37, 0, 64, 1, 130, 200], 2, 128, torch.bfloat16, interval, chunk, 303,
-           init_std=0.05, kind="0", monkeypatch=monkeypatch)
+           init_std=0.05, plan=dict(kernel=2))  # KDA_KERNEL_CHUNK_STAGED
 
 
-@pytest.mark.parametrize("kind", ["2", "3"])
-def test_bf16_internal_kernel_kinds_not_selectable(kda, oracle_mod, monkeypatch, kind):
-    """Kind 2 (fused gate) and kind 3 (the backward's bf16 blocked
-    checkpoints) are never picked for the public call: KDA_PREFILL_KIND asking
-    for them falls back to the plain pipeline, fp32 row-major checkpoints."""
+@pytest.mark.parametrize("cols", [16, 128])
+def test_bf16_pipelined_slab_widths(kda, oracle_mod, cols):
+    """Checkpoints from the pipeline at the narrowest and the widest slab:
+    fp32 row-major states whichever workgroup holds a column."""
     _check(kda, oracle_mod, [37, 0, 64, 1, 130, 200, 16], 2, 128, torch.bfloat16, 16, 0, 305, init_std=0.05,
-           kind=kind, monkeypatch=monkeypatch)
+           plan=dict(kernel=1, slab_columns=cols))
+
+
+def test_no_segment_scan_with_checkpoints(kda):
+    """Checkpoints pin every chunk to one chain: an explicit segment scan is
+    refused (KDA_ERR_UNSUPPORTED) and the library never picks one."""
+    from linear_attention_recurrence_delta_amd import synth
+    q, k, v, g, beta, _ = synth.token_inputs(2048, 1, 128, 128, torch.bfloat16, 307, DEV)
+    with pytest.raises(kda.KdaError) as e:
+        kda.kda_prefill_checkpointed(q, k, v, g, beta, checkpoint_interval=256, plan=dict(segments=4))
+    assert e.value.status == 3
+    assert kda.kda_prefill_ex_workspace_bytes(1, 1 << 20, 16, 128, 128, torch.bfloat16,
+                                              checkpoint_interval=1024, checkpoint_capacity=1024) == 0
 
 
 @pytest.mark.parametrize("d,chunk", [(16, 16), (64, 32), (128, 16)])

@@ -80,13 +80,13 @@ def test_gate_scale_extremes(kda, oracle_mod):
     _check(kda, oracle_mod, w, "a_log extremes")
 
 
-@pytest.mark.parametrize("waves", ["1", "2", "4", "8"])
-def test_slab_width_invariance(kda, monkeypatch, waves):
-    say("CASE fused slab width, KDA_PREFILL_WAVES=%s" % waves)
+@pytest.mark.parametrize("cols", [16, 32, 64, 128])
+def test_slab_width_invariance(kda, cols):
+    say("CASE fused slab width %d columns" % cols)
     w = _inputs([120, 77], 2, 405)
     ref = kda.kda_prefill_fused(w["q"], w["k"], w["v"], w["z"], w["a_log"], w["beta"], None, w["cu"])
-    monkeypatch.setenv("KDA_PREFILL_WAVES", waves)
-    got = kda.kda_prefill_fused(w["q"], w["k"], w["v"], w["z"], w["a_log"], w["beta"], None, w["cu"])
+    got = kda.kda_prefill_fused(w["q"], w["k"], w["v"], w["z"], w["a_log"], w["beta"], None, w["cu"],
+                                plan=dict(slab_columns=cols))
     torch.cuda.synchronize()
     assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
 

@@ -33,7 +33,7 @@ def _inputs(T, H, d, dtype, seed, g_mode="k3", N=None, lengths=None, init_std=No
     return dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, lengths=lengths, cu_list=[int(x) for x in cu_list])
 
 
-def _check_all(kda, oracle, inp, chunk, scale=1.0, tol=None, label=""):
+def _check_all(kda, oracle, inp, chunk, scale=1.0, tol=None, label="", plan=None):
     d = inp["q"].shape[-1]
     H = inp["q"].shape[1]
     dtype = inp["q"].dtype
@@ -41,7 +41,7 @@ def _check_all(kda, oracle, inp, chunk, scale=1.0, tol=None, label=""):
     cu = torch.tensor(inp["cu_list"], dtype=torch.int32, device=DEV) if N > 1 else None
     say("CASE", label, "T=%d N=%d H=%d d=%d dtype=%s chunk=%d" % (inp["q"].shape[0], N, H, d, dtype, chunk))
     o, S = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], cu,
-                           chunk_size=chunk, scale=scale)
+                           chunk_size=chunk, scale=scale, plan=plan)
     torch.cuda.synchronize()
     ref = oracle_units(oracle_mod_global, inp, [(n, h) for n in range(N) for h in range(H)],
                        inp["cu_list"], scale=scale)
@@ -87,6 +87,21 @@ def test_multi_head_bf16_workload(kda, chunk):
     inp = dict(q=w["q"], k=w["k"], v=w["v"], g=w["g"], beta=w["beta"], S0=w["S0"], lengths=w["lengths"],
                cu_list=[0, w["T"]])
     _check_all(kda, None, inp, chunk=chunk, label="multi_head_bf16 T=4096 H=8 C=%d S0~N(0,.02)" % chunk)
+
+
+@pytest.mark.parametrize("g_mode", ["mild", "zero"])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_multi_head_bf16_weak_and_zero_decay(kda, g_mode, chunk):
+    # The multi-head workload's shape (H = 8, T = 4096, S_0 ~ N(0, 0.02)) with
+    # g = -0.05 sigmoid(z) or g = 0: the state then carries information
+    # across all 256 (C = 16) or 64 (C = 64) chunks, so the state passing
+    # between chunks and the conditioning of the triangular solve are tested
+    # at full length (with the K3 decay the state forgets within a chunk).
+    from linear_attention_recurrence_delta_amd import synth
+    w = synth.workload_inputs("multi_head_bf16", DEV, g_mode=g_mode)
+    inp = dict(q=w["q"], k=w["k"], v=w["v"], g=w["g"], beta=w["beta"], S0=w["S0"], lengths=w["lengths"],
+               cu_list=[0, w["T"]])
+    _check_all(kda, None, inp, chunk=chunk, label="multi_head_bf16 g=%s C=%d" % (g_mode, chunk))
 
 
 # ---------------------------------------------------------------- fp32 path
@@ -205,21 +220,56 @@ def test_run_to_run_bitwise_deterministic(kda):
     assert torch.equal(r1[0], r2[0]) and torch.equal(r1[1], r2[1])
 
 
-@pytest.mark.parametrize("waves", ["1", "2", "4", "8"])
-@pytest.mark.parametrize("kind,chunk", [("0", 16), ("0", 32), ("1", 16)])
-def test_value_slab_split_invariance(kda, waves, kind, chunk, monkeypatch):
+PIPE, STAGED = 1, 2  # KDA_KERNEL_PIPELINED, KDA_KERNEL_CHUNK_STAGED
+
+
+@pytest.mark.parametrize("cols", [16, 32, 64, 128])
+@pytest.mark.parametrize("kernel,chunk", [(STAGED, 16), (STAGED, 32), (PIPE, 16)])
+def test_value_slab_split_invariance(kda, cols, kernel, chunk):
     # Splitting d_v across workgroups (column separability of the update)
     # must not change a single bit: every column is computed identically.
-    # Both kernels are built with several slab widths (16 * waves columns;
-    # the chunk-staged kernel's narrowest is 32).
+    # Both kernels are built with several slab widths (kda_prefill_ex plans;
+    # the chunk-staged kernel's narrowest is 32 columns, and a width that is
+    # not built is refused).
     inp = _inputs(700, 2, 128, torch.bfloat16, 1100 + chunk, init_std=0.05)
-    monkeypatch.setenv("KDA_PREFILL_KIND", kind)
-    monkeypatch.setenv("KDA_PREFILL_WAVES", "8")
-    ref = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], chunk_size=chunk)
-    monkeypatch.setenv("KDA_PREFILL_WAVES", waves)
-    got = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"], chunk_size=chunk)
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    ref = kda.kda_prefill(*args, chunk_size=chunk, plan=dict(kernel=kernel, slab_columns=128))
+    if kernel == STAGED and cols == 16:
+        with pytest.raises(kda.KdaError) as e:
+            kda.kda_prefill(*args, chunk_size=chunk, plan=dict(kernel=kernel, slab_columns=cols))
+        assert e.value.status == 3  # KDA_ERR_UNSUPPORTED
+        return
+    got = kda.kda_prefill(*args, chunk_size=chunk, plan=dict(kernel=kernel, slab_columns=cols))
     torch.cuda.synchronize()
     assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+
+
+def test_default_plan_is_an_explicit_plan(kda):
+    # kda_prefill's own choice (pipelined kernel, 16-column slabs for 2
+    # (sequence, head) units on a 256-CU device) is one of the explicit plans,
+    # bit for bit, and the library reads no environment variable to choose it.
+    inp = _inputs(500, 2, 128, torch.bfloat16, 1150, init_std=0.05)
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["S0"])
+    ref = kda.kda_prefill(*args)
+    got = kda.kda_prefill(*args, plan=dict(kernel=PIPE, slab_columns=16))
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+
+
+def test_plan_fields_are_checked(kda):
+    inp = _inputs(64, 1, 128, torch.bfloat16, 1160)
+    args = (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    for plan, status in ((dict(kernel=3), 2), (dict(kernel=-1), 2), (dict(slab_columns=-16), 2),
+                         (dict(slab_columns=48), 3), (dict(kernel=PIPE), 0)):
+        if status == 0:
+            kda.kda_prefill(*args, plan=plan)
+            continue
+        with pytest.raises(kda.KdaError) as e:
+            kda.kda_prefill(*args, plan=plan)
+        assert e.value.status == status, plan
+    with pytest.raises(kda.KdaError) as e:  # the pipeline is built for chunk 16 only
+        kda.kda_prefill(*args, chunk_size=32, plan=dict(kernel=PIPE))
+    assert e.value.status == 3
 
 
 def test_dense_batch_layout_matches_packed(kda):
@@ -234,12 +284,12 @@ def test_dense_batch_layout_matches_packed(kda):
     assert torch.equal(o_p.view(B, T, H, d), o_d) and torch.equal(S_p, S_d)
 
 
-@pytest.mark.parametrize("kind", ["0", "1"])
-def test_bf16_c16_both_kernels(kda, kind, monkeypatch):
+@pytest.mark.parametrize("kernel", [STAGED, PIPE])
+def test_bf16_c16_both_kernels(kda, kernel):
     # C = 16 is built twice: the chunk-staged kernel and the wave-specialised
     # pipeline (the default).  Both must meet the oracle on ragged varlen
     # input with an initial state and a readout scale.
-    monkeypatch.setenv("KDA_PREFILL_KIND", kind)
     lengths = [5, 16, 33, 300, 0, 1000, 47]
     inp = _inputs(sum(lengths), 4, 128, torch.bfloat16, 1300, lengths=lengths, init_std=0.05)
-    _check_all(kda, None, inp, chunk=16, scale=0.5, label="bf16 C=16 kind=%s scale=0.5" % kind)
+    _check_all(kda, None, inp, chunk=16, scale=0.5, plan=dict(kernel=kernel),
+               label="bf16 C=16 kernel=%d scale=0.5" % kernel)

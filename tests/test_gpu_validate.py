@@ -90,3 +90,27 @@ def test_decode_inputs(kda, monkeypatch):
     _expect_domain(kda, lambda: kda.kda_decode_step(q, k, v, g, beta, S2))
     torch.cuda.synchronize()
     assert torch.equal(S2, S)  # the state was not touched
+
+
+def test_binding_checks_output_shapes(kda):
+    """The Python binding refuses caller-supplied outputs of the wrong shape
+    or device before the C ABI is called (the kernels size their stores from
+    T, H and d, not from the buffers)."""
+    say("CASE binding: out= / final_state= shapes")
+    q, k, v, g, beta, cu = _prefill_inputs()
+    T, H = q.shape[:2]
+    bad_o = torch.empty((T - 1, H, 128), dtype=torch.bfloat16, device=DEV)
+    bad_s = torch.empty((1, H, 128, 128), dtype=torch.float32, device=DEV)  # 2 sequences
+    with pytest.raises(ValueError):
+        kda.kda_prefill(q, k, v, g, beta, None, cu, out=bad_o)
+    with pytest.raises(ValueError):
+        kda.kda_prefill(q, k, v, g, beta, None, cu, final_state=bad_s)
+    with pytest.raises(ValueError):
+        kda.kda_prefill(q, k, v, g, beta, None, cu.cpu())
+    from linear_attention_recurrence_delta_amd import synth
+    dq, dk, dv, dg, db = synth.decode_inputs(4, 2, 128, torch.bfloat16, 22, DEV)
+    S = torch.zeros((4, 2, 128, 128), device=DEV)
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(dq, dk, dv, dg, db, S, out=torch.empty((4, 1, 128), dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ValueError):
+        kda.kda_decode_step(dq, dk, dv, dg, db, S.cpu())
