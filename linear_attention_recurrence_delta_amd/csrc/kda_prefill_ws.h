@@ -955,13 +955,20 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             }
         }
     } else if (is_cons && wk.s_out) {
-        // empty sequence: the final state is the initial state
+        // empty sequence: the final state is the initial state.  Buffer
+        // accesses, as everywhere in this kernel: a generic (flat) access
+        // would make the compiler's waits on every wave's loads in flight
+        // collapse to full drains.
+        const auto ro = buffer_rsrc(wk.s_out, D * D * 4);
+        const auto ri = wk.s_in ? buffer_rsrc(wk.s_in, D * D * 4) : buffer_rsrc(p.g, 0);
         for (int t = 0; t < TPW; ++t)
             for (int ct = 0; ct < NCB; ++ct)
                 for (int pp = 0; pp < 4; ++pp) {
                     const int row = 16 * ct + 4 * g4 + pp, col = col_base + 16 * t + l16;
-                    const int64_t off = (int64_t)row * D + col;
-                    wk.s_out[off] = w_identity ? (row == col ? 1.f : 0.f) : (wk.s_in ? wk.s_in[off] : 0.f);
+                    const int off = (row * D + col) * 4;
+                    const float x = w_identity ? (row == col ? 1.f : 0.f)
+                                               : __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, 0));
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), ro, off, 0, 0);
                 }
     }
 }
