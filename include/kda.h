@@ -75,8 +75,10 @@ typedef enum {
     KDA_ERR_MISALIGNED = 4,   /* a pointer breaks the alignment rule above         */
     KDA_ERR_WORKSPACE = 5,    /* workspace smaller than kda_prefill_workspace_bytes */
     KDA_ERR_HIP = 6,          /* the HIP runtime reported an error at launch       */
-    KDA_ERR_DOMAIN = 7        /* g, beta or cu_seqlens break the preconditions;    */
+    KDA_ERR_DOMAIN = 7,       /* g, beta or cu_seqlens break the preconditions;    */
                               /* returned only when KDA_VALIDATE=1                 */
+    KDA_ERR_SCRATCH = 8       /* kda_prefill_ex_noalloc: the call needs more than  */
+                              /* kda_noalloc_scratch_bytes() of workspace          */
 } kda_status;
 
 /* KDA_ABI_VERSION of the built library. */
@@ -232,6 +234,26 @@ size_t kda_prefill_ex_workspace_bytes(const kda_prefill_desc *desc);
  * equal to a tensor pointer. */
 kda_status kda_prefill_ex(const kda_prefill_desc *desc, const kda_prefill_tensors *tensors, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/*
+ * kda_prefill_ex_noalloc -- kda_prefill_ex for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): it takes no workspace and allocates nothing.  The
+ * workspace the call needs (the segment scan's maps, kda_prefill_ex_
+ * workspace_bytes) comes from one static device buffer of
+ * kda_noalloc_scratch_bytes() bytes (64 MiB) that the library holds on every
+ * GPU it runs on until the process ends.  Calls that need no workspace (packed
+ * batches, direct chains) run as kda_prefill_ex; a call that needs more than
+ * the buffer returns KDA_ERR_SCRATCH before any HIP call (the library's own
+ * plans need at most 128 KiB per (sequence, head) per compute unit of the
+ * device: 32 MiB on 256 compute units).  The buffer keeps the last call's
+ * contents and every call on one GPU shares it: calls that overlap on one
+ * GPU (other streams, other host threads) race on it and must be serialised
+ * by the caller.  Results are bitwise those of kda_prefill_ex with the same
+ * description.  Errors as kda_prefill_ex, plus KDA_ERR_SCRATCH.
+ */
+size_t kda_noalloc_scratch_bytes(void);
+kda_status kda_prefill_ex_noalloc(const kda_prefill_desc *desc, const kda_prefill_tensors *tensors, void *stream);
 
 /*
  * kda_prefill_checkpointed -- kda_prefill that also emits the state at every

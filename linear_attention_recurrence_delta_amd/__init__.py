@@ -22,6 +22,7 @@ from .kda import (  # noqa: F401
     kda_prefill_fused,
     kda_prefill_fused_supported,
     kda_output_gate,
+    kda_noalloc_scratch_bytes,
     kda_output_gate_supported,
     kda_prefill_supported,
     kda_prefill_workspace_bytes,

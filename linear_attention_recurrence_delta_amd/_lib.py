@@ -48,6 +48,8 @@ SIGNATURES = {
                                         _i32, _vp, _i64, _vp, _sz, _vp]),
     "kda_prefill_ex_workspace_bytes": (_sz, [_pdesc]),
     "kda_prefill_ex": (_i32, [_pdesc, _ptens, _vp, _sz, _vp]),
+    "kda_noalloc_scratch_bytes": (_sz, []),
+    "kda_prefill_ex_noalloc": (_i32, [_pdesc, _ptens, _vp]),
     "kda_prefill_fused_supported": (_i32, [_i32, _i32, _i32, _i32]),
     "kda_prefill_fused": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),

@@ -213,8 +213,10 @@ size_t desc_workspace_bytes(const kda_prefill_desc& d, bool dense) {
 }
 }  // namespace
 
+// dry_run: host validation only, nothing launched (the status a call with
+// this workspace would return before its first HIP call).
 static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tensors& t, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               size_t workspace_bytes, void* stream, bool dry_run = false) {
     const int32_t num_seqs = d.num_seqs, num_heads = d.num_heads, d_k = d.d_k, d_v = d.d_v, dtype = d.qkv_dtype;
     const int64_t total_tokens = d.total_tokens;
     const bool fused = d.fused != 0;
@@ -270,6 +272,7 @@ static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tens
         for (const void* ptr : io)
             if (ptr == workspace) return KDA_ERR_BAD_SHAPE;
     }
+    if (dry_run) return KDA_OK;
 
     if (num_seqs == 0) return KDA_OK;
     if (total_tokens == 0 && !final_state) return KDA_OK;
@@ -348,6 +351,7 @@ const char* kda_status_string(int32_t s) {
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace smaller than kda_prefill_workspace_bytes";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
         case KDA_ERR_DOMAIN: return "KDA_ERR_DOMAIN: g outside [-5, 0], beta outside [0, 1] or malformed cu_seqlens (KDA_VALIDATE=1)";
+        case KDA_ERR_SCRATCH: return "KDA_ERR_SCRATCH: the call needs more workspace than the library's static buffer (kda_noalloc_scratch_bytes) holds";
         default: return "unknown kda_status";
     }
 }
@@ -418,6 +422,24 @@ kda_status kda_prefill_ex(const kda_prefill_desc* desc, const kda_prefill_tensor
                           size_t workspace_bytes, void* stream) {
     if (!desc || !tensors) return KDA_ERR_NULL_POINTER;
     return prefill_impl(*desc, *tensors, workspace, workspace_bytes, stream);
+}
+
+size_t kda_noalloc_scratch_bytes(void) { return kda::kNoallocScratchBytes; }
+
+kda_status kda_prefill_ex_noalloc(const kda_prefill_desc* desc, const kda_prefill_tensors* tensors, void* stream) {
+    if (!desc || !tensors) return KDA_ERR_NULL_POINTER;
+    // The call's workspace need, from the sizes alone (host): a plan that
+    // needs more than the static buffer is refused before any HIP call.
+    const size_t need = desc_workspace_bytes(*desc, tensors->cu_seqlens == nullptr);
+    if (need > kda::kNoallocScratchBytes) return KDA_ERR_SCRATCH;
+    if (need == 0) return prefill_impl(*desc, *tensors, nullptr, 0, stream);
+    // host validation first (invalid arguments report their own status)
+    const kda_status pre = prefill_impl(*desc, *tensors, nullptr, 0, nullptr, true);
+    if (pre == KDA_OK) return prefill_impl(*desc, *tensors, nullptr, 0, stream);
+    if (pre != KDA_ERR_WORKSPACE) return pre;
+    void* scratch = nullptr;
+    if (kda::noalloc_scratch(&scratch) != hipSuccess) return KDA_ERR_HIP;
+    return prefill_impl(*desc, *tensors, scratch, kda::kNoallocScratchBytes, stream);
 }
 
 static kda_prefill_tensors flat_tensors(const void* q, const void* k, const void* v, const float* g,

@@ -122,6 +122,12 @@ struct OutputGateParams {
     float eps;
 };
 
+// The static device buffer of kda_prefill_ex_noalloc (kda_scratch.hip): its
+// size, and its device address on the current device (taken once per device
+// with hipGetSymbolAddress).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Phase 2 of the segment scan: for g = 1 .. seg_G - 2, start(g + 1) =
 // M_g start(g) + B_g in fp32, in place of B_g, per (sequence, head) and
 // 16-column group.

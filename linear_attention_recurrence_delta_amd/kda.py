@@ -155,15 +155,25 @@ def _workspace(a, desc, packed):
     return ws, ws_bytes
 
 
-def _run_ex(a, desc, initial_state, cu_seqlens, z=None, a_log=None, checkpoints=None):
-    """kda_prefill_ex with the marshalled arguments."""
+def _run_ex(a, desc, initial_state, cu_seqlens, z=None, a_log=None, checkpoints=None, noalloc=False):
+    """kda_prefill_ex (or, noalloc, kda_prefill_ex_noalloc: no workspace
+    allocated, the library's static buffer instead) with the marshalled
+    arguments."""
     t = PrefillTensors(q=_ptr(a["q"]), k=_ptr(a["k"]), v=_ptr(a["v"]), g=None if z is not None else _ptr(a["g"]),
                        z=_ptr(z), a_log=_ptr(a_log), beta=_ptr(a["beta"]), initial_state=_ptr(initial_state),
                        cu_seqlens=_ptr(cu_seqlens), o=_ptr(a["o"]), final_state=_ptr(a["fs"]),
                        checkpoints=_ptr(checkpoints))
+    if noalloc:
+        with torch.cuda.device(a["dev"]):
+            _check(lib().kda_prefill_ex_noalloc(desc, t, _stream(a["dev"])))
+        return
     ws, ws_bytes = _workspace(a, desc, cu_seqlens is not None)
     with torch.cuda.device(a["dev"]):
         _check(lib().kda_prefill_ex(desc, t, _ptr(ws), ws_bytes, _stream(a["dev"])))
+
+
+def kda_noalloc_scratch_bytes() -> int:
+    return int(lib().kda_noalloc_scratch_bytes())
 
 
 def kda_prefill_ex_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size=0, *,
@@ -175,7 +185,7 @@ def kda_prefill_ex_workspace_bytes(num_seqs, total_tokens, num_heads, d_k, d_v, 
 
 def kda_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_size: int = 0,
                 scale: float = 1.0, output_final_state: bool = True, num_seqs: int | None = None,
-                out=None, final_state=None, plan=None):
+                out=None, final_state=None, plan=None, noalloc: bool = False):
     """Chunked KDA prefill over a packed batch.
 
     q, k, g: [T, H, d_k]; v: [T, H, d_v]; beta: [T, H].  A dense batch may be
@@ -185,12 +195,15 @@ def kda_prefill(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_
     plan: None (the library's choice, through kda_prefill) or a dict with
     any of kernel (KDA_KERNEL_*), slab_columns, segments (through
     kda_prefill_ex; include/kda.h describes the fields).
+    noalloc: through kda_prefill_ex_noalloc (no workspace is allocated; the
+    library's static device buffer serves instead; outputs are allocated here
+    unless out / final_state are given).
     Returns (o, final_state); final_state is None if output_final_state is False.
     """
     a = _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state)
     desc = _desc(a, chunk_size, scale, plan=plan)
-    if plan is not None:
-        _run_ex(a, desc, initial_state, cu_seqlens)
+    if plan is not None or noalloc:
+        _run_ex(a, desc, initial_state, cu_seqlens, noalloc=noalloc)
     else:
         ws, ws_bytes = _workspace(a, desc, cu_seqlens is not None)
         with torch.cuda.device(a["dev"]):

@@ -58,7 +58,7 @@ def header_statuses():
 def test_version_and_status_strings(lib):
     assert lib.kda_abi_version() == 4
     statuses = header_statuses()
-    assert sorted(statuses) == list(range(8))
+    assert sorted(statuses) == list(range(9))
     for s, name in statuses.items():
         txt = lib.kda_status_string(s).decode()
         assert txt.startswith(name + ":"), (s, txt)
@@ -407,3 +407,23 @@ def test_prefill_backward_validation(lib):
     assert _bwd(lib, ws_bytes=100) == WS
     assert _bwd(lib, N=0, T=0, q=None, k=None, v=None, g=None, b=None, do=None, dq=None, dk=None, dv=None,
                 dg=None, db=None, ws=None, ws_bytes=0) == OK
+
+
+def test_prefill_ex_noalloc_host_checks(lib):
+    """kda_prefill_ex_noalloc refuses, before any HIP call, a plan whose
+    workspace exceeds the static buffer (64 MiB), and validates like
+    kda_prefill_ex."""
+    import ctypes as ct
+    from linear_attention_recurrence_delta_amd._lib import PrefillTensors
+    assert lib.kda_noalloc_scratch_bytes() == 64 << 20
+    t = PrefillTensors(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE + 0x100000)
+    SCRATCH = 8
+    big = _desc(total_tokens=8192, num_heads=4, segments=256)  # 4 x 255 maps of 128 KiB = 127.5 MiB
+    assert lib.kda_prefill_ex_workspace_bytes(ct.byref(big)) == 4 * 255 * 2 * 128 * 128 * 4
+    assert lib.kda_prefill_ex_noalloc(ct.byref(big), ct.byref(t), None) == SCRATCH
+    assert lib.kda_prefill_ex_noalloc(None, ct.byref(t), None) == NULLP
+    assert lib.kda_prefill_ex_noalloc(ct.byref(_desc(num_heads=0)), ct.byref(t), None) == BAD
+    assert lib.kda_prefill_ex_noalloc(ct.byref(_desc(kernel=7)), ct.byref(t), None) == BAD
+    bad_q = PrefillTensors(q=FAKE + 8, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, o=FAKE + 0x100000)
+    assert lib.kda_prefill_ex_noalloc(ct.byref(_desc()), ct.byref(bad_q), None) == MISAL
+    assert lib.kda_prefill_ex_noalloc(ct.byref(_desc(num_seqs=0, total_tokens=0)), ct.byref(t), None) == OK
