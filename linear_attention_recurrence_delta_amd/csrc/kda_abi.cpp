@@ -112,12 +112,20 @@ const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t 
 
 // Sequence-segment scan plan (kda_internal.h, PrefillParams::seg_*): G
 // segments per sequence, segments 1 .. G-1 of Lc chunks each and segment 0
-// the rest (at least 2 Lc - 1 chunks: it runs alone while the maps of two
-// segments run one after the other on another compute unit).
+// the rest.  Segment 0 runs (with outputs) during phase 1, while the maps of
+// two segments run one after the other on other compute units; a map reads
+// no q and writes no o, so it streams far fewer bytes than a run and takes
+// less time per chunk.  Segment 0 therefore gets kSeg0Share / 16 of two
+// segments' chunks: measured on MI355X for one 1,048,576-token sequence of 16
+// heads (17 segments), a segment 0 as long as the others (share 8) took 13.3
+// ms against 16.6 ms for a double one (16); its run then ends before the
+// second round of maps does.
 struct SegPlan {
     int G = 1;
     int64_t len0 = 0, len = 0;  // tokens
 };
+
+constexpr int kSeg0Share = 8;
 
 constexpr int kMaxSegments = 256;
 
@@ -140,7 +148,11 @@ SegPlan seg_plan(int G, int64_t t_seq) {
     sp.G = G;
     if (G < 2) return sp;
     const int64_t chunks = (t_seq + 15) / 16;
-    const int64_t lc = chunks / (G + 1);
+    // chunks = L0 + (G - 1) Lc with L0 = (share / 16) 2 Lc; at least one chunk
+    // per segment, segment 0 taking the rest
+    int64_t lc = chunks * 8 / ((int64_t)(G - 1) * 8 + kSeg0Share);
+    if (lc < 1) lc = 1;
+    while ((int64_t)(G - 1) * lc >= chunks && lc > 1) --lc;
     sp.len = 16 * lc;
     sp.len0 = t_seq - (int64_t)(G - 1) * sp.len;
     return sp;

@@ -285,15 +285,19 @@ __device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
 //
 // SEG: the variant that also runs the segment-scan phases (PrefillParams::
 // seg_phase 1 and 3); the plain kernels are compiled without that code.
-template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG>
-__global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
+//
+// MAP: the body of a segment-map workgroup (segment scan, phase 1): only the
+// end state is wanted, so, as with CKB, no readout and no o; q is not read
+// either (its loads use an empty range: no memory request), and the start
+// state may be the identity and v zero (the M half of a map).
+template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG, bool MAP>
+__device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk, char* smem) {
     typedef WsCfg<NCW, TPW, NSA, FUSED> Cfg;
     typedef Elem<bf16_t> E;
     typedef uint2 Frag;
     constexpr int D = Cfg::D, C = Cfg::C, NCB = Cfg::NCB, DVW = Cfg::DVW, IPW = Cfg::IPW;
     constexpr int PD = Cfg::PD, PK = Cfg::PK, PA = Cfg::PA;
-
-    __shared__ __align__(16) char smem[Cfg::LDS];
+    constexpr bool NOOUT = CKB || MAP;  // no readout, no o
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -301,22 +305,9 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     const int g4 = lane >> 4;
     const int l16 = lane & 15;
 
-    // XCD-aware block order (ws_resolve); padding blocks exit at once.  The
-    // work description is uniform: pinned to scalar registers (integer
-    // divisions by run-time values leave their results in vector registers).
-    WsWork wk;
-    if (!ws_resolve<D, SEG>(p, blockIdx.x, wk)) return;
-    wk.t_begin = uniform_i64(wk.t_begin);
-    wk.t_end = uniform_i64(wk.t_end);
-    wk.n = __builtin_amdgcn_readfirstlane(wk.n);
-    wk.h = __builtin_amdgcn_readfirstlane(wk.h);
-    wk.z = __builtin_amdgcn_readfirstlane(wk.z);
-    wk.s_in = reinterpret_cast<const float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_in)));
-    wk.s_out = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_out)));
-    // segment-map flags: compile-time false / true in the plain kernels
-    const bool w_identity = SEG && __builtin_amdgcn_readfirstlane((int)wk.s_identity) != 0;
-    const bool w_store_o = !SEG || __builtin_amdgcn_readfirstlane((int)wk.store_o) != 0;
-    const bool w_v_zero = SEG && __builtin_amdgcn_readfirstlane((int)wk.v_zero) != 0;
+    // segment-map flags: compile-time false outside the map body
+    const bool w_identity = MAP && wk.s_identity;
+    const bool w_v_zero = MAP && wk.v_zero;
     const int z = wk.z;
     const int h = wk.h;
     const int n = wk.n;
@@ -392,8 +383,10 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                         : FUSED     ? reinterpret_cast<const char*>(p.z)
                                     : reinterpret_cast<const char*>(p.g);
     const uint32_t ld_step = 8u * (uint32_t)(H * D);  // global bytes per load (4 bf16 or 2 fp32 rows)
-    const uint32_t ld_voff = ld_none ? 0x80000000u
-                                     : (uint32_t)ld_row * (uint32_t)(H * D) * (uint32_t)ld_es + 16u * (uint32_t)(lane % ld_lpr);
+    // (a map workgroup's q loads also take the out-of-range offset: q is not needed)
+    const uint32_t ld_voff = (ld_none || (MAP && ld_u0 < 4))
+                                 ? 0x80000000u
+                                 : (uint32_t)ld_row * (uint32_t)(H * D) * (uint32_t)ld_es + 16u * (uint32_t)(lane % ld_lpr);
     // beta bytes; the other waves read out of range (zeros, no memory request)
     // so that the load and its use stay unconditional
     const uint32_t lb = sa == 0 ? (uint32_t)l16 * (uint32_t)H * 4u : 0x80000000u;
@@ -585,7 +578,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                 kl[ch] = kv * e2;
             }
             const Frag klf = E::make(kl[0], kl[1], kl[2], kl[3]);
-            if constexpr (!CKB) st_frag(QB + l16 * PD + c0, E::make(qb[0], qb[1], qb[2], qb[3]));
+            if constexpr (!NOOUT) st_frag(QB + l16 * PD + c0, E::make(qb[0], qb[1], qb[2], qb[3]));
             st_frag(KB + l16 * PD + c0, E::make(kb[0], kb[1], kb[2], kb[3]));
             st_frag(KL + l16 * PD + c0, klf);
             uint16_t* klt = reinterpret_cast<uint16_t*>(KLT) + l16;
@@ -613,7 +606,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             const Frag a0 = ld_frag(KL + l16 * PD + c0), a1 = ld_frag(KL + l16 * PD + c0 + 16);
             const Frag k0 = ld_frag(KB + l16 * PD + c0), k1 = ld_frag(KB + l16 * PD + c0 + 16);
             mma32(accA, a0, a1, k0, k1);
-            if constexpr (!CKB) {
+            if constexpr (!NOOUT) {
                 const Frag q0 = ld_frag(QB + l16 * PD + c0), q1 = ld_frag(QB + l16 * PD + c0 + 16);
                 mma32(accP, a0, a1, q0, q1);
             }
@@ -622,7 +615,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         bf16_t* P = reinterpret_cast<bf16_t*>(slotP(c));
         float* AT = reinterpret_cast<float*>(slotA(c));
         const int r = l16;
-        if constexpr (!CKB) {
+        if constexpr (!NOOUT) {
             f32x4 pv;
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? accP[pp] : 0.f;
@@ -704,11 +697,11 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 #pragma unroll
         for (int kb = 0; kb < NCB; ++kb) {
             kf[kb] = ld_frag(KB + l16 * PD + 16 * kb + 4 * g4);
-            if constexpr (!CKB) qf[kb] = ld_frag(QB + l16 * PD + 16 * kb + 4 * g4);
+            if constexpr (!NOOUT) qf[kb] = ld_frag(QB + l16 * PD + 16 * kb + 4 * g4);
         }
         const Frag Tf = ld_frag(T + l16 * PK + 4 * g4);
         Frag Pf;
-        if constexpr (!CKB) Pf = ld_frag(P + l16 * PK + 4 * g4);
+        if constexpr (!NOOUT) Pf = ld_frag(P + l16 * PK + 4 * g4);
         const float4 b4 = *reinterpret_cast<const float4*>(BETA + 4 * g4);
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
         float vv[TPW][4];
@@ -742,7 +735,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 mma32(X[t], kf[kb], kf[kb + 1], Sop[t][kb], Sop[t][kb + 1]);
-                if constexpr (!CKB) mma32(QS[t], Sop[t][kb], Sop[t][kb + 1], qf[kb], qf[kb + 1]);
+                if constexpr (!NOOUT) mma32(QS[t], Sop[t][kb], Sop[t][kb + 1], qf[kb], qf[kb + 1]);
             }
         // U = T diag(beta) (V - X), all tiles side by side.
         Frag Uf[TPW];
@@ -764,7 +757,7 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
         // O^T = (Qt S)^T + U^T P^T: lane (g4, l16) holds token l16 at the
         // value columns vcol(t, 4 g4 + pp) = 4 TPW g4 + 4 t + pp, adjacent.
         [[maybe_unused]] uint32_t ov[TPW][2];
-        if constexpr (!CKB) {
+        if constexpr (!NOOUT) {
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 // (P U)^T in its own accumulator, added to the 32-deep QS
@@ -786,10 +779,10 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
             }
         // One store per lane; rows past the end of the sequence get an offset
         // beyond the buffer's range, and buffer stores out of range are dropped.
-        if constexpr (!CKB) {
+        if constexpr (!NOOUT) {
             const int64_t e0 = chunk_base(c);
             const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
-            const uint32_t oo = (w_store_o && l16 < nv) ? o_voff : 0x80000000u;
+            const uint32_t oo = l16 < nv ? o_voff : 0x80000000u;
             if constexpr (TPW == 2)
                 __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
             else
@@ -971,6 +964,33 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), ro, off, 0, 0);
                 }
     }
+}
+
+template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG>
+__global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
+    typedef WsCfg<NCW, TPW, NSA, FUSED> Cfg;
+    __shared__ __align__(16) char smem[Cfg::LDS];
+    // XCD-aware block order (ws_resolve); padding blocks exit at once.  The
+    // work description is uniform: pinned to scalar registers (integer
+    // divisions by run-time values leave their results in vector registers).
+    WsWork wk;
+    if (!ws_resolve<Cfg::D, SEG>(p, blockIdx.x, wk)) return;
+    wk.t_begin = uniform_i64(wk.t_begin);
+    wk.t_end = uniform_i64(wk.t_end);
+    wk.n = __builtin_amdgcn_readfirstlane(wk.n);
+    wk.h = __builtin_amdgcn_readfirstlane(wk.h);
+    wk.z = __builtin_amdgcn_readfirstlane(wk.z);
+    wk.s_in = reinterpret_cast<const float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_in)));
+    wk.s_out = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_out)));
+    wk.s_identity = __builtin_amdgcn_readfirstlane((int)wk.s_identity) != 0;
+    wk.v_zero = __builtin_amdgcn_readfirstlane((int)wk.v_zero) != 0;
+    if constexpr (SEG) {
+        if (__builtin_amdgcn_readfirstlane((int)!wk.store_o)) {
+            ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, true>(p, wk, smem);
+            return;
+        }
+    }
+    ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, false>(p, wk, smem);
 }
 
 template <int NCW, int TPW, int NSA, bool FUSED = false, bool CKB = false, bool SEG = false>
