@@ -393,6 +393,34 @@ kda_status kda_output_gate(int64_t total_tokens, int32_t num_heads,
                            const void *o, const void *gate,
                            const float *weight, void *y, void *stream);
 
+/*
+ * kda_prefill_output_gated -- kda_prefill followed by the gated output of the
+ * layer, y = Sigmoid(gate) * RMSNorm(o) * weight ("Understanding Kimi K3's
+ * attention", output equation; the readout o is that of kda_prefill), with y
+ * returned in place of o.  Where one workgroup holds a whole head (bf16,
+ * d = 128, the library's whole-head slab: batches with more (sequence, head)
+ * units than half the compute units), the gate is applied before the store
+ * and o never reaches memory: each row's sum of squares is gathered across
+ * the workgroup's waves through LDS.  Otherwise o is written to y and
+ * kda_output_gate runs over it in place.  The norm is taken over the o values
+ * as rounded to qkv_dtype, as a separate pass would read them.
+ *
+ * Arguments as kda_prefill (o replaced by y), plus:
+ *   gate    [T_total, H, d_v] qkv_dtype, 16-byte aligned: the gate logits
+ *           (W_g x_t, computed upstream).  y may be the same buffer as gate.
+ *   weight  [d_v] fp32: the RMSNorm weight, shared by the heads.
+ *   eps     >= 0, added to the mean square.
+ *   y       [T_total, H, d_v] qkv_dtype, written.
+ * Supported where kda_prefill and kda_output_gate both are.  Errors as
+ * kda_prefill and kda_output_gate.
+ */
+kda_status kda_prefill_output_gated(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                                    int32_t d_v, int32_t qkv_dtype, int32_t chunk_size, float scale,
+                                    const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                                    const void *gate, const float *weight, float eps, void *y,
+                                    float *final_state, void *workspace, size_t workspace_bytes, void *stream);
+
 /* 1 if kda_prefill_backward is built for (qkv_dtype, d_k, d_v): bf16 with
  * d_k = d_v = 128. */
 int32_t kda_prefill_backward_supported(int32_t qkv_dtype, int32_t d_k,

@@ -21,6 +21,7 @@ from .kda import (  # noqa: F401
     kda_prefill_ex_workspace_bytes,
     kda_prefill_fused,
     kda_prefill_fused_supported,
+    kda_prefill_output_gated,
     kda_output_gate,
     kda_noalloc_scratch_bytes,
     kda_output_gate_supported,

@@ -53,6 +53,9 @@ SIGNATURES = {
     "kda_prefill_fused_supported": (_i32, [_i32, _i32, _i32, _i32]),
     "kda_prefill_fused": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "kda_prefill_output_gated": (_i32, [_i32, _i64, _i32, _i32, _i32, _i32, _i32, _f32,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp,
+                                        _vp, _sz, _vp]),
     "kda_output_gate_supported": (_i32, [_i32, _i32]),
     "kda_output_gate": (_i32, [_i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _vp]),
     "kda_prefill_backward_supported": (_i32, [_i32, _i32, _i32]),

@@ -225,10 +225,18 @@ size_t desc_workspace_bytes(const kda_prefill_desc& d, bool dense) {
 }
 }  // namespace
 
+// The output gate applied to o before it is stored (kda_prefill_output_gated).
+struct GateArgs {
+    const void* gate;
+    const float* weight;
+    float eps;
+};
+
 // dry_run: host validation only, nothing launched (the status a call with
 // this workspace would return before its first HIP call).
 static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tensors& t, void* workspace,
-                               size_t workspace_bytes, void* stream, bool dry_run = false) {
+                               size_t workspace_bytes, void* stream, bool dry_run = false,
+                               const GateArgs* ga = nullptr) {
     const int32_t num_seqs = d.num_seqs, num_heads = d.num_heads, d_k = d.d_k, d_v = d.d_v, dtype = d.qkv_dtype;
     const int64_t total_tokens = d.total_tokens;
     const bool fused = d.fused != 0;
@@ -272,6 +280,17 @@ static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tens
         const void* ins[] = {q, k, v, g, beta, o, initial_state, final_state};
         for (const void* ptr : ins)
             if (checkpoints && ptr == checkpoints) return KDA_ERR_BAD_SHAPE;
+    }
+    if (ga) {
+        if (fused || ckpt_interval > 0) return KDA_ERR_UNSUPPORTED;
+        if (!kda_output_gate_supported(dtype, d_v)) return KDA_ERR_UNSUPPORTED;
+        if (!(ga->eps >= 0.f) || ga->eps > 1e30f) return KDA_ERR_BAD_SHAPE;  // also rejects NaN
+        if (total_tokens > 0 && (!ga->gate || !ga->weight)) return KDA_ERR_NULL_POINTER;
+        if ((ga->gate && !aligned16(ga->gate)) || (ga->weight && !aligned4(ga->weight))) return KDA_ERR_MISALIGNED;
+        if (o && static_cast<const void*>(ga->weight) == o) return KDA_ERR_BAD_SHAPE;
+        const void* ins[] = {q, k, v, g, beta};
+        for (const void* ptr : ins)
+            if (ga->gate && ptr == ga->gate) return KDA_ERR_BAD_SHAPE;
     }
     const int kind = plan_kind(dtype, d_k, C, fused, false, d.kernel);
     if (kind < 0) return KDA_ERR_UNSUPPORTED;
@@ -326,9 +345,32 @@ static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tens
     p.z = z;
     p.a_log = a_log;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (ga && G < 2 && var->launch_gate && var->nwc * 16 == d_v) {
+        // whole heads in one workgroup: the gate is applied before the store
+        if (kda::ws_grid_blocks(p) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+        p.gate = ga->gate;
+        p.gate_weight = ga->weight;
+        p.gate_eps = ga->eps;
+        return var->launch_gate(p, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    // otherwise o goes to the output buffer and the gate is a second pass over it
+    auto gate_pass = [&]() -> kda_status {
+        if (!ga || total_tokens == 0) return KDA_OK;
+        kda::OutputGateParams gp;
+        gp.o = o;
+        gp.gate = ga->gate;
+        gp.weight = ga->weight;
+        gp.y = o;
+        gp.rows = total_tokens * num_heads;
+        gp.eps = ga->eps;
+        const hipError_t e = dtype == KDA_DTYPE_BF16 ? kda::launch_output_gate_bf16(d_v, gp, device_cu_count(), s)
+                                                     : kda::launch_output_gate_f32(d_v, gp, device_cu_count(), s);
+        return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    };
     if (G < 2) {
         if (kda::ws_grid_blocks(p) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
-        return var->launch(p, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+        if (var->launch(p, s) != hipSuccess) return KDA_ERR_HIP;
+        return gate_pass();
     }
     // Segment scan: maps (phase 1), their chain (phase 2), re-runs (phase 3).
     if (!var->launch_seg) return KDA_ERR_UNSUPPORTED;
@@ -345,7 +387,8 @@ static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tens
     if (var->launch_seg(p, s) != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_segment_combine(p, s) != hipSuccess) return KDA_ERR_HIP;
     p.seg_phase = 3;
-    return var->launch_seg(p, s) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (var->launch_seg(p, s) != hipSuccess) return KDA_ERR_HIP;
+    return gate_pass();
 }
 
 
@@ -481,6 +524,21 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens, int32_t num_heads
     const kda_prefill_desc d = flat_desc(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale);
     const kda_prefill_tensors t = flat_tensors(q, k, v, g, beta, initial_state, cu_seqlens, o, final_state);
     return prefill_impl(d, t, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_prefill_output_gated(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k,
+                                    int32_t d_v, int32_t dtype, int32_t chunk_size, float scale, const void* q,
+                                    const void* k, const void* v, const float* g, const float* beta,
+                                    const float* initial_state, const int32_t* cu_seqlens, const void* gate,
+                                    const float* weight, float eps, void* y, float* final_state, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    const kda_prefill_desc d = flat_desc(num_seqs, total_tokens, num_heads, d_k, d_v, dtype, chunk_size, scale);
+    const kda_prefill_tensors t = flat_tensors(q, k, v, g, beta, initial_state, cu_seqlens, y, final_state);
+    GateArgs ga;
+    ga.gate = gate;
+    ga.weight = weight;
+    ga.eps = eps;
+    return prefill_impl(d, t, workspace, workspace_bytes, stream, false, &ga);
 }
 
 kda_status kda_prefill_fused(int32_t num_seqs, int64_t total_tokens, int32_t num_heads, int32_t d_k, int32_t d_v,

@@ -51,6 +51,13 @@ struct PrefillParams {
     // 3 runs segments 1 .. seg_G - 1 from those states with outputs.
     // seg_ws holds [N H][seg_G - 1][2][D][D] fp32: (M_g, B_g), the B slot
     // replaced by the start state of segment g + 1 (slot 0: segment 0's end).
+    // Output gate fused into the o store (kernels built with it): o is not
+    // stored; y = Sigmoid(gate) o / sqrt(mean(o^2) + gate_eps) * gate_weight
+    // goes to the o buffer instead (gate [T_total, H, D] in the qkv dtype,
+    // gate_weight [D] fp32).
+    const void* gate = nullptr;
+    const float* gate_weight = nullptr;
+    float gate_eps = 0.f;
     int32_t seg_phase = 0;  // 0, 1 or 3
     int32_t seg_G = 1;
     int32_t seg_len0 = 0;
@@ -144,6 +151,8 @@ struct PrefillVariant {
     hipError_t (*launch)(const PrefillParams&, hipStream_t);
     // the same kernel built with the segment-scan phases, or nullptr
     hipError_t (*launch_seg)(const PrefillParams&, hipStream_t) = nullptr;
+    // the same kernel with the output gate fused into the o store, or nullptr
+    hipError_t (*launch_gate)(const PrefillParams&, hipStream_t) = nullptr;
 };
 
 // Tables defined in the kernel translation units.

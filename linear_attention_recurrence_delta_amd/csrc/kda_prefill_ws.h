@@ -57,7 +57,7 @@
 
 namespace kda {
 
-template <int NCW, int TPW, int NSA, bool FUSED = false>
+template <int NCW, int TPW, int NSA, bool FUSED = false, bool GATE = false>
 struct WsCfg {
     static constexpr int D = 128;
     static constexpr int C = 16;
@@ -118,7 +118,18 @@ struct WsCfg {
     static constexpr int RAW_STEP = 4 * 2 * PD;      // LDS bytes per raw load
     static constexpr size_t OFFV = OFFA + 2 * SA;
     static constexpr size_t OFFR = OFFV + 2 * SV;
-    static constexpr size_t LDS = OFFR + 2 * SR;
+    // Output gate (GATE): per chunk slot the consumer waves' partial sums of
+    // squares [16 tokens][NCW waves] and their bf16 o tiles (64 lanes x 16 B
+    // per wave), 2-deep; the RMSNorm weight of the slab's columns.
+    // The gate factors Sigmoid(gate) * weight reach a 2-deep [C][PGT] fp32
+    // tile from the stage-A waves.
+    static constexpr size_t G_PART = OFFR + 2 * SR;
+    static constexpr size_t G_OST = G_PART + (GATE ? 2 * 4 * C * NCW : 0);
+    static constexpr size_t G_W = G_OST + (GATE ? 2 * 1024 * NCW : 0);
+    static constexpr int PGT = DVW + 4;              // fp32 pitch of the gate factor tile
+    static constexpr size_t SGT = al16(4 * C * PGT);
+    static constexpr size_t G_GT = G_W + (GATE ? 4 * DVW : 0);
+    static constexpr size_t LDS = G_GT + (GATE ? 2 * SGT : 0);
 
     static_assert(DVW <= D && D % DVW == 0, "value slab");
     static constexpr int LPW = 16 / NSA;             // raw loads per stage-A wave and chunk
@@ -130,6 +141,7 @@ struct WsCfg {
     static_assert(VLB == VCB * VCH && (VCH == 1 || VCH == 2 || VCH == 4), "V tile split over the Gram wave");
     static_assert(PA % 4 == 0, "rows of A^T are read as float4");
     static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(!GATE || (DVW == D && TPW == 2 && !FUSED), "the fused gate needs whole heads");
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -290,9 +302,9 @@ __device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
 // end state is wanted, so, as with CKB, no readout and no o; q is not read
 // either (its loads use an empty range: no memory request), and the start
 // state may be the identity and v zero (the M half of a map).
-template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG, bool MAP>
+template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG, bool MAP, bool GATE>
 __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk, char* smem) {
-    typedef WsCfg<NCW, TPW, NSA, FUSED> Cfg;
+    typedef WsCfg<NCW, TPW, NSA, FUSED, GATE> Cfg;
     typedef Elem<bf16_t> E;
     typedef uint2 Frag;
     constexpr int D = Cfg::D, C = Cfg::C, NCB = Cfg::NCB, DVW = Cfg::DVW, IPW = Cfg::IPW;
@@ -400,6 +412,37 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         const int64_t bbase = (t_begin + (int64_t)cc * C) * H + h;
         const auto rb = rsrc(p.beta + bbase, (p.T_total * H - bbase) * 4);
         R.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lb, 0, 0));
+    };
+    // Gate logits (GATE): each stage-A wave carries 8 bytes per lane of a
+    // chunk's [C][DVW] bf16 gate tile (rows 2 sa and 2 sa + 1, 4 columns per
+    // lane) from HBM into gate slot (c & 1): loaded in iteration c + 2,
+    // parked in c + 3, read by the consumers' gated store in c + 4; the slot
+    // is next written (chunk c + 2) in c + 5.  Chunks outside the sequence
+    // read zeros without a memory request and are not parked.
+    const int gt_row = 2 * sa + (lane >> 5), gt_col = 4 * (lane & 31);
+    auto load_gt = [&](int c) -> u32x2 {
+        const bool in = c >= 0 && c < nch;
+        const int cc = in ? c : 0;
+        const int64_t base = chunk_base(cc) + z * DVW;
+        const auto rg = rsrc(static_cast<const bf16_t*>(p.gate) + base, (n_tok_elems - base) * 2);
+        const uint32_t off = in ? ((uint32_t)gt_row * (uint32_t)(H * D) + (uint32_t)gt_col) * 2u : 0x80000000u;
+        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, off, 0, 0));
+    };
+    // Parked as the gate factor Sigmoid(gate) * weight of each column (fp32),
+    // so the consumers' gated store only multiplies.
+    auto park_gt = [&](int c, u32x2 x) {
+        if (c >= 0 && c < nch) {
+            const float* wt = reinterpret_cast<const float*>(smem + Cfg::G_W) + gt_col;
+            f32x4 f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t wd = x[e >> 1];
+                const float gl = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+                f[e] = wt[e] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gl));
+            }
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(smem + Cfg::G_GT + (size_t)(c & 1) * Cfg::SGT) +
+                                      gt_row * Cfg::PGT + gt_col) = f;
+        }
     };
     // Raw tile of chunk c (two slots in rotation).
     auto raw_slot = [&](int c) { return smem + Cfg::OFFR + (size_t)(c & 1) * Cfg::SR; };
@@ -678,6 +721,39 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 
     // ------------------------------------------------------------ consumers
     const uint32_t o_voff = (uint32_t)l16 * (uint32_t)(H * D) * 2u + (uint32_t)(col_base + 4 * TPW * g4) * 2u;
+    // Output gate (GATE): chunk c is gated one iteration after it is formed,
+    // when its rows' sums of squares over all consumer waves are in LDS (the
+    // gate logits are there too, brought by the stage-A waves).
+    auto finish_gate = [&](int c) {
+        // y = Sigmoid(gate) * o / sqrt(mean over the head's d_v of o^2 + eps)
+        // * weight ("Understanding Kimi K3's attention", output equation), o
+        // as rounded to the output dtype (the value a separate pass would read).
+        // Called in every iteration, c < 0 included (before the first chunk
+        // is formed: its store goes out of range and is dropped), so that
+        // no branch separates it from the consume that follows.
+        const bool real = c >= 0;
+        if (c < 0) c = 0;
+        const int nv = rows_valid(c);
+        const float* part = reinterpret_cast<const float*>(smem + Cfg::G_PART) + ((c & 1) * C + l16) * NCW;
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < NCW; ++i) ss += part[i];
+        const float rinv = __builtin_amdgcn_rsqf(ss * (1.f / D) + p.gate_eps);
+        const u32x4 ov = *reinterpret_cast<const u32x4*>(smem + Cfg::G_OST + ((c & 1) * NCW + w) * 1024 + lane * 16);
+        const float* gf = reinterpret_cast<const float*>(smem + Cfg::G_GT + (size_t)(c & 1) * Cfg::SGT) +
+                          l16 * Cfg::PGT + (col_base - z * DVW) + 8 * g4;
+        const f32x4 f0 = *reinterpret_cast<const f32x4*>(gf), f1 = *reinterpret_cast<const f32x4*>(gf + 4);
+        const float fv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+        u32x4 yv;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            const float lo = __uint_as_float(ov[wd] << 16), hi = __uint_as_float(ov[wd] & 0xffff0000u);
+            yv[wd] = pack_bf16x2(lo * rinv * fv[2 * wd], hi * rinv * fv[2 * wd + 1]);
+        }
+        const int64_t e0 = chunk_base(c);
+        const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
+        __builtin_amdgcn_raw_buffer_store_b128(yv, ro, (real && l16 < nv) ? o_voff : 0x80000000u, 0, 0);
+    };
     auto consume = [&](int c, f32x4 (&Sm)[TPW][NCB]) {
         [[maybe_unused]] const int nv = rows_valid(c);
         char* s4 = slot4(c);
@@ -779,7 +855,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             }
         // One store per lane; rows past the end of the sequence get an offset
         // beyond the buffer's range, and buffer stores out of range are dropped.
-        if constexpr (!NOOUT) {
+        if constexpr (!NOOUT && !GATE) {
             const int64_t e0 = chunk_base(c);
             const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
             const uint32_t oo = l16 < nv ? o_voff : 0x80000000u;
@@ -787,6 +863,23 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
             else
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{ov[0][0], ov[0][1]}, ro, oo, 0, 0);
+        }
+        if constexpr (GATE) {
+            // this wave's share of each row's sum of squares (its 32 columns:
+            // 8 per lane, then the 4 lanes of a row) and the o tile, parked for
+            // the next iteration
+            const u32x4 o4 = {ov[0][0], ov[0][1], ov[1][0], ov[1][1]};
+            float ss = 0.f;
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+                const float lo = __uint_as_float(o4[wd] << 16), hi = __uint_as_float(o4[wd] & 0xffff0000u);
+                ss += lo * lo;
+                ss += hi * hi;
+            }
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (g4 == 0) reinterpret_cast<float*>(smem + Cfg::G_PART)[((c & 1) * C + l16) * NCW + w] = ss;
+            *reinterpret_cast<u32x4*>(smem + Cfg::G_OST + ((c & 1) * NCW + w) * 1024 + lane * 16) = o4;
         }
     };
 
@@ -798,7 +891,8 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     // of different roles never overlap.  The stage-A and Gram loops are
     // unrolled twice so their two prefetch register sets have fixed names.
     if (nch > 0) {
-        const int iters = nch + 3;
+        // (GATE: one more iteration, for the gated store of the last chunk)
+        const int iters = nch + 3 + (GATE ? 1 : 0);
         if (is_stageA) {
             // Iteration j requests chunk j + 3, works on chunk j (already in
             // registers), parks chunk j + 2 (requested one iteration earlier)
@@ -810,6 +904,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             // that ends iteration c - 1.
             LoadSet<LPW> rawA, rawB;
             RawSet<IPW> cur;
+            [[maybe_unused]] u32x2 gtA = {0u, 0u}, gtB = {0u, 0u};
             load_raw(0, rawA);
             load_raw(1, rawB);
             park_raw(0, rawA);
@@ -820,14 +915,18 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             __syncthreads();  // prologue 2: chunk 1 parked, chunk 0 read
             for (int j = 0; j < iters; j += 2) {
                 load_raw(j + 3, rawB);
+                if constexpr (GATE) gtB = load_gt(j - 2);
                 if (j < nch) stage_a(j, cur);
                 park_raw(j + 2, rawA);
+                if constexpr (GATE) park_gt(j - 3, gtA);
                 fetch_raw(j + 1, cur);
                 __syncthreads();
                 if (j + 1 < iters) {
                     load_raw(j + 4, rawA);
+                    if constexpr (GATE) gtA = load_gt(j - 1);
                     if (j + 1 < nch) stage_a(j + 1, cur);
                     park_raw(j + 3, rawB);
+                    if constexpr (GATE) park_gt(j - 2, gtB);
                     fetch_raw(j + 2, cur);
                     __syncthreads();
                 }
@@ -894,10 +993,18 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             // vector-register limit in the 14-wave workgroup)
             const int ck0 = p.ckpt ? __builtin_amdgcn_readfirstlane((int)ckpt_first_slot(p, n, lane)) : 0;
             const int ck_chunks = p.ckpt ? p.ckpt_interval / C : 1;
+            if constexpr (GATE) {
+                // the slab's RMSNorm weights, read before the first gated store
+                // (two barriers away)
+                if (w == 0)
+                    for (int i = lane; i < DVW; i += 64)
+                        reinterpret_cast<float*>(smem + Cfg::G_W)[i] = p.gate_weight[z * DVW + i];
+            }
             __syncthreads();
             __syncthreads();
             for (int j = 0; j < iters; ++j) {
-                if (j - 3 >= 0) {
+                if constexpr (GATE) finish_gate(j - 4);
+                if (j - 3 >= 0 && j - 3 < nch) {
                     consume(j - 3, Sm);
                     const int c = j - 3;
                     if (p.ckpt && (c + 1) % ck_chunks == 0 && (int64_t)(c + 1) * C <= ntok) {
@@ -966,9 +1073,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     }
 }
 
-template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG>
+template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG, bool GATE>
 __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
-    typedef WsCfg<NCW, TPW, NSA, FUSED> Cfg;
+    typedef WsCfg<NCW, TPW, NSA, FUSED, GATE> Cfg;
     __shared__ __align__(16) char smem[Cfg::LDS];
     // XCD-aware block order (ws_resolve); padding blocks exit at once.  The
     // work description is uniform: pinned to scalar registers (integer
@@ -986,18 +1093,18 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     wk.v_zero = __builtin_amdgcn_readfirstlane((int)wk.v_zero) != 0;
     if constexpr (SEG) {
         if (__builtin_amdgcn_readfirstlane((int)!wk.store_o)) {
-            ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, true>(p, wk, smem);
+            ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, true, false>(p, wk, smem);
             return;
         }
     }
-    ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, false>(p, wk, smem);
+    ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, false, GATE>(p, wk, smem);
 }
 
-template <int NCW, int TPW, int NSA, bool FUSED = false, bool CKB = false, bool SEG = false>
+template <int NCW, int TPW, int NSA, bool FUSED = false, bool CKB = false, bool SEG = false, bool GATE = false>
 hipError_t launch_prefill_ws(const PrefillParams& p, hipStream_t s) {
     if (!SEG && p.seg_phase != 0) return hipErrorInvalidValue;
     const int64_t blocks = ws_grid_blocks(p);  // whole groups of 8 items
-    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA, FUSED, CKB, SEG>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA, FUSED, CKB, SEG, GATE>), dim3((unsigned)blocks),
                        dim3(64 * (NCW + 2 + NSA)), 0, s, p);
     return hipGetLastError();
 }

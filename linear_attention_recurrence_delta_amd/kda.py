@@ -335,6 +335,37 @@ def kda_output_gate(o, gate, weight, *, eps: float = 1e-6, out=None):
     return y
 
 
+def kda_prefill_output_gated(q, k, v, g, beta, gate, weight, initial_state=None, cu_seqlens=None, *,
+                             eps: float = 1e-6, chunk_size: int = 0, scale: float = 1.0,
+                             output_final_state: bool = True, num_seqs: int | None = None, out=None,
+                             final_state=None):
+    """kda_prefill followed by y = sigmoid(gate) * RMSNorm(o) * weight, with y
+    returned in place of o (fused into the o store where a workgroup holds a
+    whole head).  gate: [T, H, d_v] in q's dtype; weight: fp32 [d_v].
+    Returns (y, final_state)."""
+    a = _prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, out, output_final_state, final_state)
+    if a["dense_batch"]:
+        gate = gate.view(-1, *gate.shape[2:]) if gate.is_contiguous() else gate
+    _need(gate, "gate", a["q"].dtype, 3)
+    _need(weight, "weight", torch.float32, 1)
+    if tuple(gate.shape) != (a["T"], a["H"], a["dv"]) or gate.device != a["dev"]:
+        raise ValueError("gate must be [T, H, d_v] on q's device")
+    if weight.shape[0] != a["dv"] or weight.device != a["dev"]:
+        raise ValueError("weight must have d_v entries on q's device")
+    desc = _desc(a, chunk_size, scale)
+    ws, ws_bytes = _workspace(a, desc, cu_seqlens is not None)
+    with torch.cuda.device(a["dev"]):
+        _check(lib().kda_prefill_output_gated(
+            a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dt"], chunk_size, float(scale),
+            _ptr(a["q"]), _ptr(a["k"]), _ptr(a["v"]), _ptr(a["g"]), _ptr(a["beta"]), _ptr(initial_state),
+            _ptr(cu_seqlens), _ptr(gate), _ptr(weight), float(eps), _ptr(a["o"]), _ptr(a["fs"]),
+            _ptr(ws), ws_bytes, _stream(a["dev"])))
+    y = a["o"]
+    if a["dense_batch"]:
+        y = y.view(a["N"], a["T"] // max(a["N"], 1), a["H"], a["dv"])
+    return y, a["fs"]
+
+
 def kda_prefill_backward_supported(dtype: torch.dtype, d_k: int, d_v: int) -> bool:
     return bool(lib().kda_prefill_backward_supported(_DTYPES[dtype], d_k, d_v)) if dtype in _DTYPES else False
 
