@@ -42,6 +42,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, published
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256
 # The fused entry reads bf16 decay logits z (256) instead of fp32 g.
 FUSED_BYTES_PER_TOKEN_HEAD = 3 * 256 + 256 + 4 + 256
+# Gated prefill: the gate logits (256) are read too; y (256) replaces o.
+GATED_BYTES_PER_TOKEN_HEAD = PREFILL_BYTES_PER_TOKEN_HEAD + 256
 # Backward: each input and output once -- q, k, v, g, beta and d_o read (1540),
 # dq, dk, dv, dg and dbeta written (3 x 256 + 512 + 4).
 BWD_IO_BYTES_PER_TOKEN_HEAD = 3 * 256 + 512 + 4 + 256 + 3 * 256 + 512 + 4
@@ -58,18 +60,25 @@ def log(*a):
 
 
 # Sources each measured kernel is compiled from; a counter record is used only
-# while these files are unchanged.
-# csrc/ files a record depends on; "flags:<file>" stands for the extra compiler
-# flags build_lib.py gives that translation unit.
+# while these are unchanged: the kernel's headers and translation units, the
+# C-ABI layer (it picks the kernel variant, slab width and segment plan),
+# "flags:<file>" = the extra compiler flags build_lib.py gives that
+# translation unit, and "build" = the flags every file is compiled with.
+_PREFILL = ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "kda_bounds.h", "kda_abi.cpp", "build")
 KERNEL_SOURCES = {
-    "kda_prefill_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "flags:kda_prefill_ws_ilp.hip"),
-    "kda_prefill_k3_varlen_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h", "flags:kda_prefill_bf16.hip"),
-    "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h", "flags:kda_decode.hip"),
-    "kda_prefill_fused_k3_dense_32k": ("kda_prefill_ws.h", "kda_device.h", "kda_internal.h",
-                                       "flags:kda_prefill_ws_ilp.hip"),
-    "kda_output_gate_32k_x96": ("kda_output_gate.hip", "kda_device.h", "kda_internal.h"),
-    "kda_backward_k3_dense_32k": ("kda_backward.hip", "kda_backward.h", "kda_device.h", "kda_prefill_ws.h",
-                                  "flags:kda_backward.hip", "flags:kda_prefill_ws_ilp.hip"),
+    "kda_prefill_k3_dense_32k": _PREFILL + ("kda_prefill_ws_ilp.hip", "flags:kda_prefill_ws_ilp.hip"),
+    "kda_prefill_k3_varlen_32k": _PREFILL + ("kda_prefill_bf16.hip", "flags:kda_prefill_bf16.hip"),
+    "kda_prefill_gated_k3_varlen_32k": _PREFILL + ("kda_prefill_bf16.hip", "flags:kda_prefill_bf16.hip"),
+    "kda_prefill_long_1m_h16": _PREFILL + ("kda_prefill_bf16.hip", "kda_segment.hip", "flags:kda_prefill_bf16.hip",
+                                           "flags:kda_segment.hip"),
+    "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h", "kda_bounds.h", "kda_abi.cpp",
+                          "build", "flags:kda_decode.hip"),
+    "kda_prefill_fused_k3_dense_32k": _PREFILL + ("kda_prefill_ws_ilp.hip", "flags:kda_prefill_ws_ilp.hip"),
+    "kda_output_gate_32k_x96": ("kda_output_gate.hip", "kda_device.h", "kda_internal.h", "kda_bounds.h",
+                                "kda_abi.cpp", "build"),
+    "kda_backward_k3_dense_32k": _PREFILL + ("kda_backward.hip", "kda_backward.h", "kda_prefill_ws_ilp.hip",
+                                             "kda_prefill_bf16.hip", "flags:kda_backward.hip",
+                                             "flags:kda_prefill_ws_ilp.hip"),
 }
 
 
@@ -78,7 +87,9 @@ def kernel_source_digest(kernel):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_recurrence_delta_amd", "csrc")
     for f in KERNEL_SOURCES[kernel]:
-        if f.startswith("flags:"):
+        if f == "build":
+            h.update(repr((build_lib.COMMON, build_lib.DEVICE)).encode())
+        elif f.startswith("flags:"):
             h.update(repr(build_lib.PER_FILE.get(f[len("flags:"):], [])).encode())
         else:
             h.update(open(os.path.join(csrc, f), "rb").read())
@@ -155,6 +166,25 @@ def time_launches(fn, reps, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def host_description():
+    """CPU model, logical CPUs of the host and CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(w, target_s):
     """The fp64 oracle, as it stands, on a bounded sample of the dense workload.
 
@@ -192,6 +222,7 @@ def cpu_baseline(w, target_s):
         "unit": "tokens/s",
         "cores": min(nh, threads),
         "kind": "oracle",
+        "host": host_description(),
         "sample": "%d run(s) of the first %d tokens x %d of the %d heads of the dense workload, %.1f s "
                   "of fp64 token-by-token recurrence on %d OpenMP threads; tokens/s = token-heads/s / %d heads"
                   % (reps, T_s, nh, H, total, min(nh, threads), H),
@@ -273,6 +304,26 @@ def main():
         dense_ms = time_launches(run_dense, args.steps, stream)
         wall_s = time.perf_counter() - t0
         varlen_ms = time_launches(run_varlen, args.steps, stream)
+        # the varlen pack through the gated entry: y = sigmoid(gate) * RMSNorm(o) * weight
+        # fused into the o store (whole-head workgroups), and the same as two passes
+        gen_g = torch.Generator(device=dev)
+        gen_g.manual_seed(9)
+        gv_gate = torch.randn(wv["v"].shape, generator=gen_g, device=dev).to(torch.bfloat16)
+        gv_w = torch.ones(wv["d"], device=dev)
+        y_v = torch.empty_like(wv["v"])
+
+        def run_gated():
+            kda.kda_prefill_output_gated(wv["q"], wv["k"], wv["v"], wv["g"], wv["beta"], gv_gate, gv_w, None, wv["cu"],
+                                         chunk_size=C, out=y_v, final_state=s_v)
+
+        def run_two_pass():
+            run_varlen()
+            kda.kda_output_gate(o_v, gv_gate, gv_w, eps=1e-6, out=y_v)
+
+        run_gated()
+        gated_ms = time_launches(run_gated, args.steps, stream)
+        two_pass_ms = time_launches(run_two_pass, args.steps, stream)
+        del gv_gate, y_v
         # the dense workload again with a state checkpoint every 1024 tokens
         ck_interval = 1024
         ck_buf = torch.empty((wd["T"] // ck_interval, wd["H"], wd["d"], wd["d"]), dtype=torch.float32, device=dev)
@@ -384,6 +435,16 @@ def main():
                              "bytes_per_launch": 3 * o_d.numel() * 2},
             },
             "prefill_backward": None if bw_ms is None else backward_entry(bw_ms, token_heads, wd["T"]),
+            "prefill_gated": {
+                "workload": "k3_varlen_32k through kda_prefill_output_gated: y = sigmoid(gate) * RMSNorm(o) * weight "
+                            "fused into the o store (whole-head workgroups); two_pass = kda_prefill then kda_output_gate",
+                "ms": sum(gated_ms) / len(gated_ms),
+                "vs_plain_varlen": (sum(gated_ms) / len(gated_ms)) / v_avg,
+                "two_pass_ms": sum(two_pass_ms) / len(two_pass_ms),
+                "bytes_per_token_head": GATED_BYTES_PER_TOKEN_HEAD,
+                "hbm_gbs": GATED_BYTES_PER_TOKEN_HEAD * wv["T"] * wv["H"] / (sum(gated_ms) / len(gated_ms) * 1e-3) / 1e9,
+                "traffic": measured_traffic("kda_prefill_gated_k3_varlen_32k"),
+            },
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
                 "hbm_gbs": PREFILL_BYTES_PER_TOKEN_HEAD * wv["T"] * wv["H"] / (v_avg * 1e-3) / 1e9,
@@ -408,10 +469,20 @@ def main():
         l_avg = sum(long_ms) / len(long_ms)
         l_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * wl["T"] * wl["H"]
         log("long prefill avg %.3f ms" % l_avg)
+        ws_l = kda.kda_prefill_ex_workspace_bytes(wl["N"], wl["T"], wl["H"], wl["d"], wl["d"], torch.bfloat16, C)
+        units_l = wl["N"] * wl["H"]
+        segs = ws_l // (units_l * 2 * wl["d"] * wl["d"] * 4) + 1 if ws_l else 1
         result["prefill_long_1m"] = {
             "workload": "long_1m_h16: B=1 T=1048576 H=16 d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state",
             "tokens_per_s": wl["T"] / (l_avg * 1e-3), "ms": l_avg, "runs": args.long_steps,
             "hbm_gbs": l_bytes / (l_avg * 1e-3) / 1e9,
+            "plan": {"segments_per_sequence": segs, "workspace_bytes": ws_l,
+                     "launches": "segment maps + segment 0, combine, segments 1.. again" if segs > 1 else "direct"},
+            "roofline": {"bound": "hbm", "achieved": l_bytes / (l_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": l_bytes / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("kda_prefill_long_1m_h16"),
+                         "kernel": "kda_prefill_ws_kernel<4,2,8,...,SEG> x 2 + kda_segment_combine_kernel (whole call)",
+                         "bytes_per_launch": l_bytes},
         }
         del wl, o_l, s_l
         torch.cuda.empty_cache()
@@ -474,7 +545,8 @@ def main():
                              "gbs": 2 * src.numel() * 4 / (min(copy_ms) * 1e-3) / 1e9,
                              "note": "best of 5 torch copy_ launches of 2 GiB (read + write bytes)"}
     del src, dst
-    for key in ("roofline", "mfma", "prefill_varlen", "prefill_checkpoints", "prefill_fused", "output_gate",
+    for key in ("roofline", "mfma", "prefill_varlen", "prefill_gated", "prefill_checkpoints", "prefill_fused",
+                "output_gate",
                 "prefill_backward",
                 "prefill_long_1m", "decode", "device_copy"):
         if key in result:
