@@ -153,10 +153,15 @@ def backward_entry(bw_ms, token_heads, T):
     }
 
 
-def time_launches(fn, reps, stream):
-    """Run fn reps times; return per-launch ms from events on `stream`."""
+def time_launches(fn, reps, stream, warmup=0):
+    """Run fn `warmup` times untimed, then reps times; return per-launch ms from
+    events on `stream`.  Each timed workload gets its own warm-up right before
+    it: after a change of workload the device's clocks take about ten launches
+    of the dense prefill to settle (first launch about 1.96 ms, then 1.75 ms)."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     for a, b in evs:
         a.record(stream)
@@ -298,12 +303,11 @@ def main():
         token_heads = wd["T"] * wd["H"]
         for _ in range(args.warmup):
             run_dense()
-            run_varlen()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         dense_ms = time_launches(run_dense, args.steps, stream)
         wall_s = time.perf_counter() - t0
-        varlen_ms = time_launches(run_varlen, args.steps, stream)
+        varlen_ms = time_launches(run_varlen, args.steps, stream, args.warmup)
         # the varlen pack through the gated entry: y = sigmoid(gate) * RMSNorm(o) * weight
         # fused into the o store (whole-head workgroups), and the same as two passes
         gen_g = torch.Generator(device=dev)
@@ -320,9 +324,8 @@ def main():
             run_varlen()
             kda.kda_output_gate(o_v, gv_gate, gv_w, eps=1e-6, out=y_v)
 
-        run_gated()
-        gated_ms = time_launches(run_gated, args.steps, stream)
-        two_pass_ms = time_launches(run_two_pass, args.steps, stream)
+        gated_ms = time_launches(run_gated, args.steps, stream, args.warmup)
+        two_pass_ms = time_launches(run_two_pass, args.steps, stream, args.warmup)
         del gv_gate, y_v
         # the dense workload again with a state checkpoint every 1024 tokens
         ck_interval = 1024
@@ -335,8 +338,7 @@ def main():
 
         ck_ms = None
         if not args.no_checkpoints:
-            run_dense_ck()
-            ck_ms = time_launches(run_dense_ck, args.steps, stream)
+            ck_ms = time_launches(run_dense_ck, args.steps, stream, args.warmup)
         # the dense workload through the fused entry (gate and q/k norm in the kernel)
         fu_ms = None
         if kda.kda_prefill_fused_supported(torch.bfloat16, wd["d"], wd["d"], C):
@@ -346,8 +348,7 @@ def main():
             def run_fused():
                 kda.kda_prefill_fused(fq, fk, fv, fz, fa, fb, None, None, chunk_size=C, out=o_d, final_state=s_d)
 
-            run_fused()
-            fu_ms = time_launches(run_fused, args.steps, stream)
+            fu_ms = time_launches(run_fused, args.steps, stream, args.warmup)
             del fq, fk, fv, fz, fa, fb
         # the output gate on the dense output (Sigmoid(gate) * RMSNorm(o) * weight)
         og_gate = torch.randn(o_d.shape, device=dev).to(o_d.dtype)
@@ -357,8 +358,7 @@ def main():
         def run_gate():
             kda.kda_output_gate(o_d, og_gate, og_w, eps=1e-6, out=og_y)
 
-        run_gate()
-        og_ms = time_launches(run_gate, args.steps, stream)
+        og_ms = time_launches(run_gate, args.steps, stream, args.warmup)
         del og_gate, og_y
         # the backward pass on the dense workload (forward again for its
         # 16-token states, then the reverse chunk kernel), preallocated buffers
@@ -384,8 +384,7 @@ def main():
                 if st != 0:
                     raise RuntimeError("kda_prefill_backward failed: %d" % st)
 
-            run_bwd()
-            bw_ms = time_launches(run_bwd, args.steps, stream)
+            bw_ms = time_launches(run_bwd, args.steps, stream, max(1, args.warmup // 2))
             del b_do, b_dq, b_dk, b_dv, b_dg, b_db, b_ws
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)

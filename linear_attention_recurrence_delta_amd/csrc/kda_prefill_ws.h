@@ -549,6 +549,10 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 
     // ------------------------------------------------------------ stage A
     auto stage_a = [&](int c, const RawSet<IPW>& R) {
+        // No multiply-add contraction here: contracting the scaling of g
+        // into the first scan step gives a move, a DPP move and an FMA per
+        // value where one DPP add does.
+#pragma clang fp contract(off)
         const int nv = rows_valid(c);
         const bool ok = l16 < nv;
         char* s4 = slot4(c);
