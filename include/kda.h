@@ -123,6 +123,10 @@ size_t kda_prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens,
  *   num_seqs      N >= 0 sequences.
  *   total_tokens  T_total >= 0 tokens over all sequences.
  *   num_heads     H >= 1;  d_k, d_v: head dims (see kda_prefill_supported).
+ *                 16 token rows of all heads must stay below 2^31 bytes in
+ *                 fp32 (H * max(d_k, d_v) * 64 <= INT32_MAX: H <= 262,143 at
+ *                 d = 128), else KDA_ERR_UNSUPPORTED (the kernels address a
+ *                 chunk's rows with 32-bit offsets); T_total <= INT32_MAX.
  *   qkv_dtype     kda_dtype of q, k, v and o.
  *   chunk_size    tokens per chunk (16, 32 or 64), or 0 for the default.
  *   scale         readout scale; 1.0f gives o_t = S_t^T q_t exactly.

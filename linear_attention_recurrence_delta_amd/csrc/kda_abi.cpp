@@ -205,6 +205,12 @@ kda_prefill_desc flat_desc(int32_t num_seqs, int64_t total_tokens, int32_t num_h
     return d;
 }
 
+// The kernels address 16 token rows of one chunk with 32-bit byte offsets:
+// 16 rows of H heads x max(d_k, d_v) fp32 values must stay below 2^31 bytes.
+bool heads_fit(int64_t num_heads, int64_t d_k, int64_t d_v) {
+    return num_heads * (d_k > d_v ? d_k : d_v) * 64 <= INT32_MAX;
+}
+
 bool sizes_valid(const kda_prefill_desc& d) {
     return d.num_seqs >= 0 && d.total_tokens >= 0 && d.num_heads >= 1 && d.d_k >= 1 && d.d_v >= 1;
 }
@@ -213,7 +219,7 @@ bool sizes_valid(const kda_prefill_desc& d) {
 // is absent); 0 for invalid or unsupported descriptions, which the call
 // itself rejects.
 size_t desc_workspace_bytes(const kda_prefill_desc& d, bool dense) {
-    if (!sizes_valid(d) || d.total_tokens > INT32_MAX) return 0;
+    if (!sizes_valid(d) || d.total_tokens > INT32_MAX || !heads_fit(d.num_heads, d.d_k, d.d_v)) return 0;
     if (d.qkv_dtype != KDA_DTYPE_BF16 && d.qkv_dtype != KDA_DTYPE_F32) return 0;
     if (d.d_k != d.d_v) return 0;
     const int C = resolve_chunk(d.qkv_dtype, d.chunk_size);
@@ -250,7 +256,7 @@ static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tens
 
     if (!sizes_valid(d)) return KDA_ERR_BAD_SHAPE;
     if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return KDA_ERR_UNSUPPORTED;
-    if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > INT32_MAX || !heads_fit(num_heads, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0 && total_tokens > 0) return KDA_ERR_BAD_SHAPE;
     if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
     if (d.kernel < KDA_KERNEL_AUTO || d.kernel > KDA_KERNEL_CHUNK_STAGED || d.slab_columns < 0 || d.segments < 0)
@@ -604,7 +610,7 @@ kda_status kda_prefill_backward(int32_t num_seqs, int64_t total_tokens, int32_t 
                                 void* workspace, size_t workspace_bytes, void* stream) {
     if (num_seqs < 0 || total_tokens < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_BAD_SHAPE;
     if (!kda_prefill_backward_supported(dtype, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
-    if (total_tokens > INT32_MAX) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens > INT32_MAX || !heads_fit(num_heads, d_k, d_v)) return KDA_ERR_UNSUPPORTED;
     if (num_seqs == 0 && total_tokens > 0) return KDA_ERR_BAD_SHAPE;
     if (!cu_seqlens && num_seqs > 0 && total_tokens % num_seqs != 0) return KDA_ERR_BAD_SHAPE;
     if ((int64_t)num_seqs * num_heads > INT32_MAX) return KDA_ERR_UNSUPPORTED;

@@ -40,9 +40,10 @@
 // the end of the tensor read as 0) so the compiler's counted waits never
 // collapse to a full drain.  The consumers write each 16-token output tile
 // with one 16-byte store per lane.  Rows past
-// the end of a sequence hold other (finite) tokens or zeros but get g = 0 and
-// beta = 0: then their A rows, Y rows and hence U rows are zero, they change
-// neither the state nor the earlier rows, and their outputs are not stored.
+// the end of a sequence read q = k = g = beta = 0 (the load ranges end with
+// the sequence): then their A rows, Y rows and hence U rows are zero, they
+// change neither the state nor the earlier rows, and their outputs are not
+// stored.
 //
 // Sources for what is computed: as in kda_prefill_impl.h ("Understanding Kimi
 // K3's attention" state-update / readout / g_min equations; "Inside Kimi K3",
@@ -345,8 +346,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     // Element offset of token row 0 of chunk c for head h (uniform per wave).
     auto chunk_base = [&](int c) -> int64_t { return ((t_begin + (int64_t)c * C) * H + h) * D; };
     auto rows_valid = [&](int c) -> int {
-        const int64_t left = ntok - (int64_t)c * C;
-        return left >= C ? C : (int)left;
+        // (32-bit: token counts are below 2^31, so this stays in scalar registers)
+        const int left = (int)ntok - c * C;
+        return left >= C ? C : left;
     };
 
     // ------------------------------------------------------------ role setup
@@ -360,17 +362,25 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 
 
     // Global reads of the per-chunk inputs are buffer loads: a wave-uniform
-    // resource per chunk (base = the chunk's first token row for this head,
-    // size = the bytes left to the end of the tensor) and a per-lane byte
-    // offset that is the same for every chunk.  Rows past the end of a
-    // sequence read the next tokens of the tensor (finite by precondition) or,
-    // past its end, zeros; they are masked (g and beta are zeroed, outputs not
-    // stored).  No per-lane address is recomputed per chunk, so issuing the
-    // next chunk's loads never waits on the registers of loads in flight.
+    // resource per chunk (base = the chunk's first token row for this head)
+    // and a per-lane byte offset that is the same for every chunk.  For q, k,
+    // g (or z) and beta the resource ends with the chunk's last row in the
+    // sequence (or segment), so rows past it read zeros without a memory
+    // request: g = beta = 0 there, which makes them identity transitions
+    // (fused: z = 0 is not g = 0, so g is zeroed there explicitly); their
+    // outputs are not stored.  V reads end with the tensor (their rows past
+    // the sequence meet beta = 0).  No per-lane address is recomputed per
+    // chunk, so issuing the next chunk's loads never waits on the registers
+    // of loads in flight.
     const int64_t n_tok_elems = p.T_total * H * D;  // elements of q, k, g (and v)
     auto rsrc = [](const void* base, int64_t bytes_left) {
         const int num = bytes_left > 0x7fffffff ? 0x7fffffff : (int)bytes_left;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num, 0x00020000);
+    };
+    // The same for ranges inside one chunk (at most 16 token rows of H heads:
+    // below 2^31 bytes, which the host checks), in 32-bit scalar arithmetic.
+    auto rsrc_chunk = [](const void* base, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
     };
     // Raw q, k, g, beta of chunk c.  A chunk is 16 loads of 16 B per lane
     // over whole token rows: units 0-3 the q tile and 4-7 the k tile (4 rows
@@ -405,12 +415,14 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     auto load_raw = [&](int c, LoadSet<LPW>& R) {
         const int cc = c < nch ? c : nch - 1;
         const int64_t e0 = chunk_base(cc);
-        const auto r = rsrc(ld_base + e0 * ld_es, (n_tok_elems - e0) * ld_es);
+        // the ranges end with the chunk's last row in the sequence: later rows read 0
+        const int nv = rows_valid(cc);
+        const auto r = rsrc_chunk(ld_base + e0 * ld_es, ((nv - 1) * H * D + D) * ld_es);
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
             R.x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ld_voff + i * ld_step, 0, 0));
         const int64_t bbase = (t_begin + (int64_t)cc * C) * H + h;
-        const auto rb = rsrc(p.beta + bbase, (p.T_total * H - bbase) * 4);
+        const auto rb = rsrc_chunk(p.beta + bbase, ((nv - 1) * H + 1) * 4);
         R.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lb, 0, 0));
     };
     // Gate logits (GATE): each stage-A wave carries 8 bytes per lane of a
@@ -507,8 +519,8 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     };
 
     // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / VCPR,
-    // VCB / 2 bf16 columns (buffer loads as above; rows past the end of the
-    // sequence have beta = 0).
+    // VCB / 2 bf16 columns (buffer loads as above, the range ending with the
+    // chunk's last row in the sequence).
     typedef typename std::conditional<Cfg::VCB == 16, u32x4, u32x2>::type VChunk;
     constexpr int VCOL = Cfg::VCB / 2;  // bf16 columns per chunk
     constexpr int VCPR = DVW / VCOL;    // chunks per row
@@ -519,7 +531,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     auto v_load = [&](int c, int i) -> VChunk {
         const int cc = c < 0 ? 0 : (c < nch ? c : nch - 1);
         const int64_t base = chunk_base(cc) + z * DVW;
-        const auto rv = rsrc(gv + base, w_v_zero ? 0 : (n_tok_elems - base) * 2);
+        const auto rv = rsrc_chunk(gv + base, w_v_zero ? 0 : ((rows_valid(cc) - 1) * H * D + DVW) * 2);
         if constexpr (Cfg::VCB == 16)
             return __builtin_bit_cast(VChunk, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off(i), 0, 0));
         else
@@ -553,8 +565,6 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         // into the first scan step gives a move, a DPP move and an FMA per
         // value where one DPP add does.
 #pragma clang fp contract(off)
-        const int nv = rows_valid(c);
-        const bool ok = l16 < nv;
         char* s4 = slot4(c);
         bf16_t* QB = reinterpret_cast<bf16_t*>(s4 + Cfg::S4_QB);
         bf16_t* KB = reinterpret_cast<bf16_t*>(s4 + Cfg::S4_KB);
@@ -565,13 +575,14 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         constexpr float LOG2E = 1.4426950408889634f;
         // Cumulative log-decay in base-2 units, all items and channels
         // interleaved so the dependent DPP steps of one scan overlap the others.
-        // Rows past the end of the sequence get g = 0 through the same multiply.
+        // Rows past the end of the sequence read g = 0.
         float L[IPW][4];
         if constexpr (FUSED) {
             // g = g_min Sigmoid(e^{A_h} z), g_min = -5 ("Understanding Kimi
             // K3's attention", gate equation), in base-2 units:
             // log2(e) g = -5 log2(e) / (1 + 2^{-log2(e) e^{A_h} z}).
-            const float gscale = ok ? -5.f * LOG2E : 0.f;
+            // Rows past the end read z = 0, which is not g = 0: zeroed here.
+            const float gscale = l16 < rows_valid(c) ? -5.f * LOG2E : 0.f;
 #pragma unroll
             for (int it = 0; it < IPW; ++it)
 #pragma unroll
@@ -580,13 +591,12 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                     L[it][ch] = gscale * __builtin_amdgcn_rcpf(1.f + t);
                 }
         } else {
-            const float lscale = ok ? LOG2E : 0.f;
 #pragma unroll
             for (int it = 0; it < IPW; ++it) {
-                L[it][0] = R.g[it][0] * lscale;
-                L[it][1] = R.g[it][1] * lscale;
-                L[it][2] = R.g[it][2] * lscale;
-                L[it][3] = R.g[it][3] * lscale;
+                L[it][0] = R.g[it][0] * LOG2E;
+                L[it][1] = R.g[it][1] * LOG2E;
+                L[it][2] = R.g[it][2] * LOG2E;
+                L[it][3] = R.g[it][3] * LOG2E;
             }
         }
 #pragma unroll
@@ -636,7 +646,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             if (l16 == 15)  // e^{L_15} is the decay of the whole chunk
                 *reinterpret_cast<float4*>(GAM + c0) = make_float4(e1[0], e1[1], e1[2], e1[3]);
         }
-        if (sa == 0 && lane < C) BETA[lane] = ok ? R.beta : 0.f;
+        if (sa == 0 && lane < C) BETA[lane] = R.beta;
     };
 
     // ------------------------------------------------------------ Gram tiles
@@ -857,12 +867,11 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 Sm[t][ct][2] *= gm[ct].z;
                 Sm[t][ct][3] *= gm[ct].w;
             }
-        // One store per lane; rows past the end of the sequence get an offset
-        // beyond the buffer's range, and buffer stores out of range are dropped.
+        // One store per lane; the range ends with the chunk's last row in the
+        // sequence, and buffer stores out of range are dropped.
         if constexpr (!NOOUT && !GATE) {
-            const int64_t e0 = chunk_base(c);
-            const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
-            const uint32_t oo = l16 < nv ? o_voff : 0x80000000u;
+            const auto ro = rsrc_chunk(go + chunk_base(c), ((nv - 1) * H * D + D) * 2);
+            const uint32_t oo = o_voff;
             if constexpr (TPW == 2)
                 __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
             else
@@ -1011,7 +1020,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 if (j - 3 >= 0 && j - 3 < nch) {
                     consume(j - 3, Sm);
                     const int c = j - 3;
-                    if (p.ckpt && (c + 1) % ck_chunks == 0 && (int64_t)(c + 1) * C <= ntok) {
+                    if (p.ckpt && (c + 1) % ck_chunks == 0 && (c + 1) * C <= (int)ntok) {
                         const int64_t slot = (int64_t)ck0 + (c + 1) / ck_chunks - 1;
                         if (slot < p.ckpt_cap) {
                             if constexpr (CKB) {

@@ -108,6 +108,10 @@ def test_prefill_validation(lib):
     assert _prefill(lib, C=48) == UNSUP
     assert _prefill(lib, dt=5) == UNSUP
     assert _prefill(lib, T=1 << 31) == UNSUP
+    # 16 token rows of every head (fp32, d = 128) must stay below 2^31 bytes
+    # (q = NULL: the call stops at the pointer checks, which come after the size checks)
+    assert _prefill(lib, N=1, T=16, H=262143, q=None) == NULLP
+    assert _prefill(lib, N=1, T=16, H=262144, q=None) == UNSUP
     assert _prefill(lib, q=None) == NULLP
     assert _prefill(lib, beta=None) == NULLP
     assert _prefill(lib, o=None) == NULLP
@@ -395,6 +399,8 @@ def test_prefill_backward_validation(lib):
     assert _bwd(lib, d=64) == UNSUP
     assert _bwd(lib, N=3) == BAD                        # 32 tokens do not split into 3 equal sequences
     assert _bwd(lib, N=0) == BAD                        # tokens without sequences
+    assert _bwd(lib, H=262144, q=None) == UNSUP         # 16 rows of the heads exceed 2^31 bytes
+    assert _bwd(lib, H=262143, q=None) == NULLP
     for name in ("q", "k", "v", "g", "b", "do", "dq", "dk", "dv", "dg", "db"):
         assert _bwd(lib, **{name: None}) == NULLP, name
     assert _bwd(lib, dq=FAKE + 0x600008) == MISAL
