@@ -10,8 +10,10 @@
 //                          scan), scaled tiles QB = q e^L, KB = k e^L,
 //                          KL = k e^{-L} and its transpose, gamma = e^{L_15},
 //                          beta; requests the raw inputs of chunk c + 3.
-//   Gram      (1 wave)     chunk m + 2: P = incl-lower(QB KL^T) and
-//                          A = strict-lower(diag(beta) KB KL^T) on MFMA:
+//   Gram      (1 wave)     chunk m + 2: P = scale incl-lower(QB KL^T) and
+//                          A = strict-lower(diag(beta) KB KL^T) on MFMA
+//                          (and parks V of chunk m + 1, as beta V in fp32
+//                          for slabs of up to 64 columns):
 //                          e^{L_r - L_s} = e^{L_r} e^{-L_s} with
 //                          e^{L_r} in [e^-80, 1] and e^{-L_s} in [1, e^80]
 //                          (a 16-token tile decays by at least -80), so no
@@ -19,7 +21,7 @@
 //   solve     (1 wave)     chunk m + 1: T = (I + A)^{-1} by a column sweep
 //                          (fp32; 15-way independent updates per step).
 //   consumers (NCW waves)  chunk m: X = Kt S, Qt S, U = T diag(beta)(V - X),
-//                          O = Qt S + P U, S <- Diag(gamma)(S + KL^T U)
+//                          O = scale Qt S + P U, S <- Diag(gamma)(S + KL^T U)
 //                          (= Diag(gamma) S + Kbar^T U, Kbar = k e^{tot-L}:
 //                          the decay of each contribution is applied to the
 //                          sum, which is also exact up to relative rounding
@@ -90,8 +92,13 @@ struct WsCfg {
     static constexpr size_t S2 = S2_KL + al16(2 * C * PD);
     static constexpr size_t SP = al16(2 * C * PK);   // P (3-deep) and T (2-deep)
     static constexpr size_t SA = al16(4 * C * PA);   // A^T (2-deep)
-    static constexpr int PV = DVW + 8;               // bf16 pitch of the V tile
-    static constexpr size_t SV = al16(2 * C * PV);   // V tile (2-deep)
+    // V tile (2-deep): for slabs of up to 64 columns the Gram wave parks
+    // beta V in fp32 (VF), taking that multiply off the consumers; the
+    // 128-column kernel, whose Gram wave shares a SIMD with a consumer, keeps
+    // the bf16 tile and its consumers form beta v (the same arithmetic).
+    static constexpr bool VF = DVW <= 64;
+    static constexpr int PV = VF ? DVW + 4 : DVW + 8;  // fp32 / bf16 pitch of the V tile
+    static constexpr size_t SV = al16((VF ? 4 : 2) * C * PV);
     static constexpr int VLB = C * DVW * 2 / 64;     // V tile bytes per Gram-wave lane
     static constexpr int VCB = VLB >= 16 ? 16 : 8;   // bytes per V chunk (one load)
     static constexpr int VCH = VLB / VCB;            // V chunks per Gram-wave lane: 4, 2 or 1
@@ -520,7 +527,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 
     // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / VCPR,
     // VCB / 2 bf16 columns (buffer loads as above, the range ending with the
-    // chunk's last row in the sequence).
+    // chunk's last row in the sequence).  Slabs of up to 64 columns park it
+    // as beta_r v_r in fp32, the form the consumers' Z = beta v - beta X takes
+    // it in; the 128-column kernel parks the bf16 tile.
     typedef typename std::conditional<Cfg::VCB == 16, u32x4, u32x2>::type VChunk;
     constexpr int VCOL = Cfg::VCB / 2;  // bf16 columns per chunk
     constexpr int VCPR = DVW / VCOL;    // chunks per row
@@ -537,10 +546,22 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         else
             return __builtin_bit_cast(VChunk, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off(i), 0, 0));
     };
-    auto v_dst = [&](int c, int i) -> VChunk* {
+    auto v_park = [&](int c, int i, VChunk x) {
         const int idx = lane + 64 * i;
         const int r = idx / VCPR, ch = idx % VCPR;
-        return reinterpret_cast<VChunk*>(reinterpret_cast<bf16_t*>(slotV(c)) + r * Cfg::PV + VCOL * ch);
+        if constexpr (!Cfg::VF) {
+            *reinterpret_cast<VChunk*>(reinterpret_cast<bf16_t*>(slotV(c)) + r * Cfg::PV + VCOL * ch) = x;
+            return;
+        }
+        const float br = reinterpret_cast<const float*>(slot4(c) + Cfg::S4_BETA)[r];
+        float* dst = reinterpret_cast<float*>(slotV(c)) + r * Cfg::PV + VCOL * ch;
+#pragma unroll
+        for (int q4 = 0; q4 < VCOL / 4; ++q4) {
+            const uint32_t lo = x[2 * q4], hi = x[2 * q4 + 1];
+            *reinterpret_cast<f32x4*>(dst + 4 * q4) =
+                f32x4{br * __uint_as_float(lo << 16), br * __uint_as_float(lo & 0xffff0000u),
+                      br * __uint_as_float(hi << 16), br * __uint_as_float(hi & 0xffff0000u)};
+        }
     };
     auto load_v = [&](int c, VRegs<VChunk>& V) {
         V.a = v_load(c, 0);
@@ -551,11 +572,11 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         }
     };
     auto store_v = [&](int c, const VRegs<VChunk>& V) {
-        *v_dst(c, 0) = V.a;
-        if constexpr (Cfg::VCH > 1) *v_dst(c, 1) = V.b;
+        v_park(c, 0, V.a);
+        if constexpr (Cfg::VCH > 1) v_park(c, 1, V.b);
         if constexpr (Cfg::VCH > 2) {
-            *v_dst(c, 2) = V.c;
-            *v_dst(c, 3) = V.d;
+            v_park(c, 2, V.c);
+            v_park(c, 3, V.d);
         }
     };
 
@@ -675,7 +696,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         if constexpr (!NOOUT) {
             f32x4 pv;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? accP[pp] : 0.f;
+            for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? p.scale * accP[pp] : 0.f;  // scale P
             st_frag(P + r * PK + 4 * g4, E::make(pv));
         }
         const float br = BETA[r];
@@ -778,7 +799,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         const float* BETA = reinterpret_cast<const float*>(s4 + Cfg::S4_BETA);
         const bf16_t* P = reinterpret_cast<const bf16_t*>(slotP(c));
         const bf16_t* T = reinterpret_cast<const bf16_t*>(slotT(c));
-        const uint16_t* sv = reinterpret_cast<const uint16_t*>(slotV(c)) + (col_base - z * DVW) + vcol(0, l16);
+        const int sv0 = (col_base - z * DVW) + vcol(0, l16);
 
         // Every LDS operand of this step is requested up front, so their
         // latency overlaps the state conversion and the X / QS products.
@@ -798,7 +819,13 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) vv[t][pp] = bf16_to_f32(sv[(4 * g4 + pp) * Cfg::PV + 4 * t]);
+            for (int pp = 0; pp < 4; ++pp) {
+                const int e = sv0 + (4 * g4 + pp) * Cfg::PV + 4 * t;
+                if constexpr (Cfg::VF)
+                    vv[t][pp] = reinterpret_cast<const float*>(slotV(c))[e];  // beta v, parked
+                else
+                    vv[t][pp] = bb[pp] * bf16_to_f32(reinterpret_cast<const uint16_t*>(slotV(c))[e]);
+            }
         Frag ktf[NCB];
         float4 gm[NCB];
 #pragma unroll
@@ -827,13 +854,13 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 mma32(X[t], kf[kb], kf[kb + 1], Sop[t][kb], Sop[t][kb + 1]);
                 if constexpr (!NOOUT) mma32(QS[t], Sop[t][kb], Sop[t][kb + 1], qf[kb], qf[kb + 1]);
             }
-        // U = T diag(beta) (V - X), all tiles side by side.
+        // U = T diag(beta) (V - X) = T (beta V - diag(beta) X), all tiles side by side.
         Frag Uf[TPW];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             f32x4 Z;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) Z[pp] = bb[pp] * (vv[t][pp] - X[t][pp]);
+            for (int pp = 0; pp < 4; ++pp) Z[pp] = fmaf(-bb[pp], X[t][pp], vv[t][pp]);
             f32x4 U = zero4();
             mma16(U, Tf, E::make(Z));
             Uf[t] = E::make(U);
@@ -854,8 +881,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 // product by VALU (kda_device.h: no SrcC chain across shapes)
                 f32x4 PU = zero4();
                 mma16(PU, Uf[t], Pf);
-                ov[t][0] = pack_bf16x2(p.scale * (QS[t][0] + PU[0]), p.scale * (QS[t][1] + PU[1]));
-                ov[t][1] = pack_bf16x2(p.scale * (QS[t][2] + PU[2]), p.scale * (QS[t][3] + PU[3]));
+                // O = scale Qt S + (scale P) U (P is stored scaled)
+                ov[t][0] = pack_bf16x2(fmaf(p.scale, QS[t][0], PU[0]), fmaf(p.scale, QS[t][1], PU[1]));
+                ov[t][1] = pack_bf16x2(fmaf(p.scale, QS[t][2], PU[2]), fmaf(p.scale, QS[t][3], PU[3]));
             }
         }
 #pragma unroll
