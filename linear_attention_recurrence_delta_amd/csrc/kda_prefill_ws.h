@@ -68,9 +68,12 @@ struct WsCfg {
     static constexpr int NWAVES = NCW + 2 + NSA;
     static constexpr int NT = 64 * NWAVES;
     static constexpr int DVW = NCW * TPW * 16;       // value columns per workgroup
-    static constexpr int W_SOLVE = NCW;
-    static constexpr int W_GRAM = NCW + 1;
-    static constexpr int W_A0 = NCW + 2;             // first stage-A wave
+    // Wave w runs on SIMD w mod 4.  With 14 waves, SIMDs 0 and 1 hold four
+    // waves and SIMDs 2 and 3 three: the solve and Gram waves go to the
+    // latter (waves 6 and 7), the stage-A waves are 4, 5 and 8-13.
+    static constexpr int W_SOLVE = NCW == 4 ? 6 : NCW;
+    static constexpr int W_GRAM = NCW == 4 ? 7 : NCW + 1;
+    static constexpr int W_A0 = NCW + 2;             // first stage-A wave (NCW < 4)
     static constexpr int IPW = NCB / NSA;            // stage-A items (16-channel blocks) per wave
 
     // Row pitches chosen so that the 8-byte fragment accesses of 16 lanes (16
@@ -360,8 +363,8 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 
     // ------------------------------------------------------------ role setup
     const bool is_cons = w < NCW;
-    const bool is_stageA = w >= Cfg::W_A0;
-    const int sa = w - Cfg::W_A0;  // stage-A wave index
+    const bool is_stageA = w >= NCW && w != Cfg::W_SOLVE && w != Cfg::W_GRAM;
+    const int sa = NCW == 4 ? (w < 6 ? w - 4 : w - 6) : w - Cfg::W_A0;  // stage-A wave index
     const int col_base = z * DVW + (is_cons ? w * TPW * 16 : 0);
     // Value column of MFMA column j of consumer tile t, relative to col_base:
     // the 4 TPW columns a lane's outputs fall on (see consume) are adjacent.
