@@ -584,12 +584,12 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     };
 
     // ------------------------------------------------------------ stage A
-    auto stage_a = [&](int c, const RawSet<IPW>& R) {
+    auto stage_a = [&](int c, const RawSet<IPW>& R, int u) __attribute__((always_inline)) {  // u = c & 3
         // No multiply-add contraction here: contracting the scaling of g
         // into the first scan step gives a move, a DPP move and an FMA per
         // value where one DPP add does.
 #pragma clang fp contract(off)
-        char* s4 = slot4(c);
+        char* s4 = smem + Cfg::OFF4 + (size_t)u * Cfg::S4;  // slot4(c)
         bf16_t* QB = reinterpret_cast<bf16_t*>(s4 + Cfg::S4_QB);
         bf16_t* KB = reinterpret_cast<bf16_t*>(s4 + Cfg::S4_KB);
         bf16_t* KLT = reinterpret_cast<bf16_t*>(s4 + Cfg::S4_KT);
@@ -957,23 +957,24 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             park_raw(1, rawB);
             fetch_raw(0, cur);
             __syncthreads();  // prologue 2: chunk 1 parked, chunk 0 read
-            for (int j = 0; j < iters; j += 2) {
-                load_raw(j + 3, rawB);
-                if constexpr (GATE) gtB = load_gt(j - 2);
-                if (j < nch) stage_a(j, cur);
-                park_raw(j + 2, rawA);
-                if constexpr (GATE) park_gt(j - 3, gtA);
-                fetch_raw(j + 1, cur);
+            // Unrolled four times, so that the 4-deep slot of the chunk that
+            // stage A works on (c & 3 = u) is an immediate offset.  Even steps
+            // load into set B and park set A, odd steps the other way round.
+            auto step = [&](int jj, auto uc, LoadSet<LPW>& into, const LoadSet<LPW>& from, u32x2& gt_into,
+                            const u32x2& gt_from) __attribute__((always_inline)) {
+                load_raw(jj + 3, into);
+                if constexpr (GATE) gt_into = load_gt(jj - 2);
+                if (jj < nch) stage_a(jj, cur, decltype(uc)::value);
+                park_raw(jj + 2, from);
+                if constexpr (GATE) park_gt(jj - 3, gt_from);
+                fetch_raw(jj + 1, cur);
                 __syncthreads();
-                if (j + 1 < iters) {
-                    load_raw(j + 4, rawA);
-                    if constexpr (GATE) gtA = load_gt(j - 1);
-                    if (j + 1 < nch) stage_a(j + 1, cur);
-                    park_raw(j + 3, rawB);
-                    if constexpr (GATE) park_gt(j - 2, gtB);
-                    fetch_raw(j + 2, cur);
-                    __syncthreads();
-                }
+            };
+            for (int j = 0; j < iters; j += 4) {
+                step(j, std::integral_constant<int, 0>{}, rawB, rawA, gtB, gtA);
+                if (j + 1 < iters) step(j + 1, std::integral_constant<int, 1>{}, rawA, rawB, gtA, gtB);
+                if (j + 2 < iters) step(j + 2, std::integral_constant<int, 2>{}, rawB, rawA, gtB, gtA);
+                if (j + 3 < iters) step(j + 3, std::integral_constant<int, 3>{}, rawA, rawB, gtA, gtB);
             }
         } else if (w == Cfg::W_GRAM) {
             // This wave also moves V: chunk c is loaded into registers in
