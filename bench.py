@@ -16,8 +16,11 @@ over 1000 steps) are timed in the same run and reported under
 "prefill_varlen", "prefill_long_1m" and "decode"; "device_copy" gives the
 bandwidth of a plain device copy as context for the HBM fractions.
 
-Timing: inputs are resident in HBM before the timed region; W untimed
-warm-up steps, then K timed steps bracketed by torch.cuda.synchronize();
+Timing: inputs are resident in HBM before the timed region; untimed
+warm-up steps (at least W, continued until 150 ms of back-to-back launches
+have run, so that the device clocks have settled after the change of
+workload; the counts are reported), then K timed steps bracketed by
+torch.cuda.synchronize();
 per-launch durations come from HIP events recorded on the stream the
 kernels are launched on (torch's current stream, which the binding passes
 to the C ABI).
@@ -153,16 +156,32 @@ def backward_entry(bw_ms, token_heads, T):
     }
 
 
-def time_launches(fn, reps, stream, warmup=0):
-    """Run fn `warmup` times untimed, then reps times; return per-launch ms from
-    events on `stream`.  Each timed workload gets its own warm-up right before
-    it: after a change of workload the device's clocks take about ten launches
-    of the dense prefill to settle (first launch about 1.96 ms, then 1.75 ms)."""
+# Each timed workload gets its own warm-up right before it: `warmup` launches,
+# continued until WARM_MS of back-to-back launches have run.  After a change
+# of workload the device's clocks take about 45 ms of sustained work to settle
+# (dense prefill, traced: first launches 2.0 ms, 1.58-1.60 ms from about the
+# 25th on), so W launches alone would time part of that ramp.
+WARM_MS = 150.0
+WARMUP_LAUNCHES = {}
+
+
+def time_launches(fn, reps, stream, warmup=0, name=None):
+    """Warm up (see WARM_MS), then run fn reps times; return per-launch ms
+    from events on `stream`.  The warm-up launch count goes to
+    WARMUP_LAUNCHES[name]."""
     import torch
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for _ in range(warmup):
+    n = 0
+    t0 = time.perf_counter()
+    while True:  # in groups of 4 launches, so the queue stays short and the device busy
         fn()
-    torch.cuda.synchronize()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if n >= warmup and (time.perf_counter() - t0) * 1e3 >= WARM_MS:
+                break
+    if name:
+        WARMUP_LAUNCHES[name] = n
     for a, b in evs:
         a.record(stream)
         fn()
@@ -301,13 +320,10 @@ def main():
 
     if args.only in ("all", "prefill"):
         token_heads = wd["T"] * wd["H"]
-        for _ in range(args.warmup):
-            run_dense()
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        dense_ms = time_launches(run_dense, args.steps, stream)
+        dense_ms = time_launches(run_dense, args.steps, stream, args.warmup, "prefill_dense")
         wall_s = time.perf_counter() - t0
-        varlen_ms = time_launches(run_varlen, args.steps, stream, args.warmup)
+        varlen_ms = time_launches(run_varlen, args.steps, stream, args.warmup, "prefill_varlen")
         # the varlen pack through the gated entry: y = sigmoid(gate) * RMSNorm(o) * weight
         # fused into the o store (whole-head workgroups), and the same as two passes
         gen_g = torch.Generator(device=dev)
@@ -324,8 +340,8 @@ def main():
             run_varlen()
             kda.kda_output_gate(o_v, gv_gate, gv_w, eps=1e-6, out=y_v)
 
-        gated_ms = time_launches(run_gated, args.steps, stream, args.warmup)
-        two_pass_ms = time_launches(run_two_pass, args.steps, stream, args.warmup)
+        gated_ms = time_launches(run_gated, args.steps, stream, args.warmup, "prefill_gated")
+        two_pass_ms = time_launches(run_two_pass, args.steps, stream, args.warmup, "prefill_gated_two_pass")
         del gv_gate, y_v
         # the dense workload again with a state checkpoint every 1024 tokens
         ck_interval = 1024
@@ -338,7 +354,7 @@ def main():
 
         ck_ms = None
         if not args.no_checkpoints:
-            ck_ms = time_launches(run_dense_ck, args.steps, stream, args.warmup)
+            ck_ms = time_launches(run_dense_ck, args.steps, stream, args.warmup, "prefill_checkpoints")
         # the dense workload through the fused entry (gate and q/k norm in the kernel)
         fu_ms = None
         if kda.kda_prefill_fused_supported(torch.bfloat16, wd["d"], wd["d"], C):
@@ -348,7 +364,7 @@ def main():
             def run_fused():
                 kda.kda_prefill_fused(fq, fk, fv, fz, fa, fb, None, None, chunk_size=C, out=o_d, final_state=s_d)
 
-            fu_ms = time_launches(run_fused, args.steps, stream, args.warmup)
+            fu_ms = time_launches(run_fused, args.steps, stream, args.warmup, "prefill_fused")
             del fq, fk, fv, fz, fa, fb
         # the output gate on the dense output (Sigmoid(gate) * RMSNorm(o) * weight)
         og_gate = torch.randn(o_d.shape, device=dev).to(o_d.dtype)
@@ -358,7 +374,7 @@ def main():
         def run_gate():
             kda.kda_output_gate(o_d, og_gate, og_w, eps=1e-6, out=og_y)
 
-        og_ms = time_launches(run_gate, args.steps, stream, args.warmup)
+        og_ms = time_launches(run_gate, args.steps, stream, args.warmup, "output_gate")
         del og_gate, og_y
         # the backward pass on the dense workload (forward again for its
         # 16-token states, then the reverse chunk kernel), preallocated buffers
@@ -384,7 +400,7 @@ def main():
                 if st != 0:
                     raise RuntimeError("kda_prefill_backward failed: %d" % st)
 
-            bw_ms = time_launches(run_bwd, args.steps, stream, max(1, args.warmup // 2))
+            bw_ms = time_launches(run_bwd, args.steps, stream, args.warmup, "prefill_backward")
             del b_do, b_dq, b_dk, b_dv, b_dg, b_db, b_ws
         d_avg = sum(dense_ms) / len(dense_ms)
         v_avg = sum(varlen_ms) / len(varlen_ms)
@@ -463,8 +479,7 @@ def main():
             kda.kda_prefill(wl["q"], wl["k"], wl["v"], wl["g"], wl["beta"], None, None, chunk_size=C,
                             out=o_l, final_state=s_l)
 
-        run_long()
-        long_ms = time_launches(run_long, args.long_steps, stream)
+        long_ms = time_launches(run_long, args.long_steps, stream, 1, "prefill_long_1m")
         l_avg = sum(long_ms) / len(long_ms)
         l_bytes = PREFILL_BYTES_PER_TOKEN_HEAD * wl["T"] * wl["H"]
         log("long prefill avg %.3f ms" % l_avg)
@@ -501,9 +516,7 @@ def main():
             it[0] += 1
             kda.kda_decode_step(q, k, v, g, beta, S, out=o_dec)
 
-        for _ in range(max(args.warmup, 5)):
-            run_decode()
-        dec_ms = time_launches(run_decode, args.decode_steps, stream)
+        dec_ms = time_launches(run_decode, args.decode_steps, stream, 5, "decode")
         dec_avg = sum(dec_ms) / len(dec_ms)
         dec_bytes = DECODE_BYTES_PER_UNIT * N * H
         dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
@@ -525,6 +538,10 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_note": "each timed workload: at least `warmup` launches, continued until %d ms of back-to-back "
+                       "launches have run (the device clocks ramp for about 45 ms after a change of workload); "
+                       "launches per workload in warmup_launches" % WARM_MS,
+        "warmup_launches": WARMUP_LAUNCHES,
         "ms_per_step": result.get("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
