@@ -56,7 +56,9 @@ def _all_units_check(oracle, w, o, S, cu, label, t_limit=None):
         worst_o = max(worst_o, rel_err(sl(o), ro))
         if S is not None:
             worst_s = max(worst_s, rel_err(f64(S.index_select(1, hi)), rs))
-    say("  %s: all %d heads, rel err o=%.3e S=%.3e (tol %.0e)" % (label, w["H"], worst_o, worst_s, BF16_TOL))
+    n_seq = 1 if t_limit is not None or cu is None else len(cu) - 1
+    say("  %s: all %d (sequence, head) units, rel err o=%.3e S=%.3e (tol %.0e)"
+        % (label, n_seq * w["H"], worst_o, worst_s, BF16_TOL))
     assert np.isfinite(worst_o) and np.isfinite(worst_s)
     assert worst_o <= BF16_TOL and worst_s <= BF16_TOL
 
