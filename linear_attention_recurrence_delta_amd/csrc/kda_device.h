@@ -34,6 +34,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 // Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
+// acc + lo(a) lo(b) + hi(a) hi(b) for two packed bf16 pairs (v_dot2c_f32_bf16:
+// products exact, fp32 sum).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));

@@ -492,12 +492,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 for (int i = 0; i < LPW; ++i) {
                     float ss = 0.f;
 #pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) {
-                        const uint32_t wd = R.x[i][w2];
-                        const float lo = __uint_as_float(wd << 16), hi = __uint_as_float(wd & 0xffff0000u);
-                        ss += lo * lo;
-                        ss += hi * hi;
-                    }
+                    for (int w2 = 0; w2 < 4; ++w2) ss = dot2_bf16(R.x[i][w2], R.x[i][w2], ss);
                     ss = row_inclusive_sum16(ss);
                     if (l16 == 15) rn[ld_row + 4 * i] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
                 }
@@ -915,11 +910,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             const u32x4 o4 = {ov[0][0], ov[0][1], ov[1][0], ov[1][1]};
             float ss = 0.f;
 #pragma unroll
-            for (int wd = 0; wd < 4; ++wd) {
-                const float lo = __uint_as_float(o4[wd] << 16), hi = __uint_as_float(o4[wd] & 0xffff0000u);
-                ss += lo * lo;
-                ss += hi * hi;
-            }
+            for (int wd = 0; wd < 4; ++wd) ss = dot2_bf16(o4[wd], o4[wd], ss);
             ss += __shfl_xor(ss, 16, 64);
             ss += __shfl_xor(ss, 32, 64);
             if (g4 == 0) reinterpret_cast<float*>(smem + Cfg::G_PART)[((c & 1) * C + l16) * NCW + w] = ss;
