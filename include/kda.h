@@ -176,11 +176,12 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens,
  * are too few to fill the device is cut into G segments per sequence.  The
  * state update is affine in the state ("Understanding Kimi K3's attention",
  * state-update equation), so each segment g is one map S_end = M_g S_start +
- * B_g.  Three launches: segment 0 runs from the initial state while the maps
- * of segments 1 .. G-2 are computed in parallel (M_g from the identity with
- * v = 0, B_g from zero: two 128-column state runs each); a short combine
- * chains start(g + 1) = M_g start(g) + B_g in fp32; segments 1 .. G-1 run
- * again from their start states with outputs.  This is the pages' state
+ * B_g.  Three launches: the maps of segments 0 .. G-2 are computed in
+ * parallel, M_g and B_g of one segment by one workgroup (M_g from the
+ * identity with v = 0, B_g from zero, or from the initial state for segment
+ * 0, which makes B_0 that segment's end state); a short combine chains
+ * start(g + 1) = M_g start(g) + B_g in fp32; all G segments run again from
+ * their start states with outputs.  This is the pages' state
  * passing between chunks ("Inside Kimi K3", section "Sequence mixing")
  * applied between segments, in parallel over segments instead of one chain.
  */
@@ -210,7 +211,7 @@ typedef struct {
     int32_t segments;             /* segment scan: 0 = library choice, 1 = off,        */
                                   /* 2 .. 256 = segments per sequence (dense batches,  */
                                   /* pipelined kernel, no fused gate or checkpoints,  */
-                                  /* at least segments + 1 chunks per sequence)        */
+                                  /* at least `segments` chunks per sequence)          */
 } kda_prefill_desc;
 
 typedef struct {

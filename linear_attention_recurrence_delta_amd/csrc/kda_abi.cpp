@@ -111,36 +111,28 @@ const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t 
 }
 
 // Sequence-segment scan plan (kda_internal.h, PrefillParams::seg_*): G
-// segments per sequence, segments 1 .. G-1 of Lc chunks each and segment 0
-// the rest.  Segment 0 runs (with outputs) during phase 1, while the maps of
-// two segments run one after the other on other compute units; a map reads
-// no q and writes no o, so it streams far fewer bytes than a run and takes
-// less time per chunk.  Segment 0 therefore gets kSeg0Share / 16 of two
-// segments' chunks: measured on MI355X for one 1,048,576-token sequence of 16
-// heads (17 segments), a segment 0 as long as the others (share 8) took 13.3
-// ms against 16.6 ms for a double one (16); its run then ends before the
-// second round of maps does.
+// segments per sequence of Lc chunks each, the last one taking the rest.
+// Phase 1 runs one map-pair workgroup (M and B of one segment, stage A
+// shared) for each of segments 0 .. G - 2, phase 3 one run per segment.
 struct SegPlan {
     int G = 1;
-    int64_t len0 = 0, len = 0;  // tokens
+    int64_t len = 0;  // tokens per segment (the last: the rest)
 };
-
-constexpr int kSeg0Share = 8;
 
 constexpr int kMaxSegments = 256;
 
 // The library's choice: with P = compute units per (sequence, head) unit,
-// phase 1 runs segment 0 and 2 (G - 2) maps, phase 3 the G - 1 other
-// segments, so G = P + 1 fills the device with a chain of about 3 / (G + 1)
-// of the sequence (against the whole sequence for the direct chain).  Worth
-// it from P = 4 on, with segments of at least 64 chunks.
+// G = P segments fill the device in both phases (units (G - 1) map pairs,
+// then units G runs), each workgroup a chain of 1 / G of the sequence
+// (against the whole sequence for the direct chain), twice.  Worth it from
+// P = 4 on, with segments of at least 64 chunks.
 int auto_segments(int64_t units, int64_t t_seq) {
     if (units <= 0) return 1;
     const int64_t P = device_cu_count() / units;
     if (P < 4) return 1;
-    const int G = (int)(P < 32 ? P : 32) + 1;
+    const int G = (int)(P < 32 ? P : 32);
     const int64_t chunks = (t_seq + 15) / 16;
-    return chunks >= 64 * (int64_t)(G + 1) ? G : 1;
+    return chunks >= 64 * (int64_t)G ? G : 1;
 }
 
 SegPlan seg_plan(int G, int64_t t_seq) {
@@ -148,13 +140,8 @@ SegPlan seg_plan(int G, int64_t t_seq) {
     sp.G = G;
     if (G < 2) return sp;
     const int64_t chunks = (t_seq + 15) / 16;
-    // chunks = L0 + (G - 1) Lc with L0 = (share / 16) 2 Lc; at least one chunk
-    // per segment, segment 0 taking the rest
-    int64_t lc = chunks * 8 / ((int64_t)(G - 1) * 8 + kSeg0Share);
-    if (lc < 1) lc = 1;
-    while ((int64_t)(G - 1) * lc >= chunks && lc > 1) --lc;
-    sp.len = 16 * lc;
-    sp.len0 = t_seq - (int64_t)(G - 1) * sp.len;
+    const int64_t lc = chunks / G;  // >= 1: plans need a chunk per segment
+    sp.len = 16 * (lc < 1 ? 1 : lc);
     return sp;
 }
 
@@ -175,7 +162,7 @@ int plan_segments(const kda_prefill_desc& d, bool dense, int kind) {
     if (d.segments == 0) return eligible ? auto_segments(units, t_seq) : 1;
     if (!eligible || d.segments > kMaxSegments) return 0;
     const int64_t chunks = (t_seq + 15) / 16;
-    if (chunks < d.segments + 1) return 0;  // every segment needs a chunk
+    if (chunks < d.segments) return 0;  // every segment needs a chunk
     return d.segments;
 }
 
@@ -378,11 +365,10 @@ static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tens
         if (var->launch(p, s) != hipSuccess) return KDA_ERR_HIP;
         return gate_pass();
     }
-    // Segment scan: maps (phase 1), their chain (phase 2), re-runs (phase 3).
-    if (!var->launch_seg) return KDA_ERR_UNSUPPORTED;
+    // Segment scan: map pairs (phase 1), their chain (phase 2), runs (phase 3).
+    if (!var->launch_seg || !var->launch_pair) return KDA_ERR_UNSUPPORTED;
     const SegPlan sp = seg_plan(G, p.seq_len);
     p.seg_G = sp.G;
-    p.seg_len0 = (int32_t)sp.len0;
     p.seg_len = (int32_t)sp.len;
     p.seg_ws = static_cast<float*>(workspace);
     p.seg_phase = 1;
@@ -390,7 +376,7 @@ static kda_status prefill_impl(const kda_prefill_desc& d, const kda_prefill_tens
     p.seg_phase = 3;
     if (b1 > INT32_MAX || kda::ws_grid_blocks(p) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     p.seg_phase = 1;
-    if (var->launch_seg(p, s) != hipSuccess) return KDA_ERR_HIP;
+    if (var->launch_pair(p, s) != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_segment_combine(p, s) != hipSuccess) return KDA_ERR_HIP;
     p.seg_phase = 3;
     if (var->launch_seg(p, s) != hipSuccess) return KDA_ERR_HIP;

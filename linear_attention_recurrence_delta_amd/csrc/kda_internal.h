@@ -41,16 +41,16 @@ struct PrefillParams {
     const float* a_log;
     // Sequence-segment scan (dense batches, pipelined kernel).  seg_phase 0:
     // off, one workgroup chain per (sequence, head, slab) walks the whole
-    // sequence.  Otherwise each sequence is cut into seg_G segments: segment 0
-    // holds tokens [0, seg_len0), segment g >= 1 tokens [seg_len0 + (g - 1)
-    // seg_len, + seg_len).  Phase 1 runs segment 0 from the initial state (its
-    // outputs stored, its end state kept) and, for g = 1 .. seg_G - 2, the
+    // sequence.  Otherwise each sequence is cut into seg_G segments of
+    // seg_len tokens, the last one running to the end of the sequence.
+    // Phase 1 (the map-pair kernel) computes, for g = 0 .. seg_G - 2, the
     // affine map of segment g: S_end = M_g S_start + B_g, with M_g the run
-    // from the identity with v = 0 and B_g the run from zero with the real v.
-    // A combine kernel turns the maps into every segment's start state; phase
-    // 3 runs segments 1 .. seg_G - 1 from those states with outputs.
-    // seg_ws holds [N H][seg_G - 1][2][D][D] fp32: (M_g, B_g), the B slot
-    // replaced by the start state of segment g + 1 (slot 0: segment 0's end).
+    // from the identity with v = 0 and B_g the run from zero with the real v
+    // (segment 0: from the initial state, so B_0 is its end state).  A
+    // combine kernel turns the maps into every segment's start state; phase 3
+    // runs all seg_G segments from those states with outputs.  seg_ws holds
+    // [N H][seg_G - 1][2][D][D] fp32: (M_g, B_g), the B slot replaced by the
+    // start state of segment g + 1.
     // Output gate fused into the o store (kernels built with it): o is not
     // stored; y = Sigmoid(gate) o / sqrt(mean(o^2) + gate_eps) * gate_weight
     // goes to the o buffer instead (gate [T_total, H, D] in the qkv dtype,
@@ -60,20 +60,19 @@ struct PrefillParams {
     float gate_eps = 0.f;
     int32_t seg_phase = 0;  // 0, 1 or 3
     int32_t seg_G = 1;
-    int32_t seg_len0 = 0;
     int32_t seg_len = 0;
     float* seg_ws = nullptr;
 };
 
 // Workgroups of a pipelined-kernel launch: units are padded to whole groups
-// of 8 (one per XCD), each unit or segment item with nslab slabs (segment maps
-// with 2 nslab: the M columns, then the B columns).
+// of 8 (one per XCD), each unit or segment item with nslab slabs; the
+// map-pair kernel (segment scan, phase 1) takes whole heads, one workgroup per
+// (sequence, head, segment 0 .. seg_G - 2).
 inline int64_t ws_pad8(int64_t x) { return (x + 7) / 8 * 8; }
 inline int64_t ws_grid_blocks(const PrefillParams& p) {
     const int64_t units = (int64_t)p.N * p.H;
-    if (p.seg_phase == 1)
-        return ws_pad8(units) * p.nslab + ws_pad8(units * (p.seg_G - 2)) * 2 * p.nslab;
-    if (p.seg_phase == 3) return ws_pad8(units * (p.seg_G - 1)) * p.nslab;
+    if (p.seg_phase == 1) return ws_pad8(units * (p.seg_G - 1));
+    if (p.seg_phase == 3) return ws_pad8(units * p.seg_G) * p.nslab;
     return ws_pad8(units) * p.nslab;
 }
 
@@ -149,10 +148,12 @@ struct PrefillVariant {
     int nwc;                // column waves per workgroup (16 d_v columns each)
     size_t lds_bytes;
     hipError_t (*launch)(const PrefillParams&, hipStream_t);
-    // the same kernel built with the segment-scan phases, or nullptr
+    // the same kernel built for the segment scan's runs (phase 3), or nullptr
     hipError_t (*launch_seg)(const PrefillParams&, hipStream_t) = nullptr;
     // the same kernel with the output gate fused into the o store, or nullptr
     hipError_t (*launch_gate)(const PrefillParams&, hipStream_t) = nullptr;
+    // the segment scan's map-pair kernel (phase 1), where launch_seg is built
+    hipError_t (*launch_pair)(const PrefillParams&, hipStream_t) = nullptr;
 };
 
 // Tables defined in the kernel translation units.

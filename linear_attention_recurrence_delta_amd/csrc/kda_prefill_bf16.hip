@@ -19,11 +19,13 @@ extern template hipError_t launch_prefill_ws<2, 2, 8, false, false, true>(const 
 
 static const PrefillVariant kBf16Variants[] = {
     // wave-specialised pipeline: NCW consumer waves x TPW 16 columns, 8 stage-A waves
-    // (whole-head and 64-column slabs also built with the segment-scan phases)
+    // (whole-head and 64-column slabs also built for the segment scan's runs,
+    // with the map-pair kernel <8, 2, 4, ..., SEG> for its maps)
     // (whole heads also with the output gate fused into the o store)
     {1, 1, 128, 16, 8, WsCfg<4, 2, 8>::LDS, &launch_prefill_ws<4, 2, 8>, &launch_prefill_ws<4, 2, 8, false, false, true>,
-     &launch_prefill_ws<4, 2, 8, false, false, false, true>},
-    {1, 1, 128, 16, 4, WsCfg<2, 2, 8>::LDS, &launch_prefill_ws<2, 2, 8>, &launch_prefill_ws<2, 2, 8, false, false, true>},
+     &launch_prefill_ws<4, 2, 8, false, false, false, true>, &launch_prefill_ws<8, 2, 4, false, false, true>},
+    {1, 1, 128, 16, 4, WsCfg<2, 2, 8>::LDS, &launch_prefill_ws<2, 2, 8>, &launch_prefill_ws<2, 2, 8, false, false, true>,
+     nullptr, &launch_prefill_ws<8, 2, 4, false, false, true>},
     {1, 1, 128, 16, 2, WsCfg<1, 2, 8>::LDS, &launch_prefill_ws<1, 2, 8>},
     {1, 1, 128, 16, 1, WsCfg<1, 1, 8>::LDS, &launch_prefill_ws<1, 1, 8>},
     // the same with the gate and the q/k L2 norm computed in the kernel

@@ -67,7 +67,11 @@ struct WsCfg {
     static constexpr int NCB = D / 16;               // 16-channel blocks
     static constexpr int NWAVES = NCW + 2 + NSA;
     static constexpr int NT = 64 * NWAVES;
-    static constexpr int DVW = NCW * TPW * 16;       // value columns per workgroup
+    // Eight consumer waves make the segment scan's map pair (waves 0-3 the map
+    // M, waves 4-7 the map B of the same segment, sharing stage A, Gram and
+    // solve): two parts of four waves over the same value columns.
+    static constexpr int NCWP = NCW == 8 ? 4 : NCW;  // consumer waves per part
+    static constexpr int DVW = NCWP * TPW * 16;      // value columns per workgroup (per part)
     // Wave w runs on SIMD w mod 4.  With 14 waves, SIMDs 0 and 1 hold four
     // waves and SIMDs 2 and 3 three: the solve and Gram waves go to the
     // latter (waves 6 and 7), the stage-A waves are 4, 5 and 8-13.
@@ -205,10 +209,8 @@ struct WsWork {
     int64_t t_begin, t_end;
     int n, h, z;
     const float* s_in;  // start state [D][D] of the (sequence, head), or nullptr (zeros)
-    bool s_identity;    // start from the identity (segment map M): s_in unused
     float* s_out;       // end state [D][D], or nullptr
-    bool store_o;
-    bool v_zero;        // v read as zeros (segment map M)
+    float* s_out_m;     // map pair: the end state of the part run from the identity with v = 0 (M)
 };
 
 // Block -> work.  The dispatcher deals consecutive workgroups to the 8 XCDs
@@ -216,12 +218,10 @@ struct WsWork {
 // b % 8 and neighbouring b / 8, so they run on one XCD at the same pace and
 // the q, k, g and beta they all read come from that XCD's L2 after the first
 // slab's miss.  Items are padded to whole groups of 8; padding blocks get no
-// work.  Segment-scan launches (seg_phase 1 and 3) list their items the same
-// way: phase 1 first the segment-0 runs (slabs 0 .. nslab - 1), then the
-// segment maps (slabs 0 .. nslab - 1 for M, nslab .. 2 nslab - 1 for B, so
-// the two halves of one map share an XCD); phase 3 the runs of segments 1 ..
-// seg_G - 1.
-template <int D, bool SEG>
+// work.  Segment-scan launches list their items the same way: phase 1 (the
+// map-pair kernel, whole heads) the segments 0 .. seg_G - 2 of every
+// (sequence, head), phase 3 all seg_G segments with their slabs.
+template <int D, bool SEG, bool PAIR>
 __device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
     const int units = p.N * p.H;
     const int xcd = bid & 7;
@@ -229,22 +229,33 @@ __device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
     auto map_slot = [&](int uh, int g, int part) {
         return p.seg_ws + (((int64_t)uh * (p.seg_G - 1) + g) * 2 + part) * sdd;
     };
+    // segment g: tokens [g seg_len, (g + 1) seg_len) of its sequence, the last
+    // one running to the end of the sequence
     auto seg_range = [&](int n, int g) {
         const int64_t s0 = (int64_t)n * p.seq_len;
-        if (g == 0) {
-            w.t_begin = s0;
-            w.t_end = s0 + p.seg_len0;
-        } else {
-            w.t_begin = s0 + p.seg_len0 + (int64_t)(g - 1) * p.seg_len;
-            w.t_end = w.t_begin + p.seg_len;
-        }
+        w.t_begin = s0 + (int64_t)g * p.seg_len;
+        w.t_end = g == p.seg_G - 1 ? s0 + p.seq_len : w.t_begin + p.seg_len;
     };
-    w.s_identity = false;
-    w.v_zero = false;
-    w.store_o = true;
+    w.s_out_m = nullptr;
+    if constexpr (PAIR) {
+        // phase 1: the maps of segment g <= seg_G - 2 (M into slot (g, 0), B
+        // into slot (g, 1)); segment 0's B runs from the initial state, so it
+        // is that segment's end state, the start of segment 1
+        const int item = (bid >> 3) * 8 + xcd;
+        if (item >= units * (p.seg_G - 1)) return false;
+        const int uh = item / (p.seg_G - 1), g = item % (p.seg_G - 1);
+        w.z = 0;
+        w.h = uh % p.H;
+        w.n = uh / p.H;
+        seg_range(w.n, g);
+        w.s_in = (g == 0 && p.S0) ? p.S0 + (int64_t)uh * sdd : nullptr;
+        w.s_out = map_slot(uh, g, 1);
+        w.s_out_m = map_slot(uh, g, 0);
+        return true;
+    }
+    const int rest = bid >> 3;
+    w.z = rest % p.nslab;
     if (!SEG || p.seg_phase == 0) {
-        const int rest = bid >> 3;
-        w.z = rest % p.nslab;
         const int uh = (rest / p.nslab) * 8 + xcd;
         if (uh >= units) return false;
         w.h = uh % p.H;
@@ -254,48 +265,15 @@ __device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
         w.s_out = p.Sout ? p.Sout + (int64_t)uh * sdd : nullptr;
         return true;
     }
-    if (p.seg_phase == 1) {
-        const int ra = (units + 7) / 8 * 8 * p.nslab;
-        if (bid < ra) {  // segment 0 from the initial state; its end state goes to slot (0, B)
-            const int rest = bid >> 3;
-            w.z = rest % p.nslab;
-            const int uh = (rest / p.nslab) * 8 + xcd;
-            if (uh >= units) return false;
-            w.h = uh % p.H;
-            w.n = uh / p.H;
-            seg_range(w.n, 0);
-            w.s_in = p.S0 ? p.S0 + (int64_t)uh * sdd : nullptr;
-            w.s_out = map_slot(uh, 0, 1);
-            return true;
-        }
-        const int rest = (bid - ra) >> 3;  // ra is a multiple of 8: same XCD rule
-        const int zz = rest % (2 * p.nslab);
-        const int item = (rest / (2 * p.nslab)) * 8 + xcd;
-        if (item >= units * (p.seg_G - 2)) return false;
-        const int uh = item / (p.seg_G - 2), g = 1 + item % (p.seg_G - 2);
-        const int part = zz / p.nslab;  // 0: M (identity start, v = 0), 1: B (zero start, real v)
-        w.z = zz % p.nslab;
-        w.h = uh % p.H;
-        w.n = uh / p.H;
-        seg_range(w.n, g);
-        w.s_in = nullptr;
-        w.s_identity = part == 0;
-        w.v_zero = part == 0;
-        w.s_out = map_slot(uh, g, part);
-        w.store_o = false;
-        return true;
-    }
-    // phase 3: segment g >= 1 from the start state the combine left in slot (g - 1, B)
-    const int rest = bid >> 3;
-    w.z = rest % p.nslab;
+    // phase 3: segment g from its start state (segment 0 from the initial
+    // state, segment g >= 1 from the one the combine left in slot (g - 1, 1))
     const int item = (rest / p.nslab) * 8 + xcd;
-    if (item >= units * (p.seg_G - 1)) return false;
-    const int uh = item / (p.seg_G - 1), g = 1 + item % (p.seg_G - 1);
+    if (item >= units * p.seg_G) return false;
+    const int uh = item / p.seg_G, g = item % p.seg_G;
     w.h = uh % p.H;
     w.n = uh / p.H;
     seg_range(w.n, g);
-    if (g == p.seg_G - 1) w.t_end = (int64_t)(w.n + 1) * p.seq_len;  // the last segment ends the sequence
-    w.s_in = map_slot(uh, g - 1, 1);
+    w.s_in = g == 0 ? (p.S0 ? p.S0 + (int64_t)uh * sdd : nullptr) : map_slot(uh, g - 1, 1);
     w.s_out = (g == p.seg_G - 1 && p.Sout) ? p.Sout + (int64_t)uh * sdd : nullptr;
     return true;
 }
@@ -306,13 +284,16 @@ __device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
 // row-major states of the public checkpoint call, and no output o (p.o is not
 // read): the readout products Q~ S and P U and the P tile are skipped.
 //
-// SEG: the variant that also runs the segment-scan phases (PrefillParams::
-// seg_phase 1 and 3); the plain kernels are compiled without that code.
+// SEG: the variants that run the segment-scan phases (PrefillParams::
+// seg_phase 1: the map-pair kernel, NCW = 8; seg_phase 3: the runs of the
+// segments); the plain kernels are compiled without that code.
 //
-// MAP: the body of a segment-map workgroup (segment scan, phase 1): only the
-// end state is wanted, so, as with CKB, no readout and no o; q is not read
-// either (its loads use an empty range: no memory request), and the start
-// state may be the identity and v zero (the M half of a map).
+// MAP: the body of the map-pair kernel (segment scan, phase 1): only the end
+// states are wanted, so, as with CKB, no readout and no o; q is not read
+// either (its loads use an empty range: no memory request).  Consumer waves
+// 0-3 start from the identity with v read as zero (the map M), waves 4-7 from
+// the start state (zero, or the initial state for segment 0) with v (the map
+// B); stage A, Gram and solve serve both.
 template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG, bool MAP, bool GATE>
 __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk, char* smem) {
     typedef WsCfg<NCW, TPW, NSA, FUSED, GATE> Cfg;
@@ -328,9 +309,13 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     const int g4 = lane >> 4;
     const int l16 = lane & 15;
 
-    // segment-map flags: compile-time false outside the map body
-    const bool w_identity = MAP && wk.s_identity;
-    const bool w_v_zero = MAP && wk.v_zero;
+    // Segment-map pair (MAP: eight consumer waves): waves 0-3 run the map M
+    // (from the identity, v read as zero), waves 4-7 the map B.  Compile-time
+    // false outside the map body.
+    static_assert(!MAP || (NCW == 8 && SEG), "the map body is the pair kernel's");
+    const bool w_identity = MAP && w < Cfg::NCWP;
+    const bool w_v_zero = w_identity;
+    float* const s_dst = w_identity ? wk.s_out_m : wk.s_out;  // this wave's end state
     const int z = wk.z;
     const int h = wk.h;
     const int n = wk.n;
@@ -365,7 +350,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     const bool is_cons = w < NCW;
     const bool is_stageA = w >= NCW && w != Cfg::W_SOLVE && w != Cfg::W_GRAM;
     const int sa = NCW == 4 ? (w < 6 ? w - 4 : w - 6) : w - Cfg::W_A0;  // stage-A wave index
-    const int col_base = z * DVW + (is_cons ? w * TPW * 16 : 0);
+    const int col_base = z * DVW + (is_cons ? (w % Cfg::NCWP) * TPW * 16 : 0);
     // Value column of MFMA column j of consumer tile t, relative to col_base:
     // the 4 TPW columns a lane's outputs fall on (see consume) are adjacent.
     auto vcol = [&](int t, int j) { return 4 * TPW * (j >> 2) + 4 * t + (j & 3); };
@@ -822,7 +807,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 if constexpr (Cfg::VF)
                     vv[t][pp] = reinterpret_cast<const float*>(slotV(c))[e];  // beta v, parked
                 else
-                    vv[t][pp] = bb[pp] * bf16_to_f32(reinterpret_cast<const uint16_t*>(slotV(c))[e]);
+                    vv[t][pp] = w_v_zero ? 0.f : bb[pp] * bf16_to_f32(reinterpret_cast<const uint16_t*>(slotV(c))[e]);
             }
         Frag ktf[NCB];
         float4 gm[NCB];
@@ -1078,8 +1063,8 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 }
                 __syncthreads();
             }
-            if (wk.s_out) {
-                const auto rs = buffer_rsrc(wk.s_out, D * D * 4);
+            if (s_dst) {
+                const auto rs = buffer_rsrc(s_dst, D * D * 4);
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -1090,12 +1075,12 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                                                                   s_voff + 16 * t, (16 * ct + pp) * D * 4, 0);
             }
         }
-    } else if (is_cons && wk.s_out) {
+    } else if (is_cons && s_dst) {
         // empty sequence: the final state is the initial state.  Buffer
         // accesses, as everywhere in this kernel: a generic (flat) access
         // would make the compiler's waits on every wave's loads in flight
         // collapse to full drains.
-        const auto ro = buffer_rsrc(wk.s_out, D * D * 4);
+        const auto ro = buffer_rsrc(s_dst, D * D * 4);
         const auto ri = wk.s_in ? buffer_rsrc(wk.s_in, D * D * 4) : buffer_rsrc(p.g, 0);
         for (int t = 0; t < TPW; ++t)
             for (int ct = 0; ct < NCB; ++ct)
@@ -1116,8 +1101,10 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     // XCD-aware block order (ws_resolve); padding blocks exit at once.  The
     // work description is uniform: pinned to scalar registers (integer
     // divisions by run-time values leave their results in vector registers).
+    constexpr bool PAIR = NCW == 8;  // the segment scan's map-pair kernel (phase 1)
+    static_assert(!PAIR || SEG, "map pairs belong to the segment scan");
     WsWork wk;
-    if (!ws_resolve<Cfg::D, SEG>(p, blockIdx.x, wk)) return;
+    if (!ws_resolve<Cfg::D, SEG, PAIR>(p, blockIdx.x, wk)) return;
     wk.t_begin = uniform_i64(wk.t_begin);
     wk.t_end = uniform_i64(wk.t_end);
     wk.n = __builtin_amdgcn_readfirstlane(wk.n);
@@ -1125,20 +1112,17 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     wk.z = __builtin_amdgcn_readfirstlane(wk.z);
     wk.s_in = reinterpret_cast<const float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_in)));
     wk.s_out = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_out)));
-    wk.s_identity = __builtin_amdgcn_readfirstlane((int)wk.s_identity) != 0;
-    wk.v_zero = __builtin_amdgcn_readfirstlane((int)wk.v_zero) != 0;
-    if constexpr (SEG) {
-        if (__builtin_amdgcn_readfirstlane((int)!wk.store_o)) {
-            ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, true, false>(p, wk, smem);
-            return;
-        }
-    }
-    ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, false, GATE>(p, wk, smem);
+    wk.s_out_m = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_out_m)));
+    if constexpr (PAIR)
+        ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, true, false>(p, wk, smem);
+    else
+        ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, false, GATE>(p, wk, smem);
 }
 
 template <int NCW, int TPW, int NSA, bool FUSED = false, bool CKB = false, bool SEG = false, bool GATE = false>
 hipError_t launch_prefill_ws(const PrefillParams& p, hipStream_t s) {
     if (!SEG && p.seg_phase != 0) return hipErrorInvalidValue;
+    if (SEG && p.seg_phase != (NCW == 8 ? 1 : 3)) return hipErrorInvalidValue;  // pairs: phase 1, runs: phase 3
     const int64_t blocks = ws_grid_blocks(p);  // whole groups of 8 items
     hipLaunchKernelGGL((kda_prefill_ws_kernel<NCW, TPW, NSA, FUSED, CKB, SEG, GATE>), dim3((unsigned)blocks),
                        dim3(64 * (NCW + 2 + NSA)), 0, s, p);

@@ -82,13 +82,15 @@ def test_segments_slab_width_bitwise(kda):
 
 
 def test_smallest_segments(kda, oracle_mod):
-    # 96 tokens = 6 chunks and G = 5: segments of one chunk (segment 0: two)
+    # 96 tokens = 6 chunks: G = 6 gives segments of one chunk, G = 5 a last
+    # segment of two
     say("CASE segment scan, one-chunk segments")
     w = _dense(3, 96, 2, 2200, "zero")
-    o, S = _run(kda, w, segments=5)
-    _oracle_check(oracle_mod, w, o, S, 1.0, "T=96 G=5")
-    with pytest.raises(kda.KdaError) as e:  # 6 chunks cannot hold 6 segments + segment 0's double share
-        _run(kda, w, segments=6)
+    for G in (5, 6):
+        o, S = _run(kda, w, segments=G)
+        _oracle_check(oracle_mod, w, o, S, 1.0, "T=96 G=%d" % G)
+    with pytest.raises(kda.KdaError) as e:  # 6 chunks cannot hold 7 segments
+        _run(kda, w, segments=7)
     assert e.value.status == 3
 
 

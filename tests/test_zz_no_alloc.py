@@ -40,7 +40,7 @@ def _case(kda, T, H, seed):
 
 
 def test_two_calls_second_smaller(kda):
-    _case(kda, 40000, 2, 3100)   # 2 (sequence, head) units: 33 segments
+    _case(kda, 40000, 2, 3100)   # 2 (sequence, head) units: 32 segments
     _case(kda, 36000, 1, 3101)   # 1 unit: a smaller buffer footprint
 
 
