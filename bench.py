@@ -491,11 +491,11 @@ def main():
             "tokens_per_s": wl["T"] / (l_avg * 1e-3), "ms": l_avg, "runs": args.long_steps,
             "hbm_gbs": l_bytes / (l_avg * 1e-3) / 1e9,
             "plan": {"segments_per_sequence": segs, "workspace_bytes": ws_l,
-                     "launches": "segment maps + segment 0, combine, segments 1.. again" if segs > 1 else "direct"},
+                     "launches": "segment map pairs, combine, all segments again" if segs > 1 else "direct"},
             "roofline": {"bound": "hbm", "achieved": l_bytes / (l_avg * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": l_bytes / (l_avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
                          "traffic": measured_traffic("kda_prefill_long_1m_h16"),
-                         "kernel": "kda_prefill_ws_kernel<4,2,8,...,SEG> x 2 + kda_segment_combine_kernel (whole call)",
+                         "kernel": "kda_prefill_ws_kernel<8,2,4,...,SEG> (map pairs) + kda_segment_combine_kernel + kda_prefill_ws_kernel<4,2,8,...,SEG> (runs): whole call",
                          "bytes_per_launch": l_bytes},
         }
         del wl, o_l, s_l
