@@ -103,7 +103,7 @@ int32_t kda_decode_supported(int32_t qkv_dtype, int32_t d_k, int32_t d_v);
  * workspace.  The only user is the sequence-segment scan (see
  * kda_prefill_desc.segments), which the library picks for dense batches with
  * few (sequence, head) recurrences per compute unit: about (G - 1) * 128 KiB
- * per (sequence, head) for G segments per sequence (32 MiB for one
+ * per (sequence, head) for G segments per sequence (30 MiB for one
  * 1,048,576-token sequence of 16 heads on 256 compute units).
  */
 size_t kda_prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens,
