@@ -340,6 +340,16 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     auto slotV = [&](int c) { return smem + Cfg::OFFV + (size_t)(c & 1) * Cfg::SV; };
     // Element offset of token row 0 of chunk c for head h (uniform per wave).
     auto chunk_base = [&](int c) -> int64_t { return ((t_begin + (int64_t)c * C) * H + h) * D; };
+    // Byte address of row 0 of chunk c in a [T, H, D] tensor of es-byte
+    // elements: the workgroup's first chunk plus c strides of 16 token rows.
+    // A stride is below 2^31 bytes (the host checks H D 64 < 2^31), so each
+    // chunk costs one 32 x 32 -> 64-bit scalar multiply-add instead of the
+    // 64-bit index arithmetic of chunk_base.
+    const int64_t e_first = chunk_base(0);
+    auto chunk_ptr = [&](const void* base, int es, int c) -> const char* {
+        return static_cast<const char*>(base) + e_first * es +
+               (uint64_t)(uint32_t)c * (uint32_t)(C * H * D * es);
+    };
     auto rows_valid = [&](int c) -> int {
         // (32-bit: token counts are below 2^31, so this stays in scalar registers)
         const int left = (int)ntok - c * C;
@@ -407,17 +417,16 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     // beta bytes; the other waves read out of range (zeros, no memory request)
     // so that the load and its use stay unconditional
     const uint32_t lb = sa == 0 ? (uint32_t)l16 * (uint32_t)H * 4u : 0x80000000u;
+    const char* const beta_first = reinterpret_cast<const char*>(p.beta + (t_begin * H + h));
     auto load_raw = [&](int c, LoadSet<LPW>& R) {
         const int cc = c < nch ? c : nch - 1;
-        const int64_t e0 = chunk_base(cc);
         // the ranges end with the chunk's last row in the sequence: later rows read 0
         const int nv = rows_valid(cc);
-        const auto r = rsrc_chunk(ld_base + e0 * ld_es, ((nv - 1) * H * D + D) * ld_es);
+        const auto r = rsrc_chunk(chunk_ptr(ld_base, ld_es, cc), ((nv - 1) * H * D + D) * ld_es);
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
             R.x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ld_voff + i * ld_step, 0, 0));
-        const int64_t bbase = (t_begin + (int64_t)cc * C) * H + h;
-        const auto rb = rsrc_chunk(p.beta + bbase, ((nv - 1) * H + 1) * 4);
+        const auto rb = rsrc_chunk(beta_first + (uint64_t)(uint32_t)cc * (uint32_t)(C * H * 4), ((nv - 1) * H + 1) * 4);
         R.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lb, 0, 0));
     };
     // Gate logits (GATE): each stage-A wave carries 8 bytes per lane of a
@@ -522,8 +531,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     };
     auto v_load = [&](int c, int i) -> VChunk {
         const int cc = c < 0 ? 0 : (c < nch ? c : nch - 1);
-        const int64_t base = chunk_base(cc) + z * DVW;
-        const auto rv = rsrc_chunk(gv + base, w_v_zero ? 0 : ((rows_valid(cc) - 1) * H * D + DVW) * 2);
+        const auto rv = rsrc_chunk(chunk_ptr(gv, 2, cc) + z * DVW * 2, w_v_zero ? 0 : ((rows_valid(cc) - 1) * H * D + DVW) * 2);
         if constexpr (Cfg::VCB == 16)
             return __builtin_bit_cast(VChunk, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off(i), 0, 0));
         else
@@ -881,7 +889,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         // One store per lane; the range ends with the chunk's last row in the
         // sequence, and buffer stores out of range are dropped.
         if constexpr (!NOOUT && !GATE) {
-            const auto ro = rsrc_chunk(go + chunk_base(c), ((nv - 1) * H * D + D) * 2);
+            const auto ro = rsrc_chunk(chunk_ptr(go, 2, c), ((nv - 1) * H * D + D) * 2);
             const uint32_t oo = o_voff;
             if constexpr (TPW == 2)
                 __builtin_amdgcn_raw_buffer_store_b128(u32x4{ov[0][0], ov[0][1], ov[1][0], ov[1][1]}, ro, oo, 0, 0);
