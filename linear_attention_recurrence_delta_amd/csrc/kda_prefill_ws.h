@@ -133,13 +133,11 @@ struct WsCfg {
     static constexpr int RAW_STEP = 4 * 2 * PD;      // LDS bytes per raw load
     static constexpr size_t OFFV = OFFA + 2 * SA;
     static constexpr size_t OFFR = OFFV + 2 * SV;
-    // Output gate (GATE): per chunk slot the consumer waves' partial sums of
-    // squares [16 tokens][NCW waves] and their bf16 o tiles (64 lanes x 16 B
-    // per wave), 2-deep; the RMSNorm weight of the slab's columns.
-    // The gate factors Sigmoid(gate) * weight reach a 2-deep [C][PGT] fp32
-    // tile from the stage-A waves.
-    static constexpr size_t G_PART = OFFR + 2 * SR;
-    static constexpr size_t G_OST = G_PART + (GATE ? 2 * 4 * C * NCW : 0);
+    // Output gate (GATE): per chunk slot the consumer waves' bf16 o tiles (64
+    // lanes x 16 B per wave), 2-deep; the RMSNorm weight of the slab's
+    // columns.  The gate factors Sigmoid(gate) * weight reach a 2-deep
+    // [C][PGT] fp32 tile from the stage-A waves.
+    static constexpr size_t G_OST = OFFR + 2 * SR;
     static constexpr size_t G_W = G_OST + (GATE ? 2 * 1024 * NCW : 0);
     static constexpr int PGT = DVW + 4;              // fp32 pitch of the gate factor tile
     static constexpr size_t SGT = al16(4 * C * PGT);
@@ -747,38 +745,48 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 
     // ------------------------------------------------------------ consumers
     const uint32_t o_voff = (uint32_t)l16 * (uint32_t)(H * D) * 2u + (uint32_t)(col_base + 4 * TPW * g4) * 2u;
-    // Output gate (GATE): chunk c is gated one iteration after it is formed,
-    // when its rows' sums of squares over all consumer waves are in LDS (the
-    // gate logits are there too, brought by the stage-A waves).
+    // Output gate (GATE), applied by the Gram wave one iteration after the
+    // consumers park chunk c's o tiles (the gate factors are in LDS by then
+    // too, brought by the stage-A waves): the consumers, the critical chain,
+    // only park their tiles; the Gram wave has the slack for the rest.
     auto finish_gate = [&](int c) {
         // y = Sigmoid(gate) * o / sqrt(mean over the head's d_v of o^2 + eps)
         // * weight ("Understanding Kimi K3's attention", output equation), o
         // as rounded to the output dtype (the value a separate pass would read).
-        // Called in every iteration, c < 0 included (before the first chunk
-        // is formed: its store goes out of range and is dropped), so that
-        // no branch separates it from the consume that follows.
-        const bool real = c >= 0;
-        if (c < 0) c = 0;
+        // Lane (g4, l16) takes token row l16 and, from each consumer wave's
+        // tile, the piece that wave's lane `lane` parked: columns
+        // 32 w2 + 8 g4 .. + 7.  The row's sum of squares adds the lane's 32
+        // columns, then the 4 lanes of the row.
         const int nv = rows_valid(c);
-        const float* part = reinterpret_cast<const float*>(smem + Cfg::G_PART) + ((c & 1) * C + l16) * NCW;
+        const char* ost = smem + Cfg::G_OST + (size_t)(c & 1) * NCW * 1024 + lane * 16;
+        u32x4 ov[NCW];
         float ss = 0.f;
 #pragma unroll
-        for (int i = 0; i < NCW; ++i) ss += part[i];
-        const float rinv = __builtin_amdgcn_rsqf(ss * (1.f / D) + p.gate_eps);
-        const u32x4 ov = *reinterpret_cast<const u32x4*>(smem + Cfg::G_OST + ((c & 1) * NCW + w) * 1024 + lane * 16);
-        const float* gf = reinterpret_cast<const float*>(smem + Cfg::G_GT + (size_t)(c & 1) * Cfg::SGT) +
-                          l16 * Cfg::PGT + (col_base - z * DVW) + 8 * g4;
-        const f32x4 f0 = *reinterpret_cast<const f32x4*>(gf), f1 = *reinterpret_cast<const f32x4*>(gf + 4);
-        const float fv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
-        u32x4 yv;
+        for (int w2 = 0; w2 < NCW; ++w2) {
+            ov[w2] = *reinterpret_cast<const u32x4*>(ost + w2 * 1024);
 #pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-            const float lo = __uint_as_float(ov[wd] << 16), hi = __uint_as_float(ov[wd] & 0xffff0000u);
-            yv[wd] = pack_bf16x2(lo * rinv * fv[2 * wd], hi * rinv * fv[2 * wd + 1]);
+            for (int wd = 0; wd < 4; ++wd) ss = dot2_bf16(ov[w2][wd], ov[w2][wd], ss);
         }
-        const int64_t e0 = chunk_base(c);
-        const auto ro = rsrc(go + e0, (n_tok_elems - e0) * 2);
-        __builtin_amdgcn_raw_buffer_store_b128(yv, ro, (real && l16 < nv) ? o_voff : 0x80000000u, 0, 0);
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        const float rinv = __builtin_amdgcn_rsqf(ss * (1.f / D) + p.gate_eps);
+        const float* gf = reinterpret_cast<const float*>(smem + Cfg::G_GT + (size_t)(c & 1) * Cfg::SGT) + l16 * Cfg::PGT;
+        const auto ro = rsrc_chunk(chunk_ptr(go, 2, c), ((nv - 1) * H * D + D) * 2);
+#pragma unroll
+        for (int w2 = 0; w2 < NCW; ++w2) {
+            const int col = w2 * TPW * 16 + 4 * TPW * g4;  // first of the piece's columns in the slab
+            const f32x4 f0 = *reinterpret_cast<const f32x4*>(gf + col), f1 = *reinterpret_cast<const f32x4*>(gf + col + 4);
+            const float fv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
+            u32x4 yv;
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+                const float lo = __uint_as_float(ov[w2][wd] << 16), hi = __uint_as_float(ov[w2][wd] & 0xffff0000u);
+                yv[wd] = pack_bf16x2(lo * rinv * fv[2 * wd], hi * rinv * fv[2 * wd + 1]);
+            }
+            // one 16-byte store; rows past the chunk's last row in the sequence are dropped
+            __builtin_amdgcn_raw_buffer_store_b128(
+                yv, ro, (uint32_t)l16 * (uint32_t)(H * D) * 2u + (uint32_t)(z * DVW + col) * 2u, 0, 0);
+        }
     };
     auto consume = [&](int c, f32x4 (&Sm)[TPW][NCB]) {
         [[maybe_unused]] const int nv = rows_valid(c);
@@ -897,16 +905,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{ov[0][0], ov[0][1]}, ro, oo, 0, 0);
         }
         if constexpr (GATE) {
-            // this wave's share of each row's sum of squares (its 32 columns:
-            // 8 per lane, then the 4 lanes of a row) and the o tile, parked for
-            // the next iteration
+            // the o tile, parked for the Gram wave's gated store in the next
+            // iteration
             const u32x4 o4 = {ov[0][0], ov[0][1], ov[1][0], ov[1][1]};
-            float ss = 0.f;
-#pragma unroll
-            for (int wd = 0; wd < 4; ++wd) ss = dot2_bf16(o4[wd], o4[wd], ss);
-            ss += __shfl_xor(ss, 16, 64);
-            ss += __shfl_xor(ss, 32, 64);
-            if (g4 == 0) reinterpret_cast<float*>(smem + Cfg::G_PART)[((c & 1) * C + l16) * NCW + w] = ss;
             *reinterpret_cast<u32x4*>(smem + Cfg::G_OST + ((c & 1) * NCW + w) * 1024 + lane * 16) = o4;
         }
     };
@@ -970,15 +971,23 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             VRegs<VChunk> va, vb;
             __syncthreads();  // the two prologue barriers of the stage-A waves
             __syncthreads();
+            // (GATE: it also finishes chunk j - 4, whose o tiles the consumers
+            // parked in iteration j - 1, with the gated store.)
             for (int j = 0; j < iters; j += 2) {
                 load_v(j - 1, vb);
                 if (j - 2 >= 0 && j - 2 < nch) store_v(j - 2, va);
                 if (j - 1 >= 0 && j - 1 < nch) gram(j - 1);
+                if constexpr (GATE) {
+                    if (j - 4 >= 0 && j - 4 < nch) finish_gate(j - 4);
+                }
                 __syncthreads();
                 if (j + 1 < iters) {
                     load_v(j, va);
                     if (j - 1 >= 0 && j - 1 < nch) store_v(j - 1, vb);
                     if (j < nch) gram(j);
+                    if constexpr (GATE) {
+                        if (j - 3 >= 0 && j - 3 < nch) finish_gate(j - 3);
+                    }
                     __syncthreads();
                 }
             }
@@ -1032,7 +1041,6 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             __syncthreads();
             __syncthreads();
             for (int j = 0; j < iters; ++j) {
-                if constexpr (GATE) finish_gate(j - 4);
                 if (j - 3 >= 0 && j - 3 < nch) {
                     consume(j - 3, Sm);
                     const int c = j - 3;
