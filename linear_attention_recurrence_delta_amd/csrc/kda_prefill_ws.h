@@ -19,7 +19,7 @@
 //                          (a 16-token tile decays by at least -80), so no
 //                          factor leaves the bf16/fp32 exponent range.
 //   solve     (1 wave)     chunk m + 1: T = (I + A)^{-1} by a column sweep
-//                          (fp32; 15-way independent updates per step).
+//                          (fp32; four lanes per column, four rows each).
 //   consumers (NCW waves)  chunk m: X = Kt S, Qt S, U = T diag(beta)(V - X),
 //                          O = scale Qt S + P U, S <- Diag(gamma)(S + KL^T U)
 //                          (= Diag(gamma) S + Kbar^T U, Kbar = k e^{tot-L}:
@@ -198,6 +198,22 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t x) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
     return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E - 1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Lane K of each quad (4 adjacent lanes) broadcast to the quad (DPP
+// quad_perm [K, K, K, K]).
+template <int K>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), K * 0x55, 0xf, 0xf, false));
 }
 
 // What one workgroup of a pipelined launch works on: the token range of its
@@ -698,48 +714,40 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 
     // ------------------------------------------------------------ solve
     auto solve = [&](int c) {
-        // Rows of A^T are read by all 16 active lanes at once (broadcast),
-        // through one VGPR base and immediate offsets.
-        const float4* AT4 = reinterpret_cast<const float4*>(slotA(c)) + opaque_zero();
-        bf16_t* T = reinterpret_cast<bf16_t*>(slotT(c));
-        if (lane < 16) {
-            const int col = lane;
-            float x[16];
+        // Column sweep of the unit lower-triangular system: once T[s][col] is
+        // final, remove its contribution A[r][s] T[s][col] from every later row
+        // r (all independent).  Lane (col, q) = 4 col + q holds rows
+        // 4q .. 4q + 3 of column col; at step s the lane of the quad owning row
+        // s hands T[s][col] to the other three (a DPP quad broadcast) and every
+        // lane updates its four rows (A^T is stored with zeros at r <= s, so
+        // rows that are already final subtract exactly 0).  Each element sees
+        // the same multiply-adds in the same order as a one-lane-per-column
+        // sweep, with a quarter of the instructions.  The lanes of one quad
+        // row read the same 16 bytes of A^T row s (broadcast), requested W
+        // steps ahead through one VGPR base and immediate offsets.
+        const int col = lane >> 2, q = lane & 3;
+        const float4* AT4 = reinterpret_cast<const float4*>(slotA(c)) + opaque_zero() + q;
+        float x[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] = (r == col) ? 1.f : 0.f;
-            // Column sweep: once T[s][col] is final, remove its contribution
-            // A[r][s] T[s][col] from every later row r (all independent).
-            // Row s of A^T is requested W steps before step s uses it, and
-            // only its quads that reach past the diagonal (r > s), so the
-            // sweep waits on LDS latency once rather than at every step.
-            constexpr int W = 4;
-            f32x4 row[15][4];  // fully unrolled: named registers
-            auto request = [&](int s) {
+        for (int j = 0; j < 4; ++j) x[j] = (4 * q + j == col) ? 1.f : 0.f;
+        constexpr int W = 4;
+        f32x4 row[15];  // A[4q .. 4q + 3][s], named registers
 #pragma unroll
-                for (int q = (s + 1) / 4; q < 4; ++q)
-                    row[s][q] = *reinterpret_cast<const f32x4*>(AT4 + s * (PA / 4) + q);
-            };
+        for (int st = 0; st < W; ++st) row[st] = *reinterpret_cast<const f32x4*>(AT4 + st * (PA / 4));
+        static_for<0, 15>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int st = decltype(sc)::value;
+            if constexpr (st + W < 15) row[st + W] = *reinterpret_cast<const f32x4*>(AT4 + (st + W) * (PA / 4));
+            asm volatile("" ::"v"(row[st]));  // the whole quad: no narrowing into 4-byte reads
+            const float ts = quad_bcast<st / 4>(x[st % 4]);
 #pragma unroll
-            for (int s = 0; s < W; ++s) request(s);
+            for (int j = 0; j < 4; ++j) x[j] -= row[st][j] * ts;
+        });
+        uint16_t* tq = reinterpret_cast<uint16_t*>(slotT(c)) + (4 * q) * PK + col;
 #pragma unroll
-            for (int s = 0; s < 15; ++s) {
-                if (s + W < 15) request(s + W);
-                // whole quads stay whole: no narrowing into 4-byte reads
-#pragma unroll
-                for (int q = (s + 1) / 4; q < 4; ++q) asm volatile("" ::"v"(row[s][q]));
-                const float ts = x[s];
-#pragma unroll
-                for (int r = s + 1; r < 16; ++r) {
-                    x[r] -= row[s][r >> 2][r & 3] * ts;
-                }
-            }
-            uint16_t* tcol = reinterpret_cast<uint16_t*>(T) + col;
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const uint32_t pr = pack_bf16x2(x[r], x[r + 1]);
-                tcol[r * PK] = (uint16_t)(pr & 0xffffu);
-                tcol[(r + 1) * PK] = (uint16_t)(pr >> 16);
-            }
+        for (int j = 0; j < 4; j += 2) {
+            const uint32_t pr = pack_bf16x2(x[j], x[j + 1]);
+            tq[j * PK] = (uint16_t)(pr & 0xffffu);
+            tq[(j + 1) * PK] = (uint16_t)(pr >> 16);
         }
     };
 
