@@ -405,15 +405,22 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     // over whole token rows: units 0-3 the q tile and 4-7 the k tile (4 rows
     // of 256 B each), units 8-15 the g tile (2 rows of 512 B each); fused,
     // units 8-11 the bf16 gate input z (4 rows each) and no more.  Stage-A
-    // wave sa issues units LPW sa .. LPW sa + LPW - 1 (all of one tensor) and
-    // wave 0 also beta, so every cache line is requested by exactly one load
+    // wave sa issues the LPW units of its group, LPW ld_grp .. LPW ld_grp +
+    // LPW - 1 (all of one tensor; ld_grp = sa except as below), and wave 0
+    // also beta, so every cache line is requested by exactly one load
     // instruction.  The pieces are parked row-major in LDS and read back
     // after a barrier in the layout stage A computes on.  A wave past the
     // last unit still issues its loads, at an out-of-range offset (zeros, no
     // memory request), and parks them in its own corner of LDS, so that no
     // load or its use depends on the wave.
     constexpr int LPW = Cfg::LPW;
-    const int ld_u0 = sa * LPW;
+    // Fused, the 12 units leave two stage-A waves without a raw load.  With
+    // two consumer waves (SIMDs 0 and 1, stage-A wave sa on SIMD sa mod 4) the
+    // q and k units, whose waves also form the rows' inverse norms, go to the
+    // stage-A waves on SIMDs 2 and 3, the z units to the older and no load to
+    // the younger stage-A wave of SIMDs 0 and 1: unit groups 4 5 0 1 6 7 2 3.
+    const int ld_grp = (FUSED && NCW == 2) ? (int)((0x32761054u >> (4 * sa)) & 15u) : sa;
+    const int ld_u0 = ld_grp * LPW;
     const bool ld_none = ld_u0 >= Cfg::NUNITS;
     const bool ld_bf16 = FUSED || ld_u0 < 8;
     const int ld_lpr = ld_bf16 ? 16 : 32;  // lanes per token row
