@@ -405,8 +405,9 @@ kda_status kda_output_gate(int64_t total_tokens, int32_t num_heads,
  * returned in place of o.  Where one workgroup holds a whole head (bf16,
  * d = 128, the library's whole-head slab: batches with more (sequence, head)
  * units than half the compute units), the gate is applied before the store
- * and o never reaches memory: the o tiles go through LDS to one wave of the
- * workgroup, which forms each row's sum of squares and stores y.  Otherwise o is written to y and
+ * and o never reaches memory: the o tiles go through LDS to two waves of the
+ * workgroup, each of which forms every row's sum of squares and stores half
+ * of y.  Otherwise o is written to y and
  * kda_output_gate runs over it in place.  The norm is taken over the o values
  * as rounded to qkv_dtype, as a separate pass would read them.
  *

@@ -760,18 +760,22 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 
     // ------------------------------------------------------------ consumers
     const uint32_t o_voff = (uint32_t)l16 * (uint32_t)(H * D) * 2u + (uint32_t)(col_base + 4 * TPW * g4) * 2u;
-    // Output gate (GATE), applied by the Gram wave one iteration after the
-    // consumers park chunk c's o tiles (the gate factors are in LDS by then
-    // too, brought by the stage-A waves): the consumers, the critical chain,
-    // only park their tiles; the Gram wave has the slack for the rest.
-    auto finish_gate = [&](int c) {
+    // Output gate (GATE), applied one iteration after the consumers park
+    // chunk c's o tiles (the gate factors are in LDS by then too, brought by
+    // the stage-A waves): the consumers, the critical chain, only park their
+    // tiles; the Gram wave (part 0) and the solve wave (part 1), which have
+    // the slack, each form every row's sum of squares and scale and store
+    // half of the tiles.
+    auto finish_gate = [&](int c, auto partc) {
+        constexpr int part = decltype(partc)::value;
         // y = Sigmoid(gate) * o / sqrt(mean over the head's d_v of o^2 + eps)
         // * weight ("Understanding Kimi K3's attention", output equation), o
         // as rounded to the output dtype (the value a separate pass would read).
         // Lane (g4, l16) takes token row l16 and, from each consumer wave's
         // tile, the piece that wave's lane `lane` parked: columns
         // 32 w2 + 8 g4 .. + 7.  The row's sum of squares adds the lane's 32
-        // columns, then the 4 lanes of the row.
+        // columns, then the 4 lanes of the row; the lane then stores its
+        // pieces of tiles w2 = part NCW/2 .. part NCW/2 + NCW/2 - 1.
         const int nv = rows_valid(c);
         const char* ost = smem + Cfg::G_OST + (size_t)(c & 1) * NCW * 1024 + lane * 16;
         u32x4 ov[NCW];
@@ -788,7 +792,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         const float* gf = reinterpret_cast<const float*>(smem + Cfg::G_GT + (size_t)(c & 1) * Cfg::SGT) + l16 * Cfg::PGT;
         const auto ro = rsrc_chunk(chunk_ptr(go, 2, c), ((nv - 1) * H * D + D) * 2);
 #pragma unroll
-        for (int w2 = 0; w2 < NCW; ++w2) {
+        for (int w2 = part * (NCW / 2); w2 < (part + 1) * (NCW / 2); ++w2) {
             const int col = w2 * TPW * 16 + 4 * TPW * g4;  // first of the piece's columns in the slab
             const f32x4 f0 = *reinterpret_cast<const f32x4*>(gf + col), f1 = *reinterpret_cast<const f32x4*>(gf + col + 4);
             const float fv[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
@@ -987,13 +991,14 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             __syncthreads();  // the two prologue barriers of the stage-A waves
             __syncthreads();
             // (GATE: it also finishes chunk j - 4, whose o tiles the consumers
-            // parked in iteration j - 1, with the gated store.)
+            // parked in iteration j - 1, with the gated store of half the
+            // tiles; the solve wave stores the other half.)
             for (int j = 0; j < iters; j += 2) {
                 load_v(j - 1, vb);
                 if (j - 2 >= 0 && j - 2 < nch) store_v(j - 2, va);
                 if (j - 1 >= 0 && j - 1 < nch) gram(j - 1);
                 if constexpr (GATE) {
-                    if (j - 4 >= 0 && j - 4 < nch) finish_gate(j - 4);
+                    if (j - 4 >= 0 && j - 4 < nch) finish_gate(j - 4, std::integral_constant<int, 0>{});
                 }
                 __syncthreads();
                 if (j + 1 < iters) {
@@ -1001,7 +1006,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                     if (j - 1 >= 0 && j - 1 < nch) store_v(j - 1, vb);
                     if (j < nch) gram(j);
                     if constexpr (GATE) {
-                        if (j - 3 >= 0 && j - 3 < nch) finish_gate(j - 3);
+                        if (j - 3 >= 0 && j - 3 < nch) finish_gate(j - 3, std::integral_constant<int, 0>{});
                     }
                     __syncthreads();
                 }
@@ -1011,6 +1016,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             __syncthreads();
             for (int j = 0; j < iters; ++j) {
                 if (j - 2 >= 0 && j - 2 < nch) solve(j - 2);
+                if constexpr (GATE) {
+                    if (j - 4 >= 0 && j - 4 < nch) finish_gate(j - 4, std::integral_constant<int, 1>{});
+                }
                 __syncthreads();
             }
         } else {
