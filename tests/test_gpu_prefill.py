@@ -124,6 +124,20 @@ def test_bf16_ragged_varlen(kda, chunk, scale):
     _check_all(kda, None, inp, chunk=chunk, scale=scale, label="bf16 varlen scale=%g" % scale)
 
 
+@pytest.mark.parametrize("n_seqs", [64, 65])
+def test_bf16_many_sequences_dispatch_order(kda, n_seqs):
+    # A pack of up to 64 sequences goes out longest first (the kernel ranks the
+    # lengths, ties in sequence order); 65 keep sequence order.  Ties and empty
+    # sequences included; with initial states, every output row and final
+    # state must still land on its own (sequence, head).
+    rng = np.random.default_rng(300 + n_seqs)
+    lengths = [int(x) for x in rng.integers(1, 120, n_seqs)]
+    lengths[3] = lengths[10] = lengths[40] = 77
+    lengths[5] = lengths[n_seqs - 1] = 0
+    inp = _inputs(sum(lengths), 2, 128, torch.bfloat16, 300 + n_seqs, lengths=lengths, init_std=0.05)
+    _check_all(kda, None, inp, chunk=16, label="bf16 %d sequences" % n_seqs)
+
+
 @pytest.mark.parametrize("g_mode", ["mild", "zero"])
 @pytest.mark.parametrize("chunk", [16, 64])
 def test_bf16_weak_decay_long_memory(kda, g_mode, chunk):
