@@ -250,7 +250,7 @@ __device__ inline int ws_seq_of_rank(const PrefillParams& p, int r) {
         before += (lm > len || (lm == len && m < lane)) ? 1 : 0;
     }
     const uint64_t hit = __ballot(lane < p.N && before == r);
-    return (int)__builtin_ctzll(hit);  // one lane for every r < N
+    return hit ? (int)__builtin_ctzll(hit) : r;  // one lane for every r < N
 }
 
 template <int D, bool SEG, bool PAIR>
