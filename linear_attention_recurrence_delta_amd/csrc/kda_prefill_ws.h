@@ -1079,6 +1079,10 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             // vector-register limit in the 14-wave workgroup)
             const int ck0 = p.ckpt ? __builtin_amdgcn_readfirstlane((int)ckpt_first_slot(p, n, lane)) : 0;
             const int ck_chunks = p.ckpt ? p.ckpt_interval / C : 1;
+            // the next checkpoint's chunk and how many came before it (no
+            // division per chunk: (c + 1) % ck_chunks == 0 exactly when c
+            // reaches ck_next, the chunks being visited in order)
+            int ck_next = ck_chunks - 1, ck_k = 0;
             if constexpr (GATE) {
                 // the slab's RMSNorm weights, read before the first gated store
                 // (two barriers away)
@@ -1092,9 +1096,11 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 if (j - 3 >= 0 && j - 3 < nch) {
                     consume(j - 3, Sm);
                     const int c = j - 3;
-                    if (p.ckpt && (c + 1) % ck_chunks == 0 && (c + 1) * C <= (int)ntok) {
-                        const int64_t slot = (int64_t)ck0 + (c + 1) / ck_chunks - 1;
-                        if (slot < p.ckpt_cap) {
+                    if (p.ckpt && c == ck_next) {
+                        const int64_t slot = (int64_t)ck0 + ck_k;
+                        ck_next += ck_chunks;
+                        ++ck_k;
+                        if ((c + 1) * C <= (int)ntok && slot < p.ckpt_cap) {
                             if constexpr (CKB) {
                                 // rows 16ct + 4g4 .. + 3 of a column: one 8-byte store
                                 const auto rc = buffer_rsrc(reinterpret_cast<uint16_t*>(p.ckpt) + (slot * H + h) * D * D,
