@@ -85,15 +85,22 @@ KERNEL_SOURCES = {
 }
 
 
+def _flags_key(flags, root):
+    """Compiler flags with absolute paths made relative to the repository, so
+    that a digest does not depend on where the repository is checked out."""
+    return [os.path.relpath(x, root) if os.path.isabs(x) else x for x in flags]
+
+
 def kernel_source_digest(kernel):
     from linear_attention_recurrence_delta_amd import build_lib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_recurrence_delta_amd", "csrc")
+    root = build_lib.ROOT
     for f in KERNEL_SOURCES[kernel]:
         if f == "build":
-            h.update(repr((build_lib.COMMON, build_lib.DEVICE)).encode())
+            h.update(repr((_flags_key(build_lib.COMMON, root), _flags_key(build_lib.DEVICE, root))).encode())
         elif f.startswith("flags:"):
-            h.update(repr(build_lib.PER_FILE.get(f[len("flags:"):], [])).encode())
+            h.update(repr(_flags_key(build_lib.PER_FILE.get(f[len("flags:"):], []), root)).encode())
         else:
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
