@@ -470,6 +470,7 @@ def main():
             "prefill_varlen": {
                 "tokens_per_s": wv["T"] / (v_avg * 1e-3), "ms": v_avg,
                 "hbm_gbs": PREFILL_BYTES_PER_TOKEN_HEAD * wv["T"] * wv["H"] / (v_avg * 1e-3) / 1e9,
+                "traffic": measured_traffic("kda_prefill_k3_varlen_32k"),
                 "lengths": wv["lengths"],
             },
         })
