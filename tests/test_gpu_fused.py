@@ -5,7 +5,7 @@ g = -5 Sigmoid(e^{A_h} z)) in fp64 from the very bf16/fp32 values handed to
 the GPU, then runs its token recurrence.  Cases: ragged varlen with raw q/k
 of varied norms and per-head A, zero query/key vectors, an initial state,
 bitwise invariance across value-slab widths, and the dense K3 workload on
-sampled heads.
+every head.
 """
 import numpy as np
 import pytest
@@ -91,18 +91,25 @@ def test_slab_width_invariance(kda, cols):
     assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
 
 
-def test_dense_k3_sampled_heads(kda, oracle_mod):
+def test_dense_k3_all_heads(kda, oracle_mod):
     """B=1 T=32768 H=96, a_log = 0 (the g distribution of the other
-    workloads): heads 0, 41, 95 against the oracle."""
+    workloads): every head against the oracle, 16 heads per oracle call;
+    the outputs start as NaN so that a head the kernel missed fails."""
     from linear_attention_recurrence_delta_amd import synth
-    say("CASE fused k3 dense 32K x 96, heads 0, 41, 95")
+    say("CASE fused k3 dense 32K x 96, every head")
     T, H = 32768, 96
     q, k, v, z, a_log, beta, _ = synth.fused_inputs(T, H, 128, BF16, 406, DEV, a_log_std=0.0)
-    o, S = kda.kda_prefill_fused(q, k, v, z, a_log, beta)
+    o = torch.full((T, H, 128), float("nan"), dtype=BF16, device=DEV)
+    S = torch.full((1, H, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+    kda.kda_prefill_fused(q, k, v, z, a_log, beta, out=o, final_state=S)
     torch.cuda.synchronize()
-    heads = torch.tensor([0, 41, 95], device=DEV)
-    sl = lambda x: f64(x.index_select(1, heads))
-    ro, rs = oracle_mod.prefill_fused(sl(q), sl(k), sl(v), sl(z), f64(a_log.index_select(0, heads)), sl(beta))
-    eo, es = rel_err(sl(o), ro), rel_err(f64(S[0].index_select(0, heads)), rs[0])
-    say("  dense fused: rel err o=%.3e S=%.3e" % (eo, es))
-    assert eo <= TOL[BF16] and es <= TOL[BF16]
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    worst_o = worst_s = 0.0
+    for h0 in range(0, H, 16):
+        heads = torch.arange(h0, h0 + 16, device=DEV)
+        sl = lambda x: f64(x.index_select(1, heads))
+        ro, rs = oracle_mod.prefill_fused(sl(q), sl(k), sl(v), sl(z), f64(a_log.index_select(0, heads)), sl(beta))
+        worst_o = max(worst_o, rel_err(sl(o), ro))
+        worst_s = max(worst_s, rel_err(f64(S[0].index_select(0, heads)), rs[0]))
+    say("  dense fused, all 96 heads: rel err o=%.3e S=%.3e" % (worst_o, worst_s))
+    assert worst_o <= TOL[BF16] and worst_s <= TOL[BF16]
