@@ -7,7 +7,7 @@ used for the forward outputs: max |difference| <= 2e-2 * max |reference|.
 Cases: ragged packed batches with an empty and a one-token sequence, initial
 states and final-state gradients, a readout scale, the three decay regimes of
 the synthetic workloads (K3-strength, mild and zero decay), beta at 0 and 1,
-a dense batch, determinism, and the dense 32K x 96 workload on sampled heads.
+a dense batch, determinism, and the dense 32K x 96 workload on every head.
 """
 import numpy as np
 import pytest
@@ -106,23 +106,28 @@ def test_deterministic(kda):
         assert torch.equal(x, y)
 
 
-def test_dense_k3_sampled_heads(kda, oracle_mod):
-    """B=1 T=32768 H=96: heads 0, 41 and 95 against the oracle."""
+def test_dense_k3_all_heads(kda, oracle_mod):
+    """B=1 T=32768 H=96: every head's gradients against the oracle's adjoint,
+    16 heads per oracle call."""
     from linear_attention_recurrence_delta_amd import synth
-    say("CASE backward k3 dense 32K x 96, heads 0, 41, 95")
+    say("CASE backward k3 dense 32K x 96, every head")
     T, H = 32768, 96
     q, k, v, g, beta, gen = synth.token_inputs(T, H, 128, 128, BF16, 607, DEV)
     d_o = torch.randn((T, H, 128), generator=gen, device=DEV).to(BF16)
     got = kda.kda_prefill_backward(q, k, v, g, beta, d_o)
     torch.cuda.synchronize()
-    heads = torch.tensor([0, 41, 95], device=DEV)
-    sl = lambda x: f64(x.index_select(1, heads))
-    ref = oracle_mod.prefill_backward(sl(q), sl(k), sl(v), sl(g), sl(beta), sl(d_o))
-    errs = {}
-    for name, a, b in zip(NAMES[:5], got[:5], ref[:5]):
-        errs[name] = rel_err(sl(a), b)
-    errs["dS0"] = rel_err(f64(got[5][0].index_select(0, heads)), ref[5][0])
-    say("  dense: " + " ".join("%s=%.2e" % kv for kv in errs.items()))
+    for x in got:
+        assert torch.isfinite(x.float()).all()
+    errs = {name: 0.0 for name in NAMES[:5] + ("dS0",)}
+    for h0 in range(0, H, 16):
+        heads = torch.arange(h0, h0 + 16, device=DEV)
+        sl = lambda x: f64(x.index_select(1, heads))
+        ref = oracle_mod.prefill_backward(sl(q), sl(k), sl(v), sl(g), sl(beta), sl(d_o))
+        for name, a, b in zip(NAMES[:5], got[:5], ref[:5]):
+            errs[name] = max(errs[name], rel_err(sl(a), b))
+        errs["dS0"] = max(errs["dS0"], rel_err(f64(got[5][0].index_select(0, heads)), ref[5][0]))
+        say("  heads %d..%d done" % (h0, h0 + 15))
+    say("  dense, all 96 heads: " + " ".join("%s=%.2e" % kv for kv in errs.items()))
     for name, e in errs.items():
         assert e <= TOL[BF16], (name, e)
 
