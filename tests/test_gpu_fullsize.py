@@ -16,7 +16,9 @@ kernels never wrote cannot pass:
   chain's split-and-resume is bitwise;
 * batched decode 256 sequences x 96 heads: every output and every state
   after the first step, then 1000 steps with a seeded sample of 256 units
-  tracked against the oracle on every step.
+  tracked against the oracle on every step;
+* the dense workload with a state checkpoint every 4096 tokens: all 8
+  checkpoints of every head against the oracle's.
 """
 import numpy as np
 import pytest
@@ -172,8 +174,8 @@ def test_k3_decode_1000_steps(kda, oracle_mod):
 
 
 def test_k3_dense_32k_checkpoints(kda, oracle_mod):
-    """State checkpoints every 4096 tokens of the dense workload: sampled
-    checkpoints against the oracle, the last one equal to the final state,
+    """State checkpoints every 4096 tokens of the dense workload: every
+    checkpoint against the oracle, the last one equal to the final state,
     and prefill resumed from a checkpoint reproducing the rest of the run."""
     from linear_attention_recurrence_delta_amd import synth
     say("CASE k3_dense_32k checkpoints every 4096 tokens")
@@ -186,13 +188,17 @@ def test_k3_dense_32k_checkpoints(kda, oracle_mod):
     assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
     assert ck.shape[0] == w["T"] // I == 8 and first.cpu().tolist() == [0, 8]
     assert torch.equal(ck[7], S[0])
-    # checkpoint 0 of three heads against the oracle's 4096-token prefix
-    heads = [0, 41, 95]
-    hi = torch.tensor(heads, device=DEV)
-    sl = lambda x: f64(x[:I].index_select(1, hi))
-    _, rs = oracle_mod.prefill(sl(w["q"]), sl(w["k"]), sl(w["v"]), sl(w["g"]), sl(w["beta"]))
-    err = rel_err(f64(ck[0].index_select(0, hi)), rs[0])
-    say("  checkpoint 0, heads %s: rel err %.3e" % (heads, err))
+    # every checkpoint of every head against the oracle's, which are the final
+    # states of its recurrence over the 4096, 8192, ... token prefixes
+    err = 0.0
+    for h0 in range(0, w["H"], HEAD_BATCH):
+        hi = torch.arange(h0, min(h0 + HEAD_BATCH, w["H"]), device=DEV)
+        sl = lambda x: f64(x.index_select(1, hi))
+        rck, rfirst = oracle_mod.prefill_checkpoints(sl(w["q"]), sl(w["k"]), sl(w["v"]), sl(w["g"]), sl(w["beta"]),
+                                                     interval=I)
+        assert list(rfirst) == [0, 8]
+        err = max(err, rel_err(f64(ck.index_select(1, hi)), rck))
+    say("  all 8 checkpoints of all %d heads: rel err %.3e" % (w["H"], err))
     assert err <= BF16_TOL
     # resume from checkpoint 3 (after 16384 tokens): the rest of the run again
     R = 4 * I
