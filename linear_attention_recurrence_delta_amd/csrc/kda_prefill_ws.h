@@ -478,9 +478,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     // Gate logits (GATE): each stage-A wave carries 8 bytes per lane of a
     // chunk's [C][DVW] bf16 gate tile (rows 2 sa and 2 sa + 1, 4 columns per
     // lane) from HBM into gate slot (c & 1): loaded in iteration c + 2,
-    // parked in c + 3, read by the consumers' gated store in c + 4; the slot
-    // is next written (chunk c + 2) in c + 5.  Chunks outside the sequence
-    // read zeros without a memory request and are not parked.
+    // parked in c + 3, read by the gated store (Gram and solve waves) in
+    // c + 4; the slot is next written (chunk c + 2) in c + 5.  Chunks outside
+    // the sequence read zeros without a memory request and are not parked.
     const int gt_row = 2 * sa + (lane >> 5), gt_col = 4 * (lane & 31);
     auto load_gt = [&](int c) -> u32x2 {
         const bool in = c >= 0 && c < nch;
@@ -491,7 +491,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, off, 0, 0));
     };
     // Parked as the gate factor Sigmoid(gate) * weight of each column (fp32),
-    // so the consumers' gated store only multiplies.
+    // so the gated store only multiplies.
     auto park_gt = [&](int c, u32x2 x) {
         if (c >= 0 && c < nch) {
             const float* wt = reinterpret_cast<const float*>(smem + Cfg::G_W) + gt_col;
@@ -949,8 +949,8 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{ov[0][0], ov[0][1]}, ro, oo, 0, 0);
         }
         if constexpr (GATE) {
-            // the o tile, parked for the Gram wave's gated store in the next
-            // iteration
+            // the o tile, parked for the gated store of the Gram and solve
+            // waves in the next iteration
             const u32x4 o4 = {ov[0][0], ov[0][1], ov[1][0], ov[1][1]};
             *reinterpret_cast<u32x4*>(smem + Cfg::G_OST + ((c & 1) * NCW + w) * 1024 + lane * 16) = o4;
         }
