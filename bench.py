@@ -283,9 +283,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each (sequence, head) "
-              "recurrence is independent; sharding is described in DESIGN.md). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (each (sequence, head) "
+              "recurrence is independent, so heads and sequences split across GPUs with no "
+              "communication). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
