@@ -486,35 +486,50 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         const auto rb = rsrc_chunk(beta_first + (uint64_t)(uint32_t)cc * (uint32_t)(C * H * 4), ((nv - 1) * H + 1) * 4);
         R.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, lb, 0, 0));
     };
-    // Gate logits (GATE): each stage-A wave carries 8 bytes per lane of a
-    // chunk's [C][DVW] bf16 gate tile (rows 2 sa and 2 sa + 1, 4 columns per
-    // lane) from HBM into gate slot (c & 1): loaded in iteration c + 2,
-    // parked in c + 3, read by the gated store (Gram and solve waves) in
-    // c + 4; the slot is next written (chunk c + 2) in c + 5.  Chunks outside
-    // the sequence read zeros without a memory request and are not parked.
-    const int gt_row = 2 * sa + (lane >> 5), gt_col = 4 * (lane & 31);
-    auto load_gt = [&](int c) -> u32x2 {
+    // Gate logits (GATE): stage-A waves carry a chunk's [C][DVW] bf16 gate
+    // tile from HBM into gate slot (c & 1), as two row pairs (8 bytes per lane
+    // each, 4 columns per lane): loaded in iteration c + 2, parked in c + 3,
+    // read by the gated store (Gram and solve waves) in c + 4; the slot is
+    // next written (chunk c + 2) in c + 5.  The older stage-A waves of SIMDs 0
+    // and 1 (0 and 1), which have the slack, take rows 0-3 and 4-7; waves 2-5
+    // rows 8-15, two each; the youngest, 6 and 7, none (a timing copy of the
+    // gated launch: 2.6% shorter than with two rows on every stage-A wave).
+    // A wave's unused pair, and chunks outside the sequence, read
+    // zeros without a memory request and are not parked, so every wave issues
+    // the same two loads.
+    const int gt_col = 4 * (lane & 31);
+    const bool gt_a = sa < 6, gt_b = sa < 2;
+    const int gt_row_a = (sa < 2 ? 4 * sa : 8 + 2 * (sa - 2)) + (lane >> 5);
+    const int gt_row_b = 4 * sa + 2 + (lane >> 5);
+    struct GtSet {
+        u32x2 a, b;
+    };
+    auto load_gt = [&](int c) -> GtSet {
         const bool in = c >= 0 && c < nch;
         const int cc = in ? c : 0;
         const int64_t base = chunk_base(cc) + z * DVW;
         const auto rg = rsrc(static_cast<const bf16_t*>(p.gate) + base, (n_tok_elems - base) * 2);
-        const uint32_t off = in ? ((uint32_t)gt_row * (uint32_t)(H * D) + (uint32_t)gt_col) * 2u : 0x80000000u;
-        return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, off, 0, 0));
+        const uint32_t oa = in && gt_a ? ((uint32_t)gt_row_a * (uint32_t)(H * D) + (uint32_t)gt_col) * 2u : 0x80000000u;
+        const uint32_t ob = in && gt_b ? ((uint32_t)gt_row_b * (uint32_t)(H * D) + (uint32_t)gt_col) * 2u : 0x80000000u;
+        return GtSet{__builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, oa, 0, 0)),
+                     __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, ob, 0, 0))};
     };
-    // Parked as the gate factor Sigmoid(gate) * weight of each column (fp32),
-    // so the gated store only multiplies.
-    auto park_gt = [&](int c, u32x2 x) {
-        if (c >= 0 && c < nch) {
-            const float* wt = reinterpret_cast<const float*>(smem + Cfg::G_W) + gt_col;
-            f32x4 f;
+    auto park_one = [&](int c, u32x2 x, int row) {
+        const float* wt = reinterpret_cast<const float*>(smem + Cfg::G_W) + gt_col;
+        f32x4 f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t wd = x[e >> 1];
-                const float gl = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
-                f[e] = wt[e] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gl));
-            }
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(smem + Cfg::G_GT + (size_t)(c & 1) * Cfg::SGT) +
-                                      gt_row * Cfg::PGT + gt_col) = f;
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t wd = x[e >> 1];
+            const float gl = __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+            f[e] = wt[e] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gl));
+        }
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(smem + Cfg::G_GT + (size_t)(c & 1) * Cfg::SGT) +
+                                  row * Cfg::PGT + gt_col) = f;
+    };
+    auto park_gt = [&](int c, const GtSet& x) {
+        if (c >= 0 && c < nch) {
+            if (gt_a) park_one(c, x.a, gt_row_a);
+            if (gt_b) park_one(c, x.b, gt_row_b);
         }
     };
     // Raw tile of chunk c (two slots in rotation).
@@ -988,7 +1003,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             // that ends iteration c - 1.
             LoadSet<LPW> rawA, rawB;
             RawSet<IPW> cur;
-            [[maybe_unused]] u32x2 gtA = {0u, 0u}, gtB = {0u, 0u};
+            [[maybe_unused]] GtSet gtA = {}, gtB = {};
             load_raw(0, rawA);
             load_raw(1, rawB);
             park_raw(0, rawA);
@@ -1000,8 +1015,8 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             // Unrolled four times, so that the 4-deep slot of the chunk that
             // stage A works on (c & 3 = u) is an immediate offset.  Even steps
             // load into set B and park set A, odd steps the other way round.
-            auto step = [&](int jj, auto uc, LoadSet<LPW>& into, const LoadSet<LPW>& from, u32x2& gt_into,
-                            const u32x2& gt_from) __attribute__((always_inline)) {
+            auto step = [&](int jj, auto uc, LoadSet<LPW>& into, const LoadSet<LPW>& from, GtSet& gt_into,
+                            const GtSet& gt_from) __attribute__((always_inline)) {
                 load_raw(jj + 3, into);
                 if constexpr (GATE) gt_into = load_gt(jj - 2);
                 if (jj < nch) stage_a(jj, cur, decltype(uc)::value);
