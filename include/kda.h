@@ -103,8 +103,8 @@ int32_t kda_decode_supported(int32_t qkv_dtype, int32_t d_k, int32_t d_v);
  * workspace.  The only user is the sequence-segment scan (see
  * kda_prefill_desc.segments), which the library picks for dense batches with
  * few (sequence, head) recurrences per compute unit: about (G - 1) * 128 KiB
- * per (sequence, head) for G segments per sequence (30 MiB for one
- * 1,048,576-token sequence of 16 heads on 256 compute units).
+ * per (sequence, head) for G segments per sequence (32 MiB for one
+ * 1,048,576-token sequence of 16 heads on 256 compute units, G = 17).
  */
 size_t kda_prefill_workspace_bytes(int32_t num_seqs, int64_t total_tokens,
                                    int32_t num_heads, int32_t d_k, int32_t d_v,
@@ -176,12 +176,12 @@ kda_status kda_prefill(int32_t num_seqs, int64_t total_tokens,
  * are too few to fill the device is cut into G segments per sequence.  The
  * state update is affine in the state ("Understanding Kimi K3's attention",
  * state-update equation), so each segment g is one map S_end = M_g S_start +
- * B_g.  Three launches: the maps of segments 0 .. G-2 are computed in
+ * B_g.  Three launches: the maps of segments 1 .. G-2 are computed in
  * parallel, M_g and B_g of one segment by one workgroup (M_g from the
- * identity with v = 0, B_g from zero, or from the initial state for segment
- * 0, which makes B_0 that segment's end state); a short combine chains
- * start(g + 1) = M_g start(g) + B_g in fp32; all G segments run again from
- * their start states with outputs.  This is the pages' state
+ * identity with v = 0, B_g from zero), beside segment 0, which runs from the
+ * initial state with its outputs and leaves its end state; a short combine
+ * chains start(g + 1) = M_g start(g) + B_g in fp32; segments 1 .. G-1 run
+ * again from their start states with outputs.  This is the pages' state
  * passing between chunks ("Inside Kimi K3", section "Sequence mixing")
  * applied between segments, in parallel over segments instead of one chain.
  */

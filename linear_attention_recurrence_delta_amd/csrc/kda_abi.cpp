@@ -113,7 +113,8 @@ const PrefillVariant* pick_variant(int32_t dtype, int32_t D, int32_t C, int64_t 
 // Sequence-segment scan plan (kda_internal.h, PrefillParams::seg_*): G
 // segments per sequence of Lc chunks each, the last one taking the rest.
 // Phase 1 runs one map-pair workgroup (M and B of one segment, stage A
-// shared) for each of segments 0 .. G - 2, phase 3 one run per segment.
+// shared) for each of segments 1 .. G - 2 and segment 0 with its outputs,
+// phase 3 one run for each of segments 1 .. G - 1.
 struct SegPlan {
     int G = 1;
     int64_t len = 0;  // tokens per segment (the last: the rest)
@@ -122,15 +123,15 @@ struct SegPlan {
 constexpr int kMaxSegments = 256;
 
 // The library's choice: with P = compute units per (sequence, head) unit,
-// G = P segments fill the device in both phases (units (G - 1) map pairs,
-// then units G runs), each workgroup a chain of 1 / G of the sequence
-// (against the whole sequence for the direct chain), twice.  Worth it from
-// P = 4 on, with segments of at least 64 chunks.
+// G = P + 1 segments fill the device in both phases (units (G - 1)
+// workgroups each), each workgroup a chain of 1 / G of the sequence (against
+// the whole sequence for the direct chain), twice.  Worth it from P = 4 on,
+// with segments of at least 64 chunks.
 int auto_segments(int64_t units, int64_t t_seq) {
     if (units <= 0) return 1;
     const int64_t P = device_cu_count() / units;
     if (P < 4) return 1;
-    const int G = (int)(P < 32 ? P : 32);
+    const int G = (int)(P < 32 ? P + 1 : 33);
     const int64_t chunks = (t_seq + 15) / 16;
     return chunks >= 64 * (int64_t)G ? G : 1;
 }

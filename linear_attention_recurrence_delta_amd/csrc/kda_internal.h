@@ -43,14 +43,15 @@ struct PrefillParams {
     // off, one workgroup chain per (sequence, head, slab) walks the whole
     // sequence.  Otherwise each sequence is cut into seg_G segments of
     // seg_len tokens, the last one running to the end of the sequence.
-    // Phase 1 (the map-pair kernel) computes, for g = 0 .. seg_G - 2, the
+    // Phase 1 (the map-pair kernel) computes, for g = 1 .. seg_G - 2, the
     // affine map of segment g: S_end = M_g S_start + B_g, with M_g the run
-    // from the identity with v = 0 and B_g the run from zero with the real v
-    // (segment 0: from the initial state, so B_0 is its end state).  A
+    // from the identity with v = 0 and B_g the run from zero with the real v,
+    // and runs segment 0 from the initial state with its outputs (its end
+    // state into the B slot of segment 0; the M slot stays unused).  A
     // combine kernel turns the maps into every segment's start state; phase 3
-    // runs all seg_G segments from those states with outputs.  seg_ws holds
-    // [N H][seg_G - 1][2][D][D] fp32: (M_g, B_g), the B slot replaced by the
-    // start state of segment g + 1.
+    // runs segments 1 .. seg_G - 1 from those states with outputs.  seg_ws
+    // holds [N H][seg_G - 1][2][D][D] fp32: (M_g, B_g), the B slot replaced
+    // by the start state of segment g + 1.
     // Output gate fused into the o store (kernels built with it): o is not
     // stored; y = Sigmoid(gate) o / sqrt(mean(o^2) + gate_eps) * gate_weight
     // goes to the o buffer instead (gate [T_total, H, D] in the qkv dtype,
@@ -67,12 +68,13 @@ struct PrefillParams {
 // Workgroups of a pipelined-kernel launch: units are padded to whole groups
 // of 8 (one per XCD), each unit or segment item with nslab slabs; the
 // map-pair kernel (segment scan, phase 1) takes whole heads, one workgroup per
-// (sequence, head, segment 0 .. seg_G - 2).
+// (sequence, head, segment 0 .. seg_G - 2); phase 3 one per (sequence, head,
+// segment 1 .. seg_G - 1, slab).
 inline int64_t ws_pad8(int64_t x) { return (x + 7) / 8 * 8; }
 inline int64_t ws_grid_blocks(const PrefillParams& p) {
     const int64_t units = (int64_t)p.N * p.H;
     if (p.seg_phase == 1) return ws_pad8(units * (p.seg_G - 1));
-    if (p.seg_phase == 3) return ws_pad8(units * p.seg_G) * p.nslab;
+    if (p.seg_phase == 3) return ws_pad8(units * (p.seg_G - 1)) * p.nslab;
     return ws_pad8(units) * p.nslab;
 }
 

@@ -243,8 +243,11 @@ struct WsWork {
 // the q, k, g and beta they all read come from that XCD's L2 after the first
 // slab's miss.  Items are padded to whole groups of 8; padding blocks get no
 // work.  Segment-scan launches list their items the same way: phase 1 (the
-// map-pair kernel, whole heads) the segments 0 .. seg_G - 2 of every
-// (sequence, head), phase 3 all seg_G segments with their slabs.
+// map-pair kernel, whole heads) the map pairs of segments 1 .. seg_G - 2 of
+// every (sequence, head), then segment 0 of each, run with its outputs from
+// the initial state (it needs no map: its start is known), on the compute
+// units the pairs leave free; phase 3 segments 1 .. seg_G - 1 with their
+// slabs.
 // Sequence of descending-length rank r (ties in sequence order), for a packed
 // batch of at most 64 sequences: lane m holds the length of sequence m and
 // counts the sequences that go before it.  Called by every lane of a wave;
@@ -280,19 +283,30 @@ __device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
     };
     w.s_out_m = nullptr;
     if constexpr (PAIR) {
-        // phase 1: the maps of segment g <= seg_G - 2 (M into slot (g, 0), B
-        // into slot (g, 1)); segment 0's B runs from the initial state, so it
-        // is that segment's end state, the start of segment 1
+        // phase 1: the maps of segment 1 <= g <= seg_G - 2 (M into slot (g, 0),
+        // B into slot (g, 1)); then segment 0, run from the initial state with
+        // its outputs: its end state, the start of segment 1, into slot (0, 1)
+        // (s_out_m = nullptr marks the run)
         const int item = (bid >> 3) * 8 + xcd;
-        if (item >= units * (p.seg_G - 1)) return false;
-        const int uh = item / (p.seg_G - 1), g = item % (p.seg_G - 1);
+        const int npair = units * (p.seg_G - 2);
+        if (item >= npair + units) return false;
         w.z = 0;
-        w.h = uh % p.H;
-        w.n = uh / p.H;
-        seg_range(w.n, g);
-        w.s_in = (g == 0 && p.S0) ? p.S0 + (int64_t)uh * sdd : nullptr;
-        w.s_out = map_slot(uh, g, 1);
-        w.s_out_m = map_slot(uh, g, 0);
+        if (item < npair) {
+            const int uh = item / (p.seg_G - 2), g = 1 + item % (p.seg_G - 2);
+            w.h = uh % p.H;
+            w.n = uh / p.H;
+            seg_range(w.n, g);
+            w.s_in = nullptr;
+            w.s_out = map_slot(uh, g, 1);
+            w.s_out_m = map_slot(uh, g, 0);
+        } else {
+            const int uh = item - npair;
+            w.h = uh % p.H;
+            w.n = uh / p.H;
+            seg_range(w.n, 0);
+            w.s_in = p.S0 ? p.S0 + (int64_t)uh * sdd : nullptr;
+            w.s_out = map_slot(uh, 0, 1);
+        }
         return true;
     }
     const int rest = bid >> 3;
@@ -314,15 +328,15 @@ __device__ inline bool ws_resolve(const PrefillParams& p, int bid, WsWork& w) {
         w.s_out = p.Sout ? p.Sout + (int64_t)uh * sdd : nullptr;
         return true;
     }
-    // phase 3: segment g from its start state (segment 0 from the initial
-    // state, segment g >= 1 from the one the combine left in slot (g - 1, 1))
+    // phase 3: segment g >= 1 from the start state the combine (or, for
+    // g = 1, phase 1's run of segment 0) left in slot (g - 1, 1)
     const int item = (rest / p.nslab) * 8 + xcd;
-    if (item >= units * p.seg_G) return false;
-    const int uh = item / p.seg_G, g = item % p.seg_G;
+    if (item >= units * (p.seg_G - 1)) return false;
+    const int uh = item / (p.seg_G - 1), g = 1 + item % (p.seg_G - 1);
     w.h = uh % p.H;
     w.n = uh / p.H;
     seg_range(w.n, g);
-    w.s_in = g == 0 ? (p.S0 ? p.S0 + (int64_t)uh * sdd : nullptr) : map_slot(uh, g - 1, 1);
+    w.s_in = map_slot(uh, g - 1, 1);
     w.s_out = (g == p.seg_G - 1 && p.Sout) ? p.Sout + (int64_t)uh * sdd : nullptr;
     return true;
 }
@@ -1193,7 +1207,10 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 template <int NCW, int TPW, int NSA, bool FUSED, bool CKB, bool SEG, bool GATE>
 __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(PrefillParams p) {
     typedef WsCfg<NCW, TPW, NSA, FUSED, GATE> Cfg;
-    __shared__ __align__(16) char smem[Cfg::LDS];
+    // (the map-pair kernel also runs segment 0 with the whole-head layout)
+    typedef WsCfg<4, 2, 8, FUSED, false> RunCfg;
+    constexpr size_t kLds = NCW == 8 && RunCfg::LDS > Cfg::LDS ? RunCfg::LDS : Cfg::LDS;
+    __shared__ __align__(16) char smem[kLds];
     // XCD-aware block order (ws_resolve); padding blocks exit at once.  The
     // work description is uniform: pinned to scalar registers (integer
     // divisions by run-time values leave their results in vector registers).
@@ -1209,9 +1226,12 @@ __global__ __launch_bounds__(64 * (NCW + 2 + NSA)) void kda_prefill_ws_kernel(Pr
     wk.s_in = reinterpret_cast<const float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_in)));
     wk.s_out = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_out)));
     wk.s_out_m = reinterpret_cast<float*>(uniform_i64(reinterpret_cast<int64_t>(wk.s_out_m)));
-    if constexpr (PAIR)
-        ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, true, false>(p, wk, smem);
-    else
+    if constexpr (PAIR) {
+        if (wk.s_out_m)
+            ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, true, false>(p, wk, smem);
+        else  // segment 0 with its outputs, whole heads, 14 waves as the pair
+            ws_body<4, 2, 8, FUSED, CKB, SEG, false, false>(p, wk, smem);
+    } else
         ws_body<NCW, TPW, NSA, FUSED, CKB, SEG, false, GATE>(p, wk, smem);
 }
 

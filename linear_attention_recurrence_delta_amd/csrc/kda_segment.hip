@@ -9,7 +9,9 @@
 // kernel chains them, start(g + 1) = M_g start(g) + B_g, which is the state
 // passed between segments as the pages pass it between chunks ("Inside Kimi
 // K3", section "Sequence mixing"), so that every segment can then be re-run
-// in parallel from its true start state.
+// in parallel from its true start state.  Segment 0 needs no map: the
+// map-pair launch runs it outright from the initial state and leaves its end
+// state, start(1), in the B slot of segment 0.
 //
 // Work: one workgroup per (sequence, head, 16 value columns); value columns
 // never mix (the map acts on the key side), so the 8 column groups of a head

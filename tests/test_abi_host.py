@@ -164,11 +164,12 @@ def test_desc_layout_matches_header():
 
 def test_segment_scan_workspace(lib):
     # One 1,048,576-token sequence of 16 heads on a 256-CU device (the count
-    # used when no device answers): 16 segments, 15 map pairs of 2 x 64 KiB per
-    # head.  Packed or checkpointed or fp32 calls need none.
+    # used when no device answers): 17 segments (16 workgroups per head in
+    # both launches), 16 slots of 2 x 64 KiB per head.  Packed or checkpointed
+    # or fp32 calls need none.
     import ctypes as ct
     ex = lambda **kw: lib.kda_prefill_ex_workspace_bytes(ct.byref(_desc(**kw)))
-    assert ex() == 16 * 15 * 2 * 128 * 128 * 4
+    assert ex() == 16 * 16 * 2 * 128 * 128 * 4
     assert ex(segments=1) == 0
     assert ex(segments=5) == 16 * 4 * 2 * 128 * 128 * 4
     assert ex(segments=300) == 0                      # beyond the built maximum
