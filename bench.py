@@ -363,7 +363,7 @@ def main():
         if not args.no_checkpoints:
             ck_ms = time_launches(run_dense_ck, args.steps, stream, args.warmup, "prefill_checkpoints")
         # the dense workload through the fused entry (gate and q/k norm in the kernel)
-        fu_ms = None
+        fu_ms = fu_v_ms = None
         if kda.kda_prefill_fused_supported(torch.bfloat16, wd["d"], wd["d"], C):
             fq, fk, fv, fz, fa, fb, _ = synth.fused_inputs(wd["T"], wd["H"], wd["d"], torch.bfloat16, 7, dev,
                                                            a_log_std=0.0)
@@ -372,6 +372,13 @@ def main():
                 kda.kda_prefill_fused(fq, fk, fv, fz, fa, fb, None, None, chunk_size=C, out=o_d, final_state=s_d)
 
             fu_ms = time_launches(run_fused, args.steps, stream, args.warmup, "prefill_fused")
+
+            # the varlen pack through the same entry (whole-head workgroups)
+            def run_fused_varlen():
+                kda.kda_prefill_fused(fq, fk, fv, fz, fa, fb, None, wv["cu"], chunk_size=C, out=o_v,
+                                      final_state=s_v)
+
+            fu_v_ms = time_launches(run_fused_varlen, args.steps, stream, args.warmup, "prefill_fused_varlen")
             del fq, fk, fv, fz, fa, fb
         # the output gate on the dense output (Sigmoid(gate) * RMSNorm(o) * weight)
         og_gate = torch.randn(o_d.shape, device=dev).to(o_d.dtype)
@@ -445,6 +452,13 @@ def main():
                 "hbm_gbs": FUSED_BYTES_PER_TOKEN_HEAD * token_heads / (sum(fu_ms) / len(fu_ms) * 1e-3) / 1e9,
                 "bytes_per_token_head": FUSED_BYTES_PER_TOKEN_HEAD,
                 "traffic": measured_traffic("kda_prefill_fused_k3_dense_32k"),
+                "vs_plain": (sum(fu_ms) / len(fu_ms)) / d_avg,
+                "varlen": None if fu_v_ms is None else {
+                    "workload": "k3_varlen_32k through kda_prefill_fused (same raw inputs, cu_seqlens of the pack)",
+                    "ms": sum(fu_v_ms) / len(fu_v_ms),
+                    "vs_plain_varlen": (sum(fu_v_ms) / len(fu_v_ms)) / v_avg,
+                    "hbm_gbs": FUSED_BYTES_PER_TOKEN_HEAD * wv["T"] * wv["H"] / (sum(fu_v_ms) / len(fu_v_ms) * 1e-3) / 1e9,
+                },
             },
             "output_gate": {
                 "workload": "Sigmoid(gate) * RMSNorm(o) * weight over 32768 x 96 rows of 128 bf16",

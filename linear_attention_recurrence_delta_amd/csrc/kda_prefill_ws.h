@@ -119,15 +119,14 @@ struct WsCfg {
     // assembled in LDS by the stage-A waves (2-deep).  A q, k or z load covers
     // 4 token rows (1056 B of the tile at pitch PD), a g load 2 rows (1056 B
     // at pitch PG): the same step, so every parking store has a constant
-    // offset.  The fused kernel also parks the inverse L2 norms of the 16 q
-    // and 16 k rows.
+    // offset.
     static constexpr int PG = D + 4;                 // fp32 pitch of the raw g tile
     static constexpr size_t R_Q = 0;
     static constexpr size_t R_K = R_Q + al16(2 * C * PD);
     static constexpr size_t R_G = R_K + al16(2 * C * PD);
     static constexpr size_t R_B = R_G + (FUSED ? al16(2 * C * PD) : al16(4 * C * PG));
-    static constexpr size_t R_N = R_B + 4 * 64 * NSA;  // beta: 64 floats per stage-A wave
-    static constexpr size_t R_X = R_N + (FUSED ? 4 * 2 * C : 0);    // parking area of waves without a raw load
+    static constexpr size_t R_X = R_B + 4 * 64 * NSA;  // beta: 64 floats per stage-A wave; then the
+                                                       // parking area of waves without a raw load
     static constexpr size_t SR = R_X + (FUSED ? (size_t)(16 / NSA - 1) * 4 * 2 * PD + 64 * 16 : 0);
     static constexpr int NUNITS = FUSED ? 12 : 16;     // raw loads per chunk
     static constexpr int RAW_STEP = 4 * 2 * PD;      // LDS bytes per raw load
@@ -142,7 +141,13 @@ struct WsCfg {
     static constexpr int PGT = DVW + 4;              // fp32 pitch of the gate factor tile
     static constexpr size_t SGT = al16(4 * C * PGT);
     static constexpr size_t G_GT = G_W + (GATE ? 4 * DVW : 0);
-    static constexpr size_t LDS = G_GT + (GATE ? 2 * SGT : 0);
+    // Fused kernel: per chunk the row factors of the L2 norms (8-deep ring):
+    // r_k, scale r_q (from the Gram wave one chunk ahead) and beta r_k (from
+    // the Gram wave with the chunk's Gram tiles).
+    static constexpr size_t NR_RK = 0, NR_SQ = 4 * C, NR_BK = 8 * C;
+    static constexpr size_t SNR = 12 * C;
+    static constexpr size_t OFFN = G_GT + (GATE ? 2 * SGT : 0);
+    static constexpr size_t LDS = OFFN + (FUSED ? 8 * SNR : 0);
 
     static_assert(DVW <= D && D % DVW == 0, "value slab");
     static constexpr int LPW = 16 / NSA;             // raw loads per stage-A wave and chunk
@@ -185,7 +190,6 @@ struct RawSet {
     f32x4 g[IPW];   // 4 channels of g (fused: of the gate input z)
     u32x4 qk[IPW];  // 4 bf16 channels of q (words 0, 1) and of k (words 2, 3)
     float beta;
-    float rq, rk;   // fused: inverse L2 norms of the token's q and k
 };
 
 // V tile of one chunk held by the Gram wave between its load and its copy
@@ -401,6 +405,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     auto slotT = [&](int c) { return smem + Cfg::OFFT + (size_t)(c & 1) * Cfg::SP; };
     auto slotA = [&](int c) { return smem + Cfg::OFFA + (size_t)(c & 1) * Cfg::SA; };
     auto slotV = [&](int c) { return smem + Cfg::OFFV + (size_t)(c & 1) * Cfg::SV; };
+    auto slotN = [&](int c) { return reinterpret_cast<float*>(smem + Cfg::OFFN + (size_t)(c & 7) * Cfg::SNR); };
     // Element offset of token row 0 of chunk c for head h (uniform per wave).
     auto chunk_base = [&](int c) -> int64_t { return ((t_begin + (int64_t)c * C) * H + h) * D; };
     // Byte address of row 0 of chunk c in a [T, H, D] tensor of es-byte
@@ -466,9 +471,10 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     constexpr int kRawPolicy = DVW == D ? kStream : 0;  // whole heads: no other workgroup reads these lines
     // Fused, the 12 units leave two stage-A waves without a raw load.  With
     // two consumer waves (SIMDs 0 and 1, stage-A wave sa on SIMD sa mod 4) the
-    // q and k units, whose waves also form the rows' inverse norms, go to the
-    // stage-A waves on SIMDs 2 and 3, the z units to the older and no load to
-    // the younger stage-A wave of SIMDs 0 and 1: unit groups 4 5 0 1 6 7 2 3.
+    // q and k units go to the stage-A waves on SIMDs 2 and 3, the z units to
+    // the older and no load to the younger stage-A wave of SIMDs 0 and 1 (the
+    // parking stores stay off the consumers' SIMDs where they can): unit
+    // groups 4 5 0 1 6 7 2 3.
     const int ld_grp = (FUSED && NCW == 2) ? (int)((0x32761054u >> (4 * sa)) & 15u) : sa;
     const int ld_u0 = ld_grp * LPW;
     const bool ld_none = ld_u0 >= Cfg::NUNITS;
@@ -561,23 +567,6 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             *reinterpret_cast<u32x2*>(b + i * Cfg::RAW_STEP + 8) = R.x[i].zw;
         }
         reinterpret_cast<float*>(raw_slot(c) + Cfg::R_B)[64 * sa + lane] = R.beta;  // wave 0's rows 0-15 are used
-        if constexpr (FUSED) {
-            if (ld_u0 < 8) {
-                // Inverse L2 norm of each loaded q or k row (L2Norm of the
-                // query and key, "Understanding Kimi K3's attention", symbol
-                // table): the 16 lanes of a DPP row hold one token row; the
-                // zero vector keeps norm factor 0.
-                float* rn = reinterpret_cast<float*>(raw_slot(c) + Cfg::R_N) + (ld_u0 < 4 ? 0 : C);
-#pragma unroll
-                for (int i = 0; i < LPW; ++i) {
-                    float ss = 0.f;
-#pragma unroll
-                    for (int w2 = 0; w2 < 4; ++w2) ss = dot2_bf16(R.x[i][w2], R.x[i][w2], ss);
-                    ss = row_inclusive_sum16(ss);
-                    if (l16 == 15) rn[ld_row + 4 * i] = ss > 0.f ? __builtin_amdgcn_rsqf(ss) : 0.f;
-                }
-            }
-        }
     };
     // Stage-A layout: token row l16, channels c0..c0+3 of each item.
     auto fetch_raw = [&](int c, RawSet<IPW>& R) {
@@ -597,10 +586,6 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             R.qk[it] = u32x4{qv.x, qv.y, kv.x, kv.y};
         }
         R.beta = reinterpret_cast<const float*>(b + Cfg::R_B)[l16];
-        if constexpr (FUSED) {
-            R.rq = reinterpret_cast<const float*>(b + Cfg::R_N)[l16];
-            R.rk = reinterpret_cast<const float*>(b + Cfg::R_N)[C + l16];
-        }
     };
 
     // V tile [C][DVW] of chunk c: lane chunk i covers row (lane + 64 i) / VCPR,
@@ -724,10 +709,6 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 const uint32_t qw = R.qk[it][ch >> 1], kw = R.qk[it][2 + (ch >> 1)];
                 float qv = __uint_as_float((ch & 1) ? (qw & 0xffff0000u) : (qw << 16));
                 float kv = __uint_as_float((ch & 1) ? (kw & 0xffff0000u) : (kw << 16));
-                if constexpr (FUSED) {  // L2-normalised query and key
-                    qv *= R.rq;
-                    kv *= R.rk;
-                }
                 qb[ch] = qv * e1[ch];
                 kb[ch] = kv * e1[ch];
                 kl[ch] = kv * e2;
@@ -770,17 +751,73 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         bf16_t* P = reinterpret_cast<bf16_t*>(slotP(c));
         float* AT = reinterpret_cast<float*>(slotA(c));
         const int r = l16;
-        if constexpr (!NOOUT) {
+        if constexpr (FUSED) {
+            static_assert(!NOOUT, "the fused kernels read out");
+            // Raw q and k: the norms enter as row and column factors of the
+            // 16 x 16 tiles.  A = Diag(beta r_k) A_raw Diag(r_k); P keeps only
+            // its row factor scale r_q, the column factor r_k travels with U
+            // (the solve wave scales the rows of T by r_k), and beta r_k goes
+            // to the consumers for Z = beta v - beta r_k X_raw.
+            const float* nr = slotN(c);
+            const float sqr = nr[Cfg::NR_SQ / 4 + r];
+            const float bkr = BETA[r] * nr[Cfg::NR_RK / 4 + r];
+            const float4 rks = *reinterpret_cast<const float4*>(nr + Cfg::NR_RK / 4 + 4 * g4);
+            const float rk4[4] = {rks.x, rks.y, rks.z, rks.w};
             f32x4 pv;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? p.scale * accP[pp] : 0.f;  // scale P
+            for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? sqr * accP[pp] : 0.f;
             st_frag(P + r * PK + 4 * g4, E::make(pv));
-        }
-        const float br = BETA[r];
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-            const int s = 4 * g4 + pp;
-            AT[s * PA + r] = (r > s) ? br * accA[pp] : 0.f;  // AT[s][r] = A[r][s]
+            for (int pp = 0; pp < 4; ++pp) {
+                const int s = 4 * g4 + pp;
+                AT[s * PA + r] = (r > s) ? bkr * rk4[pp] * accA[pp] : 0.f;  // AT[s][r] = A[r][s]
+            }
+            if (g4 == 0) slotN(c)[Cfg::NR_BK / 4 + r] = bkr;
+        } else {
+            if constexpr (!NOOUT) {
+                f32x4 pv;
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) pv[pp] = (4 * g4 + pp <= r) ? p.scale * accP[pp] : 0.f;  // scale P
+                st_frag(P + r * PK + 4 * g4, E::make(pv));
+            }
+            const float br = BETA[r];
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int s = 4 * g4 + pp;
+                AT[s * PA + r] = (r > s) ? br * accA[pp] : 0.f;  // AT[s][r] = A[r][s]
+            }
+        }
+    };
+
+    // ------------------------------------------------------------ row norms (fused)
+    // Inverse L2 norms of the 16 raw q and k rows of chunk c (L2Norm of the
+    // query and key, "Understanding Kimi K3's attention", symbol table), from
+    // the raw tile while it is parked: the diagonals of q q^T and k k^T on
+    // MFMA (bf16 products exact, fp32 sums).  The zero vector gets factor 0.
+    // Stored for the Gram, solve and consumer waves of that chunk: r_k and
+    // scale r_q.
+    auto row_norms = [&](int c) {
+        const char* b = raw_slot(c);
+        const bf16_t* Qr = reinterpret_cast<const bf16_t*>(b + Cfg::R_Q);
+        const bf16_t* Kr = reinterpret_cast<const bf16_t*>(b + Cfg::R_K);
+        f32x4 aq = zero4(), ak = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NCB; kb += 2) {
+            const int c0 = 16 * kb + 4 * g4;
+            const Frag q0 = ld_frag(Qr + l16 * PD + c0), q1 = ld_frag(Qr + l16 * PD + c0 + 16);
+            const Frag k0 = ld_frag(Kr + l16 * PD + c0), k1 = ld_frag(Kr + l16 * PD + c0 + 16);
+            mma32(aq, q0, q1, q0, q1);
+            mma32(ak, k0, k1, k0, k1);
+        }
+        // acc[pp] = G[4 g4 + pp][l16]: the diagonal entry of row l16 is in
+        // the lane with g4 = l16 / 4, register l16 % 4
+        const int pd = l16 & 3;
+        const float sq = pd == 0 ? aq[0] : pd == 1 ? aq[1] : pd == 2 ? aq[2] : aq[3];
+        const float sk = pd == 0 ? ak[0] : pd == 1 ? ak[1] : pd == 2 ? ak[2] : ak[3];
+        if ((l16 >> 2) == g4) {
+            float* nr = slotN(c);
+            nr[Cfg::NR_RK / 4 + l16] = sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f;
+            nr[Cfg::NR_SQ / 4 + l16] = sq > 0.f ? p.scale * __builtin_amdgcn_rsqf(sq) : 0.f;
         }
     };
 
@@ -814,6 +851,13 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] -= row[st][j] * ts;
         });
+        if constexpr (FUSED) {  // T' = Diag(r_k) T: U' = T' Z carries the key norms
+            const float4 rk = *reinterpret_cast<const float4*>(slotN(c) + Cfg::NR_RK / 4 + 4 * q);
+            x[0] *= rk.x;
+            x[1] *= rk.y;
+            x[2] *= rk.z;
+            x[3] *= rk.w;
+        }
         uint16_t* tq = reinterpret_cast<uint16_t*>(slotT(c)) + (4 * q) * PK + col;
 #pragma unroll
         for (int j = 0; j < 4; j += 2) {
@@ -898,6 +942,16 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         if constexpr (!NOOUT) Pf = ld_frag(P + l16 * PK + 4 * g4);
         const float4 b4 = *reinterpret_cast<const float4*>(BETA + 4 * g4);
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+        // fused: Z = beta v - beta r_k X_raw and O = scale r_q (Q_raw S) + P' U'
+        // (row factors from the Gram wave); otherwise beta and the scale
+        float bx[4] = {b4.x, b4.y, b4.z, b4.w};
+        if constexpr (FUSED) {
+            const float4 bk4 = *reinterpret_cast<const float4*>(slotN(c) + Cfg::NR_BK / 4 + 4 * g4);
+            bx[0] = bk4.x;
+            bx[1] = bk4.y;
+            bx[2] = bk4.z;
+            bx[3] = bk4.w;
+        }
         float vv[TPW][4];
 #pragma unroll
         for (int t = 0; t < TPW; ++t)
@@ -943,7 +997,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         for (int t = 0; t < TPW; ++t) {
             f32x4 Z;
 #pragma unroll
-            for (int pp = 0; pp < 4; ++pp) Z[pp] = fmaf(-bb[pp], X[t][pp], vv[t][pp]);
+            for (int pp = 0; pp < 4; ++pp) Z[pp] = fmaf(-bx[pp], X[t][pp], vv[t][pp]);
             f32x4 U = zero4();
             mma16(U, Tf, E::make(Z));
             Uf[t] = E::make(U);
@@ -958,6 +1012,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         // value columns vcol(t, 4 g4 + pp) = 4 TPW g4 + 4 t + pp, adjacent.
         [[maybe_unused]] uint32_t ov[TPW][2];
         if constexpr (!NOOUT) {
+            const float o_scale = FUSED ? slotN(c)[Cfg::NR_SQ / 4 + l16] : p.scale;
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
                 // (P U)^T in its own accumulator, added to the 32-deep QS
@@ -965,8 +1020,8 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 f32x4 PU = zero4();
                 mma16(PU, Uf[t], Pf);
                 // O = scale Qt S + (scale P) U (P is stored scaled)
-                ov[t][0] = pack_bf16x2(fmaf(p.scale, QS[t][0], PU[0]), fmaf(p.scale, QS[t][1], PU[1]));
-                ov[t][1] = pack_bf16x2(fmaf(p.scale, QS[t][2], PU[2]), fmaf(p.scale, QS[t][3], PU[3]));
+                ov[t][0] = pack_bf16x2(fmaf(o_scale, QS[t][0], PU[0]), fmaf(o_scale, QS[t][1], PU[1]));
+                ov[t][1] = pack_bf16x2(fmaf(o_scale, QS[t][2], PU[2]), fmaf(o_scale, QS[t][3], PU[3]));
             }
         }
 #pragma unroll
@@ -1054,6 +1109,7 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             // copy cannot be hoisted above the barrier that follows the load.
             VRegs<VChunk> va, vb;
             __syncthreads();  // the two prologue barriers of the stage-A waves
+            if constexpr (FUSED) row_norms(0);  // chunk 0 parked
             __syncthreads();
             // (GATE: it also finishes chunk j - 4, whose o tiles the consumers
             // parked in iteration j - 1, with the gated store of half the
@@ -1062,6 +1118,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 load_v(j - 1, vb);
                 if (j - 2 >= 0 && j - 2 < nch) store_v(j - 2, va);
                 if (j - 1 >= 0 && j - 1 < nch) gram(j - 1);
+                if constexpr (FUSED) {
+                    if (j + 1 < nch) row_norms(j + 1);  // parked in iteration j - 1, read by stage A at the end of j
+                }
                 if constexpr (GATE) {
                     if (j - 4 >= 0 && j - 4 < nch) finish_gate(j - 4, std::integral_constant<int, 0>{});
                 }
@@ -1070,6 +1129,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                     load_v(j, va);
                     if (j - 1 >= 0 && j - 1 < nch) store_v(j - 1, vb);
                     if (j < nch) gram(j);
+                    if constexpr (FUSED) {
+                        if (j + 2 < nch) row_norms(j + 2);
+                    }
                     if constexpr (GATE) {
                         if (j - 3 >= 0 && j - 3 < nch) finish_gate(j - 3, std::integral_constant<int, 0>{});
                     }
