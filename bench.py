@@ -77,6 +77,7 @@ KERNEL_SOURCES = {
     "kda_decode_256x96": ("kda_decode.hip", "kda_device.h", "kda_internal.h", "kda_bounds.h", "kda_abi.cpp",
                           "build", "flags:kda_decode.hip"),
     "kda_prefill_fused_k3_dense_32k": _PREFILL + ("kda_prefill_ws_ilp.hip", "flags:kda_prefill_ws_ilp.hip"),
+    "kda_prefill_fused_k3_varlen_32k": _PREFILL + ("kda_prefill_bf16.hip", "flags:kda_prefill_bf16.hip"),
     "kda_output_gate_32k_x96": ("kda_output_gate.hip", "kda_device.h", "kda_internal.h", "kda_bounds.h",
                                 "kda_abi.cpp", "build"),
     "kda_backward_k3_dense_32k": _PREFILL + ("kda_backward.hip", "kda_backward.h", "kda_prefill_ws_ilp.hip",
@@ -104,6 +105,105 @@ def kernel_source_digest(kernel):
         else:
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
+
+
+# The kernels of each counter record, as rocprofv3 names them (demangled),
+# one entry per launch of the call: the record is the sum over the call's
+# launches of each kernel's mean per dispatch.
+RECORD_KERNELS = {
+    "kda_prefill_k3_dense_32k": ["kda_prefill_ws_kernel<2, 2, 8, false, false, false, false>"],
+    "kda_prefill_k3_varlen_32k": ["kda_prefill_ws_kernel<4, 2, 8, false, false, false, false>"],
+    "kda_prefill_gated_k3_varlen_32k": ["kda_prefill_ws_kernel<4, 2, 8, false, false, false, true>"],
+    "kda_prefill_fused_k3_dense_32k": ["kda_prefill_ws_kernel<2, 2, 8, true, false, false, false>"],
+    "kda_prefill_fused_k3_varlen_32k": ["kda_prefill_ws_kernel<4, 2, 8, true, false, false, false>"],
+    "kda_prefill_long_1m_h16": ["kda_prefill_ws_kernel<8, 2, 4, false, false, true, false>",
+                                "kda_segment_combine_kernel",
+                                "kda_prefill_ws_kernel<4, 2, 8, false, false, true, false>"],
+    "kda_decode_256x96": ["kda_decode_kernel<kda::bf16_t, 128>"],
+    "kda_output_gate_32k_x96": ["kda_output_gate_kernel<kda::bf16_t, 128>"],
+    "kda_backward_k3_dense_32k": ["kda_prefill_ws_kernel<2, 2, 8, false, true, false, false>",
+                                  "kda_backward_kernel", "kda_backward_sum_kernel"],
+}
+MFMA_RECORDS = ("kda_prefill_k3_dense_32k", "kda_prefill_k3_varlen_32k", "kda_prefill_gated_k3_varlen_32k",
+                "kda_prefill_fused_k3_dense_32k", "kda_prefill_fused_k3_varlen_32k")
+
+
+def _counter_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _kernel_means(rows, counter):
+    """Mean counter value per dispatch for each kernel name of RECORD_KERNELS."""
+    out = {}
+    for names in RECORD_KERNELS.values():
+        for name in names:
+            v = [float(r["Counter_Value"]) for r in rows
+                 if r["Counter_Name"] == counter and name in r["Kernel_Name"]]
+            if v:
+                out[name] = (sum(v) / len(v), len(v))
+    return out
+
+
+def _copy_factor(rows, counter, copy_bytes=1 << 30):
+    """Bytes per counter unit, from the device copies that bench.py
+    --calibrate-copy issues before any library launch (1 GiB each)."""
+    first_kda = min((int(r["Dispatch_Id"]) for r in rows if "kda" in r["Kernel_Name"]), default=None)
+    v = sorted((float(r["Counter_Value"]) for r in rows
+                if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]
+                and (first_kda is None or int(r["Dispatch_Id"]) < first_kda)), reverse=True)[:3]
+    if not v:
+        raise SystemExit("no calibration copies in the %s pass (run it with --calibrate-copy)" % counter)
+    return copy_bytes / (sum(v) / len(v) * 1024.0), v
+
+
+def record_counters(fetch_csv, write_csv, sq_csv=None, out_path=None):
+    """Rebuild profiles/pmc_traffic.json from rocprofv3 --pmc passes (csv
+    output) of bench.py: FETCH_SIZE and WRITE_SIZE (with --calibrate-copy)
+    and optionally SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE.  Records are keyed by the current source digests."""
+    fr, ww = _counter_rows(fetch_csv), _counter_rows(write_csv)
+    f_fac, f_cal = _copy_factor(fr, "FETCH_SIZE")
+    w_fac, w_cal = _copy_factor(ww, "WRITE_SIZE")
+    fm, wm = _kernel_means(fr, "FETCH_SIZE"), _kernel_means(ww, "WRITE_SIZE")
+    sq = None
+    if sq_csv:
+        sr = _counter_rows(sq_csv)
+        sq = {c: _kernel_means(sr, c) for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES",
+                                               "GRBM_GUI_ACTIVE")}
+    rec = {"_note": (
+        "HBM bytes per launch = 1024 (FETCH_SIZE * %.4f + WRITE_SIZE * %.4f) (counters in KiB), the factors from the 1 GiB "
+        "device copies of the same passes (FETCH_SIZE %s KiB, WRITE_SIZE %s KiB per copy). A record lists "
+        "the call's kernels; fetch_kib and write_kib are the sums over them of the mean per dispatch. "
+        "source_digest = first 16 hex digits of the sha256 of the listed csrc/ files and, for flags:<file>, "
+        "of the extra compiler flags build_lib.py gives that file, in order; a record is used only while it "
+        "matches. mfma_counters: SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE "
+        "(summed over the 8 XCDs) per launch. Written by bench.py --record-counters."
+        % (f_fac, w_fac, ", ".join("%.1f" % x for x in f_cal),
+           ", ".join("%.1f" % x for x in w_cal)))}
+    for key, names in RECORD_KERNELS.items():
+        if not all(n in fm and n in wm for n in names):
+            log("no dispatches for %s: not recorded" % key)
+            continue
+        fk = sum(fm[n][0] for n in names)
+        wk = sum(wm[n][0] for n in names)
+        ent = {"source_digest": kernel_source_digest(key), "sources": list(KERNEL_SOURCES[key]),
+               "kernels": {n: {"fetch_kib": round(fm[n][0], 1), "write_kib": round(wm[n][0], 1),
+                               "dispatches": fm[n][1]} for n in names},
+               "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+               "hbm_bytes_per_launch": int(round(1024.0 * (fk * f_fac + wk * w_fac)))}
+        if sq and key in MFMA_RECORDS and all(names[0] in sq[c] for c in sq):
+            ent["mfma_counters"] = {"mops_bf16": sq["SQ_INSTS_VALU_MFMA_MOPS_BF16"][names[0]][0],
+                                    "busy_cycles": sq["SQ_VALU_MFMA_BUSY_CYCLES"][names[0]][0],
+                                    "grbm_gui_active": sq["GRBM_GUI_ACTIVE"][names[0]][0],
+                                    "xcds": 8, "simds": 1024}
+        rec[key] = ent
+    path = out_path or os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec
 
 
 def measured_traffic(kernel):
@@ -277,9 +377,20 @@ def main():
                          "launch is a variant of the same kernel)")
     ap.add_argument("--no-checkpoints", action="store_true",
                     help="skip the checkpointed prefill timing (counter runs per kernel launch)")
+    ap.add_argument("--record-counters", nargs="+", metavar="CSV",
+                    help="rebuild profiles/pmc_traffic.json from rocprofv3 --pmc csv files "
+                         "(FETCH_SIZE, WRITE_SIZE[, SQ counters]) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
+    if args.record_counters:
+        if len(args.record_counters) not in (2, 3):
+            raise SystemExit("--record-counters FETCH_CSV WRITE_CSV [SQ_CSV]")
+        rec = record_counters(*args.record_counters)
+        for k, v in rec.items():
+            if not k.startswith("_"):
+                log("%-34s %14d B per launch" % (k, v["hbm_bytes_per_launch"]))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
