@@ -142,10 +142,11 @@ struct WsCfg {
     static constexpr size_t SGT = al16(4 * C * PGT);
     static constexpr size_t G_GT = G_W + (GATE ? 4 * DVW : 0);
     // Fused kernel: per chunk the row factors of the L2 norms (8-deep ring):
-    // r_k, scale r_q (from the Gram wave one chunk ahead) and beta r_k (from
-    // the Gram wave with the chunk's Gram tiles).
-    static constexpr size_t NR_RK = 0, NR_SQ = 4 * C, NR_BK = 8 * C;
-    static constexpr size_t SNR = 12 * C;
+    // r_k, |k| = 1 / r_k (0 for the zero vector) and scale r_q (from the Gram
+    // wave one chunk ahead), beta r_k and beta r_k^2 (from the Gram wave with
+    // the chunk's Gram tiles).
+    static constexpr size_t NR_RK = 0, NR_NK = 4 * C, NR_SQ = 8 * C, NR_BK = 12 * C, NR_B2 = 16 * C;
+    static constexpr size_t SNR = 20 * C;
     static constexpr size_t OFFN = G_GT + (GATE ? 2 * SGT : 0);
     static constexpr size_t LDS = OFFN + (FUSED ? 8 * SNR : 0);
 
@@ -615,7 +616,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             *reinterpret_cast<VChunk*>(reinterpret_cast<bf16_t*>(slotV(c)) + r * Cfg::PV + VCOL * ch) = x;
             return;
         }
-        const float br = reinterpret_cast<const float*>(slot4(c) + Cfg::S4_BETA)[r];
+        // (fused: beta r_k, which the Gram wave stored with chunk c's tiles)
+        const float br = FUSED ? slotN(c)[Cfg::NR_BK / 4 + r]
+                               : reinterpret_cast<const float*>(slot4(c) + Cfg::S4_BETA)[r];
         float* dst = reinterpret_cast<float*>(slotV(c)) + r * Cfg::PV + VCOL * ch;
 #pragma unroll
         for (int q4 = 0; q4 < VCOL / 4; ++q4) {
@@ -755,9 +758,11 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
             static_assert(!NOOUT, "the fused kernels read out");
             // Raw q and k: the norms enter as row and column factors of the
             // 16 x 16 tiles.  A = Diag(beta r_k) A_raw Diag(r_k); P keeps only
-            // its row factor scale r_q, the column factor r_k travels with U
-            // (the solve wave scales the rows of T by r_k), and beta r_k goes
-            // to the consumers for Z = beta v - beta r_k X_raw.
+            // its row factor scale r_q, the column factor r_k travels with
+            // U' = Diag(r_k) U = (Diag(r_k) T Diag(1 / r_k)) (Diag(r_k) Z):
+            // the solve wave scales T that way (its unit diagonal stays
+            // exact) and the consumers form Diag(r_k) Z = (beta r_k) v -
+            // (beta r_k^2) X_raw from the row factors stored here.
             const float* nr = slotN(c);
             const float sqr = nr[Cfg::NR_SQ / 4 + r];
             const float bkr = BETA[r] * nr[Cfg::NR_RK / 4 + r];
@@ -772,7 +777,10 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
                 const int s = 4 * g4 + pp;
                 AT[s * PA + r] = (r > s) ? bkr * rk4[pp] * accA[pp] : 0.f;  // AT[s][r] = A[r][s]
             }
-            if (g4 == 0) slotN(c)[Cfg::NR_BK / 4 + r] = bkr;
+            if (g4 == 0) {
+                slotN(c)[Cfg::NR_BK / 4 + r] = bkr;
+                slotN(c)[Cfg::NR_B2 / 4 + r] = bkr * nr[Cfg::NR_RK / 4 + r];
+            }
         } else {
             if constexpr (!NOOUT) {
                 f32x4 pv;
@@ -794,8 +802,8 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
     // query and key, "Understanding Kimi K3's attention", symbol table), from
     // the raw tile while it is parked: the diagonals of q q^T and k k^T on
     // MFMA (bf16 products exact, fp32 sums).  The zero vector gets factor 0.
-    // Stored for the Gram, solve and consumer waves of that chunk: r_k and
-    // scale r_q.
+    // Stored for the Gram, solve and consumer waves of that chunk: r_k, |k|
+    // and scale r_q.
     auto row_norms = [&](int c) {
         const char* b = raw_slot(c);
         const bf16_t* Qr = reinterpret_cast<const bf16_t*>(b + Cfg::R_Q);
@@ -816,7 +824,9 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         const float sk = pd == 0 ? ak[0] : pd == 1 ? ak[1] : pd == 2 ? ak[2] : ak[3];
         if ((l16 >> 2) == g4) {
             float* nr = slotN(c);
-            nr[Cfg::NR_RK / 4 + l16] = sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f;
+            const float rk = sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f;
+            nr[Cfg::NR_RK / 4 + l16] = rk;
+            nr[Cfg::NR_NK / 4 + l16] = sk * rk;  // |k|, 0 for the zero vector
             nr[Cfg::NR_SQ / 4 + l16] = sq > 0.f ? p.scale * __builtin_amdgcn_rsqf(sq) : 0.f;
         }
     };
@@ -851,12 +861,16 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
 #pragma unroll
             for (int j = 0; j < 4; ++j) x[j] -= row[st][j] * ts;
         });
-        if constexpr (FUSED) {  // T' = Diag(r_k) T: U' = T' Z carries the key norms
+        if constexpr (FUSED) {
+            // Diag(r_k) T Diag(1 / r_k): row factor r_k of the row, column
+            // factor |k| of the column (a zero key row or column gets 0 off
+            // the diagonal; its Z' row is 0 too); the unit diagonal is kept.
             const float4 rk = *reinterpret_cast<const float4*>(slotN(c) + Cfg::NR_RK / 4 + 4 * q);
-            x[0] *= rk.x;
-            x[1] *= rk.y;
-            x[2] *= rk.z;
-            x[3] *= rk.w;
+            const float nk = slotN(c)[Cfg::NR_NK / 4 + col];
+            const float rr[4] = {rk.x, rk.y, rk.z, rk.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (4 * q + j != col) x[j] *= rr[j] * nk;
         }
         uint16_t* tq = reinterpret_cast<uint16_t*>(slotT(c)) + (4 * q) * PK + col;
 #pragma unroll
@@ -940,17 +954,19 @@ __device__ __forceinline__ void ws_body(const PrefillParams& p, const WsWork& wk
         const Frag Tf = ld_frag(T + l16 * PK + 4 * g4);
         Frag Pf;
         if constexpr (!NOOUT) Pf = ld_frag(P + l16 * PK + 4 * g4);
-        const float4 b4 = *reinterpret_cast<const float4*>(BETA + 4 * g4);
+        // Row factors of Z = (beta v) - (beta) X; fused, of Diag(r_k) Z =
+        // (beta r_k) v - (beta r_k^2) X_raw (from the Gram wave, which also
+        // parks beta r_k v for the slabs that take V in fp32), and O = scale
+        // r_q (Q_raw S) + P' U'.
+        const float4 b4 = *reinterpret_cast<const float4*>((FUSED ? slotN(c) + Cfg::NR_BK / 4 : BETA) + 4 * g4);
         const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
-        // fused: Z = beta v - beta r_k X_raw and O = scale r_q (Q_raw S) + P' U'
-        // (row factors from the Gram wave); otherwise beta and the scale
         float bx[4] = {b4.x, b4.y, b4.z, b4.w};
         if constexpr (FUSED) {
-            const float4 bk4 = *reinterpret_cast<const float4*>(slotN(c) + Cfg::NR_BK / 4 + 4 * g4);
-            bx[0] = bk4.x;
-            bx[1] = bk4.y;
-            bx[2] = bk4.z;
-            bx[3] = bk4.w;
+            const float4 b24 = *reinterpret_cast<const float4*>(slotN(c) + Cfg::NR_B2 / 4 + 4 * g4);
+            bx[0] = b24.x;
+            bx[1] = b24.y;
+            bx[2] = b24.z;
+            bx[3] = b24.w;
         }
         float vv[TPW][4];
 #pragma unroll

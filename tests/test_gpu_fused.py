@@ -113,3 +113,31 @@ def test_dense_k3_all_heads(kda, oracle_mod):
         worst_s = max(worst_s, rel_err(f64(S[0].index_select(0, heads)), rs[0]))
     say("  dense fused, all 96 heads: rel err o=%.3e S=%.3e" % (worst_o, worst_s))
     assert worst_o <= TOL[BF16] and worst_s <= TOL[BF16]
+
+
+def test_varlen_k3_all_units(kda, oracle_mod):
+    """The 16-sequence K3 varlen pack (32768 tokens, H=96, a_log = 0), which
+    runs whole-head workgroups: every (sequence, head) unit against the
+    oracle, 16 heads per oracle call; outputs start as NaN."""
+    from linear_attention_recurrence_delta_amd import synth
+    L = synth.varlen_lengths()
+    T, H = int(sum(L)), 96
+    say("CASE fused k3 varlen 32K x 96, 16 sequences, every unit")
+    q, k, v, z, a_log, beta, _ = synth.fused_inputs(T, H, 128, BF16, 407, DEV, a_log_std=0.0)
+    cu_list = [0] + [int(x) for x in np.cumsum(L)]
+    cu = torch.tensor(cu_list, dtype=torch.int32, device=DEV)
+    o = torch.full((T, H, 128), float("nan"), dtype=BF16, device=DEV)
+    S = torch.full((len(L), H, 128, 128), float("nan"), dtype=torch.float32, device=DEV)
+    kda.kda_prefill_fused(q, k, v, z, a_log, beta, None, cu, out=o, final_state=S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    worst_o = worst_s = 0.0
+    for h0 in range(0, H, 16):
+        heads = torch.arange(h0, h0 + 16, device=DEV)
+        sl = lambda x: f64(x.index_select(1, heads))
+        ro, rs = oracle_mod.prefill_fused(sl(q), sl(k), sl(v), sl(z), f64(a_log.index_select(0, heads)), sl(beta),
+                                          None, np.array(cu_list))
+        worst_o = max(worst_o, rel_err(sl(o), ro))
+        worst_s = max(worst_s, rel_err(f64(S.index_select(1, heads)), rs))
+    say("  varlen fused, all %d units: rel err o=%.3e S=%.3e" % (len(L) * H, worst_o, worst_s))
+    assert worst_o <= TOL[BF16] and worst_s <= TOL[BF16]
