@@ -569,6 +569,7 @@ def main():
                     "ms": sum(fu_v_ms) / len(fu_v_ms),
                     "vs_plain_varlen": (sum(fu_v_ms) / len(fu_v_ms)) / v_avg,
                     "hbm_gbs": FUSED_BYTES_PER_TOKEN_HEAD * wv["T"] * wv["H"] / (sum(fu_v_ms) / len(fu_v_ms) * 1e-3) / 1e9,
+                    "traffic": measured_traffic("kda_prefill_fused_k3_varlen_32k"),
                 },
             },
             "output_gate": {
