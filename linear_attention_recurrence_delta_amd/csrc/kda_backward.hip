@@ -754,14 +754,18 @@ __global__ __launch_bounds__(256) void kda_backward_sum_kernel(BackwardParams p)
     const int seg = threadIdx.x & 31;
     if (row >= rows) return;
     const int64_t e = row * BD + 4 * seg;
-    const f32x4 q = *reinterpret_cast<const f32x4*>(p.part + e) + *reinterpret_cast<const f32x4*>(p.part + nel + e);
-    const f32x4 k =
-        *reinterpret_cast<const f32x4*>(p.part + 2 * nel + e) + *reinterpret_cast<const f32x4*>(p.part + 3 * nel + e);
-    const f32x4 g =
-        *reinterpret_cast<const f32x4*>(p.part + 4 * nel + e) + *reinterpret_cast<const f32x4*>(p.part + 5 * nel + e);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.dq) + e) = make_uint2(pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3]));
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.dk) + e) = make_uint2(pack_bf16x2(k[0], k[1]), pack_bf16x2(k[2], k[3]));
-    *reinterpret_cast<f32x4*>(p.dg + e) = g;
+    // every partial is read once and every result written once: non-temporal
+    // accesses (a wave covers whole rows, so no line is split between waves)
+    auto ld = [&](int64_t i) { return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p.part + i)); };
+    const f32x4 q = ld(e) + ld(nel + e);
+    const f32x4 k = ld(2 * nel + e) + ld(3 * nel + e);
+    const f32x4 g = ld(4 * nel + e) + ld(5 * nel + e);
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2v{pack_bf16x2(q[0], q[1]), pack_bf16x2(q[2], q[3])},
+                                reinterpret_cast<u32x2v*>(static_cast<uint16_t*>(p.dq) + e));
+    __builtin_nontemporal_store(u32x2v{pack_bf16x2(k[0], k[1]), pack_bf16x2(k[2], k[3])},
+                                reinterpret_cast<u32x2v*>(static_cast<uint16_t*>(p.dk) + e));
+    __builtin_nontemporal_store(g, reinterpret_cast<f32x4*>(p.dg + e));
     if (seg == 0) p.dbeta[row] = p.part[6 * nel + row] + p.part[6 * nel + rows + row];
 }
 
